@@ -1,0 +1,151 @@
+/* moeq.h — C ABI of the routed Mixture-of-Experts feed-forward layer over
+ * block-quantised expert weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (what the pages describe, restated):
+ *   - the router gives every token one logit per expert and keeps k experts with
+ *     normalised weights ("Nebula" page, "How it works"; "How Neural runs a
+ *     120-billion-parameter model on one gaming PC", section "How one token and
+ *     one prompt are processed": the router emits expert ids and weights);
+ *   - (token, expert) pairs are grouped by expert on the GPU and each selected
+ *     expert's rows are read once for all of its tokens through a device table
+ *     of expert base pointers (NInfer Qwen3.8-Flash-Next page, MoE execution
+ *     notes; Neural page, "Prompt processing");
+ *   - each expert applies a fused gate/up projection, SwiGLU and a down
+ *     projection, and the gate-weighted expert outputs are summed per token in a
+ *     fixed order (NInfer page, MoE execution notes: the result must not depend
+ *     on the order experts finish in), plus an optional always-on shared expert
+ *     ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers",
+ *     "Architecture").
+ *
+ * Formulas (notation: T tokens, H hidden, I intermediate, E experts, top-k):
+ *   l[t,e]  = sum_h x[t,h] * router_w[e,h] + router_b[e]
+ *   ids[t]  = the k experts with the largest l[t,.], ordered by (-l, e): ties go
+ *             to the lower expert index
+ *   g[t,j]  = exp(l[t,ids[t,j]] - l[t,ids[t,0]]) / sum_j' exp(...)
+ *   pair p  = t*k + j (routed) or T*k + t (shared expert, bucket E)
+ *   h_p[i]  = silu(Wg_e[i,:] . x[t]) * (Wu_e[i,:] . x[t]),  silu(a) = a/(1+e^-a)
+ *   o_p[n]  = Wd_e[n,:] . h_p
+ *   y[t]    = sum_j g[t,j] * o_(t*k+j) + s_t * o_(T*k+t)   (j ascending, shared last)
+ *   s_t     = 1, or sigmoid(shared_gate_w . x[t]) when shared_gate_w != NULL
+ *
+ * Packed matrix [N rows][K cols] (K a multiple of 32), blocks of 32 along a row:
+ *   code plane at byte 0: N*K/2 bytes row-major; byte j of a block holds element
+ *     2j in its low nibble and element 2j+1 in its high nibble;
+ *   scale plane at byte round_up(N*K/2, 256): N*K/32 scales, row-major;
+ *   MXFP4: code = FP4 E2M1, scale = E8M0 byte u, element = e2m1 * 2^(u-127)
+ *     (OCP Microscaling v1.0; the Neural page names MXFP4 experts, "What it runs
+ *     on and what it runs": 13,219,200 bytes per gpt-oss-120B expert, which this
+ *     layout reproduces exactly);
+ *   CB4: code = index into a 16-entry int8 codebook, scale = IEEE fp16 bits,
+ *     element = fp16 * codebook[index]; 18 bytes per 32 values (NInfer page,
+ *     n-gram table paragraph: 1,440 bytes for 16 rows of 160 IQ4_NL values).
+ *   Expert e's gate_up matrix is [2I][H] (rows 0..I-1 gate, I..2I-1 up); its
+ *   down matrix is [H][I].
+ *
+ * Conventions for every entry point:
+ *   - Pointers are HIP device pointers unless marked [host].  The caller owns
+ *     every buffer; the library keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` and the call returns without waiting.  No
+ *     call allocates memory, synchronises, or reads device memory on the host,
+ *     so every call can be captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     failure a negative moe_status is returned and no output is touched.
+ *     T == 0 returns MOE_OK and enqueues nothing.
+ *   - A launch failure returns MOE_ERR_HIP; faults during execution surface at
+ *     the caller's next synchronisation, as with any stream API.
+ *   - No C++ exception crosses the ABI and nothing is printed.  The library is
+ *     reentrant; it has no global mutable state.
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by events).
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad size or dtype */
+  MOE_ERR_UNSUPPORTED = -2,  /* outside the supported shape range */
+  MOE_ERR_ALIGNMENT = -3,    /* a buffer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -4,    /* workspace missing or smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = -5           /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2 } moe_wfmt;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Path selection for moe_forward: AUTO picks the decode kernels for small
+ * batches and the grouped-GEMM prefill kernels otherwise; the other two force
+ * one path (both compute the same layer). */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+
+/* [host] layer descriptor; read during a call only. */
+typedef struct {
+  int32_t hidden;              /* H: multiple of 32, 32..16384 */
+  int32_t inter;               /* I: multiple of 32, 32..16384 */
+  int32_t n_experts;           /* E: 1..1024 */
+  int32_t top_k;               /* k: 1..min(E, 16) */
+  int32_t wfmt;                /* moe_wfmt, the same for every expert */
+  int32_t has_shared;          /* 1: slot E of the pointer tables is an always-on shared expert */
+  const float *router_w;       /* [E][H] fp32 */
+  const float *router_b;       /* [E] fp32, or NULL */
+  const void *const *gate_up;  /* device array of E+has_shared device pointers -> packed [2I][H] */
+  const void *const *down;     /* device array of E+has_shared device pointers -> packed [H][I] */
+  const int8_t *codebook;      /* CB4: [16] int8; MXFP4: must be NULL */
+  const float *shared_gate_w;  /* [H] fp32, or NULL (shared weight 1); ignored without a shared expert */
+} moe_layer;
+
+/* [host] Bytes of one packed matrix; 0 if cols is not a positive multiple of 32
+ * or rows <= 0 or the format is unknown. */
+size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols);
+
+/* [host] Workspace bytes moe_forward / moe_router_topk / moe_bucket need for up
+ * to T_max tokens (0 if the descriptor is invalid).  The workspace is scratch:
+ * no contents need to survive between calls and no initialisation is needed. */
+size_t moe_workspace_bytes(const moe_layer *L, int32_t T_max);
+
+/* Router logits, top-k and softmax gates for T tokens of x ([T][H], dtype
+ * x_dtype).  Writes topk_ids [T][k] int32 and topk_w [T][k] fp32. */
+int moe_router_topk(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T,
+                    int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Stable counting sort of the pairs p = t*k + j by expert (increasing p inside
+ * a bucket); with a shared expert, pairs T*k + t form bucket E.
+ * counts [E+1], offsets [E+2] (exclusive prefix sums, offsets[E+1] = #pairs),
+ * perm [T*k + T*has_shared] (pair ids in bucket order).  Every topk_ids value
+ * must lie in [0, E). */
+int moe_bucket(const moe_layer *L, const int32_t *topk_ids, int32_t T, int32_t *counts,
+               int32_t *offsets, int32_t *perm, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: y [T][H] fp32.  The dbg_* outputs are optional (NULL: not
+ * written): the routing and bucketing the call used, in the shapes above.
+ * path is a moe_path. */
+int moe_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *y,
+                void *ws, size_t ws_bytes, void *stream, int32_t path, int32_t *dbg_ids,
+                float *dbg_w, int32_t *dbg_counts, int32_t *dbg_offsets, int32_t *dbg_perm);
+
+/* Test export: decode one packed matrix to fp32 out [rows][cols], bit-exact
+ * (every element is exactly representable in fp32 for MXFP4 scales u <= 252
+ * and every finite fp16 scale).  codebook: CB4 [16] int8, NULL for MXFP4. */
+int moe_dequant(int32_t wfmt, const void *packed, const int8_t *codebook, int32_t rows,
+                int32_t cols, float *out, void *stream);
+
+/* Helper between stacked layers (not part of the layer):
+ * x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y[t][n]^2 + eps)), bf16 bits. */
+int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_next_bf16,
+                    void *stream);
+
+/* [host] Static description of a status code. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEQ_H */

@@ -1,0 +1,287 @@
+"""Plain fp64 CPU oracle of the routed MoE feed-forward layer over block-quantised experts.
+
+TEST INFRASTRUCTURE ONLY.  The parity tests, the smoke check and the CPU-baseline
+leg of the benchmark use this module; the GPU library never imports or calls it,
+and it shares no code with the GPU library.  It is written to be checked by eye:
+each function is the plain definition of one step, in float64, with numpy's
+matmul/exp as the only library primitives.
+
+What the layer computes, in the order the pages describe it:
+
+* the router turns each token's hidden state into one logit per expert and
+  keeps k experts with their normalised weights ("Nebula" page, "How it works":
+  the router assigns normalised weights to each expert; "How Neural runs a
+  120-billion-parameter model on one gaming PC", section "How one token and one
+  prompt are processed": the router kernels emit 4 expert ids and 4 weights);
+* (token, expert) pairs are grouped by expert, and each selected expert is read
+  once for all of its tokens (NInfer Qwen3.8-Flash-Next page, MoE execution
+  notes: pairs grouped by expert on the GPU, one pass over each selected
+  expert's rows for all of its tokens; Neural page, "Prompt processing":
+  tokens are grouped by expert on the GPU);
+* each expert runs a fused gate/up projection, the middle activation, and a
+  down projection (NInfer page, MoE execution notes: the fused gate/up kernel
+  and the down pass row by row over all of a token's experts);
+* the weighted expert outputs are summed per token (NInfer page, MoE execution
+  notes: weighted expert outputs are summed so the result does not depend on
+  the order experts finish in), plus an always-on shared expert where the layer
+  has one ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers",
+  "Architecture": 512 routed experts plus one shared expert per layer).
+
+Where the pages leave a step open the plainest reading is taken:
+
+* MXFP4 element = E2M1(code) * 2^(u-127), u the block's E8M0 byte (OCP
+  Microscaling Formats v1.0; the pages only name "MXFP4", Neural page, "What it
+  runs on and what it runs");
+* CB4 element = fp16(scale) * codebook[index], 32 values per block with one fp16
+  scale and 16 bytes of 4-bit indices, 18 bytes per 32 values (NInfer page,
+  n-gram table paragraph: 16 rows of 160 values take 1,440 bytes in IQ4_NL);
+  the 16-entry int8 codebook is an input (a seeded sorted table stands in for
+  the real IQ4_NL table, which the pages do not list);
+* nibble order: low nibble = even element; code plane then scale plane per
+  matrix; gate_up = [gate rows; up rows] concatenated;
+* activation = SwiGLU, h = silu(gate) * up, silu(a) = a / (1 + exp(-a));
+* top-k order = descending logit, ties to the lower expert index; gates =
+  softmax over the k kept logits; a router bias is added to the logit;
+* bucket order inside an expert = increasing pair id p = t*k + j; the shared
+  expert is bucket E with pairs T*k + t;
+* the shared expert's weight is 1, or sigmoid(w_sg . x_t) when a shared-gate
+  vector is given ("Nebula" page, components table: an F32 shared expert gate).
+
+Every function here is pinned by CPU tests against something other than itself
+(closed forms of the formats, brute force over subsets, a dense masked
+evaluation, 50-digit decimal arithmetic, library sorts).  The RMS rescale
+helper between stacked layers is pinned by closed forms as well.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+WFMT_MXFP4 = 1
+WFMT_CB4 = 2
+X_F32 = 0
+X_BF16 = 1
+
+
+# ---------------------------------------------------------------------------
+# Formats
+# ---------------------------------------------------------------------------
+
+def e2m1_value(code):
+    """FP4 E2M1 (OCP MX v1.0): sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+    exponent 0 is subnormal: m * 0.5; otherwise (1 + m/2) * 2^(e-1).  Code 8 is -0."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def e8m0_value(u):
+    """E8M0 scale (OCP MX v1.0): 2^(u - 127); byte 255 encodes NaN."""
+    u = np.asarray(u, dtype=np.int64)
+    with np.errstate(invalid="ignore"):
+        return np.where(u == 255, np.nan, np.exp2(u - 127.0))
+
+
+def fp16_value(bits):
+    """IEEE binary16 bits -> value (sign, 5-bit exponent with bias 15, 10-bit fraction)."""
+    b = np.asarray(bits, dtype=np.int64)
+    sign = np.where((b >> 15) & 1 == 1, -1.0, 1.0)
+    ex = (b >> 10) & 0x1F
+    fr = (b & 0x3FF).astype(np.float64)
+    normal = (1024.0 + fr) * np.exp2(ex - 25.0)
+    subnormal = fr * 2.0 ** -24
+    special = np.where(fr == 0, np.inf, np.nan)
+    return sign * np.where(ex == 0, subnormal, np.where(ex == 31, special, normal))
+
+
+def bf16_value(bits):
+    """bfloat16 bits -> value: the upper 16 bits of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def packed_size(wfmt: int, rows: int, cols: int) -> int:
+    """Bytes of one packed matrix: code plane, padded to 256 bytes, then the scale plane."""
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    code_bytes = rows * cols // 2
+    scale_off = (code_bytes + 255) // 256 * 256
+    nblocks = rows * cols // 32
+    return scale_off + nblocks * (1 if wfmt == WFMT_MXFP4 else 2)
+
+
+def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np.ndarray:
+    """Dense fp64 [rows][cols] from one packed matrix (every element exact in fp64)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    code_bytes = rows * cols // 2
+    scale_off = (code_bytes + 255) // 256 * 256
+    nblocks = rows * cols // 32
+    codes = packed[:code_bytes].astype(np.int64)
+    nib = np.empty(rows * cols, dtype=np.int64)
+    nib[0::2] = codes & 0xF       # element 2j: low nibble of byte j
+    nib[1::2] = codes >> 4        # element 2j+1: high nibble
+    if wfmt == WFMT_MXFP4:
+        scales = e8m0_value(packed[scale_off:scale_off + nblocks])
+        vals = e2m1_value(nib)
+    elif wfmt == WFMT_CB4:
+        sbits = packed[scale_off:scale_off + 2 * nblocks].view("<u2")
+        scales = fp16_value(sbits)
+        vals = np.asarray(codebook, dtype=np.int64)[nib].astype(np.float64)
+    else:
+        raise ValueError("unknown weight format")
+    w = vals.reshape(rows, cols // 32, 32) * scales.reshape(rows, cols // 32, 1)
+    return w.reshape(rows, cols)
+
+
+def activations_f64(x, x_dtype: int) -> np.ndarray:
+    if x_dtype == X_F32:
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if x_dtype == X_BF16:
+        return bf16_value(np.asarray(x, dtype=np.uint16))
+    raise ValueError("unknown activation dtype")
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+
+def router_logits(x64: np.ndarray, router_w, router_b) -> np.ndarray:
+    """l[t,e] = sum_h x[t,h] * W_r[e,h] + b[e], fp64."""
+    l = x64 @ np.asarray(router_w, dtype=np.float64).T
+    if router_b is not None:
+        l = l + np.asarray(router_b, dtype=np.float64)[None, :]
+    return l
+
+
+def topk_softmax(logits: np.ndarray, k: int):
+    """Per token: the k largest logits ordered by (-logit, expert index); gates are the
+    softmax over those k logits (equal to the full softmax renormalised over the k)."""
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -logits[t]))  # primary -logit, then index
+        sel = order[:k]
+        ids[t] = sel
+        z = np.exp(logits[t, sel] - logits[t, sel[0]])
+        gates[t] = z / z.sum()
+    return ids, gates
+
+
+def shared_weights(x64: np.ndarray, shared_gate_w) -> np.ndarray:
+    """Weight of the always-on shared expert: 1, or sigmoid(w . x_t) with a gate vector."""
+    if shared_gate_w is None:
+        return np.ones(x64.shape[0])
+    z = x64 @ np.asarray(shared_gate_w, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def bucket(ids: np.ndarray, n_experts: int, has_shared: int):
+    """Counting sort of pairs p = t*k + j by expert (stable: increasing p in a bucket).
+    Shared-expert pairs p = T*k + t form bucket E.  Returns counts [E+1],
+    offsets [E+2] (exclusive prefix sums), perm (bucketed pair ids), inv (perm^-1)."""
+    T, k = ids.shape
+    expert_of = list(int(e) for e in ids.reshape(-1))
+    if has_shared:
+        expert_of += [n_experts] * T
+    P = len(expert_of)
+    counts = np.zeros(n_experts + 1, dtype=np.int32)
+    for e in expert_of:
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 2, dtype=np.int32)
+    for e in range(n_experts + 1):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:n_experts + 1].copy()
+    perm = np.empty(P, dtype=np.int32)
+    for p in range(P):
+        e = expert_of[p]
+        perm[fill[e]] = p
+        fill[e] += 1
+    inv = np.empty(P, dtype=np.int32)
+    for i in range(P):
+        inv[perm[i]] = i
+    return counts, offsets, perm, inv
+
+
+# ---------------------------------------------------------------------------
+# Experts and combine
+# ---------------------------------------------------------------------------
+
+def silu(a: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def expert_ffn(w_gate_up: np.ndarray, w_down: np.ndarray, X: np.ndarray):
+    """One expert on the rows of X [n][H]: gate/up projection, SwiGLU, down projection.
+    Returns (h [n][I], o [n][H])."""
+    I = w_gate_up.shape[0] // 2
+    a = X @ w_gate_up.T
+    h = silu(a[:, :I]) * a[:, I:]
+    return h, h @ w_down.T
+
+
+def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = False):
+    """The whole layer for the tokens in x.  When `ids`/`gates` are given, routing is
+    taken from them (steps after routing only).  Returns a dict with y [T][H] fp64 and
+    every intermediate the GPU library exposes."""
+    H, I, E, k = layer.hidden, layer.inter, layer.n_experts, layer.top_k
+    x64 = activations_f64(x, x_dtype)
+    T = x64.shape[0]
+    logits = router_logits(x64, layer.router_w, layer.router_b)
+    if ids is None:
+        ids, gates = topk_softmax(logits, k)
+    ids = np.asarray(ids, dtype=np.int32).reshape(T, k)
+    gates = np.asarray(gates, dtype=np.float64).reshape(T, k)
+    s = shared_weights(x64, layer.shared_gate_w) if layer.has_shared else None
+    counts, offsets, perm, inv = bucket(ids, E, layer.has_shared)
+    P = perm.shape[0]
+    o = np.zeros((P, H))
+    h_all = np.zeros((P, I)) if want_h else None
+    for e in range(E + layer.has_shared):
+        pairs = perm[offsets[e]:offsets[e + 1]]
+        if pairs.size == 0:
+            continue
+        tokens = np.where(pairs < T * k, pairs // k, pairs - T * k)
+        wgu = dequant(layer.wfmt, layer.gate_up[e], layer.codebook, 2 * I, H)
+        wd = dequant(layer.wfmt, layer.down[e], layer.codebook, H, I)
+        h, oe = expert_ffn(wgu, wd, x64[tokens])
+        o[pairs] = oe
+        if want_h:
+            h_all[pairs] = h
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            y[t] += gates[t, j] * o[t * k + j]
+        if layer.has_shared:
+            y[t] += s[t] * o[T * k + t]
+    return dict(y=y, logits=logits, ids=ids, gates=gates, shared_w=s, counts=counts,
+                offsets=offsets, perm=perm, inv=inv, h=h_all, o=o)
+
+
+def rms_rescale(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """Input of the next stacked layer: y / sqrt(mean(y^2) + eps) per token, rounded to
+    bfloat16 (nearest, ties to even).  Returns uint16 bits."""
+    y = np.asarray(y, dtype=np.float64)
+    r = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+    return round_to_bf16_bits(r)
+
+
+def round_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even); returns the bits.
+    bfloat16 keeps 8 significant bits: with val = m * 2^e (0.5 <= |m| < 1), the result is
+    round_half_even(m * 2^8) * 2^(e-8).  Normal range only (|val| >= 2^-126)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
+    for i, val in enumerate(flat_v):
+        m, e = math.frexp(float(val))
+        r = math.ldexp(round(m * 256.0), e - 8)   # Python's round() is half-to-even
+        bits32 = int(np.array([r], dtype=np.float32).view(np.uint32)[0])  # exact: 8 bits
+        flat_o[i] = bits32 >> 16
+    return out

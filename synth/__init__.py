@@ -1,0 +1,242 @@
+"""Seeded synthetic inputs for the routed MoE layer.
+
+This module only draws random inputs and writes them in the packed storage
+layout; it computes none of the layer's arithmetic (no decoding, routing,
+projection or combine).  Both the CPU oracle (through the tests) and the GPU
+library (through the tests and the benchmark) consume what it produces.
+
+Packed storage of one quantised matrix with N rows and K columns (K a multiple
+of 32), blocks of 32 consecutive values along a row:
+
+* code plane: N*K/2 bytes, row-major; byte j of a 16-byte block holds element
+  2j in its low nibble and element 2j+1 in its high nibble;
+* scale plane: starts at round_up(N*K/2, 256); N*K/32 scales, row-major, one
+  per block: an E8M0 byte for MXFP4, the little-endian IEEE fp16 bits for the
+  4-bit codebook format (CB4).
+
+Shapes follow the pages' models: gpt-oss-120B (hidden 2880, 128 experts,
+top-4, 36 layers; "Neural Server" page, "What it runs on and what it runs")
+and a Flash-Next-like layer (256 routed experts plus one shared expert,
+top-8), with decode windows of at most 17 tokens and 1,024-token prefill
+chunks.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+WFMT_MXFP4 = 1
+WFMT_CB4 = 2
+X_F32 = 0
+X_BF16 = 1
+
+# tensor ids inside one (config, layer, expert) seed tuple
+_T_CODES_GU, _T_SCALES_GU, _T_CODES_D, _T_SCALES_D = 0, 1, 2, 3
+_T_ROUTER_W, _T_ROUTER_B, _T_X, _T_CODEBOOK, _T_PERM, _T_SHGATE = 10, 11, 12, 13, 14, 15
+_SHARED_SLOT = 100_000  # expert index used in the seed tuple of the shared expert
+
+
+def round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def scale_plane_offset(rows: int, cols: int) -> int:
+    return round_up(rows * cols // 2, 256)
+
+
+def packed_nbytes(wfmt: int, rows: int, cols: int) -> int:
+    nblk = rows * cols // 32
+    return scale_plane_offset(rows, cols) + nblk * (1 if wfmt == WFMT_MXFP4 else 2)
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng([int(k) for k in key])
+
+
+def random_bytes(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n uniformly distributed bytes (both nibbles uniform over 16 codes)."""
+    words = rng.bit_generator.random_raw((n + 7) // 8)
+    return words.view(np.uint8)[:n].copy() if n % 8 else words.view(np.uint8)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+@dataclasses.dataclass
+class WeightSpec:
+    wfmt: int
+    scale_lo: float = 0.01      # CB4: fp16 scale ~ U(lo, hi)
+    scale_hi: float = 0.05
+    e8m0_lo: int = 118          # MXFP4: E8M0 byte uniform in [lo, hi]
+    e8m0_hi: int = 124
+
+
+@dataclasses.dataclass
+class LayerSpec:
+    name: str
+    T: int
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+    has_shared: int
+    weights: WeightSpec
+    x_dtype: int
+    router_std: float
+    bias: str                   # "none" | "normal" | "zipf"
+    bias_std: float = 0.0
+    zipf_s: float = 1.1
+    n_layers: int = 1
+    seed: int = 0
+
+
+def make_packed(spec: WeightSpec, rows: int, cols: int, seed_key: Sequence[int],
+                codes_tid: int, scales_tid: int) -> np.ndarray:
+    """One packed matrix [rows][cols] in the layout described in the module docstring."""
+    assert cols % 32 == 0
+    nblk = rows * cols // 32
+    out = np.zeros(packed_nbytes(spec.wfmt, rows, cols), dtype=np.uint8)
+    ncode = rows * cols // 2
+    out[:ncode] = random_bytes(_rng(*seed_key, codes_tid), ncode)
+    off = scale_plane_offset(rows, cols)
+    srng = _rng(*seed_key, scales_tid)
+    if spec.wfmt == WFMT_MXFP4:
+        out[off:off + nblk] = srng.integers(spec.e8m0_lo, spec.e8m0_hi + 1, size=nblk, dtype=np.uint8)
+    else:
+        s = srng.uniform(spec.scale_lo, spec.scale_hi, size=nblk).astype(np.float16)
+        out[off:off + 2 * nblk] = s.view(np.uint8)
+    return out
+
+
+def make_codebook(seed: int, layer: int) -> np.ndarray:
+    """16 distinct integers from [-127, 127], drawn with the seed, sorted ascending (int8)."""
+    rng = _rng(seed, layer, 0, _T_CODEBOOK)
+    vals = rng.choice(np.arange(-127, 128), size=16, replace=False)
+    return np.sort(vals).astype(np.int8)
+
+
+def zipf_log_prior(seed: int, layer: int, n_experts: int, s: float) -> np.ndarray:
+    """Per-expert bias ln p, p the Zipf(s) rank probabilities over a seeded rank permutation."""
+    ranks = np.arange(1, n_experts + 1, dtype=np.float64)
+    p = ranks ** (-s)
+    p /= p.sum()
+    perm = _rng(seed, layer, 0, _T_PERM).permutation(n_experts)
+    return np.log(p[perm]).astype(np.float32)
+
+
+@dataclasses.dataclass
+class Layer:
+    """Host copy of one synthetic layer (all arrays numpy)."""
+    spec: LayerSpec
+    layer_index: int
+    router_w: np.ndarray                    # [E][H] float32
+    router_b: Optional[np.ndarray]          # [E] float32 or None
+    gate_up: List[np.ndarray]               # E(+1) packed [2I][H] uint8
+    down: List[np.ndarray]                  # E(+1) packed [H][I] uint8
+    codebook: Optional[np.ndarray]          # [16] int8 (CB4) or None
+    shared_gate_w: Optional[np.ndarray]     # [H] float32 or None
+
+    @property
+    def hidden(self): return self.spec.hidden
+    @property
+    def inter(self): return self.spec.inter
+    @property
+    def n_experts(self): return self.spec.n_experts
+    @property
+    def top_k(self): return self.spec.top_k
+    @property
+    def wfmt(self): return self.spec.weights.wfmt
+    @property
+    def has_shared(self): return self.spec.has_shared
+
+
+def _expert_pair(spec: LayerSpec, layer: int, e: int):
+    key = (spec.seed, layer, e)
+    gu = make_packed(spec.weights, 2 * spec.inter, spec.hidden, key, _T_CODES_GU, _T_SCALES_GU)
+    dn = make_packed(spec.weights, spec.hidden, spec.inter, key, _T_CODES_D, _T_SCALES_D)
+    return gu, dn
+
+
+def make_layer(spec: LayerSpec, layer: int = 0, experts: Optional[Sequence[int]] = None,
+               threads: Optional[int] = None, shared_gate: bool = False) -> Layer:
+    """Generate one layer.  `experts` restricts which routed experts get weights
+    (the others are left as None, for CPU runs that only need the selected ones)."""
+    E, H = spec.n_experts, spec.hidden
+    rw = _rng(spec.seed, layer, 0, _T_ROUTER_W).normal(0.0, spec.router_std, size=(E, H)).astype(np.float32)
+    if spec.bias == "normal":
+        rb = _rng(spec.seed, layer, 0, _T_ROUTER_B).normal(0.0, spec.bias_std, size=E).astype(np.float32)
+    elif spec.bias == "zipf":
+        rb = zipf_log_prior(spec.seed, layer, E, spec.zipf_s)
+    else:
+        rb = None
+    want = list(range(E)) if experts is None else sorted(set(int(e) for e in experts))
+    slots = want + ([_SHARED_SLOT] if spec.has_shared else [])
+    nthr = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max(1, nthr)) as ex:
+        pairs = list(ex.map(lambda e: _expert_pair(spec, layer, e), slots))
+    gate_up: List[Optional[np.ndarray]] = [None] * (E + spec.has_shared)
+    down: List[Optional[np.ndarray]] = [None] * (E + spec.has_shared)
+    for e, (gu, dn) in zip(slots, pairs):
+        idx = E if e == _SHARED_SLOT else e
+        gate_up[idx], down[idx] = gu, dn
+    cb = make_codebook(spec.seed, layer) if spec.weights.wfmt == WFMT_CB4 else None
+    sg = None
+    if shared_gate and spec.has_shared:
+        sg = _rng(spec.seed, layer, 0, _T_SHGATE).normal(0.0, spec.router_std, size=H).astype(np.float32)
+    return Layer(spec, layer, rw, rb, gate_up, down, cb, sg)
+
+
+def make_x(spec: LayerSpec, T: Optional[int] = None, layer: int = 0, stream: int = 0) -> np.ndarray:
+    """Activations [T][H]: float32 for X_F32, uint16 bfloat16 bits for X_BF16 (RNE of N(0,1) fp32)."""
+    T = spec.T if T is None else T
+    v = _rng(spec.seed, layer, stream, _T_X).standard_normal(size=(T, spec.hidden)).astype(np.float32)
+    return v if spec.x_dtype == X_F32 else f32_to_bf16_bits(v)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Seeds are 1000 + config number.
+# ---------------------------------------------------------------------------
+_CB4 = WeightSpec(WFMT_CB4, 0.01, 0.05)
+_MX = WeightSpec(WFMT_MXFP4, e8m0_lo=118, e8m0_hi=124)
+
+CONFIGS = {
+    # tiny 4-bit codebook layer, fp32 activations
+    "c1": LayerSpec("c1_tiny_cb4", T=4, hidden=256, inter=128, n_experts=8, top_k=2, has_shared=0,
+                    weights=_CB4, x_dtype=X_F32, router_std=0.05, bias="none", seed=1001),
+    # gpt-oss-120B-shaped decode layer, MXFP4 experts
+    "c2": LayerSpec("c2_gptoss_mxfp4_decode", T=1, hidden=2880, inter=2880, n_experts=128, top_k=4,
+                    has_shared=0, weights=_MX, x_dtype=X_BF16, router_std=0.02, bias="normal",
+                    bias_std=0.5, seed=1002),
+    # Flash-Next-like draft/verify window, CB4, shared expert, Zipf routing prior
+    "c3": LayerSpec("c3_flashnext_cb4_verify", T=17, hidden=2048, inter=512, n_experts=256, top_k=8,
+                    has_shared=1, weights=_CB4, x_dtype=X_BF16, router_std=0.02, bias="zipf",
+                    zipf_s=1.1, seed=1003),
+    # 36 stacked c2 layers
+    "c4": LayerSpec("c4_gptoss_36layer_decode", T=1, hidden=2880, inter=2880, n_experts=128, top_k=4,
+                    has_shared=0, weights=_MX, x_dtype=X_BF16, router_std=0.02, bias="normal",
+                    bias_std=0.5, n_layers=36, seed=1004),
+    # prefill chunks, no bias
+    "c5a": LayerSpec("c5a_prefill_cb4", T=1024, hidden=2048, inter=512, n_experts=256, top_k=8,
+                     has_shared=1, weights=_CB4, x_dtype=X_BF16, router_std=0.02, bias="none", seed=1005),
+    "c5b": LayerSpec("c5b_prefill_mxfp4", T=1024, hidden=2880, inter=2880, n_experts=128, top_k=4,
+                     has_shared=0, weights=_MX, x_dtype=X_BF16, router_std=0.02, bias="none", seed=1006),
+}
+
+
+def small_spec(name: str, T: int, hidden: int, inter: int, n_experts: int, top_k: int, wfmt: int,
+               has_shared: int = 0, x_dtype: int = X_BF16, bias: str = "none", seed: int = 7,
+               router_std: float = 0.05, bias_std: float = 0.5) -> LayerSpec:
+    """A layer shape for parity sweeps (several tiles plus ragged tails, seconds on the CPU)."""
+    w = WeightSpec(wfmt) if wfmt == WFMT_CB4 else WeightSpec(WFMT_MXFP4, e8m0_lo=118, e8m0_hi=124)
+    return LayerSpec(name, T=T, hidden=hidden, inter=inter, n_experts=n_experts, top_k=top_k,
+                     has_shared=has_shared, weights=w, x_dtype=x_dtype, router_std=router_std,
+                     bias=bias, bias_std=bias_std, seed=seed)

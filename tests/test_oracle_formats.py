@@ -1,0 +1,177 @@
+"""Pins of the oracle's format decoding against closed forms, library routines and
+the byte counts the pages print."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# FP4 E2M1 code points as the OCP Microscaling v1.0 spec tabulates them.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+              -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def _pack_block_codes(codes):
+    """32 4-bit codes -> 16 bytes (element 2j low nibble, 2j+1 high nibble)."""
+    codes = list(codes)
+    return bytes((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4) for j in range(16))
+
+
+def _one_block_matrix(codes, scale_bytes, wfmt):
+    """A 1x32 packed matrix: 16 code bytes, zero padding to 256, then the scale."""
+    buf = bytearray(_pack_block_codes(codes))
+    buf += bytes(256 - len(buf))
+    buf += bytes(scale_bytes)
+    assert len(buf) == oracle.packed_size(wfmt, 1, 32)
+    return np.frombuffer(bytes(buf), dtype=np.uint8)
+
+
+def test_mxfp4_hand_block_unit_scale():
+    codes = list(range(16)) + list(range(16))
+    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, [127], oracle.WFMT_MXFP4), None, 1, 32)
+    assert list(w[0, :16]) == E2M1_TABLE
+    assert list(w[0, 16:]) == E2M1_TABLE
+    # code 8 is negative zero
+    assert np.signbit(w[0, 8]) and w[0, 8] == 0.0
+    assert not np.signbit(w[0, 0])
+
+
+def test_mxfp4_hand_block_eighth_scale():
+    codes = [15 - (i % 16) for i in range(32)]
+    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, [124], oracle.WFMT_MXFP4), None, 1, 32)
+    expect = [E2M1_TABLE[c] / 8.0 for c in codes]
+    assert list(w[0]) == expect
+
+
+def test_e2m1_e8m0_exhaustive_closed_form():
+    for u in range(256):
+        for c in range(16):
+            got = float(oracle.e2m1_value(c) * oracle.e8m0_value(u))
+            if u == 255:
+                assert math.isnan(got)
+                continue
+            want = math.ldexp(E2M1_TABLE[c], u - 127)
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (c, u)
+
+
+def test_fp16_scale_exhaustive_vs_numpy_half():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.fp16_value(bits)
+    lib = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], lib[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(lib[~nan]))
+
+
+@pytest.mark.parametrize("scale_bits,factor", [(0x3C00, 1.0), (0x3800, 0.5), (0x0001, 2.0 ** -24),
+                                               (0xC000, -2.0), (0x7BFF, 65504.0)])
+def test_cb4_hand_block(scale_bits, factor):
+    cb = np.array([-127, -100, -64, -33, -17, -8, -3, -1, 0, 2, 5, 9, 21, 47, 88, 127], dtype=np.int8)
+    codes = [(7 * i + 3) % 16 for i in range(32)]
+    sb = [scale_bits & 0xFF, scale_bits >> 8]
+    w = oracle.dequant(oracle.WFMT_CB4, _one_block_matrix(codes, sb, oracle.WFMT_CB4), cb, 1, 32)
+    assert list(w[0]) == [float(cb[c]) * factor for c in codes]
+
+
+def test_cb4_exhaustive_scale_times_index():
+    """Every fp16 scale pattern times every codebook entry, against numpy's half decoding."""
+    cb = np.array(sorted(np.random.default_rng(5).choice(np.arange(-127, 128), 16, replace=False)),
+                  dtype=np.int8)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = bits.view(np.float16).astype(np.float64)
+    # one packed matrix with 2048 rows x 32 cols would need all patterns; decode row by row instead
+    rows = 65536
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)           # indices 0..15 twice
+    code_bytes = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    plane = np.tile(code_bytes, rows)
+    buf = np.zeros(oracle.packed_size(oracle.WFMT_CB4, rows, 32), dtype=np.uint8)
+    buf[:plane.size] = plane
+    off = (plane.size + 255) // 256 * 256
+    buf[off:off + 2 * rows] = bits.view(np.uint8)
+    w = oracle.dequant(oracle.WFMT_CB4, buf, cb, rows, 32)
+    with np.errstate(invalid="ignore"):
+        want = s[:, None] * cb.astype(np.float64)[np.tile(np.arange(16), 2)][None, :]
+    both_nan = np.isnan(w) & np.isnan(want)
+    assert np.array_equal(np.isnan(w), np.isnan(want))
+    assert np.array_equal(w[~both_nan], want[~both_nan])
+
+
+def test_packed_sizes_match_page_figures():
+    g = json.load(open(os.path.join(GOLDEN, "page_byte_counts.json")))
+    H = I = 2880
+    expert = oracle.packed_size(oracle.WFMT_MXFP4, 2 * I, H) + oracle.packed_size(oracle.WFMT_MXFP4, H, I)
+    assert expert == g["mxfp4_expert_bytes"]["value"] == 13_219_200
+    per_token = g["experts_touched_per_token"]["value"] * expert
+    assert per_token == 1_903_564_800
+    assert abs(per_token - g["experts_touched_per_token"]["approx_bytes"]) / 1.9e9 < 0.01
+    cb = g["cb4_rows_bytes"]
+    assert oracle.packed_size(oracle.WFMT_CB4, cb["rows"], cb["values_per_row"]) == cb["value"] == 1440
+    assert oracle.packed_size(oracle.WFMT_CB4, 1, 32) - 256 + 16 == g["q4_0_bytes_per_32"]["value"]
+    # the generator writes the same sizes
+    assert synth.packed_nbytes(synth.WFMT_MXFP4, 2 * I, H) + synth.packed_nbytes(synth.WFMT_MXFP4, H, I) == expert
+
+
+def test_packed_scale_store_reading_size():
+    """The page's packed-scale store size is reproduced by one byte per row plus a
+    4-bit delta per block (a reading of the page, used only as a size check)."""
+    g = json.load(open(os.path.join(GOLDEN, "page_byte_counts.json")))
+    rows = 2 * 2880 + 2880
+    blocks = rows * 2880 // 32
+    codes = rows * 2880 // 2
+    assert codes + blocks // 2 + rows == g["mxfp4_packed_scale_expert_bytes"]["value"]
+
+
+@pytest.mark.parametrize("wfmt", [oracle.WFMT_MXFP4, oracle.WFMT_CB4])
+def test_layout_single_nonzero_positions(wfmt):
+    """One nonzero code at (r, c) lands at (r, c): checks nibble order, row-major codes
+    and the 256-aligned scale plane (rows*cols/2 = 240 is not a multiple of 256)."""
+    rows, cols = 5, 96
+    cb = np.arange(-8, 8, dtype=np.int8) * 3  # index 8 -> 0
+    zero_code = 0 if wfmt == oracle.WFMT_MXFP4 else 8
+    one_code = 2 if wfmt == oracle.WFMT_MXFP4 else 9   # e2m1(2) = 1.0; cb[9] = 3
+    one_val = 1.0 if wfmt == oracle.WFMT_MXFP4 else 3.0
+    for r, c in [(0, 0), (0, 1), (2, 33), (4, 95), (3, 64)]:
+        codes = np.full(rows * cols, zero_code, dtype=np.uint8)
+        codes[r * cols + c] = one_code
+        plane = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        buf = np.zeros(oracle.packed_size(wfmt, rows, cols), dtype=np.uint8)
+        buf[:plane.size] = plane
+        off = 256
+        nblk = rows * cols // 32
+        if wfmt == oracle.WFMT_MXFP4:
+            buf[off:off + nblk] = 127
+        else:
+            buf[off:off + 2 * nblk] = np.full(nblk, 0x3C00, dtype=np.uint16).view(np.uint8)
+        w = oracle.dequant(wfmt, buf, cb, rows, cols)
+        want = np.zeros((rows, cols))
+        want[r, c] = one_val
+        assert np.array_equal(w, want)
+        # the scale of block (r, c // 32) multiplies it
+        bi = r * (cols // 32) + c // 32
+        if wfmt == oracle.WFMT_MXFP4:
+            buf[off + bi] = 130
+            scale = 8.0
+        else:
+            buf[off + 2 * bi: off + 2 * bi + 2] = np.array([0x4400], dtype=np.uint16).view(np.uint8)
+            scale = 4.0
+        w = oracle.dequant(wfmt, buf, cb, rows, cols)
+        assert w[r, c] == one_val * scale and np.count_nonzero(w) == 1
+
+
+def test_bf16_rounding_two_implementations():
+    """The oracle's nearest-even bf16 rounding against the generator's integer-bit rounding."""
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(4000).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e4).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 - 2 ** -9, 3.0], dtype=np.float32)])
+    assert np.array_equal(oracle.round_to_bf16_bits(v.astype(np.float64)), synth.f32_to_bf16_bits(v))
+    # ties go to even
+    assert oracle.round_to_bf16_bits(np.array([1 + 2 ** -8]))[0] == 0x3F80
+    assert oracle.round_to_bf16_bits(np.array([1 + 3 * 2 ** -8]))[0] == 0x3F82
