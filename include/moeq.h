@@ -50,7 +50,8 @@
  *     so every call can be captured in a HIP graph.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     failure a negative moe_status is returned and no output is touched.
- *     T == 0 returns MOE_OK and enqueues nothing.
+ *     T == 0 returns MOE_OK once the layer descriptor is valid and enqueues nothing
+ *     (buffers of zero size may then be NULL).
  *   - A launch failure returns MOE_ERR_HIP; faults during execution surface at
  *     the caller's next synchronisation, as with any stream API.
  *   - No C++ exception crosses the ABI and nothing is printed.  The library is
@@ -130,6 +131,27 @@ int moe_bucket(const moe_layer *L, const int32_t *topk_ids, int32_t T, int32_t *
 int moe_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *y,
                 void *ws, size_t ws_bytes, void *stream, int32_t path, int32_t *dbg_ids,
                 float *dbg_w, int32_t *dbg_counts, int32_t *dbg_offsets, int32_t *dbg_perm);
+
+/* Stages of one forward call, for moe_forward_timed. */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,   /* router logits */
+  MOE_STAGE_TOPK = 1,     /* top-k and gates */
+  MOE_STAGE_BUCKET = 2,   /* bucketing by expert */
+  MOE_STAGE_GATEUP = 3,   /* fused dequant + gate/up + SwiGLU */
+  MOE_STAGE_DOWN = 4,     /* dequant + down projection */
+  MOE_STAGE_COMBINE = 5,  /* gate-weighted combine */
+  MOE_NUM_STAGES = 6
+} moe_stage;
+
+/* moe_forward with per-stage timing: stage_events holds 2*MOE_NUM_STAGES hipEvent_t
+ * handles (created by the caller with timing enabled; any may be NULL).  Event
+ * 2s / 2s+1 is stamped at the start / end of the kernel that runs stage s, by the
+ * dispatch packet itself, so hipEventElapsedTime gives that kernel's execution
+ * time.  A stage fused into another kernel on the chosen path leaves its events
+ * untouched.  No debug outputs. */
+int moe_forward_timed(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *y,
+                      void *ws, size_t ws_bytes, void *stream, int32_t path,
+                      void *const *stage_events);
 
 /* Test export: decode one packed matrix to fp32 out [rows][cols], bit-exact
  * (every element is exactly representable in fp32 for MXFP4 scales u <= 252

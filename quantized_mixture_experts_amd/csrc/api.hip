@@ -1,0 +1,225 @@
+// C ABI of the MoE layer: host-side validation, workspace carving, kernel launches.
+// Validation runs entirely on the host before anything is enqueued and touches no
+// HIP API, so the error paths can be exercised without a GPU.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moeq.h"
+#include "device.h"
+#include "launch.h"
+
+namespace {
+
+using moeq::LayerArgs;
+using moeq::Work;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int32_t kMaxDim = 16384;
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxTopK = 16;
+constexpr int32_t kMaxTokens = 1 << 16;
+
+int validate_layer(const moe_layer* L) {
+  if (!L) return MOE_ERR_INVALID_ARG;
+  if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0) return MOE_ERR_INVALID_ARG;
+  if (L->hidden % 32 || L->inter % 32) return MOE_ERR_INVALID_ARG;
+  if (L->hidden > kMaxDim || L->inter > kMaxDim || L->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (L->top_k > L->n_experts || L->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_CB4) return MOE_ERR_INVALID_ARG;
+  if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (!L->router_w || !L->gate_up || !L->down) return MOE_ERR_INVALID_ARG;
+  if (L->wfmt == MOE_WFMT_CB4 && !L->codebook) return MOE_ERR_INVALID_ARG;
+  if (L->wfmt == MOE_WFMT_MXFP4 && L->codebook) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(L->router_w) || (L->router_b && !aligned4(L->router_b))) return MOE_ERR_ALIGNMENT;
+  if (L->has_shared && L->shared_gate_w && !aligned16(L->shared_gate_w)) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(L->gate_up) || !aligned16(L->down)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, total;
+};
+
+Layout layout_for(const moe_layer* L, int32_t T) {
+  const size_t E = (size_t)L->n_experts, k = (size_t)L->top_k, H = (size_t)L->hidden, I = (size_t)L->inter;
+  const size_t P = (size_t)T * k + (L->has_shared ? (size_t)T : 0);
+  Layout o{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) { size_t r = at; at = align_up(at + bytes, kAlign); return r; };
+  o.logits = take((size_t)T * (E + 1) * 8);
+  o.ids = take((size_t)T * k * 4);
+  o.pair_w = take(P * 4);
+  o.counts = take((E + 1) * 4);
+  o.offsets = take((E + 2) * 4);
+  o.perm = take(P * 4);
+  o.active = take((E + 2) * 4);
+  o.xplanes = take(3 * (size_t)T * H * 2);
+  o.hplanes = take(2 * P * I * 2);
+  o.o = take(P * H * 4);
+  o.total = at;
+  return o;
+}
+
+Work carve(void* ws, const Layout& lo) {
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  Work w;
+  w.logits = reinterpret_cast<double*>(b + lo.logits);
+  w.ids = reinterpret_cast<int32_t*>(b + lo.ids);
+  w.pair_w = reinterpret_cast<float*>(b + lo.pair_w);
+  w.counts = reinterpret_cast<int32_t*>(b + lo.counts);
+  w.offsets = reinterpret_cast<int32_t*>(b + lo.offsets);
+  w.perm = reinterpret_cast<int32_t*>(b + lo.perm);
+  w.active = reinterpret_cast<int32_t*>(b + lo.active);
+  w.xplanes = reinterpret_cast<uint16_t*>(b + lo.xplanes);
+  w.hplanes = reinterpret_cast<uint16_t*>(b + lo.hplanes);
+  w.o = reinterpret_cast<float*>(b + lo.o);
+  return w;
+}
+
+LayerArgs args_of(const moe_layer* L) {
+  LayerArgs a;
+  a.H = L->hidden; a.I = L->inter; a.E = L->n_experts; a.k = L->top_k;
+  a.wfmt = L->wfmt; a.has_shared = L->has_shared;
+  a.router_w = L->router_w; a.router_b = L->router_b;
+  a.gate_up = reinterpret_cast<const uint8_t* const*>(L->gate_up);
+  a.down = reinterpret_cast<const uint8_t* const*>(L->down);
+  a.codebook = L->codebook;
+  a.shared_gate_w = L->has_shared ? L->shared_gate_w : nullptr;
+  return a;
+}
+
+int check_ws(const moe_layer* L, int32_t T, void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < layout_for(L, T).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
+                        size_t ws_bytes, void* stream, int32_t path, int32_t* dbg_ids, float* dbg_w,
+                        int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, const moeq::Timing& tm) {
+  int st = validate_layer(L);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y)) return MOE_ERR_ALIGNMENT;
+  if ((dbg_ids && !aligned4(dbg_ids)) || (dbg_w && !aligned4(dbg_w)) || (dbg_counts && !aligned4(dbg_counts)) ||
+      (dbg_offsets && !aligned4(dbg_offsets)) || (dbg_perm && !aligned4(dbg_perm)))
+    return MOE_ERR_ALIGNMENT;
+  if ((st = check_ws(L, T, ws, ws_bytes))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Work w = carve(ws, layout_for(L, T));
+  const LayerArgs a = args_of(L);
+  hipError_t e = moeq::launch_router_topk(a, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
+  if (e == hipSuccess)
+    e = moeq::launch_bucket(T, a.k, a.E, a.has_shared, w.ids, w, dbg_counts, dbg_offsets, dbg_perm, s, tm);
+  if (e == hipSuccess) e = moeq::launch_experts(a, x, x_dtype, T, w, y, s, tm);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return 0;
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return 0;
+  const size_t code = (size_t)rows * cols / 2;
+  const size_t nblk = (size_t)rows * cols / 32;
+  return align_up(code, 256) + nblk * (wfmt == MOE_WFMT_MXFP4 ? 1 : 2);
+}
+
+size_t moe_workspace_bytes(const moe_layer* L, int32_t T_max) {
+  if (validate_layer(L) != MOE_OK || T_max < 0 || T_max > kMaxTokens) return 0;
+  return layout_for(L, T_max).total;
+}
+
+int moe_router_topk(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, int32_t* topk_ids,
+                    float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_layer(L);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;  // nothing is read or written; empty buffers may be NULL
+  if (!x || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned4(topk_ids) || !aligned4(topk_w)) return MOE_ERR_ALIGNMENT;
+  if ((st = check_ws(L, T, ws, ws_bytes))) return st;
+  const Work w = carve(ws, layout_for(L, T));
+  return hip_status(moeq::launch_router_topk(args_of(L), x, x_dtype, T, w, topk_ids, topk_w,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_bucket(const moe_layer* L, const int32_t* topk_ids, int32_t T, int32_t* counts, int32_t* offsets,
+               int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_layer(L);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(topk_ids) || !aligned4(counts) || !aligned4(offsets) || !aligned4(perm)) return MOE_ERR_ALIGNMENT;
+  if ((st = check_ws(L, T, ws, ws_bytes))) return st;
+  const Work w = carve(ws, layout_for(L, T));
+  return hip_status(moeq::launch_bucket(T, L->top_k, L->n_experts, L->has_shared, topk_ids, w, counts, offsets,
+                                        perm, static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
+                size_t ws_bytes, void* stream, int32_t path, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
+                int32_t* dbg_offsets, int32_t* dbg_perm) {
+  return forward_impl(L, x, x_dtype, T, y, ws, ws_bytes, stream, path, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                      dbg_perm, moeq::Timing());
+}
+
+int moe_forward_timed(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
+                      size_t ws_bytes, void* stream, int32_t path, void* const* stage_events) {
+  moeq::Timing tm;
+  tm.ev = stage_events;
+  return forward_impl(L, x, x_dtype, T, y, ws, ws_bytes, stream, path, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, tm);
+}
+
+int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,
+                void* stream) {
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if ((size_t)rows * (size_t)cols > ((size_t)1 << 34)) return MOE_ERR_UNSUPPORTED;
+  if (!packed || !out) return MOE_ERR_INVALID_ARG;
+  if (wfmt == MOE_WFMT_CB4 && !codebook) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moeq::launch_dequant(wfmt, static_cast<const uint8_t*>(packed), codebook, rows, cols, out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_rms_rescale(const float* y, int32_t T, int32_t H, float eps, void* x_next_bf16, void* stream) {
+  if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!y || !x_next_bf16) return MOE_ERR_INVALID_ARG;
+  return hip_status(moeq::launch_rms_rescale(y, T, H, eps, static_cast<uint16_t*>(x_next_bf16),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_ALIGNMENT: return "misaligned buffer";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

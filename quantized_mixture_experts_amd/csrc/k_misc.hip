@@ -1,0 +1,75 @@
+// Dequantisation export (bit-exact, through the same decode helpers the projection
+// kernels use) and the RMS rescale applied between stacked layers.
+#include "device.h"
+#include "launch.h"
+
+namespace moeq {
+
+// One thread per 32-value block: out[row][32kb .. 32kb+31].
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed, const int8_t* __restrict__ codebook,
+                                                 int rows, int cols, float* __restrict__ out) {
+  __shared__ uint32_t lut[256];
+  if (FMT == 2) {
+    build_cb4_lut(lut, codebook);
+    __syncthreads();
+  }
+  const int nkb = cols >> 5;
+  const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= (size_t)rows * nkb) return;
+  const size_t scale_off = ((size_t)rows * cols / 2 + 255) / 256 * 256;
+  const u32x4_t c = *(const u32x4_t*)(packed + blk * 16);
+  float* dst = out + blk * 32;
+  if (FMT == 1) {
+    const float s = e8m0_to_f32(packed[scale_off + blk]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t v = fp4x8_to_bf16(c[q], s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[8 * q + i] = (float)v[i];
+    }
+  } else {
+    const uint16_t sb = *(const uint16_t*)(packed + scale_off + 2 * blk);
+    const float s = half_bits_to_f32(sb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t v = cb4x8_to_bf16(c[q], lut);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[8 * q + i] = s * (float)v[i];
+    }
+  }
+}
+
+// x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y^2 + eps)); one block per token.
+__global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y, int H, float eps,
+                                                     uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int t = blockIdx.x;
+  const float* yt = y + (size_t)t * H;
+  float s = 0.f;
+  for (int n = threadIdx.x; n < H; n += 256) s = fmaf(yt[n], yt[n], s);
+  s = wave_sum_f32(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float ms = (part[0] + part[1] + part[2] + part[3]) / (float)H;
+  const float d = sqrtf(ms + eps);
+  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(yt[n] / d);
+}
+
+hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,
+                          float* out, hipStream_t s) {
+  const size_t nblk = (size_t)rows * (cols / 32);
+  const dim3 grid((unsigned)((nblk + 255) / 256));
+  if (wfmt == 1)
+    hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
+  else
+    hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_rms_rescale, dim3(T), dim3(256), 0, s, y, H, eps, out);
+  return hipGetLastError();
+}
+
+}  // namespace moeq

@@ -1,0 +1,36 @@
+// Host-side launchers of the kernels (one per kernel family).
+#pragma once
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include "device.h"
+
+namespace moeq {
+
+// Kernel stages of one forward call.  A stage whose work is fused into another
+// kernel on the chosen path launches nothing and leaves its events untouched.
+enum Stage { kStageRouter = 0, kStageTopk, kStageBucket, kStageGateUp, kStageDown, kStageCombine, kNumStages };
+
+// Optional start/stop events per stage, stamped by the dispatch packet itself
+// (hipExtLaunchKernel), i.e. the kernel's own execution interval.
+struct Timing {
+  void* const* ev = nullptr;  // [2 * kNumStages] hipEvent_t, each may be null
+  hipEvent_t start(int s) const { return ev ? static_cast<hipEvent_t>(ev[2 * s]) : nullptr; }
+  hipEvent_t stop(int s) const { return ev ? static_cast<hipEvent_t>(ev[2 * s + 1]) : nullptr; }
+};
+
+#define MOEQ_LAUNCH(tm, stage, kernel, grid, block, shmem, stream, ...) \
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm).start(stage), (tm).stop(stage), 0, __VA_ARGS__)
+
+hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
+                              int32_t* dbg_ids, float* dbg_w, hipStream_t s,
+                              const Timing& tm = Timing());
+hipError_t launch_bucket(int T, int k, int E, int has_shared, const int32_t* ids, const Work& w,
+                         int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s,
+                         const Timing& tm = Timing());
+hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
+                          hipStream_t s, const Timing& tm = Timing());
+hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,
+                          float* out, hipStream_t s);
+hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* out, hipStream_t s);
+
+}  // namespace moeq

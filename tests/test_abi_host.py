@@ -1,0 +1,125 @@
+"""The C ABI on the host (no GPU): the library loads, exports every symbol the header
+declares, and its validation rejects bad arguments before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_mixture_experts_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q.LIB_PATH):
+        from quantized_mixture_experts_amd import build
+        build.build()
+    return q.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(q.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_packed_bytes(L):
+    assert q.packed_bytes(q.WFMT_MXFP4, 5760, 2880) + q.packed_bytes(q.WFMT_MXFP4, 2880, 2880) == 13_219_200
+    assert q.packed_bytes(q.WFMT_CB4, 16, 160) == 1440
+    assert q.packed_bytes(q.WFMT_CB4, 16, 100) == 0
+    assert q.packed_bytes(3, 16, 64) == 0
+    assert q.packed_bytes(q.WFMT_MXFP4, 0, 64) == 0
+
+
+FAKE = 0x10000  # a non-null, 256-aligned stand-in for device pointers (never dereferenced)
+
+
+def layer(**kw):
+    d = dict(hidden=256, inter=128, n_experts=8, top_k=2, wfmt=q.WFMT_CB4, has_shared=0,
+             router_w=FAKE, router_b=None, gate_up=FAKE, down=FAKE, codebook=FAKE, shared_gate_w=None)
+    d.update(kw)
+    return q.MoeLayerC(*[d[f] for f, _ in q.MoeLayerC._fields_])
+
+
+def ws_bytes(L, lay, T):
+    return L.moe_workspace_bytes(ctypes.byref(lay), T)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(hidden=100), q.MOE_ERR_INVALID_ARG), (dict(inter=0), q.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), q.MOE_ERR_UNSUPPORTED), (dict(top_k=0), q.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=2000, top_k=2), q.MOE_ERR_UNSUPPORTED), (dict(wfmt=7), q.MOE_ERR_INVALID_ARG),
+    (dict(codebook=None), q.MOE_ERR_INVALID_ARG), (dict(wfmt=q.WFMT_MXFP4), q.MOE_ERR_INVALID_ARG),
+    (dict(router_w=None), q.MOE_ERR_INVALID_ARG), (dict(gate_up=None), q.MOE_ERR_INVALID_ARG),
+    (dict(router_w=FAKE + 4), q.MOE_ERR_ALIGNMENT), (dict(has_shared=2), q.MOE_ERR_INVALID_ARG),
+    (dict(hidden=32768), q.MOE_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_bad_layers(L, bad, status):
+    lay = layer(**bad)
+    assert ws_bytes(L, lay, 4) == 0
+    r = L.moe_forward(ctypes.byref(lay), FAKE, q.DT_F32, 4, FAKE, FAKE, 1 << 30, None, 0,
+                      None, None, None, None, None)
+    assert r == status
+
+
+def test_forward_rejects_bad_calls(L):
+    lay = layer()
+    need = ws_bytes(L, lay, 4)
+    assert need > 0
+    f = lambda x=FAKE, dt=q.DT_F32, T=4, y=FAKE, ws=FAKE, n=need, path=0, ids=None: L.moe_forward(
+        ctypes.byref(lay), x, dt, T, y, ws, n, None, path, ids, None, None, None, None)
+    assert f(x=None) == q.MOE_ERR_INVALID_ARG
+    assert f(y=None) == q.MOE_ERR_INVALID_ARG
+    assert f(dt=5) == q.MOE_ERR_INVALID_ARG
+    assert f(T=-1) == q.MOE_ERR_INVALID_ARG
+    assert f(T=1 << 20) == q.MOE_ERR_UNSUPPORTED
+    assert f(path=9) == q.MOE_ERR_INVALID_ARG
+    assert f(x=FAKE + 8) == q.MOE_ERR_ALIGNMENT
+    assert f(ids=FAKE + 2) == q.MOE_ERR_ALIGNMENT
+    assert f(ws=None) == q.MOE_ERR_WORKSPACE
+    assert f(n=need - 1) == q.MOE_ERR_WORKSPACE
+    assert f(ws=FAKE + 16) == q.MOE_ERR_ALIGNMENT
+    assert f(T=0) == q.MOE_OK     # nothing is enqueued for zero tokens
+
+
+def test_router_and_bucket_validation(L):
+    lay = layer()
+    need = ws_bytes(L, lay, 3)
+    assert L.moe_router_topk(ctypes.byref(lay), FAKE, q.DT_BF16, 3, None, FAKE, FAKE, need, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_router_topk(ctypes.byref(lay), FAKE, q.DT_BF16, 3, FAKE, FAKE, FAKE, 8, None) == q.MOE_ERR_WORKSPACE
+    assert L.moe_router_topk(ctypes.byref(lay), FAKE, q.DT_BF16, 0, FAKE, FAKE, FAKE, need, None) == q.MOE_OK
+    assert L.moe_bucket(ctypes.byref(lay), FAKE, 3, FAKE, None, FAKE, FAKE, need, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_bucket(ctypes.byref(lay), FAKE + 1, 3, FAKE, FAKE, FAKE, FAKE, need, None) == q.MOE_ERR_ALIGNMENT
+    assert L.moe_bucket(ctypes.byref(lay), FAKE, 0, FAKE, FAKE, FAKE, FAKE, need, None) == q.MOE_OK
+
+
+def test_dequant_and_rescale_validation(L):
+    assert L.moe_dequant(q.WFMT_CB4, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_MXFP4, FAKE, None, 4, 48, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_MXFP4, FAKE + 4, None, 4, 64, FAKE, None) == q.MOE_ERR_ALIGNMENT
+    assert L.moe_dequant(9, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_rms_rescale(FAKE, 2, 0, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_rms_rescale(None, 2, 8, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_rms_rescale(FAKE, 0, 8, 1e-6, FAKE, None) == q.MOE_OK
+
+
+def test_status_strings(L):
+    for s in range(-5, 1):
+        assert q.status_str(s) not in ("", "unknown status")
+    assert q.status_str(-99) == "unknown status"
+
+
+def test_workspace_grows_with_tokens(L):
+    lay = layer()
+    assert ws_bytes(L, lay, 0) < ws_bytes(L, lay, 1) < ws_bytes(L, lay, 1024)

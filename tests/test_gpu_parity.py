@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import check_forward
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+q = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global q
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_mixture_experts_amd as qq
+    qq.lib()  # fails loudly when the library is not built
+    q = qq
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run(spec, layer=None, x=None, path=0):
+    layer = synth.make_layer(spec) if layer is None else layer
+    x = synth.make_x(spec) if x is None else x
+    dl = q.DeviceLayer.from_layer(layer)
+    y, dbg = q.forward(dl, _dev(x), spec.x_dtype, path=path, debug=True)
+    torch.cuda.synchronize()
+    return layer, x, dl, y, dbg
+
+
+# ---------------------------------------------------------------------------
+# dequantisation: bit-exact
+# ---------------------------------------------------------------------------
+def test_dequant_mxfp4_bit_exact_all_codes_and_scales():
+    rows, cols = 253, 64
+    rng = np.random.default_rng(1)
+    buf = np.zeros(q.packed_bytes(q.WFMT_MXFP4, rows, cols), dtype=np.uint8)
+    nc = rows * cols // 2
+    buf[:nc] = rng.integers(0, 256, nc, dtype=np.uint8)
+    # every row r uses E8M0 = r (0..252) for both of its blocks; all 256 byte values appear
+    buf[:256] = np.arange(256, dtype=np.uint8)
+    off = (nc + 255) // 256 * 256
+    buf[off:off + rows * 2] = np.repeat(np.arange(rows, dtype=np.uint8), 2)
+    out = q.dequant(q.WFMT_MXFP4, _dev(buf), rows, cols).cpu().numpy()
+    ref = oracle.dequant(oracle.WFMT_MXFP4, buf, None, rows, cols)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)  # exact in fp32
+    assert np.array_equal(out.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+def test_dequant_cb4_bit_exact_all_fp16_scales():
+    rows, cols = 2048, 32 * 32          # 65,536 blocks: one per fp16 pattern
+    cb = synth.make_codebook(77, 0)
+    rng = np.random.default_rng(2)
+    buf = np.zeros(q.packed_bytes(q.WFMT_CB4, rows, cols), dtype=np.uint8)
+    nc = rows * cols // 2
+    buf[:nc] = rng.integers(0, 256, nc, dtype=np.uint8)
+    off = (nc + 255) // 256 * 256
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 10) & 31) != 31
+    bits = np.where(finite, bits, 0x3C00).astype(np.uint16)
+    buf[off:off + 2 * 65536] = bits.view(np.uint8)
+    out = q.dequant(q.WFMT_CB4, _dev(buf), rows, cols, codebook=_dev(cb)).cpu().numpy()
+    ref = oracle.dequant(oracle.WFMT_CB4, buf, cb, rows, cols)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    assert np.array_equal(out.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# routing and bucketing: exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3"])
+def test_router_topk_matches_oracle(cfg):
+    spec = synth.CONFIGS[cfg]
+    layer = synth.make_layer(spec, experts=[])
+    x = synth.make_x(spec)
+    dl = q.DeviceLayer.from_layer(layer)
+    ids, w = q.router_topk(dl, _dev(x), spec.x_dtype)
+    torch.cuda.synchronize()
+    x64 = oracle.activations_f64(x, spec.x_dtype)
+    l = oracle.router_logits(x64, layer.router_w, layer.router_b)
+    ids_ref, g_ref = oracle.topk_softmax(l, spec.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - g_ref).max() <= 1e-6
+
+
+def test_router_exact_ties_go_to_lower_index():
+    spec = synth.small_spec("tie", 9, 256, 64, 40, 6, synth.WFMT_CB4, bias="none")
+    layer = synth.make_layer(spec, experts=[])
+    layer.router_w[17] = layer.router_w[3]
+    layer.router_w[33] = layer.router_w[3]
+    layer.router_w[9] = layer.router_w[30]
+    x = synth.make_x(spec)
+    dl = q.DeviceLayer.from_layer(layer)
+    ids, w = q.router_topk(dl, _dev(x), spec.x_dtype)
+    l = oracle.router_logits(oracle.activations_f64(x, spec.x_dtype), layer.router_w, None)
+    ids_ref, g_ref = oracle.topk_softmax(l, spec.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+
+
+@pytest.mark.parametrize("T,k,E,shared", [(1, 4, 128, 0), (17, 8, 256, 1), (1024, 8, 256, 1), (1024, 4, 128, 0),
+                                          (300, 3, 7, 1), (5, 16, 1024, 0)])
+def test_bucket_matches_oracle(T, k, E, shared):
+    rng = np.random.default_rng(T + k + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    spec = synth.small_spec("b", T, 64, 32, E, k, synth.WFMT_MXFP4, has_shared=shared)
+    layer = synth.make_layer(spec, experts=[])
+    dl = q.DeviceLayer.from_layer(layer)
+    counts, offsets, perm = q.bucket(dl, _dev(ids))
+    c, o, p, _ = oracle.bucket(ids, E, shared)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy(), p)
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3"])
+def test_forward_decode_configs(cfg):
+    spec = synth.CONFIGS[cfg]
+    layer, x, dl, y, dbg = _run(spec)
+    (err, tol), nex = check_forward(layer, x, spec.x_dtype, y, dbg, what=cfg)
+    print(f"{cfg}: max err {err:.3e} tol {tol:.3e} near-ties {nex}")
+
+
+SWEEP_T = [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+
+
+@pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
+@pytest.mark.parametrize("T", SWEEP_T)
+def test_forward_token_sweep(wfmt, T):
+    """Every tile threshold of the token dimension (16-row MFMA tiles, 4 tiles per pass),
+    with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4."""
+    H = 160 if wfmt == synth.WFMT_MXFP4 else 256
+    spec = synth.small_spec(f"sweep{T}", T, H, 96, 12, 3, wfmt, has_shared=1, x_dtype=synth.X_BF16,
+                            bias="normal", seed=100 + T)
+    layer, x, dl, y, dbg = _run(spec)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"T={T}")
+
+
+@pytest.mark.parametrize("xd", [synth.X_F32, synth.X_BF16])
+def test_forward_shared_gate_and_fp32_inputs(xd):
+    spec = synth.small_spec("sg", 21, 256, 64, 9, 2, synth.WFMT_CB4, has_shared=1, x_dtype=xd, bias="zipf")
+    layer = synth.make_layer(spec, shared_gate=True)
+    layer, x, dl, y, dbg = _run(spec, layer=layer)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what="shared gate")
+
+
+def test_forward_deterministic_and_batch_invariant():
+    spec = synth.CONFIGS["c3"]
+    layer, x, dl, y, dbg = _run(spec)
+    y2 = q.forward(dl, _dev(x), spec.x_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    # token 5 alone gives the same bits as inside the batch
+    y1 = q.forward(dl, _dev(x[5:6]), spec.x_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[0], y[5])
+
+
+def test_forward_zero_tokens_is_noop():
+    spec = synth.CONFIGS["c1"]
+    layer = synth.make_layer(spec)
+    dl = q.DeviceLayer.from_layer(layer)
+    x = torch.empty((0, spec.hidden), dtype=torch.float32, device="cuda")
+    y = q.forward(dl, x, spec.x_dtype)
+    assert y.shape == (0, spec.hidden)
+
+
+@pytest.mark.parametrize("cfg", ["c5a", "c5b"])
+def test_forward_prefill_full_size_sampled(cfg):
+    """T = 1024 at full shape: routing and bucketing compared in full, y on sampled tokens."""
+    spec = synth.CONFIGS[cfg]
+    layer, x, dl, y, dbg = _run(spec)
+    x64 = oracle.activations_f64(x, spec.x_dtype)
+    l = oracle.router_logits(x64, layer.router_w, layer.router_b)
+    ids_ref, g_ref = oracle.topk_softmax(l, spec.top_k)
+    ids_gpu = dbg["ids"].cpu().numpy()
+    assert np.array_equal(ids_gpu, ids_ref)
+    c, o, p, _ = oracle.bucket(ids_ref, spec.n_experts, spec.has_shared)
+    assert np.array_equal(dbg["counts"].cpu().numpy(), c)
+    assert np.array_equal(dbg["perm"].cpu().numpy(), p)
+    sample = np.array([0, 1, 255, 511, 512, 777, 1022, 1023])
+    ref = oracle.moe_forward(layer, x[sample], spec.x_dtype)
+    check_forward(layer, x, spec.x_dtype, y, dbg, ref=ref, tokens=sample, what=cfg)
+
+
+def test_rms_rescale_within_one_bf16_ulp():
+    rng = np.random.default_rng(4)
+    y = (rng.standard_normal((4, 2880)) * 1e3).astype(np.float32)
+    out = q.rms_rescale(_dev(y)).cpu().numpy().view(np.uint16)
+    ref = oracle.rms_rescale(y.astype(np.float64))
+    diff = np.abs(out.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1 and (diff == 0).mean() > 0.99
