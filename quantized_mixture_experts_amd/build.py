@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoeq.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "k_routing.hip", "k_experts.hip", "k_misc.hip"]
+SOURCES = ["api.hip", "k_routing.hip", "k_experts.hip", "k_decode.hip", "k_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fno-gpu-rdc",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,7 +28,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     r = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs],

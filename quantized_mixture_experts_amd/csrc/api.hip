@@ -41,7 +41,7 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, total;
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, total;
 };
 
 Layout layout_for(const moe_layer* L, int32_t T) {
@@ -60,6 +60,7 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.xplanes = take(3 * (size_t)T * H * 2);
   o.hplanes = take(2 * P * I * 2);
   o.o = take(P * H * 4);
+  o.tickets = take((H / 16) * 4);
   o.total = at;
   return o;
 }
@@ -77,6 +78,7 @@ Work carve(void* ws, const Layout& lo) {
   w.xplanes = reinterpret_cast<uint16_t*>(b + lo.xplanes);
   w.hplanes = reinterpret_cast<uint16_t*>(b + lo.hplanes);
   w.o = reinterpret_cast<float*>(b + lo.o);
+  w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
   return w;
 }
 
@@ -120,6 +122,11 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Work w = carve(ws, layout_for(L, T));
   const LayerArgs a = args_of(L);
+  const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype);
+  if (path == MOE_PATH_DECODE && !dec_ok) return MOE_ERR_UNSUPPORTED;
+  if (path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && dec_ok))
+    return hip_status(moeq::launch_decode(a, x, x_dtype, T, w, y, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm,
+                                          s, tm));
   hipError_t e = moeq::launch_router_topk(a, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
   if (e == hipSuccess)
     e = moeq::launch_bucket(T, a.k, a.E, a.has_shared, w.ids, w, dbg_counts, dbg_offsets, dbg_perm, s, tm);

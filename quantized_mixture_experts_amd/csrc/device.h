@@ -35,6 +35,7 @@ struct Work {
   uint16_t* xplanes;   // [3][T][H] bf16 planes of fp32 activations (x = p0 + p1 + p2)
   uint16_t* hplanes;   // [2][P][I] bf16 planes of the SwiGLU output (h ~= p0 + p1)
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
+  uint32_t* tickets;   // [H/16] arrival counters of the decode down/combine kernel
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

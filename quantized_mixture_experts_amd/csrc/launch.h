@@ -18,8 +18,16 @@ struct Timing {
   hipEvent_t stop(int s) const { return ev ? static_cast<hipEvent_t>(ev[2 * s + 1]) : nullptr; }
 };
 
-#define MOEQ_LAUNCH(tm, stage, kernel, grid, block, shmem, stream, ...) \
-  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm).start(stage), (tm).stop(stage), 0, __VA_ARGS__)
+// Plain launches when no events are requested (stream capture friendly); otherwise the
+// dispatch packet carries the stage's start/stop events.
+#define MOEQ_LAUNCH(tm, stage, kernel, grid, block, shmem, stream, ...)                                   \
+  do {                                                                                                    \
+    if ((tm).ev)                                                                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm).start(stage), (tm).stop(stage), 0,   \
+                            __VA_ARGS__);                                                                 \
+    else                                                                                                  \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                \
+  } while (0)
 
 hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
                               int32_t* dbg_ids, float* dbg_w, hipStream_t s,
@@ -29,6 +37,11 @@ hipError_t launch_bucket(int T, int k, int E, int has_shared, const int32_t* ids
                          const Timing& tm = Timing());
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
                           hipStream_t s, const Timing& tm = Timing());
+// Decode path (T <= 32 and the activation tiles fit in LDS).
+bool decode_path_fits(const LayerArgs& L, int T, int x_dtype);
+hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
+                         int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts, int32_t* dbg_offsets,
+                         int32_t* dbg_perm, hipStream_t s, const Timing& tm);
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,
                           float* out, hipStream_t s);
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* out, hipStream_t s);

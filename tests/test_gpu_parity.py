@@ -133,16 +133,41 @@ def test_forward_decode_configs(cfg):
 SWEEP_T = [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
 
 
+@pytest.mark.parametrize("path", [0, 2])
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T", SWEEP_T)
-def test_forward_token_sweep(wfmt, T):
+def test_forward_token_sweep(wfmt, T, path):
     """Every tile threshold of the token dimension (16-row MFMA tiles, 4 tiles per pass),
-    with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4."""
+    with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4.  path 0
+    picks the decode kernels up to 32 tokens; path 2 forces the grouped kernels."""
     H = 160 if wfmt == synth.WFMT_MXFP4 else 256
     spec = synth.small_spec(f"sweep{T}", T, H, 96, 12, 3, wfmt, has_shared=1, x_dtype=synth.X_BF16,
                             bias="normal", seed=100 + T)
-    layer, x, dl, y, dbg = _run(spec)
-    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"T={T}")
+    layer, x, dl, y, dbg = _run(spec, path=path)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"T={T} path={path}")
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3"])
+def test_decode_and_grouped_paths_agree(cfg):
+    """Both kernel paths on the same decode-sized inputs, each within tolerance of the oracle."""
+    spec = synth.CONFIGS[cfg]
+    layer = synth.make_layer(spec)
+    x = synth.make_x(spec)
+    dl = q.DeviceLayer.from_layer(layer)
+    ref = oracle.moe_forward(layer, x, spec.x_dtype)
+    for path in (1, 2):
+        y, dbg = q.forward(dl, _dev(x), spec.x_dtype, path=path, debug=True)
+        torch.cuda.synchronize()
+        check_forward(layer, x, spec.x_dtype, y, dbg, ref=ref, what=f"{cfg} path={path}")
+
+
+def test_decode_path_rejects_large_batches():
+    spec = synth.small_spec("big", 40, 64, 32, 4, 2, synth.WFMT_CB4)
+    layer = synth.make_layer(spec)
+    dl = q.DeviceLayer.from_layer(layer)
+    with pytest.raises(q.MoeError) as ei:
+        q.forward(dl, _dev(synth.make_x(spec)), spec.x_dtype, path=1)
+    assert ei.value.status == q.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("xd", [synth.X_F32, synth.X_BF16])
@@ -163,6 +188,30 @@ def test_forward_deterministic_and_batch_invariant():
     y1 = q.forward(dl, _dev(x[5:6]), spec.x_dtype)
     torch.cuda.synchronize()
     assert torch.equal(y1[0], y[5])
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3"])
+def test_graph_replay_matches_eager(cfg):
+    """The forward captured in a HIP graph: every replay, with eager work and syncs in
+    between, gives the eager result bit for bit."""
+    spec = synth.CONFIGS[cfg]
+    layer, x, dl, y_eager, _ = _run(spec)
+    xt = _dev(x)
+    ws = dl.workspace(spec.T)
+    y = torch.empty_like(y_eager)
+    q.forward(dl, xt, spec.x_dtype, y=y, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.forward(dl, xt, spec.x_dtype, y=y, ws=ws)
+    for r in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+        # eager work on the same workspace between replays
+        q.forward(dl, xt, spec.x_dtype, y=torch.empty_like(y), ws=ws)
+        torch.cuda.synchronize()
 
 
 def test_forward_zero_tokens_is_noop():
