@@ -41,7 +41,7 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, total;
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, wq, total;
 };
 
 Layout layout_for(const moe_layer* L, int32_t T) {
@@ -61,6 +61,8 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.hplanes = take(2 * P * I * 2);
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
+  o.slots = take((E + 2) * sizeof(moeq::Slot));
+  o.wq = take((E + 3) * 4);
   o.total = at;
   return o;
 }
@@ -79,6 +81,9 @@ Work carve(void* ws, const Layout& lo) {
   w.hplanes = reinterpret_cast<uint16_t*>(b + lo.hplanes);
   w.o = reinterpret_cast<float*>(b + lo.o);
   w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
+  w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
+  w.wq = reinterpret_cast<uint32_t*>(b + lo.wq);
+  w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
   return w;
 }
 

@@ -23,6 +23,8 @@ struct LayerArgs {
   const float* shared_gate_w;
 };
 
+struct Slot;
+
 // Per-call scratch carved out of the caller's workspace.
 struct Work {
   double* logits;      // [T][E + 1] (column E: shared-gate logit)
@@ -35,9 +37,22 @@ struct Work {
   uint16_t* xplanes;   // [3][T][H] bf16 planes of fp32 activations (x = p0 + p1 + p2)
   uint16_t* hplanes;   // [2][P][I] bf16 planes of the SwiGLU output (h ~= p0 + p1)
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
-  uint32_t* tickets;   // [H/16] arrival counters of the decode down/combine kernel
+  uint32_t* tickets;   // [H/16] arrival counters of the decode combine
+  uint32_t* wq;        // [1 + E + 1] decode work queue: next item, then finished gate/up tiles per slot
+  float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)
+  struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
 };
 
+// One active expert of a decode call: everything a projection block needs, in one
+// 128-byte record (scalar loads).  cnt == 0 marks an unused slot.  rows[] holds the
+// first kSlotRows pair ids of the expert's bucket (the rest are read from perm).
+constexpr int kSlotRows = 24;
+struct __align__(128) Slot {
+  int32_t e, cnt, off, n_active;
+  const uint8_t* gate_up;
+  const uint8_t* down;
+  int32_t rows[kSlotRows];
+};
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // IEEE fp16 bits -> fp32 (exact, subnormals included).
@@ -49,22 +64,82 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---- cross-lane helpers on DPP row rotations (a few cycles each) plus readlane ----
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = dpp_i32<CTRL>((int)(b & 0xFFFFFFFFll));
+  const int hi = dpp_i32<CTRL>((int)(b >> 32));
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+constexpr int kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+
+// Sum over the 64 lanes, returned to every lane; fixed association order.
 __device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppRowRor1>(v);
+  v += dpp_f64<kDppRowRor2>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppRowRor8>(v);  // every lane of a 16-lane row holds the row sum
+  return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+
+// (value, index) maximum over the wave: larger value first, lower index on ties;
+// index 0x7FFFFFFF marks an empty candidate.  Returned to every lane.
+__device__ __forceinline__ bool argmax_better(double ov, int oi, double bv, int bi) {
+  return oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& bv, int& bi) {
+  const double ov = dpp_f64<CTRL>(bv);
+  const int oi = dpp_i32<CTRL>(bi);
+  if (argmax_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+__device__ __forceinline__ void wave_argmax(double& bv, int& bi) {
+  argmax_step<kDppRowRor1>(bv, bi);
+  argmax_step<kDppRowRor2>(bv, bi);
+  argmax_step<kDppRowRor4>(bv, bi);
+  argmax_step<kDppRowRor8>(bv, bi);
+  double v = readlane_f64(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  for (int r = 16; r < 64; r += 16) {
+    const double ov = readlane_f64(bv, r);
+    const int oi = __builtin_amdgcn_readlane(bi, r);
+    if (argmax_better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+  bv = v;
+  bi = i;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += __builtin_bit_cast(float, dpp_i32<kDppRowRor1>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i32<kDppRowRor2>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i32<kDppRowRor4>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i32<kDppRowRor8>(__builtin_bit_cast(int, v)));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_i32<kDppRowRor1>(v);
+  v += dpp_i32<kDppRowRor2>(v);
+  v += dpp_i32<kDppRowRor4>(v);
+  v += dpp_i32<kDppRowRor8>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
 }
 
 // E8M0 byte -> fp32 2^(u-127) (u = 0 gives the subnormal 2^-127).

@@ -20,7 +20,15 @@
 
 namespace moeq {
 
-constexpr int kDecKSW = 6;         // k-steps (of 128 columns) per wave per k-chunk
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of this wave are outstanding, leaving the other counters alone.
+constexpr int waitcnt_vm_le(int n) {
+  return (n > 63 ? 63 : n) & 15 | (7 << 4) | (15 << 8) | (((n > 63 ? 63 : n) >> 4) << 14);
+}
+// vector-memory instructions one prefetch_step issues per 16-row tile
+template <int FMT>
+constexpr int loads_per_step() { return FMT == 1 ? 2 : 8; }
 constexpr int kDecMaxTokens = 32;  // two 16-slot MFMA token tiles
 
 __device__ __forceinline__ int dec_token_of_pair(int p, int T, int k) { return p < T * k ? p / k : p - T * k; }
@@ -41,10 +49,10 @@ __global__ __launch_bounds__(256) void k_dec_router(LayerArgs L, const void* __r
                                                     double* __restrict__ logits, uint16_t* __restrict__ xplanes,
                                                     uint32_t* __restrict__ tickets, int ntickets) {
   __shared__ double part[4][kDecMaxTokens];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.x;
   const int H = L.H;
-  if (e == 0) {
+  if (e == 0) {  // arrival counters of this call's combine
     for (int i = threadIdx.x; i < ntickets; i += 256) tickets[i] = 0u;
   }
   if (XDT == 0 && e == 0) {
@@ -61,38 +69,58 @@ __global__ __launch_bounds__(256) void k_dec_router(LayerArgs L, const void* __r
     }
   }
   const float* w = (e < L.E) ? L.router_w + (size_t)e * H : L.shared_gate_w;
-  // wave `wave` owns float4 columns c = wave*64 + lane + 256*i
+  // thread owns float4 columns c = threadIdx.x + 256 i; tokens in tiles of 8, with all
+  // of a tile's loads issued before its fp64 products
   constexpr int kMaxPer = 16;  // H <= 16384
+  constexpr int kTT = 8;
   const int nf4 = H / 4;
   float4 wv[kMaxPer];
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
-    const int c = wave * 64 + lane + 256 * i;
+    const int c = threadIdx.x + 256 * i;
     wv[i] = (c < nf4) ? *(const float4*)(w + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int t = 0; t < T; ++t) {
-    double acc = 0.0;
+  for (int t0 = 0; t0 < T; t0 += kTT) {
+    double acc[kTT];
+#pragma unroll
+    for (int u = 0; u < kTT; ++u) acc[u] = 0.0;
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
-      const int c = wave * 64 + lane + 256 * i;
+      const int c = threadIdx.x + 256 * i;
       if (c < nf4) {
-        float x0, x1, x2, x3;
-        if (XDT == 0) {
-          const float4 xv = *(const float4*)((const float*)x + (size_t)t * H + 4 * c);
-          x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
-        } else {
-          const uint2 xb = *(const uint2*)((const uint16_t*)x + (size_t)t * H + 4 * c);
-          x0 = bf16_bits_to_f32(xb.x & 0xFFFFu); x1 = bf16_bits_to_f32(xb.x >> 16);
-          x2 = bf16_bits_to_f32(xb.y & 0xFFFFu); x3 = bf16_bits_to_f32(xb.y >> 16);
+        float xv[kTT][4];
+#pragma unroll
+        for (int u = 0; u < kTT; ++u) {
+          const int t = t0 + u;
+          if (t < T) {
+            if (XDT == 0) {
+              const float4 q = *(const float4*)((const float*)x + (size_t)t * H + 4 * c);
+              xv[u][0] = q.x; xv[u][1] = q.y; xv[u][2] = q.z; xv[u][3] = q.w;
+            } else {
+              const uint2 q = *(const uint2*)((const uint16_t*)x + (size_t)t * H + 4 * c);
+              xv[u][0] = bf16_bits_to_f32(q.x & 0xFFFFu); xv[u][1] = bf16_bits_to_f32(q.x >> 16);
+              xv[u][2] = bf16_bits_to_f32(q.y & 0xFFFFu); xv[u][3] = bf16_bits_to_f32(q.y >> 16);
+            }
+          } else {
+            xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
+          }
         }
-        acc = fma((double)wv[i].x, (double)x0, acc);
-        acc = fma((double)wv[i].y, (double)x1, acc);
-        acc = fma((double)wv[i].z, (double)x2, acc);
-        acc = fma((double)wv[i].w, (double)x3, acc);
+#pragma unroll
+        for (int u = 0; u < kTT; ++u) {
+          double a = acc[u];
+          a = fma((double)wv[i].x, (double)xv[u][0], a);
+          a = fma((double)wv[i].y, (double)xv[u][1], a);
+          a = fma((double)wv[i].z, (double)xv[u][2], a);
+          a = fma((double)wv[i].w, (double)xv[u][3], a);
+          acc[u] = a;
+        }
       }
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) part[wave][t] = acc;
+#pragma unroll
+    for (int u = 0; u < kTT; ++u) {
+      const double sum = wave_sum_f64(acc[u]);
+      if (lane == 0 && t0 + u < T) part[wave][t0 + u] = sum;
+    }
   }
   __syncthreads();
   if (threadIdx.x < T) {
@@ -111,11 +139,65 @@ __global__ __launch_bounds__(256) void k_dec_router(LayerArgs L, const void* __r
 //    (count, non-empty flag), then each pair's stable rank among earlier pairs of
 //    the same expert.
 // ---------------------------------------------------------------------------
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
+// Best remaining candidate of this lane: largest logit, lowest expert on ties.
+__device__ __forceinline__ void lane_best(const double (&v)[16], uint32_t taken, int nper, int E, double& bv,
+                                          int& bi) {
+  const int lane = threadIdx.x & 63;
+  bv = -__builtin_inf();
+  bi = 0x7FFFFFFF;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = (i < nper) & (lane + 64 * i < E) & !((taken >> i) & 1u);
+    const bool better = ok & ((bi == 0x7FFFFFFF) | (v[i] > bv));
+    bv = better ? v[i] : bv;
+    bi = better ? lane + 64 * i : bi;
+  }
+}
+
+// top-k of one token held as candidate logits v[i] of expert lane + 64 i (i < nper);
+// experts >= E hold -inf.  Each round: DPP max of the lanes' best values, a ballot of
+// the lanes holding it (exact ties resolved to the lowest expert index), and only the
+// winning lane rescans its candidates.
+__device__ __forceinline__ void topk_token(const double (&v)[16], int nper, int E, int k, int t, int* s_exp,
+                                           double* s_l) {
+  const int lane = threadIdx.x & 63;
+  uint32_t taken = 0;
+  double bv;
+  int bi;
+  lane_best(v, taken, nper, E, bv, bi);
+  for (int j = 0; j < k; ++j) {
+    // wave maximum of bv (empty lanes hold -inf)
+    double m = bv;
+    m = fmax(m, dpp_f64<kDppRowRor1>(m));
+    m = fmax(m, dpp_f64<kDppRowRor2>(m));
+    m = fmax(m, dpp_f64<kDppRowRor4>(m));
+    m = fmax(m, dpp_f64<kDppRowRor8>(m));
+    m = fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
+    uint64_t hold = __ballot(bi != 0x7FFFFFFF && bv == m);
+    int win;
+    if (__popcll(hold) == 1) {
+      win = __builtin_amdgcn_readlane(bi, (int)__ffsll((long long)hold) - 1);
+    } else {  // exact tie between lanes: the lowest expert index wins
+      win = 0x7FFFFFFF;
+      while (hold) {
+        const int l = (int)__ffsll((long long)hold) - 1;
+        hold &= hold - 1;
+        win = min(win, __builtin_amdgcn_readlane(bi, l));
+      }
+    }
+    if (lane == 0) { s_exp[t * k + j] = win; s_l[t * k + j] = m; }
+    if ((win & 63) == lane) {
+      taken |= 1u << (win >> 6);
+      lane_best(v, taken, nper, E, bv, bi);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T, const double* __restrict__ logits,
-                                                             Work w, int32_t* __restrict__ dbg_ids,
+                                                             Work w, int max_slots, int32_t* __restrict__ dbg_ids,
                                                              float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
                                                              int32_t* __restrict__ dbg_offsets,
                                                              int32_t* __restrict__ dbg_perm) {
@@ -123,77 +205,79 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
+  __shared__ const uint8_t* s_gu[1024 + 1];
+  __shared__ const uint8_t* s_dn[1024 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kRouteThreads / 64;
   const int E = L.E, k = L.k;
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  for (int i = tid; i <= E; i += kRouteThreads) s_cnt[i] = 0;
-
-  for (int t = wave; t < T; t += kRouteThreads / 64) {
-    const double* lt = logits + (size_t)t * (E + 1);
-    double v[16];
+  const int nb = E + 1;
+  // expert pointer tables and zeroed counts (independent of the logits)
+  for (int i = tid; i < nb; i += kRouteThreads) {
+    s_cnt[i] = 0;
+    const bool ok = i < E || L.has_shared;
+    s_gu[i] = ok ? L.gate_up[i] : nullptr;
+    s_dn[i] = ok ? L.down[i] : nullptr;
+  }
+  // top-k: wave w takes tokens w and w + 16 (T <= 32); both tokens' logits load first
+  {
+    const int t0 = wave, t1 = wave + kWaves;
+    const int nper = (E + 63) >> 6;
+    double v0[16], v1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + 64 * i;
-      v[i] = (e < E) ? lt[e] : 0.0;
+      v0[i] = (i < nper && t0 < T && e < E) ? logits[(size_t)t0 * (E + 1) + e] : -__builtin_inf();
+      v1[i] = (i < nper && t1 < T && e < E) ? logits[(size_t)t1 * (E + 1) + e] : -__builtin_inf();
     }
-    uint32_t taken = 0;
-    for (int j = 0; j < k; ++j) {
-      double bv = 0.0;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; bi = e; }
+    if (t0 < T) topk_token(v0, nper, E, k, t0, s_exp, s_l);
+    if (t1 < T) topk_token(v1, nper, E, k, t1, s_exp, s_l);
+    for (int t = t0; t < T && t <= t1; t += kWaves) {
+      const double* lt = logits + (size_t)t * (E + 1);
+      const double l0 = s_l[t * k];
+      const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
+      const double zs = wave_sum_f64(z);
+      if (lane < k) {
+        const int p = t * k + lane;
+        const float gte = (float)(z / zs);
+        const int id = s_exp[p];
+        w.ids[p] = id;
+        w.pair_w[p] = gte;
+        if (dbg_ids) dbg_ids[p] = id;
+        if (dbg_w) dbg_w[p] = gte;
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const double ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+      if (L.has_shared && lane == 0) {
+        w.pair_w[Pr + t] = L.shared_gate_w ? (float)(1.0 / (1.0 + exp(-lt[E]))) : 1.0f;
+        s_exp[Pr + t] = E;
       }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { s_exp[t * k + j] = bi; s_l[t * k + j] = bv; }
-    }
-    // gates: lane j < k
-    const double l0 = s_l[t * k];
-    const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
-    const double zs = wave_sum_f64(z);
-    if (lane < k) {
-      const int p = t * k + lane;
-      const float gte = (float)(z / zs);
-      const int id = s_exp[p];
-      w.ids[p] = id;
-      w.pair_w[p] = gte;
-      if (dbg_ids) dbg_ids[p] = id;
-      if (dbg_w) dbg_w[p] = gte;
-    }
-    if (L.has_shared && lane == 0) {
-      w.pair_w[Pr + t] = L.shared_gate_w ? (float)(1.0 / (1.0 + exp(-lt[E]))) : 1.0f;
-      s_exp[Pr + t] = E;
     }
   }
   __syncthreads();
   for (int p = tid; p < P; p += kRouteThreads) atomicAdd(&s_cnt[s_exp[p]], 1);
   __syncthreads();
-  const int nb = E + 1;
   if (wave == 0) {
     int carry = 0;
     for (int base = 0; base < nb; base += 64) {
       const int i = base + lane;
       const int c = i < nb ? s_cnt[i] : 0;
       int x = c | ((c > 0 ? 1 : 0) << 16);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
+      // inclusive scan: DPP row shifts inside 16-lane rows, then the row totals
+      x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+      x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+      x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+      x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+      const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+      const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+      const int row = lane >> 4;
+      x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
       x += carry;
       if (i < nb) s_incl[i] = x;
-      carry = __shfl(x, 63, kWave);
+      carry += r0 + r1 + r2 + r3;
     }
   }
   __syncthreads();
+  const int n_active = s_incl[nb - 1] >> 16;
   for (int e = tid; e < nb; e += kRouteThreads) {
     const int c = s_cnt[e];
     const int off = (s_incl[e] & 0xFFFF) - c;
@@ -201,12 +285,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
     w.offsets[e] = off;
     if (dbg_counts) dbg_counts[e] = c;
     if (dbg_offsets) dbg_offsets[e] = off;
-    if (c > 0) w.active[1 + (s_incl[e] >> 16) - 1] = e;
+    if (c > 0) {
+      const int a = (s_incl[e] >> 16) - 1;
+      w.active[1 + a] = e;
+      Slot& sl = w.slots[a];
+      sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
+      sl.gate_up = s_gu[e];
+      sl.down = s_dn[e];
+    }
+  }
+  for (int a = n_active + tid; a < max_slots; a += kRouteThreads) {
+    Slot& sl = w.slots[a];
+    sl.e = 0; sl.cnt = 0; sl.off = 0; sl.n_active = n_active;
+    sl.gate_up = nullptr;
+    sl.down = nullptr;
   }
   if (tid == 0) {
     w.offsets[nb] = P;
     if (dbg_offsets) dbg_offsets[nb] = P;
-    w.active[0] = s_incl[nb - 1] >> 16;
+    w.active[0] = n_active;
   }
   for (int p = tid; p < P; p += kRouteThreads) {
     const int e = s_exp[p];
@@ -215,6 +312,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
     const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
     w.perm[pos] = p;
     if (dbg_perm) dbg_perm[pos] = p;
+    if (r < kSlotRows) w.slots[(s_incl[e] >> 16) - 1].rows[r] = p;
   }
 }
 
@@ -230,66 +328,85 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
 //        supplies x[32(4ks+j) + 8g ..]; the fp16 scale multiplies the block's
 //        fp32 MFMA result (scale * codebook value is not exact in bf16).
 // ---------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int KSW>
 struct WeightRegs;
 
-template <>
-struct WeightRegs<1> {
-  u32x4_t c[kDecKSW];
-  uint32_t s[kDecKSW];
+template <int KSW>
+struct WeightRegs<1, KSW> {
+  u32x4_t c[KSW];
+  uint32_t s[KSW];
 };
-template <>
-struct WeightRegs<2> {
-  uint32_t c[kDecKSW][4];
-  uint32_t s[kDecKSW][2];  // 4 fp16 scales of blocks 4ks..4ks+3
+template <int KSW>
+struct WeightRegs<2, KSW> {
+  uint32_t c[KSW][4];
+  uint32_t s[KSW][4];  // fp16 scale bits of blocks 4ks..4ks+3
 };
 
-template <int FMT>
-__device__ __forceinline__ void prefetch_weights(WeightRegs<FMT>& r, const uint8_t* codes_row,
-                                                 const uint8_t* scales_row, int nkb, int ks0, int nks, int g) {
-#pragma unroll
-  for (int i = 0; i < kDecKSW; ++i) {
+// Loads of one wave's k-steps ks0, ks0+4, ... of one 16-row weight tile.  Straight-line
+// code with clamped addresses and no use of the loaded values here, so each k-step's
+// MFMAs wait only for their own loads.  Out-of-range data is never used: k-steps past
+// the row are skipped and k blocks past the row meet a zero activation operand.
+template <int FMT, int KSW>
+__device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, const uint8_t* codes_row,
+                                              const uint8_t* scales_row, int nkb, int ks0, int nks, int g) {
+  {
     const int ks = ks0 + 4 * i;
     if constexpr (FMT == 1) {
       const int kb = 4 * ks + g;
-      const bool v = ks < nks && kb < nkb;
-      r.c[i] = v ? __builtin_nontemporal_load((const u32x4_t*)(codes_row + (size_t)kb * 16)) : u32x4_t{0, 0, 0, 0};
-      r.s[i] = v ? scales_row[kb] : 127u;
+      const int kbc = (ks < nks && kb < nkb) ? kb : 0;
+      r.c[i] = __builtin_nontemporal_load((const u32x4_t*)(codes_row + (size_t)kbc * 16));
+      r.s[i] = scales_row[kbc];
     } else {
+      const int ksc = ks < nks ? ks : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int kb = 4 * ks + j;
-        const bool v = ks < nks && kb < nkb;
-        r.c[i][j] = v ? __builtin_nontemporal_load((const uint32_t*)(codes_row + (size_t)kb * 16 + 4 * g)) : 0u;
+        const int kbc = min(4 * ksc + j, nkb - 1);
+        r.c[i][j] = __builtin_nontemporal_load((const uint32_t*)(codes_row + (size_t)kbc * 16 + 4 * g));
       }
       const uint16_t* sp = (const uint16_t*)scales_row;
-      uint32_t s01 = 0, s23 = 0;
-      if (ks < nks) {
-        const int kb = 4 * ks;
-        const uint32_t a = sp[kb];
-        const uint32_t b = (kb + 1 < nkb) ? sp[kb + 1] : 0u;
-        const uint32_t c = (kb + 2 < nkb) ? sp[kb + 2] : 0u;
-        const uint32_t d = (kb + 3 < nkb) ? sp[kb + 3] : 0u;
-        s01 = a | (b << 16);
-        s23 = c | (d << 16);
-      }
-      r.s[i][0] = s01;
-      r.s[i][1] = s23;
+      const int kb = 4 * ksc;
+      r.s[i][0] = sp[kb];
+      r.s[i][1] = sp[min(kb + 1, nkb - 1)];
+      r.s[i][2] = sp[min(kb + 2, nkb - 1)];
+      r.s[i][3] = sp[min(kb + 3, nkb - 1)];
     }
   }
 }
 
+template <int FMT, int KSW>
+__device__ __forceinline__ void prefetch_weights(WeightRegs<FMT, KSW>& r, const uint8_t* codes_row,
+                                                 const uint8_t* scales_row, int nkb, int ks0, int nks, int g) {
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) prefetch_step<FMT, KSW>(r, i, codes_row, scales_row, nkb, ks0, nks, g);
+}
+
+// Two tiles (gate and up rows) k-step by k-step, so a k-step's MFMAs of both tiles
+// depend only on that step's loads.
+template <int FMT, int KSW>
+__device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, const uint8_t* ca, const uint8_t* sa,
+                                                  WeightRegs<FMT, KSW>& rb, const uint8_t* cb, const uint8_t* sbp,
+                                                  int nkb, int ks0, int nks, int g) {
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) {
+    prefetch_step<FMT, KSW>(ra, i, ca, sa, nkb, ks0, nks, g);
+    prefetch_step<FMT, KSW>(rb, i, cb, sbp, nkb, ks0, nks, g);
+  }
+}
+
 // acc[tt] += A(token tile tt, planes) x B(weights of k-step i) for one weight matrix.
-// xrows = activation rows staged in LDS; A is zero for slots >= xrows and for k >= K.
-template <int FMT, int NP, int NTT>
-__device__ __forceinline__ void mma_kstep(const WeightRegs<FMT>& r, int i, int ks, int nkb, const uint16_t* xs,
-                                          int xstride, size_t plane_stride, int live, int xrows,
+// xrows = activation rows staged in LDS.  Branch-free: the activation operand is zero
+// for slots >= xrows, for k-steps past the row (ks >= nks) and for 32-blocks past it,
+// so those MFMAs add exact zeros (the weights they meet are clamped real blocks).
+template <int FMT, int NP, int NTT, int KSW>
+__device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, int ks, int nks, int nkb,
+                                          const uint16_t* xs, int xstride, size_t plane_stride, int live, int xrows,
                                           const uint32_t* lut, f32x4_t (&acc)[NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
+  const bool ksv = ks < nks;
   if constexpr (FMT == 1) {
     const float sc = e8m0_to_f32(r.s[i]);
-    const bool kval = 4 * ks + g < nkb;
+    const bool kval = ksv && (4 * ks + g < nkb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8_t b = fp4x8_to_bf16(r.c[i][j], sc);
@@ -301,7 +418,7 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT>& r, int i, int k
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
             u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
-            if (!ok) av = u32x4_t{0, 0, 0, 0};
+            av = ok ? av : u32x4_t{0, 0, 0, 0};
             acc[tt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, acc[tt]);
           }
         }
@@ -310,25 +427,23 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT>& r, int i, int k
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (4 * ks + j < nkb) {
-        const bf16x8_t b = cb4x8_to_bf16(r.c[i][j], lut);
-        const uint32_t sbits = (r.s[i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        const float sc = half_bits_to_f32((uint16_t)sbits);
+      const bool kval = ksv && (4 * ks + j < nkb);
+      const bf16x8_t b = cb4x8_to_bf16(r.c[i][j], lut);
+      const float sc = half_bits_to_f32((uint16_t)r.s[i][j]);
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          if (tt < live) {
-            const bool ok = 16 * tt + m < xrows;
-            const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + 128 * ks + 32 * j + 8 * g;
-            f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < NTT; ++tt) {
+        if (tt < live) {
+          const bool ok = kval && (16 * tt + m < xrows);
+          const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + (ok ? 128 * ks + 32 * j + 8 * g : 0);
+          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-              u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
-              if (!ok) av = u32x4_t{0, 0, 0, 0};
-              tmp = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, tmp);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(sc, tmp[q], acc[tt][q]);
+          for (int p = 0; p < NP; ++p) {
+            u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
+            av = ok ? av : u32x4_t{0, 0, 0, 0};
+            tmp = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, tmp);
           }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(sc, tmp[q], acc[tt][q]);
         }
       }
     }
@@ -356,12 +471,55 @@ __device__ __forceinline__ void stage_rows(uint16_t* xs, int xstride, size_t lds
   }
 }
 
+// The 4 waves copy the activation rows of slots tb .. tb+nrows-1 of this expert into
+// LDS with direct global->LDS loads (64 lanes x 16 bytes per instruction, no
+// registers).  Issued before the weight loads, they complete first in each wave's
+// in-order load counter, so waiting for them leaves the weights in flight.  Pair ids
+// come from the slot record (scalar) or, past its first rows, from perm.
+// Direct global->LDS copy of 16 bytes per lane to LDS address lds + 16 * lane (the
+// LDS base is wave-uniform).  Issued as inline assembly so that the compiler does not
+// track it: the caller waits for it explicitly (s_waitcnt vmcnt) before a barrier,
+// while later loads stay in flight.
+__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds) {
+  const uint32_t lds_addr =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr),
+               "v"((const __attribute__((address_space(1))) void*)gptr)
+               : "memory");
+}
+
+template <int NP, bool BY_TOKEN>
+__device__ __forceinline__ void stage_rows_lds(uint16_t* xs, int xstride, size_t lds_plane, const uint16_t* src,
+                                               size_t src_plane, int K, const Slot* __restrict__ slot_rec,
+                                               const int32_t* __restrict__ perm_e, int tb, int nrows, int T, int k) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_bytes = K * 2;
+  const int nchunk = (row_bytes + 1023) >> 10;  // 1 KB per instruction
+  // lane s holds the source row of slot tb + s (one load for all rows of the pass)
+  int myrow = 0;
+  {
+    const int slot = tb + lane;
+    const int pair = lane < nrows ? (slot < kSlotRows ? slot_rec->rows[slot] : perm_e[slot]) : 0;
+    myrow = BY_TOKEN ? dec_token_of_pair(pair, T, k) : pair;
+  }
+  const int jobs = nrows * nchunk * NP;
+  for (int job = wave; job < jobs; job += 4) {  // wave-uniform
+    const int q = job % NP;
+    const int rc = job / NP;
+    const int srow = rc / nchunk, ch = rc % nchunk;
+    const int r = __builtin_amdgcn_readlane(myrow, srow);
+    const uint8_t* g = (const uint8_t*)(src + q * src_plane + (size_t)r * K) + 1024 * ch + 16 * lane;
+    uint8_t* d = (uint8_t*)(xs + q * lds_plane + (size_t)srow * xstride) + 1024 * ch;
+    if (1024 * ch + 16 * lane < row_bytes) load_lds_16(g, d);
+  }
+}
+
 // Sum the 4 waves' partial tiles (split-K) in wave order into wave 0.
 template <int NV>
 __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   __syncthreads();
-  if (wave > 0) {
+  if (wave > 0 && wave < 4) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) red[((wave - 1) * NV + i) * 64 + lane] = v[i];
   }
@@ -376,17 +534,21 @@ __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
 
 // ---------------------------------------------------------------------------
 // 3. Fused gate/up + SwiGLU.  grid = (I/16, max active slots), 4 waves split K.
-// dynamic LDS: [NP][slots][xstride] bf16 activations, then the CB4 table.
+//    Each wave first issues direct-to-LDS loads of its share of the expert's
+//    activation rows, then all its weight loads; it waits only for the former before
+//    the staging barrier, and each k-step's MFMAs then wait only for that step's
+//    weights while the rest are still in flight.
+// dynamic LDS: 1 KB CB4 table, then [NP][xrows][xstride] bf16 activations (reused by
+// the split-K reduction).
 // ---------------------------------------------------------------------------
-template <int FMT, int NP, int NTT>
+template <int FMT, int NP, int NTT, int KSW>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                    size_t act_plane, int xrows_max) {
+                                                       size_t act_plane, int xrows_max) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int a = blockIdx.y;
-  if (a >= w.active[0]) return;
-  const int e = w.active[1 + a];
-  const int cnt = w.counts[e], off = w.offsets[e];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Slot* slot_rec = w.slots + blockIdx.y;
+  const int cnt = slot_rec->cnt, off = slot_rec->off;
+  if (cnt == 0) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
   const int K = H, nkb = K >> 5, nks = (nkb + 3) >> 2;
@@ -395,41 +557,41 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-
-  const uint8_t* base = L.gate_up[e];
+  const uint8_t* base = slot_rec->gate_up;
   const size_t scale_off = ((size_t)2 * I * K / 2 + 255) / 256 * 256;
   const int rg = 16 * blockIdx.x + n, ru = I + rg;
   const int sb = FMT == 1 ? 1 : 2;
-
-  // k-chunks of 4 waves x kDecKSW k-steps; weights of a chunk are prefetched first
-  const int nchunks = (nks + 4 * kDecKSW - 1) / (4 * kDecKSW);
-  f32x4_t accg[NTT], accu[NTT];
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) { accg[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accu[tt] = accg[tt]; }
+  const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += nslots) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
+    f32x4_t accg[NTT], accu[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) { accg[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accu[tt] = accg[tt]; }
     for (int ch = 0; ch < nchunks; ++ch) {
-      WeightRegs<FMT> wg, wu;
-      const int ks0 = ch * 4 * kDecKSW + wave;
-      prefetch_weights<FMT>(wg, base + (size_t)rg * (K / 2), base + scale_off + (size_t)rg * nkb * sb, nkb, ks0,
-                            nks, g);
-      prefetch_weights<FMT>(wu, base + (size_t)ru * (K / 2), base + scale_off + (size_t)ru * nkb * sb, nkb, ks0,
-                            nks, g);
+      const int ks0 = ch * 4 * KSW + wave;
       if (ch == 0) {
-        __syncthreads();  // the previous pass finished with the LDS tile
-        if (FMT == 2 && tb == 0) build_cb4_lut(lut, L.codebook);
-        stage_rows<NP, true>(xs, xstride, lds_plane, act, act_plane, K, w.perm + off + tb, xrows, T, k);
-        __syncthreads();
+        if (tb > 0) __syncthreads();  // the previous pass finished with the LDS tile
+        else if (FMT == 2) build_cb4_lut(lut, L.codebook);
+        stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, slot_rec, w.perm + off, tb, xrows, T,
+                                 k);
+      }
+      WeightRegs<FMT, KSW> wg, wu;
+      prefetch_weights2<FMT, KSW>(wg, base + (size_t)rg * (K / 2), base + scale_off + (size_t)rg * nkb * sb, wu,
+                             base + (size_t)ru * (K / 2), base + scale_off + (size_t)ru * nkb * sb, nkb, ks0, nks,
+                             g);
+      if (ch == 0) {
+        // this wave's staging loads are complete once at most the weight loads issued
+        // after them are outstanding; then every wave's rows are in LDS after the barrier
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(2 * KSW * loads_per_step<FMT>()));
+        __builtin_amdgcn_s_barrier();
       }
 #pragma unroll
-      for (int i = 0; i < kDecKSW; ++i) {
+      for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        if (ks < nks) {
-          mma_kstep<FMT, NP, NTT>(wg, i, ks, nkb, xs, xstride, lds_plane, live, xrows, lut, accg);
-          mma_kstep<FMT, NP, NTT>(wu, i, ks, nkb, xs, xstride, lds_plane, live, xrows, lut, accu);
-        }
+        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, accg);
+        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, accu);
       }
     }
     // split-K reduction (fixed wave order), SwiGLU, two bf16 planes of h
@@ -458,27 +620,25 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
         }
       }
     }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) { accg[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accu[tt] = accg[tt]; }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 4. Down projection + combine.  grid = (H/16, max active slots), 4 waves split K=I.
-// Each block writes o_p[16 cols] for its expert's pairs; the last block to arrive
-// at a column tile computes y[t][tile] for every token in a fixed order.
+// Each block writes o_p[16 cols] for its expert's pairs; the last block to arrive at
+// a column tile computes y[t][tile] for every token in a fixed order.  The o values
+// travel as write-through stores and a relaxed device-scope ticket counts arrivals,
+// so no full L2 write-back is needed.
 // ---------------------------------------------------------------------------
-template <int FMT, int NTT>
+template <int FMT, int NTT, int KSW>
 __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
-                                                  uint32_t* __restrict__ tickets, int xrows_max) {
+                                                     uint32_t* __restrict__ tickets, int xrows_max) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int is_last;
-  const int a = blockIdx.y;
-  const int n_active = w.active[0];
-  if (a >= n_active) return;
-  const int e = w.active[1 + a];
-  const int cnt = w.counts[e], off = w.offsets[e];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Slot* slot_rec = w.slots + blockIdx.y;
+  const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
+  if (cnt == 0) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
   const int P = T * k + (L.has_shared ? T : 0);
@@ -488,34 +648,37 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-
-  const uint8_t* base = L.down[e];
+  const uint8_t* base = slot_rec->down;
   const size_t scale_off = ((size_t)H * K / 2 + 255) / 256 * 256;
   const int r = 16 * blockIdx.x + n;
   const int sb = FMT == 1 ? 1 : 2;
-  const int nchunks = (nks + 4 * kDecKSW - 1) / (4 * kDecKSW);
-  f32x4_t acc[NTT];
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += nslots) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int ch = 0; ch < nchunks; ++ch) {
-      WeightRegs<FMT> wd;
-      const int ks0 = ch * 4 * kDecKSW + wave;
-      prefetch_weights<FMT>(wd, base + (size_t)r * (K / 2), base + scale_off + (size_t)r * nkb * sb, nkb, ks0, nks,
+      const int ks0 = ch * 4 * KSW + wave;
+      if (ch == 0) {
+        if (tb > 0) __syncthreads();
+        else if (FMT == 2) build_cb4_lut(lut, L.codebook);
+        stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb,
+                                 xrows, T, k);
+      }
+      WeightRegs<FMT, KSW> wd;
+      prefetch_weights<FMT, KSW>(wd, base + (size_t)r * (K / 2), base + scale_off + (size_t)r * nkb * sb, nkb, ks0, nks,
                             g);
       if (ch == 0) {
-        __syncthreads();
-        if (FMT == 2 && tb == 0) build_cb4_lut(lut, L.codebook);
-        stage_rows<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, w.perm + off + tb, xrows, T, k);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
+        __builtin_amdgcn_s_barrier();
       }
 #pragma unroll
-      for (int i = 0; i < kDecKSW; ++i) {
+      for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        if (ks < nks) mma_kstep<FMT, 2, NTT>(wd, i, ks, nkb, xs, xstride, lds_plane, live, xrows, lut, acc);
+        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, acc);
       }
     }
     float v[4 * NTT];
@@ -531,20 +694,13 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int slot = tb + 16 * tt + 4 * g + q;
-          // write-through store (device coherence point), read back by the tile's last block
           if (slot < cnt)
             __hip_atomic_store(&w.o[(size_t)w.perm[off + slot] * H + col], v[4 * tt + q], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Arrival at this column tile; the last of the n_active blocks combines it.  The o
-  // values were stored write-through (scope agent); waiting for their completion
-  // before the ticket makes them visible to the last block's coherent loads, without
-  // a full L2 write-back.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -581,23 +737,52 @@ static size_t dec_lds_bytes(int K, int NP, int NTT, int xrows) {
   return 1024 + (x > red ? x : red);
 }
 
+// k-steps per wave: the smallest supported count that covers a quarter of the row's
+// 128-column steps (longer rows loop over chunks of 8).
+static int pick_ksw(int K) {
+  const int nks = (K / 32 + 3) / 4;
+  const int per = (nks + 3) / 4;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
+}
+
+template <int FMT, int NTT, int KSW>
+static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
+                            hipStream_t s, const Timing& tm) {
+  const dim3 g1(L.I / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
+  if (x_dtype == 1)
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 1, NTT, xrows),
+                s, L, T, w, (const uint16_t*)x, (size_t)0, xrows);
+  else
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 3, NTT, xrows),
+                s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows);
+}
+
+template <int FMT, int NTT, int KSW>
+static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
+                          hipStream_t s, const Timing& tm) {
+  const dim3 g2(L.H / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
+  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW>), g2, dim3(256), dec_lds_bytes(L.I, 2, NTT, xrows), s, L,
+              T, w, y, tickets, xrows);
+}
+
 template <int FMT, int NTT>
 static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
                                      uint32_t* tickets, hipStream_t s, const Timing& tm) {
-  const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const dim3 g1(L.I / 16, max_slots), g2(L.H / 16, max_slots);
   const int xrows = min(T, 16 * NTT);  // an expert holds at most T pairs
-  if (x_dtype == 1) {
-    const size_t lds = dec_lds_bytes(L.H, 1, NTT, xrows);
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT>), g1, dim3(256), lds, s, L, T, w,
-                (const uint16_t*)x, (size_t)0, xrows);
-  } else {
-    const size_t lds = dec_lds_bytes(L.H, 3, NTT, xrows);
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT>), g1, dim3(256), lds, s, L, T, w,
-                (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows);
+  switch (pick_ksw(L.H)) {
+    case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, s, tm); break;
+    case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, s, tm); break;
+    case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, s, tm); break;
+    case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, s, tm); break;
+    default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, s, tm); break;
   }
-  const size_t lds2 = dec_lds_bytes(L.I, 2, NTT, xrows);
-  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT>), g2, dim3(256), lds2, s, L, T, w, y, tickets, xrows);
+  switch (pick_ksw(L.I)) {
+    case 1: launch_down_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm); break;
+    case 2: launch_down_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, s, tm); break;
+    case 4: launch_down_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, s, tm); break;
+    case 6: launch_down_k<FMT, NTT, 6>(L, T, w, y, tickets, xrows, s, tm); break;
+    default: launch_down_k<FMT, NTT, 8>(L, T, w, y, tickets, xrows, s, tm); break;
+  }
   return hipGetLastError();
 }
 
@@ -620,8 +805,9 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   else
     MOEQ_LAUNCH(tm, kStageRouter, k_dec_router<1>, dim3(erows), dim3(256), 0, s, L, x, T, erows, w.logits,
                 w.xplanes, w.tickets, ntickets);
+  const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
   MOEQ_LAUNCH(tm, kStageTopk, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, (const double*)w.logits, w,
-              dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+              max_slots, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (T <= 16)

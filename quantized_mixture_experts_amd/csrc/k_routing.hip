@@ -128,13 +128,7 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
       }
     }
     // wave argmax with the same order
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool better = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-      if (better) { bv = ov; bi = oi; }
-    }
+    wave_argmax(bv, bi);
     lsel[j] = bv;
     isel[j] = bi;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
