@@ -37,8 +37,10 @@ Where the pages leave a step open the plainest reading is taken:
   n-gram table paragraph: 16 rows of 160 values take 1,440 bytes in IQ4_NL);
   the 16-entry int8 codebook is an input (a seeded sorted table stands in for
   the real IQ4_NL table, which the pages do not list);
-* nibble order: low nibble = even element; code plane then scale plane per
-  matrix; gate_up = [gate rows; up rows] concatenated;
+* nibble order: low nibble = even element; per matrix a code plane then a
+  scale plane, each stored tile-major (16-row tiles, 4-block steps; see
+  storage_index) so that one 16-row step of codes is one contiguous 1 KB unit;
+  gate_up = [gate rows; up rows] concatenated;
 * activation = SwiGLU, h = silu(gate) * up, silu(a) = a / (1 + exp(-a));
 * top-k order = descending logit, ties to the lower expert index; gates =
   softmax over the k kept logits; a router bias is added to the logit;
@@ -107,12 +109,31 @@ def bf16_value(bits):
 
 def packed_size(wfmt: int, rows: int, cols: int) -> int:
     """Bytes of one packed matrix: code plane, padded to 256 bytes, then the scale plane."""
-    if cols % 32:
-        raise ValueError("cols must be a multiple of 32")
+    if cols % 32 or rows % 16:
+        raise ValueError("rows must be a multiple of 16 and cols a multiple of 32")
     code_bytes = rows * cols // 2
     scale_off = (code_bytes + 255) // 256 * 256
     nblocks = rows * cols // 32
     return scale_off + nblocks * (1 if wfmt == WFMT_MXFP4 else 2)
+
+
+def storage_index(wfmt: int, rows: int, cols: int):
+    """Where the tile-major storage keeps each block (row, b), b < cols/32:
+    (byte offset of its 16 code bytes, index of its scale in the scale plane).
+    Rows form tiles of 16 and a row's blocks form steps of 4 (the last step may hold
+    r < 4 blocks).  Tile t, step s is one 1,024-byte code unit at t*8*cols + 1024*s,
+    block g of the step for row m at (16g + m)*16 inside it; its scales are one unit at
+    index t*16*nblk + 64*s, MXFP4 ordered (g, m) -> 16g + m, CB4 ordered (m, g) -> m*r + g."""
+    nkb = cols // 32
+    row = np.arange(rows)[:, None]
+    b = np.arange(nkb)[None, :]
+    t, m = row // 16, row % 16
+    st, g = b // 4, b % 4
+    r = np.minimum(4, nkb - 4 * st)
+    code_off = t * 8 * cols + 1024 * st + (16 * g + m) * 16
+    unit = t * 16 * nkb + 64 * st
+    scale_idx = unit + (16 * g + m if wfmt == WFMT_MXFP4 else m * r + g)
+    return code_off, scale_idx
 
 
 def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np.ndarray:
@@ -121,20 +142,22 @@ def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np
     code_bytes = rows * cols // 2
     scale_off = (code_bytes + 255) // 256 * 256
     nblocks = rows * cols // 32
-    codes = packed[:code_bytes].astype(np.int64)
-    nib = np.empty(rows * cols, dtype=np.int64)
-    nib[0::2] = codes & 0xF       # element 2j: low nibble of byte j
-    nib[1::2] = codes >> 4        # element 2j+1: high nibble
+    code_off, scale_idx = storage_index(wfmt, rows, cols)
+    # the 16 code bytes of every block, in block order: [rows][cols/32][16]
+    blk = packed[code_off[:, :, None] + np.arange(16)[None, None, :]].astype(np.int64)
+    nib = np.empty((rows, cols // 32, 32), dtype=np.int64)
+    nib[:, :, 0::2] = blk & 0xF   # element 2j: low nibble of byte j
+    nib[:, :, 1::2] = blk >> 4    # element 2j+1: high nibble
     if wfmt == WFMT_MXFP4:
-        scales = e8m0_value(packed[scale_off:scale_off + nblocks])
+        scales = e8m0_value(packed[scale_off:scale_off + nblocks][scale_idx])
         vals = e2m1_value(nib)
     elif wfmt == WFMT_CB4:
-        sbits = packed[scale_off:scale_off + 2 * nblocks].view("<u2")
+        sbits = packed[scale_off:scale_off + 2 * nblocks].view("<u2")[scale_idx]
         scales = fp16_value(sbits)
         vals = np.asarray(codebook, dtype=np.int64)[nib].astype(np.float64)
     else:
         raise ValueError("unknown weight format")
-    w = vals.reshape(rows, cols // 32, 32) * scales.reshape(rows, cols // 32, 1)
+    w = vals * scales[:, :, None]
     return w.reshape(rows, cols)
 
 

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoeq.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "k_routing.hip", "k_experts.hip", "k_decode.hip", "k_misc.hip"]
+SOURCES = ["api.hip", "k_routing.hip", "k_prefill.hip", "k_decode.hip", "k_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fno-gpu-rdc",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

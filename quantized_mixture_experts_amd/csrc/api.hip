@@ -41,7 +41,8 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, wq, total;
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, wq, groups,
+      n_groups, total;
 };
 
 Layout layout_for(const moe_layer* L, int32_t T) {
@@ -63,6 +64,8 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
   o.wq = take((E + 3) * 4);
+  o.groups = take((size_t)moeq::max_groups((int)P, (int)E) * 16);
+  o.n_groups = take(4);
   o.total = at;
   return o;
 }
@@ -84,6 +87,8 @@ Work carve(void* ws, const Layout& lo) {
   w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
   w.wq = reinterpret_cast<uint32_t*>(b + lo.wq);
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
+  w.groups = reinterpret_cast<int4*>(b + lo.groups);
+  w.n_groups = reinterpret_cast<int32_t*>(b + lo.n_groups);
   return w;
 }
 
@@ -144,7 +149,7 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
 extern "C" {
 
 size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols) {
-  if (rows <= 0 || cols <= 0 || cols % 32) return 0;
+  if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return 0;
   if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return 0;
   const size_t code = (size_t)rows * cols / 2;
   const size_t nblk = (size_t)rows * cols / 32;
@@ -205,7 +210,7 @@ int moe_forward_timed(const moe_layer* L, const void* x, int32_t x_dtype, int32_
 int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,
                 void* stream) {
   if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return MOE_ERR_INVALID_ARG;
-  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return MOE_ERR_INVALID_ARG;
   if ((size_t)rows * (size_t)cols > ((size_t)1 << 34)) return MOE_ERR_UNSUPPORTED;
   if (!packed || !out) return MOE_ERR_INVALID_ARG;
   if (wfmt == MOE_WFMT_CB4 && !codebook) return MOE_ERR_INVALID_ARG;

@@ -12,6 +12,40 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
+// Global-memory views of pointers that come from memory (expert tables, slot records):
+// loads through them compile to global_load (vector memory only) instead of flat_load,
+// whose completion also counts against the LDS counter and forces full waits.
+typedef const __attribute__((address_space(1))) uint8_t gbyte_t;
+__device__ __forceinline__ gbyte_t* as_global(const void* p) { return (gbyte_t*)p; }
+
+// ---- packed storage of one matrix [N][K] (N % 16 == 0, K % 32 == 0), tile-major ----
+// Rows form tiles of 16 and a row's nkb = K/32 blocks form steps of 4 (the last step may
+// hold r = nkb - 4s < 4 blocks).  Code unit (tile t, step s) starts at byte t*8K + 1024s
+// and holds block g of the step for row m at (16g + m)*16, so the 64 lanes of a load with
+// lane = 16g + m read one contiguous kilobyte.  The scale plane starts at
+// round_up(N*K/2, 256); scale unit (t, s) starts at index t*16*nkb + 64s and holds MXFP4
+// (g, m) at 16g + m, CB4 (m, g) at m*r + g (fp16, so 8 contiguous bytes per row and step).
+// Keeping a 16-row step contiguous lets DRAM serve it from one open page.
+struct PackedTile {
+  gbyte_t* codes;   // code unit (t, 0)
+  gbyte_t* scales;  // scale unit (t, 0), bytes
+};
+__device__ __forceinline__ PackedTile packed_tile(const void* base, int N, int K, int t, int scale_bytes) {
+  const size_t soff = ((size_t)N * K / 2 + 255) / 256 * 256;
+  gbyte_t* b = as_global(base);
+  return {b + (size_t)t * 8 * K, b + soff + (size_t)t * 16 * (K / 32) * scale_bytes};
+}
+// block kb (< nkb) of row m of a tile: byte offset of its 16 code bytes in the tile
+__device__ __forceinline__ uint32_t pk_code(int kb, int m) {
+  return (uint32_t)(kb >> 2) * 1024u + (uint32_t)(((kb & 3) * 16 + m) * 16);
+}
+// its scale's index within the tile's scales (MXFP4 bytes / CB4 fp16 entries)
+__device__ __forceinline__ uint32_t pk_scale_mx(int kb, int m) { return (uint32_t)(kb >> 2) * 64u + (kb & 3) * 16 + m; }
+__device__ __forceinline__ uint32_t pk_scale_cb(int kb, int m, int nkb) {
+  const int s = kb >> 2, r = min(4, nkb - 4 * s);
+  return (uint32_t)s * 64u + (uint32_t)(m * r + (kb & 3));
+}
+
 // Layer descriptor as the kernels see it (copied by value into kernel arguments).
 struct LayerArgs {
   int H, I, E, k, wfmt, has_shared;
@@ -41,7 +75,15 @@ struct Work {
   uint32_t* wq;        // [1 + E + 1] decode work queue: next item, then finished gate/up tiles per slot
   float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)
   struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
+  int4* groups;        // prefill work groups: (expert, first bucket position, pairs <= 64, 0)
+  int32_t* n_groups;   // [1] number of valid entries of groups
 };
+
+// Pairs per prefill work group (four 16-row MFMA token tiles).
+constexpr int kGroupPairs = 64;
+// Upper bound of the number of prefill groups: every non-empty bucket adds at most one
+// partial group to the P / kGroupPairs full ones.
+__host__ __device__ inline int max_groups(int P, int E) { return P / kGroupPairs + E + 2; }
 
 // One active expert of a decode call: everything a projection block needs, in one
 // 128-byte record (scalar loads).  cnt == 0 marks an unused slot.  rows[] holds the

@@ -347,49 +347,46 @@ struct WeightRegs<2, KSW> {
 // MFMAs wait only for their own loads.  Out-of-range data is never used: k-steps past
 // the row are skipped and k blocks past the row meet a zero activation operand.
 template <int FMT, int KSW>
-__device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, const uint8_t* codes_row,
-                                              const uint8_t* scales_row, int nkb, int ks0, int nks, int g) {
+__device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, const PackedTile& pt, int nkb, int ks0,
+                                              int nks, int m, int g) {
   {
     const int ks = ks0 + 4 * i;
     if constexpr (FMT == 1) {
       const int kb = 4 * ks + g;
       const int kbc = (ks < nks && kb < nkb) ? kb : 0;
-      r.c[i] = __builtin_nontemporal_load((const u32x4_t*)(codes_row + (size_t)kbc * 16));
-      r.s[i] = scales_row[kbc];
+      r.c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(pt.codes +
+                                                                                             pk_code(kbc, m)));
+      r.s[i] = pt.scales[pk_scale_mx(kbc, m)];
     } else {
       const int ksc = ks < nks ? ks : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kbc = min(4 * ksc + j, nkb - 1);
-        r.c[i][j] = __builtin_nontemporal_load((const uint32_t*)(codes_row + (size_t)kbc * 16 + 4 * g));
+        r.c[i][j] = __builtin_nontemporal_load(
+            (const __attribute__((address_space(1))) uint32_t*)(pt.codes + pk_code(kbc, m) + 4 * g));
+        r.s[i][j] = *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + 2 * pk_scale_cb(kbc, m, nkb));
       }
-      const uint16_t* sp = (const uint16_t*)scales_row;
-      const int kb = 4 * ksc;
-      r.s[i][0] = sp[kb];
-      r.s[i][1] = sp[min(kb + 1, nkb - 1)];
-      r.s[i][2] = sp[min(kb + 2, nkb - 1)];
-      r.s[i][3] = sp[min(kb + 3, nkb - 1)];
     }
   }
 }
 
 template <int FMT, int KSW>
-__device__ __forceinline__ void prefetch_weights(WeightRegs<FMT, KSW>& r, const uint8_t* codes_row,
-                                                 const uint8_t* scales_row, int nkb, int ks0, int nks, int g) {
+__device__ __forceinline__ void prefetch_weights(WeightRegs<FMT, KSW>& r, const PackedTile& pt, int nkb, int ks0,
+                                                 int nks, int m, int g) {
 #pragma unroll
-  for (int i = 0; i < KSW; ++i) prefetch_step<FMT, KSW>(r, i, codes_row, scales_row, nkb, ks0, nks, g);
+  for (int i = 0; i < KSW; ++i) prefetch_step<FMT, KSW>(r, i, pt, nkb, ks0, nks, m, g);
 }
 
 // Two tiles (gate and up rows) k-step by k-step, so a k-step's MFMAs of both tiles
 // depend only on that step's loads.
 template <int FMT, int KSW>
-__device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, const uint8_t* ca, const uint8_t* sa,
-                                                  WeightRegs<FMT, KSW>& rb, const uint8_t* cb, const uint8_t* sbp,
-                                                  int nkb, int ks0, int nks, int g) {
+__device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, const PackedTile& pa,
+                                                  WeightRegs<FMT, KSW>& rb, const PackedTile& pb, int nkb, int ks0,
+                                                  int nks, int m, int g) {
 #pragma unroll
   for (int i = 0; i < KSW; ++i) {
-    prefetch_step<FMT, KSW>(ra, i, ca, sa, nkb, ks0, nks, g);
-    prefetch_step<FMT, KSW>(rb, i, cb, sbp, nkb, ks0, nks, g);
+    prefetch_step<FMT, KSW>(ra, i, pa, nkb, ks0, nks, m, g);
+    prefetch_step<FMT, KSW>(rb, i, pb, nkb, ks0, nks, m, g);
   }
 }
 
@@ -557,10 +554,8 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-  const uint8_t* base = slot_rec->gate_up;
-  const size_t scale_off = ((size_t)2 * I * K / 2 + 255) / 256 * 256;
-  const int rg = 16 * blockIdx.x + n, ru = I + rg;
-  const int sb = FMT == 1 ? 1 : 2;
+  const PackedTile pg = packed_tile(slot_rec->gate_up, 2 * I, K, blockIdx.x, FMT == 1 ? 1 : 2);
+  const PackedTile pu = packed_tile(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x, FMT == 1 ? 1 : 2);
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += nslots) {
@@ -578,9 +573,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
                                  k);
       }
       WeightRegs<FMT, KSW> wg, wu;
-      prefetch_weights2<FMT, KSW>(wg, base + (size_t)rg * (K / 2), base + scale_off + (size_t)rg * nkb * sb, wu,
-                             base + (size_t)ru * (K / 2), base + scale_off + (size_t)ru * nkb * sb, nkb, ks0, nks,
-                             g);
+      prefetch_weights2<FMT, KSW>(wg, pg, wu, pu, nkb, ks0, nks, n, g);
       if (ch == 0) {
         // this wave's staging loads are complete once at most the weight loads issued
         // after them are outstanding; then every wave's rows are in LDS after the barrier
@@ -648,10 +641,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-  const uint8_t* base = slot_rec->down;
-  const size_t scale_off = ((size_t)H * K / 2 + 255) / 256 * 256;
-  const int r = 16 * blockIdx.x + n;
-  const int sb = FMT == 1 ? 1 : 2;
+  const PackedTile pd = packed_tile(slot_rec->down, H, K, blockIdx.x, FMT == 1 ? 1 : 2);
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += nslots) {
@@ -669,8 +659,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
                                  xrows, T, k);
       }
       WeightRegs<FMT, KSW> wd;
-      prefetch_weights<FMT, KSW>(wd, base + (size_t)r * (K / 2), base + scale_off + (size_t)r * nkb * sb, nkb, ks0, nks,
-                            g);
+      prefetch_weights<FMT, KSW>(wd, pd, nkb, ks0, nks, n, g);
       if (ch == 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
         __builtin_amdgcn_s_barrier();

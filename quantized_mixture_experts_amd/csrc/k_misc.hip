@@ -5,7 +5,7 @@
 
 namespace moeq {
 
-// One thread per 32-value block: out[row][32kb .. 32kb+31].
+// One thread per 32-value block (row, kb): out[row][32kb .. 32kb+31].
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed, const int8_t* __restrict__ codebook,
                                                  int rows, int cols, float* __restrict__ out) {
@@ -17,11 +17,13 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   const int nkb = cols >> 5;
   const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (blk >= (size_t)rows * nkb) return;
-  const size_t scale_off = ((size_t)rows * cols / 2 + 255) / 256 * 256;
-  const u32x4_t c = *(const u32x4_t*)(packed + blk * 16);
+  const int row = (int)(blk / nkb), kb = (int)(blk % nkb);
+  const int m = row & 15;
+  const PackedTile pt = packed_tile(packed, rows, cols, row >> 4, FMT == 1 ? 1 : 2);
+  const u32x4_t c = *(const __attribute__((address_space(1))) u32x4_t*)(pt.codes + pk_code(kb, m));
   float* dst = out + blk * 32;
   if (FMT == 1) {
-    const float s = e8m0_to_f32(packed[scale_off + blk]);
+    const float s = e8m0_to_f32(pt.scales[pk_scale_mx(kb, m)]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bf16x8_t v = fp4x8_to_bf16(c[q], s);
@@ -29,7 +31,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
       for (int i = 0; i < 8; ++i) dst[8 * q + i] = (float)v[i];
     }
   } else {
-    const uint16_t sb = *(const uint16_t*)(packed + scale_off + 2 * blk);
+    const uint16_t sb =
+        *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + 2 * pk_scale_cb(kb, m, nkb));
     const float s = half_bits_to_f32(sb);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

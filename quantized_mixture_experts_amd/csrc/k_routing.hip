@@ -153,61 +153,70 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
 
 // ---------------------------------------------------------------------------
 // Bucketing.  One block per bucket e in [0, E]; bucket E is the shared expert.
-//   offsets[e] = #{p : id_p < e} (order-independent count), counts[e] = #{p : id_p = e}
-//   perm[offsets[e] + r] = the r-th pair (increasing p) with id_p = e (ballot compaction)
-//   active[0] = number of non-empty buckets, active[1 + a] = a-th non-empty bucket.
-// Every block scans the (small) id list itself, so no grid-wide scan or atomics on
-// the order are needed, and the result is deterministic.
+// Every block builds the full histogram of the routed ids in LDS, so each one knows
+//   counts[e] = #{p : id_p = e}, offsets[e] = #{p : id_p < e},
+//   its rank among the non-empty buckets (the active list), and
+//   its first prefill work group (groups of up to kGroupPairs consecutive bucket
+//   positions of one expert, numbered in bucket order),
+// with no grid-wide scan.  perm[offsets[e] + r] = the r-th pair (increasing p) with
+// id_p = e, by ballot compaction.  The result is deterministic.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_shared,
                                                 const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                int32_t* __restrict__ active, int32_t* __restrict__ dbg_counts,
+                                                int32_t* __restrict__ active, int4* __restrict__ groups,
+                                                int32_t* __restrict__ n_groups, int32_t* __restrict__ dbg_counts,
                                                 int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
-  __shared__ uint32_t present[32];
-  __shared__ int red_lt[4], red_eq[4];
+  __shared__ int hist[1024];
+  __shared__ int red[5][4];
   __shared__ int wave_tot[4];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Pr = T * k;
-  if (tid < 32) present[tid] = 0u;
+  for (int i = tid; i < E; i += 256) hist[i] = 0;
   __syncthreads();
-  int lt = 0, eq = 0;
   for (int p = tid; p < Pr; p += 256) {
     const int id = ids[p];
-    lt += id < e;
-    eq += id == e;
-    if (id >= 0 && id < E) atomicOr(&present[id >> 5], 1u << (id & 31));
+    if (id >= 0 && id < E) atomicAdd(&hist[id], 1);
   }
-  lt = wave_sum_i32(lt);
-  eq = wave_sum_i32(eq);
-  if (lane == 0) { red_lt[wave] = lt; red_eq[wave] = eq; }
   __syncthreads();
-  lt = red_lt[0] + red_lt[1] + red_lt[2] + red_lt[3];
-  eq = red_eq[0] + red_eq[1] + red_eq[2] + red_eq[3];
-  // rank of e among non-empty routed buckets, and their total
-  int below = 0, total = 0;
-  for (int w = 0; w < 32; ++w) {
-    const uint32_t bits = present[w];
-    total += __popc(bits);
-    if (w * 32 + 31 < e) below += __popc(bits);
-    else if (w * 32 < e) below += __popc(bits & ((1u << (e - w * 32)) - 1u));
+  // pairs, non-empty buckets and groups below e; non-empty buckets and groups overall
+  int v[5] = {0, 0, 0, 0, 0};
+  for (int i = tid; i < E; i += 256) {
+    const int c = hist[i], ng = (c + kGroupPairs - 1) / kGroupPairs;
+    if (i < e) { v[0] += c; v[1] += c > 0; v[2] += ng; }
+    v[3] += c > 0;
+    v[4] += ng;
   }
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int r = wave_sum_i32(v[q]);
+    if (lane == 0) red[q][wave] = r;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 5; ++q) v[q] = red[q][0] + red[q][1] + red[q][2] + red[q][3];
+  const int lt = v[0], below = v[1], g_below = v[2], total = v[3], g_total = v[4];
   if (e == E) {
     const int cnt = has_shared ? T : 0;
+    const int ngs = (cnt + kGroupPairs - 1) / kGroupPairs;
     if (tid == 0) {
       counts[E] = cnt; offsets[E] = Pr; offsets[E + 1] = Pr + cnt;
       active[0] = total + (cnt > 0);
       if (cnt > 0) active[1 + total] = E;
+      *n_groups = g_total + ngs;
       if (dbg_counts) dbg_counts[E] = cnt;
       if (dbg_offsets) { dbg_offsets[E] = Pr; dbg_offsets[E + 1] = Pr + cnt; }
     }
+    for (int i = tid; i < ngs; i += 256)
+      groups[g_total + i] = make_int4(E, Pr + kGroupPairs * i, min(kGroupPairs, cnt - kGroupPairs * i), 0);
     for (int t = tid; t < cnt; t += 256) {
       perm[Pr + t] = Pr + t;
       if (dbg_perm) dbg_perm[Pr + t] = Pr + t;
     }
     return;
   }
+  const int eq = hist[e];
   if (tid == 0) {
     counts[e] = eq; offsets[e] = lt;
     if (eq > 0) active[1 + below] = e;
@@ -215,6 +224,9 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
     if (dbg_offsets) dbg_offsets[e] = lt;
   }
   if (eq == 0) return;
+  const int ng = (eq + kGroupPairs - 1) / kGroupPairs;
+  for (int i = tid; i < ng; i += 256)
+    groups[g_below + i] = make_int4(e, lt + kGroupPairs * i, min(kGroupPairs, eq - kGroupPairs * i), 0);
   int running = 0;
   for (int base = 0; base < Pr; base += 256) {
     const int p = base + tid;
@@ -255,7 +267,7 @@ hipError_t launch_bucket(int T, int k, int E, int has_shared, const int32_t* ids
                          int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s,
                          const Timing& tm) {
   MOEQ_LAUNCH(tm, kStageBucket, k_bucket, dim3(E + 1), dim3(256), 0, s, T, k, E, has_shared, ids, w.counts,
-              w.offsets, w.perm, w.active, dbg_counts, dbg_offsets, dbg_perm);
+              w.offsets, w.perm, w.active, w.groups, w.n_groups, dbg_counts, dbg_offsets, dbg_perm);
   return hipGetLastError();
 }
 

@@ -5,14 +5,21 @@ layout; it computes none of the layer's arithmetic (no decoding, routing,
 projection or combine).  Both the CPU oracle (through the tests) and the GPU
 library (through the tests and the benchmark) consume what it produces.
 
-Packed storage of one quantised matrix with N rows and K columns (K a multiple
-of 32), blocks of 32 consecutive values along a row:
+Packed storage of one quantised matrix with N rows (a multiple of 16) and K
+columns (a multiple of 32), blocks of 32 consecutive values along a row; byte j
+of a block's 16 code bytes holds element 2j in its low nibble and element 2j+1
+in its high nibble.  The storage is tile-major: rows go in tiles of 16, a row's
+blocks in steps of 4 (the last step of a row may hold fewer, r = nkb - 4s).
 
-* code plane: N*K/2 bytes, row-major; byte j of a 16-byte block holds element
-  2j in its low nibble and element 2j+1 in its high nibble;
-* scale plane: starts at round_up(N*K/2, 256); N*K/32 scales, row-major, one
-  per block: an E8M0 byte for MXFP4, the little-endian IEEE fp16 bits for the
-  4-bit codebook format (CB4).
+* code plane: tile t, step s is one unit at byte t*8K + s*1024 holding, for
+  block g < r of the step and row m < 16 of the tile, the block's 16 code
+  bytes at (16g + m)*16 inside the unit;
+* scale plane: starts at round_up(N*K/2, 256); tile t, step s is one unit at
+  scale index t*16*nkb + 64*s; inside it MXFP4 keeps the E8M0 byte of (block g,
+  row m) at 16g + m and CB4 keeps the little-endian fp16 bits of (row m, block
+  g) at m*r + g (units of two bytes).
+
+The total size equals the row-major size (N*K/2 code bytes + N*K/32 scales).
 
 Shapes follow the pages' models: gpt-oss-120B (hidden 2880, 128 experts,
 top-4, 36 layers; "Neural Server" page, "What it runs on and what it runs")
@@ -99,22 +106,46 @@ class LayerSpec:
     seed: int = 0
 
 
+def to_tile_major(code_rows: np.ndarray, scale_rows: np.ndarray, wfmt: int) -> np.ndarray:
+    """Arrange row-major code bytes [N][K/2] and scales [N][K/32] (uint8 E8M0 or uint16
+    fp16 bits) into the packed tile-major storage described in the module docstring."""
+    N, half = code_rows.shape
+    nkb = half // 16
+    assert N % 16 == 0 and scale_rows.shape == (N, nkb)
+    T = N // 16
+    codes = code_rows.reshape(T, 16, nkb, 16)                   # tile, row m, block, byte
+    code_units, scale_units = [], []
+    for s in range(0, nkb, 4):
+        r = min(4, nkb - s)
+        code_units.append(codes[:, :, s:s + r, :].transpose(0, 2, 1, 3).reshape(T, r * 256))
+        sc = scale_rows.reshape(T, 16, nkb)[:, :, s:s + r]       # tile, row m, block g
+        if wfmt == WFMT_MXFP4:
+            scale_units.append(sc.transpose(0, 2, 1).reshape(T, r * 16))
+        else:
+            scale_units.append(sc.reshape(T, 16 * r))
+    code_plane = np.concatenate(code_units, axis=1).reshape(-1)
+    scale_plane = np.concatenate(scale_units, axis=1).reshape(-1)
+    out = np.zeros(packed_nbytes(wfmt, N, nkb * 32), dtype=np.uint8)
+    out[:code_plane.size] = code_plane
+    off = scale_plane_offset(N, nkb * 32)
+    sb = scale_plane.astype(np.uint8 if wfmt == WFMT_MXFP4 else np.dtype("<u2")).view(np.uint8)
+    out[off:off + sb.size] = sb
+    return out
+
+
 def make_packed(spec: WeightSpec, rows: int, cols: int, seed_key: Sequence[int],
                 codes_tid: int, scales_tid: int) -> np.ndarray:
-    """One packed matrix [rows][cols] in the layout described in the module docstring."""
-    assert cols % 32 == 0
+    """One packed matrix [rows][cols].  The code bytes (row-major, both nibbles uniform) and
+    the scales (row-major) are drawn first, then stored tile-major."""
+    assert cols % 32 == 0 and rows % 16 == 0
     nblk = rows * cols // 32
-    out = np.zeros(packed_nbytes(spec.wfmt, rows, cols), dtype=np.uint8)
-    ncode = rows * cols // 2
-    out[:ncode] = random_bytes(_rng(*seed_key, codes_tid), ncode)
-    off = scale_plane_offset(rows, cols)
+    code_rows = random_bytes(_rng(*seed_key, codes_tid), rows * cols // 2).reshape(rows, cols // 2)
     srng = _rng(*seed_key, scales_tid)
     if spec.wfmt == WFMT_MXFP4:
-        out[off:off + nblk] = srng.integers(spec.e8m0_lo, spec.e8m0_hi + 1, size=nblk, dtype=np.uint8)
+        sc = srng.integers(spec.e8m0_lo, spec.e8m0_hi + 1, size=nblk, dtype=np.uint8)
     else:
-        s = srng.uniform(spec.scale_lo, spec.scale_hi, size=nblk).astype(np.float16)
-        out[off:off + 2 * nblk] = s.view(np.uint8)
-    return out
+        sc = srng.uniform(spec.scale_lo, spec.scale_hi, size=nblk).astype(np.float16).view(np.uint16)
+    return to_tile_major(code_rows, sc.reshape(rows, cols // 32), spec.wfmt)
 
 
 def make_codebook(seed: int, layer: int) -> np.ndarray:

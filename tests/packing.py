@@ -1,0 +1,39 @@
+"""Test-side encoder of the packed tile-major storage, written from its definition
+independently of the generator's packer (which a test compares with this one).
+
+Definition: rows in tiles of 16, a row's 32-value blocks in steps of 4 (the last step
+may hold r < 4).  Code unit (tile t, step s) starts at byte t*8*cols + 1024*s and holds
+block g of the step for row m at (16g + m)*16.  The scale plane starts at
+round_up(rows*cols/2, 256); scale unit (t, s) starts at index t*16*nblk + 64*s and holds
+MXFP4 (g, m) at 16g + m, CB4 (m, g) at m*r + g.
+"""
+import numpy as np
+
+MXFP4, CB4 = 1, 2
+
+
+def pack(wfmt, codes, scales):
+    """codes: [rows][cols] 4-bit values; scales: [rows][cols/32] E8M0 bytes (MXFP4) or fp16
+    bit patterns (CB4).  Returns the packed bytes."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    assert rows % 16 == 0 and cols % 32 == 0
+    nblk = cols // 32
+    code_bytes = rows * cols // 2
+    scale_off = (code_bytes + 255) // 256 * 256
+    sbytes = 1 if wfmt == MXFP4 else 2
+    out = np.zeros(scale_off + rows * nblk * sbytes, dtype=np.uint8)
+    pairs = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8).reshape(rows, nblk, 16)
+    sc = np.asarray(scales).reshape(rows, nblk)
+    splane = np.zeros(rows * nblk, dtype=np.uint8 if wfmt == MXFP4 else np.uint16)
+    for row in range(rows):
+        t, m = divmod(row, 16)
+        for b in range(nblk):
+            s, g = divmod(b, 4)
+            r = min(4, nblk - 4 * s)
+            at = t * 8 * cols + 1024 * s + (16 * g + m) * 16
+            out[at:at + 16] = pairs[row, b]
+            unit = t * 16 * nblk + 64 * s
+            splane[unit + (16 * g + m if wfmt == MXFP4 else m * r + g)] = sc[row, b]
+    out[scale_off:] = splane.astype("<u2" if wfmt == CB4 else np.uint8).view(np.uint8)
+    return out

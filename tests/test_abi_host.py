@@ -40,6 +40,7 @@ def test_packed_bytes(L):
     assert q.packed_bytes(q.WFMT_CB4, 16, 100) == 0
     assert q.packed_bytes(3, 16, 64) == 0
     assert q.packed_bytes(q.WFMT_MXFP4, 0, 64) == 0
+    assert q.packed_bytes(q.WFMT_MXFP4, 8, 64) == 0   # rows come in tiles of 16
 
 
 FAKE = 0x10000  # a non-null, 256-aligned stand-in for device pointers (never dereferenced)
@@ -105,10 +106,11 @@ def test_router_and_bucket_validation(L):
 
 
 def test_dequant_and_rescale_validation(L):
-    assert L.moe_dequant(q.WFMT_CB4, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
-    assert L.moe_dequant(q.WFMT_MXFP4, FAKE, None, 4, 48, FAKE, None) == q.MOE_ERR_INVALID_ARG
-    assert L.moe_dequant(q.WFMT_MXFP4, FAKE + 4, None, 4, 64, FAKE, None) == q.MOE_ERR_ALIGNMENT
-    assert L.moe_dequant(9, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_CB4, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_MXFP4, FAKE, None, 16, 48, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_MXFP4, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant(q.WFMT_MXFP4, FAKE + 4, None, 16, 64, FAKE, None) == q.MOE_ERR_ALIGNMENT
+    assert L.moe_dequant(9, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_rms_rescale(FAKE, 2, 0, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_rms_rescale(None, 2, 8, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_rms_rescale(FAKE, 0, 8, 1e-6, FAKE, None) == q.MOE_OK

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
+import packing
 import synth
 from parity_util import check_forward
 
@@ -39,15 +40,13 @@ def _run(spec, layer=None, x=None, path=0):
 # dequantisation: bit-exact
 # ---------------------------------------------------------------------------
 def test_dequant_mxfp4_bit_exact_all_codes_and_scales():
-    rows, cols = 253, 64
+    rows, cols = 256, 96                 # 16 row tiles, 3 blocks per row (a partial step)
     rng = np.random.default_rng(1)
-    buf = np.zeros(q.packed_bytes(q.WFMT_MXFP4, rows, cols), dtype=np.uint8)
-    nc = rows * cols // 2
-    buf[:nc] = rng.integers(0, 256, nc, dtype=np.uint8)
-    # every row r uses E8M0 = r (0..252) for both of its blocks; all 256 byte values appear
-    buf[:256] = np.arange(256, dtype=np.uint8)
-    off = (nc + 255) // 256 * 256
-    buf[off:off + rows * 2] = np.repeat(np.arange(rows, dtype=np.uint8), 2)
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
+    # row r uses E8M0 = min(r, 252) for its blocks: every finite scale byte appears
+    scales = np.repeat(np.minimum(np.arange(rows), 252).astype(np.uint8)[:, None], cols // 32, axis=1)
+    buf = packing.pack(packing.MXFP4, codes, scales)
+    assert buf.size == q.packed_bytes(q.WFMT_MXFP4, rows, cols)
     out = q.dequant(q.WFMT_MXFP4, _dev(buf), rows, cols).cpu().numpy()
     ref = oracle.dequant(oracle.WFMT_MXFP4, buf, None, rows, cols)
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)  # exact in fp32
@@ -58,14 +57,11 @@ def test_dequant_cb4_bit_exact_all_fp16_scales():
     rows, cols = 2048, 32 * 32          # 65,536 blocks: one per fp16 pattern
     cb = synth.make_codebook(77, 0)
     rng = np.random.default_rng(2)
-    buf = np.zeros(q.packed_bytes(q.WFMT_CB4, rows, cols), dtype=np.uint8)
-    nc = rows * cols // 2
-    buf[:nc] = rng.integers(0, 256, nc, dtype=np.uint8)
-    off = (nc + 255) // 256 * 256
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     finite = ((bits >> 10) & 31) != 31
     bits = np.where(finite, bits, 0x3C00).astype(np.uint16)
-    buf[off:off + 2 * 65536] = bits.view(np.uint8)
+    buf = packing.pack(packing.CB4, codes, bits.reshape(rows, cols // 32))
     out = q.dequant(q.WFMT_CB4, _dev(buf), rows, cols, codebook=_dev(cb)).cpu().numpy()
     ref = oracle.dequant(oracle.WFMT_CB4, buf, cb, rows, cols)
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import packing
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -17,24 +18,30 @@ E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
               -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
 
 
-def _pack_block_codes(codes):
-    """32 4-bit codes -> 16 bytes (element 2j low nibble, 2j+1 high nibble)."""
-    codes = list(codes)
-    return bytes((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4) for j in range(16))
+def _one_block_matrix(codes, scale, wfmt):
+    """A 16x32 packed matrix whose row 0 holds the given block; rows 1..15 hold code 0
+    with unit scales.  Built with the test-side encoder."""
+    c = np.zeros((16, 32), dtype=np.uint8)
+    c[0] = codes
+    sc = np.full((16, 1), 127 if wfmt == oracle.WFMT_MXFP4 else 0x3C00)
+    sc[0, 0] = scale
+    buf = packing.pack(wfmt, c, sc)
+    assert buf.size == oracle.packed_size(wfmt, 16, 32)
+    return buf
 
 
-def _one_block_matrix(codes, scale_bytes, wfmt):
-    """A 1x32 packed matrix: 16 code bytes, zero padding to 256, then the scale."""
-    buf = bytearray(_pack_block_codes(codes))
-    buf += bytes(256 - len(buf))
-    buf += bytes(scale_bytes)
-    assert len(buf) == oracle.packed_size(wfmt, 1, 32)
-    return np.frombuffer(bytes(buf), dtype=np.uint8)
+def test_block_bytes_land_where_the_storage_definition_says():
+    """Row 0's block is the first 16 bytes of the code plane: byte j = element 2j (low
+    nibble) | element 2j+1 (high nibble); its scale is the first scale entry."""
+    codes = [(5 * i + 1) % 16 for i in range(32)]
+    buf = _one_block_matrix(codes, 124, oracle.WFMT_MXFP4)
+    assert list(buf[:16]) == [codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(16)]
+    assert buf[256] == 124
 
 
 def test_mxfp4_hand_block_unit_scale():
     codes = list(range(16)) + list(range(16))
-    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, [127], oracle.WFMT_MXFP4), None, 1, 32)
+    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, 127, oracle.WFMT_MXFP4), None, 16, 32)
     assert list(w[0, :16]) == E2M1_TABLE
     assert list(w[0, 16:]) == E2M1_TABLE
     # code 8 is negative zero
@@ -44,7 +51,7 @@ def test_mxfp4_hand_block_unit_scale():
 
 def test_mxfp4_hand_block_eighth_scale():
     codes = [15 - (i % 16) for i in range(32)]
-    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, [124], oracle.WFMT_MXFP4), None, 1, 32)
+    w = oracle.dequant(oracle.WFMT_MXFP4, _one_block_matrix(codes, 124, oracle.WFMT_MXFP4), None, 16, 32)
     expect = [E2M1_TABLE[c] / 8.0 for c in codes]
     assert list(w[0]) == expect
 
@@ -75,8 +82,7 @@ def test_fp16_scale_exhaustive_vs_numpy_half():
 def test_cb4_hand_block(scale_bits, factor):
     cb = np.array([-127, -100, -64, -33, -17, -8, -3, -1, 0, 2, 5, 9, 21, 47, 88, 127], dtype=np.int8)
     codes = [(7 * i + 3) % 16 for i in range(32)]
-    sb = [scale_bits & 0xFF, scale_bits >> 8]
-    w = oracle.dequant(oracle.WFMT_CB4, _one_block_matrix(codes, sb, oracle.WFMT_CB4), cb, 1, 32)
+    w = oracle.dequant(oracle.WFMT_CB4, _one_block_matrix(codes, scale_bits, oracle.WFMT_CB4), cb, 16, 32)
     assert list(w[0]) == [float(cb[c]) * factor for c in codes]
 
 
@@ -86,15 +92,10 @@ def test_cb4_exhaustive_scale_times_index():
                   dtype=np.int8)
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     s = bits.view(np.float16).astype(np.float64)
-    # one packed matrix with 2048 rows x 32 cols would need all patterns; decode row by row instead
+    # one 32-value row per fp16 pattern: 65,536 rows x 32 cols, indices 0..15 twice per row
     rows = 65536
-    codes = np.tile(np.arange(16, dtype=np.uint8), 2)           # indices 0..15 twice
-    code_bytes = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
-    plane = np.tile(code_bytes, rows)
-    buf = np.zeros(oracle.packed_size(oracle.WFMT_CB4, rows, 32), dtype=np.uint8)
-    buf[:plane.size] = plane
-    off = (plane.size + 255) // 256 * 256
-    buf[off:off + 2 * rows] = bits.view(np.uint8)
+    codes = np.tile(np.tile(np.arange(16, dtype=np.uint8), 2), (rows, 1))
+    buf = packing.pack(oracle.WFMT_CB4, codes, bits.reshape(rows, 1))
     w = oracle.dequant(oracle.WFMT_CB4, buf, cb, rows, 32)
     with np.errstate(invalid="ignore"):
         want = s[:, None] * cb.astype(np.float64)[np.tile(np.arange(16), 2)][None, :]
@@ -113,7 +114,7 @@ def test_packed_sizes_match_page_figures():
     assert abs(per_token - g["experts_touched_per_token"]["approx_bytes"]) / 1.9e9 < 0.01
     cb = g["cb4_rows_bytes"]
     assert oracle.packed_size(oracle.WFMT_CB4, cb["rows"], cb["values_per_row"]) == cb["value"] == 1440
-    assert oracle.packed_size(oracle.WFMT_CB4, 1, 32) - 256 + 16 == g["q4_0_bytes_per_32"]["value"]
+    assert oracle.packed_size(oracle.WFMT_CB4, 16, 32) - 256 + 16 * 16 == 16 * g["q4_0_bytes_per_32"]["value"]
     # the generator writes the same sizes
     assert synth.packed_nbytes(synth.WFMT_MXFP4, 2 * I, H) + synth.packed_nbytes(synth.WFMT_MXFP4, H, I) == expert
 
@@ -130,39 +131,42 @@ def test_packed_scale_store_reading_size():
 
 @pytest.mark.parametrize("wfmt", [oracle.WFMT_MXFP4, oracle.WFMT_CB4])
 def test_layout_single_nonzero_positions(wfmt):
-    """One nonzero code at (r, c) lands at (r, c): checks nibble order, row-major codes
-    and the 256-aligned scale plane (rows*cols/2 = 240 is not a multiple of 256)."""
-    rows, cols = 5, 96
+    """One nonzero code at (r, c) lands at (r, c) and only its own block's scale
+    multiplies it: checks nibble order, the tile-major code units (two tiles, a partial
+    last step of 3 blocks) and the 256-aligned scale plane (rows*cols/2 = 1536 is not
+    a multiple of 256 in general; here it is, the partial step covers the other case)."""
+    rows, cols = 32, 96
     cb = np.arange(-8, 8, dtype=np.int8) * 3  # index 8 -> 0
     zero_code = 0 if wfmt == oracle.WFMT_MXFP4 else 8
     one_code = 2 if wfmt == oracle.WFMT_MXFP4 else 9   # e2m1(2) = 1.0; cb[9] = 3
     one_val = 1.0 if wfmt == oracle.WFMT_MXFP4 else 3.0
-    for r, c in [(0, 0), (0, 1), (2, 33), (4, 95), (3, 64)]:
-        codes = np.full(rows * cols, zero_code, dtype=np.uint8)
-        codes[r * cols + c] = one_code
-        plane = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
-        buf = np.zeros(oracle.packed_size(wfmt, rows, cols), dtype=np.uint8)
-        buf[:plane.size] = plane
-        off = 256
-        nblk = rows * cols // 32
-        if wfmt == oracle.WFMT_MXFP4:
-            buf[off:off + nblk] = 127
-        else:
-            buf[off:off + 2 * nblk] = np.full(nblk, 0x3C00, dtype=np.uint16).view(np.uint8)
-        w = oracle.dequant(wfmt, buf, cb, rows, cols)
+    unit = 127 if wfmt == oracle.WFMT_MXFP4 else 0x3C00
+    for r, c in [(0, 0), (0, 1), (17, 33), (31, 95), (3, 64), (16, 70)]:
+        codes = np.full((rows, cols), zero_code, dtype=np.uint8)
+        codes[r, c] = one_code
+        scales = np.full((rows, cols // 32), unit)
+        w = oracle.dequant(wfmt, packing.pack(wfmt, codes, scales), cb, rows, cols)
         want = np.zeros((rows, cols))
         want[r, c] = one_val
         assert np.array_equal(w, want)
-        # the scale of block (r, c // 32) multiplies it
-        bi = r * (cols // 32) + c // 32
-        if wfmt == oracle.WFMT_MXFP4:
-            buf[off + bi] = 130
-            scale = 8.0
-        else:
-            buf[off + 2 * bi: off + 2 * bi + 2] = np.array([0x4400], dtype=np.uint16).view(np.uint8)
-            scale = 4.0
-        w = oracle.dequant(wfmt, buf, cb, rows, cols)
+        scales[r, c // 32] = 130 if wfmt == oracle.WFMT_MXFP4 else 0x4400
+        scale = 8.0 if wfmt == oracle.WFMT_MXFP4 else 4.0
+        w = oracle.dequant(wfmt, packing.pack(wfmt, codes, scales), cb, rows, cols)
         assert w[r, c] == one_val * scale and np.count_nonzero(w) == 1
+
+
+@pytest.mark.parametrize("wfmt", [oracle.WFMT_MXFP4, oracle.WFMT_CB4])
+@pytest.mark.parametrize("rows,cols", [(16, 32), (32, 96), (48, 160), (16, 2880)])
+def test_generator_packer_matches_test_encoder(wfmt, rows, cols):
+    """The generator's reshape-based packer and the test-side loop encoder agree byte for byte."""
+    rng = np.random.default_rng(rows + cols + wfmt)
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
+    if wfmt == oracle.WFMT_MXFP4:
+        sc = rng.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
+    else:
+        sc = rng.integers(0, 65536, (rows, cols // 32)).astype(np.uint16)
+    code_rows = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(synth.to_tile_major(code_rows, sc, wfmt), packing.pack(wfmt, codes, sc))
 
 
 def test_bf16_rounding_two_implementations():

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import packing
 import synth
 
 
@@ -136,17 +137,7 @@ def test_decimal_50_digits_tiny_layer(wfmt, xd, sh):
 
 def _packed_from_dense_codes(wfmt, codes, scale_byte_or_bits):
     rows, cols = codes.shape
-    flat = codes.reshape(-1).astype(np.uint8)
-    plane = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)
-    buf = np.zeros(oracle.packed_size(wfmt, rows, cols), dtype=np.uint8)
-    buf[:plane.size] = plane
-    off = (plane.size + 255) // 256 * 256
-    nblk = rows * cols // 32
-    if wfmt == synth.WFMT_MXFP4:
-        buf[off:off + nblk] = scale_byte_or_bits
-    else:
-        buf[off:off + 2 * nblk] = np.full(nblk, scale_byte_or_bits, dtype=np.uint16).view(np.uint8)
-    return buf
+    return packing.pack(wfmt, codes, np.full((rows, cols // 32), scale_byte_or_bits))
 
 
 def test_single_nonzero_closed_form():
