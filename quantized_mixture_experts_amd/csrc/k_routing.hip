@@ -13,80 +13,93 @@
 namespace moeq {
 
 // ---------------------------------------------------------------------------
-// Router logits: l[t][e] = sum_h x[t][h] * W[e][h] + b[e].
-// Products of an fp32 weight and an fp32/bf16 activation are exact in fp64 and are
-// summed in fp64, so the result differs from any other fp64 summation order only
-// in the last bits; ties and near-ties are then ordered the same way as a plain
-// fp64 evaluation.  Row E (when a shared-gate vector exists) holds w_sg . x[t].
-// A wave owns one expert row for a tile of kTokTile tokens.
-// For fp32 activations the first block column also writes the exact 3-plane bf16
-// split of x used by the MFMA kernels.
+// Router logits for larger batches on the fp64 matrix cores (v_mfma_f64_16x16x4f64:
+// lane l supplies A[l%16][l/16] and B[l/16][l%16] and holds D[4r + l/16][l%16]).
+// A = activations (tokens x k), B = router rows (k x experts); every product of a
+// bf16/fp32 activation and an fp32 weight is exact in fp64 and the matrix core sums in
+// fp64, so only the summation order differs from a plain fp64 loop.
+// Block: 32 tokens x 16 expert rows; its 4 waves split K in 16-column chunks (wave w
+// takes chunks w, w+4, ...) and are summed in wave order.  Each lane loads 4
+// consecutive k of its token rows and its expert row; MFMA step q pairs element q of
+// both, so a chunk's 4 steps cover its 16 columns.  Row E (with a shared-gate vector)
+// is w_sg.  Blocks of the first expert tile also write the exact 3-plane bf16 split of
+// fp32 x used by the projections.
 // ---------------------------------------------------------------------------
-constexpr int kTokTile = 8;
+typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 
 template <int XDT>
-__global__ __launch_bounds__(256) void k_router_logits(LayerArgs L, const void* __restrict__ x, int T,
-                                                       int erows, double* __restrict__ logits,
-                                                       uint16_t* __restrict__ xplanes) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 4 + wave;
-  const int t0 = blockIdx.y * kTokTile;
+__global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __restrict__ x, int T, int erows,
+                                                     double* __restrict__ logits, uint16_t* __restrict__ xplanes) {
+  __shared__ double red[3][2][4][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, kk = lane >> 4;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 16;
   const int H = L.H;
-  const int nt = min(kTokTile, T - t0);
 
-  if (XDT == 0 && blockIdx.x == 0) {
-    // exact split x = hi + mid + lo (each bf16) for the tokens of this tile
+  if (XDT == 0 && blockIdx.y == 0) {
     const float* xf = (const float*)x;
-    for (int idx = threadIdx.x; idx < nt * H; idx += blockDim.x) {
-      const int t = t0 + idx / H, h = idx % H;
-      const float v = xf[(size_t)t * H + h];
+    const int nt = min(32, T - t0);
+    for (int idx = threadIdx.x; idx < nt * H; idx += 256) {
+      const size_t o = (size_t)t0 * H + idx;
+      const float v = xf[o];
       const uint32_t p0 = f32_to_bf16_rne(v);
       const float r1 = v - bf16_bits_to_f32(p0);
       const uint32_t p1 = f32_to_bf16_rne(r1);
-      const float r2 = r1 - bf16_bits_to_f32(p1);
-      const uint32_t p2 = f32_to_bf16_rne(r2);
-      const size_t o = (size_t)t * H + h;
+      const uint32_t p2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p1));
       xplanes[o] = (uint16_t)p0;
       xplanes[(size_t)T * H + o] = (uint16_t)p1;
       xplanes[(size_t)2 * T * H + o] = (uint16_t)p2;
     }
   }
-  if (e >= erows) return;
-
-  const float* w = (e < L.E) ? L.router_w + (size_t)e * H : L.shared_gate_w;
-  double acc[kTokTile];
+  // this lane's rows (clamped into range; clamped results are not stored)
+  const int ta = min(t0 + i, T - 1), tb = min(t0 + 16 + i, T - 1);
+  const int e = e0 + i;
+  const float* wrow = e < L.E ? L.router_w + (size_t)e * H : (e < erows ? L.shared_gate_w : L.router_w);
+  f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  const int nch = H >> 4;
+#pragma unroll 4
+  for (int ch = wave; ch < nch; ch += 4) {
+    const int k = 16 * ch + 4 * kk;
+    double a0[4], a1[4], b[4];
+    const float4 wv = *(const float4*)(wrow + k);
+    b[0] = wv.x; b[1] = wv.y; b[2] = wv.z; b[3] = wv.w;
+    if (XDT == 0) {
+      const float4 xa = *(const float4*)((const float*)x + (size_t)ta * H + k);
+      const float4 xb = *(const float4*)((const float*)x + (size_t)tb * H + k);
+      a0[0] = xa.x; a0[1] = xa.y; a0[2] = xa.z; a0[3] = xa.w;
+      a1[0] = xb.x; a1[1] = xb.y; a1[2] = xb.z; a1[3] = xb.w;
+    } else {
+      const uint2 xa = *(const uint2*)((const uint16_t*)x + (size_t)ta * H + k);
+      const uint2 xb = *(const uint2*)((const uint16_t*)x + (size_t)tb * H + k);
+      a0[0] = bf16_bits_to_f32(xa.x & 0xFFFFu); a0[1] = bf16_bits_to_f32(xa.x >> 16);
+      a0[2] = bf16_bits_to_f32(xa.y & 0xFFFFu); a0[3] = bf16_bits_to_f32(xa.y >> 16);
+      a1[0] = bf16_bits_to_f32(xb.x & 0xFFFFu); a1[1] = bf16_bits_to_f32(xb.x >> 16);
+      a1[2] = bf16_bits_to_f32(xb.y & 0xFFFFu); a1[3] = bf16_bits_to_f32(xb.y >> 16);
+    }
 #pragma unroll
-  for (int t = 0; t < kTokTile; ++t) acc[t] = 0.0;
-
-  for (int h = lane * 4; h < H; h += 4 * kWave) {
-    const float4 wv = *(const float4*)(w + h);
-#pragma unroll
-    for (int t = 0; t < kTokTile; ++t) {
-      if (t < nt) {
-        float x0, x1, x2, x3;
-        if (XDT == 0) {
-          const float4 xv = *(const float4*)((const float*)x + (size_t)(t0 + t) * H + h);
-          x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
-        } else {
-          const uint2 xb = *(const uint2*)((const uint16_t*)x + (size_t)(t0 + t) * H + h);
-          x0 = bf16_bits_to_f32(xb.x & 0xFFFFu); x1 = bf16_bits_to_f32(xb.x >> 16);
-          x2 = bf16_bits_to_f32(xb.y & 0xFFFFu); x3 = bf16_bits_to_f32(xb.y >> 16);
-        }
-        double a = acc[t];
-        a = fma((double)wv.x, (double)x0, a);
-        a = fma((double)wv.y, (double)x1, a);
-        a = fma((double)wv.z, (double)x2, a);
-        a = fma((double)wv.w, (double)x3, a);
-        acc[t] = a;
-      }
+    for (int q = 0; q < 4; ++q) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[q], b[q], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[q], b[q], acc1, 0, 0, 0);
     }
   }
-  const double bias = (e < L.E && L.router_b) ? (double)L.router_b[e] : 0.0;
+  if (wave > 0) {
 #pragma unroll
-  for (int t = 0; t < kTokTile; ++t) {
-    const double s = wave_sum_f64(acc[t]);
-    if (lane == 0 && t < nt) logits[(size_t)(t0 + t) * (L.E + 1) + e] = s + bias;
+    for (int r = 0; r < 4; ++r) { red[wave - 1][0][r][lane] = acc0[r]; red[wave - 1][1][r][lane] = acc1[r]; }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int col = e0 + i;  // expert of this lane's outputs
+    const double bias = (col < L.E && L.router_b) ? (double)L.router_b[col] : 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double s0 = ((acc0[r] + red[0][0][r][lane]) + red[1][0][r][lane]) + red[2][0][r][lane];
+      const double s1 = ((acc1[r] + red[0][1][r][lane]) + red[1][1][r][lane]) + red[2][1][r][lane];
+      const int row = 4 * r + kk;  // token within the 16-token tile
+      if (col < erows) {
+        if (t0 + row < T) logits[(size_t)(t0 + row) * (L.E + 1) + col] = s0 + bias;
+        if (t0 + 16 + row < T) logits[(size_t)(t0 + 16 + row) * (L.E + 1) + col] = s1 + bias;
+      }
+    }
   }
 }
 
@@ -253,11 +266,11 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
 hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
                               int32_t* dbg_ids, float* dbg_w, hipStream_t s, const Timing& tm) {
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
-  dim3 grid((erows + 3) / 4, (T + kTokTile - 1) / kTokTile);
+  dim3 grid((T + 31) / 32, (erows + 15) / 16);
   if (x_dtype == 0)
-    MOEQ_LAUNCH(tm, kStageRouter, k_router_logits<0>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
+    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<0>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
   else
-    MOEQ_LAUNCH(tm, kStageRouter, k_router_logits<1>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
+    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<1>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
   MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits, w.ids,
               w.pair_w, dbg_ids, dbg_w);
   return hipGetLastError();
