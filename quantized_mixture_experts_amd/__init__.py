@@ -141,11 +141,13 @@ class DeviceLayer:
         return lib().moe_workspace_bytes(ctypes.byref(self.c), T)
 
     def workspace(self, T: int):
+        """A zero-filled workspace for up to T tokens (its header must be zero before the
+        first call; every call leaves it zero)."""
         import torch
         n = self.workspace_bytes(T)
         if n == 0 and T > 0:
             raise MoeError(MOE_ERR_INVALID_ARG, "moe_workspace_bytes")
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.router_w.device)
+        return torch.zeros(max(n, 2048), dtype=torch.uint8, device=self.router_w.device)
 
 
 def router_topk(L: DeviceLayer, x, x_dtype: int, ws=None, stream=None):

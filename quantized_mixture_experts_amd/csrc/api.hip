@@ -14,6 +14,10 @@ using moeq::LayerArgs;
 using moeq::Work;
 
 constexpr size_t kAlign = 256;
+// Workspace header at offset 0 whatever T is: words that must read zero when a call
+// starts (each call leaves them zero): the decode router's arrival flags, one word
+// per router block (at most (1024 + 1 + 3) / 4 = 257 blocks).
+constexpr size_t kHeaderBytes = 2048;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -49,7 +53,7 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   const size_t E = (size_t)L->n_experts, k = (size_t)L->top_k, H = (size_t)L->hidden, I = (size_t)L->inter;
   const size_t P = (size_t)T * k + (L->has_shared ? (size_t)T : 0);
   Layout o{};
-  size_t at = 0;
+  size_t at = kHeaderBytes;  // the fixed header (synchronisation words) comes first
   auto take = [&](size_t bytes) { size_t r = at; at = align_up(at + bytes, kAlign); return r; };
   o.logits = take((size_t)T * (E + 1) * 8);
   o.ids = take((size_t)T * k * 4);
@@ -89,6 +93,7 @@ Work carve(void* ws, const Layout& lo) {
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
   w.groups = reinterpret_cast<int4*>(b + lo.groups);
   w.n_groups = reinterpret_cast<int32_t*>(b + lo.n_groups);
+  w.rr_flags = reinterpret_cast<uint32_t*>(b);
   return w;
 }
 

@@ -77,6 +77,8 @@ struct Work {
   struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
   int4* groups;        // prefill work groups: (expert, first bucket position, pairs <= 64, 0)
   int32_t* n_groups;   // [1] number of valid entries of groups
+  uint32_t* rr_flags;  // decode router arrival flags, one per block: in the workspace's fixed
+                       // header, zero between calls
 };
 
 // Pairs per prefill work group (four 16-row MFMA token tiles).

@@ -1,10 +1,10 @@
 // Decode path (few tokens per call, e.g. a draft/verify window of up to 17 tokens):
-//   1. k_dec_router:   router logits, one expert row per block, loads issued up front;
-//                      block 0 also clears the per-tile arrival counters of step 4.
-//   2. k_dec_route:    one block: top-k + gates for every token, then the stable
-//                      bucketing of the pairs and the active-expert list.
-//   3. k_dec_gateup:   fused dequant + gate/up + SwiGLU per (16-row tile, active expert).
-//   4. k_dec_down:     dequant + down per (16-row tile, active expert); the last block
+//   1. k_dec_rr:       router logits (4 expert rows per block), then block 0, once
+//                      every block has arrived, does the top-k + gates, the stable
+//                      bucketing of the pairs and the active-expert slot records;
+//                      block 0 also clears the per-tile arrival counters of step 3.
+//   2. k_dec_gateup:   fused dequant + gate/up + SwiGLU per (16-row tile, active expert).
+//   3. k_dec_down:     dequant + down per (16-row tile, active expert); the last block
 //                      to finish a tile sums the gate-weighted expert outputs of that
 //                      tile in a fixed order (routed j ascending, then shared), so no
 //                      float atomics and a run-to-run identical result (NInfer
@@ -41,105 +41,22 @@ __host__ __device__ __forceinline__ int lds_row_stride(int K) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Router logits (fp64 accumulation of exact products), one expert row per block,
-//    4 waves splitting H.  x is read from global memory (tiny for decode batches).
-// ---------------------------------------------------------------------------
-template <int XDT>
-__global__ __launch_bounds__(256) void k_dec_router(LayerArgs L, const void* __restrict__ x, int T, int erows,
-                                                    double* __restrict__ logits, uint16_t* __restrict__ xplanes,
-                                                    uint32_t* __restrict__ tickets, int ntickets) {
-  __shared__ double part[4][kDecMaxTokens];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e = blockIdx.x;
-  const int H = L.H;
-  if (e == 0) {  // arrival counters of this call's combine
-    for (int i = threadIdx.x; i < ntickets; i += 256) tickets[i] = 0u;
-  }
-  if (XDT == 0 && e == 0) {
-    const float* xf = (const float*)x;
-    for (int idx = threadIdx.x; idx < T * H; idx += 256) {
-      const float v = xf[idx];
-      const uint32_t p0 = f32_to_bf16_rne(v);
-      const float r1 = v - bf16_bits_to_f32(p0);
-      const uint32_t p1 = f32_to_bf16_rne(r1);
-      const uint32_t p2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p1));
-      xplanes[idx] = (uint16_t)p0;
-      xplanes[(size_t)T * H + idx] = (uint16_t)p1;
-      xplanes[(size_t)2 * T * H + idx] = (uint16_t)p2;
-    }
-  }
-  const float* w = (e < L.E) ? L.router_w + (size_t)e * H : L.shared_gate_w;
-  // thread owns float4 columns c = threadIdx.x + 256 i; tokens in tiles of 8, with all
-  // of a tile's loads issued before its fp64 products
-  constexpr int kMaxPer = 16;  // H <= 16384
-  constexpr int kTT = 8;
-  const int nf4 = H / 4;
-  float4 wv[kMaxPer];
-#pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    wv[i] = (c < nf4) ? *(const float4*)(w + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    double acc[kTT];
-#pragma unroll
-    for (int u = 0; u < kTT; ++u) acc[u] = 0.0;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      if (c < nf4) {
-        float xv[kTT][4];
-#pragma unroll
-        for (int u = 0; u < kTT; ++u) {
-          const int t = t0 + u;
-          if (t < T) {
-            if (XDT == 0) {
-              const float4 q = *(const float4*)((const float*)x + (size_t)t * H + 4 * c);
-              xv[u][0] = q.x; xv[u][1] = q.y; xv[u][2] = q.z; xv[u][3] = q.w;
-            } else {
-              const uint2 q = *(const uint2*)((const uint16_t*)x + (size_t)t * H + 4 * c);
-              xv[u][0] = bf16_bits_to_f32(q.x & 0xFFFFu); xv[u][1] = bf16_bits_to_f32(q.x >> 16);
-              xv[u][2] = bf16_bits_to_f32(q.y & 0xFFFFu); xv[u][3] = bf16_bits_to_f32(q.y >> 16);
-            }
-          } else {
-            xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kTT; ++u) {
-          double a = acc[u];
-          a = fma((double)wv[i].x, (double)xv[u][0], a);
-          a = fma((double)wv[i].y, (double)xv[u][1], a);
-          a = fma((double)wv[i].z, (double)xv[u][2], a);
-          a = fma((double)wv[i].w, (double)xv[u][3], a);
-          acc[u] = a;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kTT; ++u) {
-      const double sum = wave_sum_f64(acc[u]);
-      if (lane == 0 && t0 + u < T) part[wave][t0 + u] = sum;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < T) {
-    const int t = threadIdx.x;
-    double s = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
-    if (e < L.E && L.router_b) s += (double)L.router_b[e];
-    logits[(size_t)t * (L.E + 1) + e] = s;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. Top-k + gates + bucketing in one block (T <= kDecMaxTokens).
+// 1+2. Router and route in one kernel.  Each 1024-thread block computes 4 expert rows
+// of router logits (4 waves per row split its columns; all tokens; fp64 accumulation
+// of exact products, partial sums added in a fixed order) and writes them through to
+// the device-coherent level, then raises its arrival flag; block 0 waits for every
+// flag, reads every logit back coherently and does the top-k, the softmax gates and
+// the bucketing:
 //    top-k: one wave per token, k rounds of a wave argmax (ties to the lower index);
 //    gates: lane j < k computes exp(l_j - l_0), a wave sum normalises them (fp64);
 //    buckets: integer counts, one wave-scan over the E+1 buckets of the packed pair
 //    (count, non-empty flag), then each pair's stable rank among earlier pairs of
-//    the same expert.
+//    the same expert; one slot record per active expert for the projections.
+// The flags live in the workspace's fixed header; block 0 clears them, so they read
+// zero at the start of every call once the header was zeroed before the first use.
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 1024;
+constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
 // Best remaining candidate of this lane: largest logit, lowest expert on ties.
@@ -196,30 +113,159 @@ __device__ __forceinline__ void topk_token(const double (&v)[16], int nper, int 
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T, const double* __restrict__ logits,
-                                                             Work w, int max_slots, int32_t* __restrict__ dbg_ids,
-                                                             float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
-                                                             int32_t* __restrict__ dbg_offsets,
-                                                             int32_t* __restrict__ dbg_perm) {
+// Partial logits of one expert row for all T tokens over the columns [h0, h1), by one
+// wave: sum_h x[t][h] w[h] in fp64 (every product exact).  Weights come in chunks of 8
+// float4 per lane with every load issued before the products; tokens in tiles of 4.
+// part[t] receives the wave's sums.
+template <int XDT>
+__device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
+                                            int h0, int h1, double* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kPer = 8;
+  constexpr int kTT = 4;
+  const int c_end = h1 / 4;
+  for (int t0 = 0; t0 < T; t0 += kTT) {
+    double acc[kTT];
+#pragma unroll
+    for (int u = 0; u < kTT; ++u) acc[u] = 0.0;
+    for (int c0 = h0 / 4; c0 < c_end; c0 += 64 * kPer) {
+      float4 wv[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = c0 + lane + 64 * i;
+        wv[i] = c < c_end ? *(const float4*)(wrow + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = c0 + lane + 64 * i;
+        if (c < c_end) {
+#pragma unroll
+          for (int u = 0; u < kTT; ++u) {
+            const int t = t0 + u;
+            if (t < T) {
+              float x0, x1, x2, x3;
+              if (XDT == 0) {
+                const float4 q = *(const float4*)((const float*)x + (size_t)t * H + 4 * c);
+                x0 = q.x; x1 = q.y; x2 = q.z; x3 = q.w;
+              } else {
+                const uint2 q = *(const uint2*)((const uint16_t*)x + (size_t)t * H + 4 * c);
+                x0 = bf16_bits_to_f32(q.x & 0xFFFFu); x1 = bf16_bits_to_f32(q.x >> 16);
+                x2 = bf16_bits_to_f32(q.y & 0xFFFFu); x3 = bf16_bits_to_f32(q.y >> 16);
+              }
+              double a = acc[u];
+              a = fma((double)wv[i].x, (double)x0, a);
+              a = fma((double)wv[i].y, (double)x1, a);
+              a = fma((double)wv[i].z, (double)x2, a);
+              a = fma((double)wv[i].w, (double)x3, a);
+              acc[u] = a;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTT; ++u) {
+      const double sum = wave_sum_f64(acc[u]);
+      if (lane == 0 && t0 + u < T) part[t0 + u] = sum;
+    }
+  }
+}
+
+// Bounded wait of block 0 for the arrival flags of blocks 1..n-1 (all blocks of this
+// small grid are resident together, so the flags arrive; the bound only guarantees an
+// exit).  The flags are then cleared for the next call.
+__device__ __forceinline__ void wait_arrivals(uint32_t* __restrict__ flags, int n) {
+  if (threadIdx.x < 64) {
+    for (int base = 1; base < n; base += 64) {
+      const int b = base + (int)threadIdx.x;
+      uint32_t spins = 0;
+      while (true) {
+        const uint32_t f = b < n ? __hip_atomic_load(flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+        if (__ballot(f == 0u) == 0ull || ++spins > (1u << 24)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (b < n) __hip_atomic_store(flags + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
+                                                          Work w, int max_slots, uint32_t* __restrict__ rr_flags,
+                                                          int ntickets, int32_t* __restrict__ dbg_ids,
+                                                          float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
+                                                          int32_t* __restrict__ dbg_offsets,
+                                                          int32_t* __restrict__ dbg_perm) {
   __shared__ int s_exp[kMaxPairsDec];   // expert of each pair
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
   __shared__ const uint8_t* s_gu[1024 + 1];
   __shared__ const uint8_t* s_dn[1024 + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double s_part[kRouteThreads / 64][kDecMaxTokens];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int kWaves = kRouteThreads / 64;
-  const int E = L.E, k = L.k;
-  const int Pr = T * k;
-  const int P = Pr + (L.has_shared ? T : 0);
+  const int E = L.E, k = L.k, H = L.H;
   const int nb = E + 1;
-  // expert pointer tables and zeroed counts (independent of the logits)
+
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < ntickets; i += kRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
+    if (XDT == 0) {  // exact 3-plane bf16 split of fp32 x for the projections
+      const float* xf = (const float*)x;
+      for (int idx = tid; idx < T * H; idx += kRouteThreads) {
+        const float v = xf[idx];
+        const uint32_t p0 = f32_to_bf16_rne(v);
+        const float r1 = v - bf16_bits_to_f32(p0);
+        const uint32_t p1 = f32_to_bf16_rne(r1);
+        const uint32_t p2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p1));
+        w.xplanes[idx] = (uint16_t)p0;
+        w.xplanes[(size_t)T * H + idx] = (uint16_t)p1;
+        w.xplanes[(size_t)2 * T * H + idx] = (uint16_t)p2;
+      }
+    }
+  }
+  // expert pointer tables and zeroed counts for the route (only the elected block uses
+  // them; loading them here keeps them off its critical path)
   for (int i = tid; i < nb; i += kRouteThreads) {
     s_cnt[i] = 0;
     const bool ok = i < E || L.has_shared;
     s_gu[i] = ok ? L.gate_up[i] : nullptr;
     s_dn[i] = ok ? L.down[i] : nullptr;
   }
+  {
+    // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns
+    const int e = blockIdx.x * kRouterRows + (wave >> 2);
+    const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
+    if (e < erows) {
+      const float* wrow = e < E ? L.router_w + (size_t)e * H : L.shared_gate_w;
+      router_part<XDT>(wrow, x, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave]);
+    }
+    __syncthreads();
+    if (tid < kRouterRows * T) {
+      const int r = tid / T, t = tid % T;
+      const int er = blockIdx.x * kRouterRows + r;
+      if (er < erows) {
+        double v = ((s_part[4 * r][t] + s_part[4 * r + 1][t]) + s_part[4 * r + 2][t]) + s_part[4 * r + 3][t];
+        if (er < E && L.router_b) v += (double)L.router_b[er];
+        __hip_atomic_store(w.logits + (size_t)t * (E + 1) + er, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // arrival: this block's logits are written through and complete before its flag
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (blockIdx.x != 0) {
+    if (tid == 0) __hip_atomic_store(rr_flags + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  wait_arrivals(rr_flags, gridDim.x);
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  const int Pr = T * k;
+  const int P = Pr + (L.has_shared ? T : 0);
+  const double* logits = w.logits;
   // top-k: wave w takes tokens w and w + 16 (T <= 32); both tokens' logits load first
   {
     const int t0 = wave, t1 = wave + kWaves;
@@ -228,13 +274,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + 64 * i;
-      v0[i] = (i < nper && t0 < T && e < E) ? logits[(size_t)t0 * (E + 1) + e] : -__builtin_inf();
-      v1[i] = (i < nper && t1 < T && e < E) ? logits[(size_t)t1 * (E + 1) + e] : -__builtin_inf();
+      v0[i] = (i < nper && t0 < T && e < E)
+                  ? __hip_atomic_load(logits + (size_t)t0 * (E + 1) + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : -__builtin_inf();
+      v1[i] = (i < nper && t1 < T && e < E)
+                  ? __hip_atomic_load(logits + (size_t)t1 * (E + 1) + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : -__builtin_inf();
     }
     if (t0 < T) topk_token(v0, nper, E, k, t0, s_exp, s_l);
     if (t1 < T) topk_token(v1, nper, E, k, t1, s_exp, s_l);
     for (int t = t0; t < T && t <= t1; t += kWaves) {
-      const double* lt = logits + (size_t)t * (E + 1);
       const double l0 = s_l[t * k];
       const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
       const double zs = wave_sum_f64(z);
@@ -248,7 +297,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T,
         if (dbg_w) dbg_w[p] = gte;
       }
       if (L.has_shared && lane == 0) {
-        w.pair_w[Pr + t] = L.shared_gate_w ? (float)(1.0 / (1.0 + exp(-lt[E]))) : 1.0f;
+        double sg = 1.0;
+        if (L.shared_gate_w) {
+          const double ls =
+              __hip_atomic_load(logits + (size_t)t * (E + 1) + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sg = 1.0 / (1.0 + exp(-ls));
+        }
+        w.pair_w[Pr + t] = (float)sg;
         s_exp[Pr + t] = E;
       }
     }
@@ -788,15 +843,14 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
                          int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
   const int ntickets = L.H / 16;
-  if (x_dtype == 0)
-    MOEQ_LAUNCH(tm, kStageRouter, k_dec_router<0>, dim3(erows), dim3(256), 0, s, L, x, T, erows, w.logits,
-                w.xplanes, w.tickets, ntickets);
-  else
-    MOEQ_LAUNCH(tm, kStageRouter, k_dec_router<1>, dim3(erows), dim3(256), 0, s, L, x, T, erows, w.logits,
-                w.xplanes, w.tickets, ntickets);
   const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  MOEQ_LAUNCH(tm, kStageTopk, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, (const double*)w.logits, w,
-              max_slots, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+  const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
+  if (x_dtype == 0)
+    MOEQ_LAUNCH(tm, kStageRouter, k_dec_rr<0>, grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w, max_slots,
+                w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+  else
+    MOEQ_LAUNCH(tm, kStageRouter, k_dec_rr<1>, grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w, max_slots,
+                w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (T <= 16)
