@@ -59,57 +59,98 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
-// Best remaining candidate of this lane: largest logit, lowest expert on ties.
-__device__ __forceinline__ void lane_best(const double (&v)[16], uint32_t taken, int nper, int E, double& bv,
-                                          int& bi) {
-  const int lane = threadIdx.x & 63;
-  bv = -__builtin_inf();
-  bi = 0x7FFFFFFF;
+// ---- top-k of NT tokens per wave (NT = 1 or 2, processed side by side) -------------------
+// Lane l holds the candidates e = l + 64 i, i < NPER, of each token, sorted once by
+// (-logit, e); every round takes the wave maximum of the lanes' heads, finds the lane
+// holding it (exact ties between lanes go to the lowest expert index) and that lane
+// pops its head.  Empty candidates hold -inf and index 0x7FFFFFFF.
+__device__ __forceinline__ bool cand_before(double va, int ia, double vb, int ib) {
+  return ia != 0x7FFFFFFF && (ib == 0x7FFFFFFF || va > vb || (va == vb && ia < ib));
+}
+template <int NPER>
+__device__ __forceinline__ void sort_lane(double (&v)[NPER], int (&id)[NPER]) {
+  // odd-even transposition sort (NPER passes), static indices only
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const bool ok = (i < nper) & (lane + 64 * i < E) & !((taken >> i) & 1u);
-    const bool better = ok & ((bi == 0x7FFFFFFF) | (v[i] > bv));
-    bv = better ? v[i] : bv;
-    bi = better ? lane + 64 * i : bi;
+  for (int pass = 0; pass < NPER; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < NPER; i += 2) {
+      const bool sw = cand_before(v[i + 1], id[i + 1], v[i], id[i]);
+      const double tv = v[i];
+      const int ti = id[i];
+      v[i] = sw ? v[i + 1] : v[i];
+      id[i] = sw ? id[i + 1] : id[i];
+      v[i + 1] = sw ? tv : v[i + 1];
+      id[i + 1] = sw ? ti : id[i + 1];
+    }
+  }
+}
+__device__ __forceinline__ double wave_max_f64(double m) {
+  m = fmax(m, dpp_f64<kDppRowRor1>(m));
+  m = fmax(m, dpp_f64<kDppRowRor2>(m));
+  m = fmax(m, dpp_f64<kDppRowRor4>(m));
+  m = fmax(m, dpp_f64<kDppRowRor8>(m));
+  return fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
+}
+template <int NPER, int NT>
+__device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
+                                            int* s_exp, double* s_l) {
+  const int lane = threadIdx.x & 63;
+  double v[NT][NPER];
+  int id[NT][NPER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      id[t][i] = e < E ? e : 0x7FFFFFFF;
+      v[t][i] = e < E ? __hip_atomic_load(logits + (size_t)tok[t] * (E + 1) + e, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                      : -__builtin_inf();
+    }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t], id[t]);
+  for (int j = 0; j < k; ++j) {
+    double m[NT];
+    int win[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m[t] = wave_max_f64(v[t][0]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint64_t hold = __ballot(id[t][0] != 0x7FFFFFFF && v[t][0] == m[t]);
+      int wl = (int)__ffsll((long long)hold) - 1;
+      int w0 = __builtin_amdgcn_readlane(id[t][0], wl);
+      hold &= hold - 1;
+      while (hold) {  // exact tie between lanes: the lowest expert index wins
+        const int l = (int)__ffsll((long long)hold) - 1;
+        hold &= hold - 1;
+        w0 = min(w0, __builtin_amdgcn_readlane(id[t][0], l));
+      }
+      win[t] = w0;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (lane == 0) { s_exp[tok[t] * k + j] = win[t]; s_l[tok[t] * k + j] = m[t]; }
+      const bool pop = (win[t] & 63) == lane;
+#pragma unroll
+      for (int i = 0; i + 1 < NPER; ++i) {
+        v[t][i] = pop ? v[t][i + 1] : v[t][i];
+        id[t][i] = pop ? id[t][i + 1] : id[t][i];
+      }
+      v[t][NPER - 1] = pop ? -__builtin_inf() : v[t][NPER - 1];
+      id[t][NPER - 1] = pop ? 0x7FFFFFFF : id[t][NPER - 1];
+    }
   }
 }
 
-// top-k of one token held as candidate logits v[i] of expert lane + 64 i (i < nper);
-// experts >= E hold -inf.  Each round: DPP max of the lanes' best values, a ballot of
-// the lanes holding it (exact ties resolved to the lowest expert index), and only the
-// winning lane rescans its candidates.
-__device__ __forceinline__ void topk_token(const double (&v)[16], int nper, int E, int k, int t, int* s_exp,
-                                           double* s_l) {
-  const int lane = threadIdx.x & 63;
-  uint32_t taken = 0;
-  double bv;
-  int bi;
-  lane_best(v, taken, nper, E, bv, bi);
-  for (int j = 0; j < k; ++j) {
-    // wave maximum of bv (empty lanes hold -inf)
-    double m = bv;
-    m = fmax(m, dpp_f64<kDppRowRor1>(m));
-    m = fmax(m, dpp_f64<kDppRowRor2>(m));
-    m = fmax(m, dpp_f64<kDppRowRor4>(m));
-    m = fmax(m, dpp_f64<kDppRowRor8>(m));
-    m = fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
-    uint64_t hold = __ballot(bi != 0x7FFFFFFF && bv == m);
-    int win;
-    if (__popcll(hold) == 1) {
-      win = __builtin_amdgcn_readlane(bi, (int)__ffsll((long long)hold) - 1);
-    } else {  // exact tie between lanes: the lowest expert index wins
-      win = 0x7FFFFFFF;
-      while (hold) {
-        const int l = (int)__ffsll((long long)hold) - 1;
-        hold &= hold - 1;
-        win = min(win, __builtin_amdgcn_readlane(bi, l));
-      }
-    }
-    if (lane == 0) { s_exp[t * k + j] = win; s_l[t * k + j] = m; }
-    if ((win & 63) == lane) {
-      taken |= 1u << (win >> 6);
-      lane_best(v, taken, nper, E, bv, bi);
-    }
+template <int NPER>
+__device__ __forceinline__ void topk_wave(const double* __restrict__ logits, int E, int k, int T, int t0, int t1,
+                                          int* s_exp, double* s_l) {
+  if (t1 < T) {
+    const int tok[2] = {t0, t1};
+    topk_tokens<NPER, 2>(logits, E, k, tok, s_exp, s_l);
+  } else if (t0 < T) {
+    const int tok[1] = {t0};
+    topk_tokens<NPER, 1>(logits, E, k, tok, s_exp, s_l);
   }
 }
 
@@ -266,23 +307,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
   const double* logits = w.logits;
-  // top-k: wave w takes tokens w and w + 16 (T <= 32); both tokens' logits load first
+  // top-k: wave w takes tokens w and w + 16 (T <= 32), side by side
   {
     const int t0 = wave, t1 = wave + kWaves;
     const int nper = (E + 63) >> 6;
-    double v0[16], v1[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      v0[i] = (i < nper && t0 < T && e < E)
-                  ? __hip_atomic_load(logits + (size_t)t0 * (E + 1) + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                  : -__builtin_inf();
-      v1[i] = (i < nper && t1 < T && e < E)
-                  ? __hip_atomic_load(logits + (size_t)t1 * (E + 1) + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                  : -__builtin_inf();
-    }
-    if (t0 < T) topk_token(v0, nper, E, k, t0, s_exp, s_l);
-    if (t1 < T) topk_token(v1, nper, E, k, t1, s_exp, s_l);
+    if (nper <= 1) topk_wave<1>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 2) topk_wave<2>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 4) topk_wave<4>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 8) topk_wave<8>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else topk_wave<16>(logits, E, k, T, t0, t1, s_exp, s_l);
     for (int t = t0; t < T && t <= t1; t += kWaves) {
       const double l0 = s_l[t * k];
       const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
