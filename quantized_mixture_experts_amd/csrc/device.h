@@ -186,6 +186,91 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
          __builtin_amdgcn_readlane(v, 48);
 }
 
+// ---- top-k of NT tokens per wave (NT = 1 or 2, processed side by side) -------------------
+// Lane l holds the candidates e = l + 64 i, i < NPER, of each token, sorted once by
+// (-logit, e); every round takes the wave maximum of the lanes' heads, finds the lane
+// holding it (exact ties between lanes go to the lowest expert index) and that lane
+// pops its head.  Empty candidates hold -inf and index 0x7FFFFFFF.
+__device__ __forceinline__ bool cand_before(double va, int ia, double vb, int ib) {
+  return ia != 0x7FFFFFFF && (ib == 0x7FFFFFFF || va > vb || (va == vb && ia < ib));
+}
+template <int NPER>
+__device__ __forceinline__ void sort_lane(double (&v)[NPER], int (&id)[NPER]) {
+  // odd-even transposition sort (NPER passes), static indices only
+#pragma unroll
+  for (int pass = 0; pass < NPER; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < NPER; i += 2) {
+      const bool sw = cand_before(v[i + 1], id[i + 1], v[i], id[i]);
+      const double tv = v[i];
+      const int ti = id[i];
+      v[i] = sw ? v[i + 1] : v[i];
+      id[i] = sw ? id[i + 1] : id[i];
+      v[i + 1] = sw ? tv : v[i + 1];
+      id[i + 1] = sw ? ti : id[i + 1];
+    }
+  }
+}
+__device__ __forceinline__ double wave_max_f64(double m) {
+  m = fmax(m, dpp_f64<kDppRowRor1>(m));
+  m = fmax(m, dpp_f64<kDppRowRor2>(m));
+  m = fmax(m, dpp_f64<kDppRowRor4>(m));
+  m = fmax(m, dpp_f64<kDppRowRor8>(m));
+  return fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
+}
+// COHERENT: the logits were written by other blocks of the running kernel.  Token t's
+// selections go to s_exp/s_l[slot[t] * k + j] (written by lane 0).
+template <int NPER, int NT, bool COHERENT>
+__device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
+                                            const int (&slot)[NT], int* s_exp, double* s_l) {
+  const int lane = threadIdx.x & 63;
+  double v[NT][NPER];
+  int id[NT][NPER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      id[t][i] = e < E ? e : 0x7FFFFFFF;
+      const double* src = logits + (size_t)tok[t] * (E + 1) + e;
+      v[t][i] = e >= E ? -__builtin_inf()
+                       : (COHERENT ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src);
+    }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t], id[t]);
+  for (int j = 0; j < k; ++j) {
+    double m[NT];
+    int win[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m[t] = wave_max_f64(v[t][0]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint64_t hold = __ballot(id[t][0] != 0x7FFFFFFF && v[t][0] == m[t]);
+      int wl = (int)__ffsll((long long)hold) - 1;
+      int w0 = __builtin_amdgcn_readlane(id[t][0], wl);
+      hold &= hold - 1;
+      while (hold) {  // exact tie between lanes: the lowest expert index wins
+        const int l = (int)__ffsll((long long)hold) - 1;
+        hold &= hold - 1;
+        w0 = min(w0, __builtin_amdgcn_readlane(id[t][0], l));
+      }
+      win[t] = w0;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (lane == 0) { s_exp[slot[t] * k + j] = win[t]; s_l[slot[t] * k + j] = m[t]; }
+      const bool pop = (win[t] & 63) == lane;
+#pragma unroll
+      for (int i = 0; i + 1 < NPER; ++i) {
+        v[t][i] = pop ? v[t][i + 1] : v[t][i];
+        id[t][i] = pop ? id[t][i + 1] : id[t][i];
+      }
+      v[t][NPER - 1] = pop ? -__builtin_inf() : v[t][NPER - 1];
+      id[t][NPER - 1] = pop ? 0x7FFFFFFF : id[t][NPER - 1];
+    }
+  }
+}
+
 // E8M0 byte -> fp32 2^(u-127) (u = 0 gives the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t u) {
   return __uint_as_float(u == 0 ? 0x00400000u : (u << 23));

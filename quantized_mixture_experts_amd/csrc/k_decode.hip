@@ -59,98 +59,15 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
-// ---- top-k of NT tokens per wave (NT = 1 or 2, processed side by side) -------------------
-// Lane l holds the candidates e = l + 64 i, i < NPER, of each token, sorted once by
-// (-logit, e); every round takes the wave maximum of the lanes' heads, finds the lane
-// holding it (exact ties between lanes go to the lowest expert index) and that lane
-// pops its head.  Empty candidates hold -inf and index 0x7FFFFFFF.
-__device__ __forceinline__ bool cand_before(double va, int ia, double vb, int ib) {
-  return ia != 0x7FFFFFFF && (ib == 0x7FFFFFFF || va > vb || (va == vb && ia < ib));
-}
-template <int NPER>
-__device__ __forceinline__ void sort_lane(double (&v)[NPER], int (&id)[NPER]) {
-  // odd-even transposition sort (NPER passes), static indices only
-#pragma unroll
-  for (int pass = 0; pass < NPER; ++pass) {
-#pragma unroll
-    for (int i = pass & 1; i + 1 < NPER; i += 2) {
-      const bool sw = cand_before(v[i + 1], id[i + 1], v[i], id[i]);
-      const double tv = v[i];
-      const int ti = id[i];
-      v[i] = sw ? v[i + 1] : v[i];
-      id[i] = sw ? id[i + 1] : id[i];
-      v[i + 1] = sw ? tv : v[i + 1];
-      id[i + 1] = sw ? ti : id[i + 1];
-    }
-  }
-}
-__device__ __forceinline__ double wave_max_f64(double m) {
-  m = fmax(m, dpp_f64<kDppRowRor1>(m));
-  m = fmax(m, dpp_f64<kDppRowRor2>(m));
-  m = fmax(m, dpp_f64<kDppRowRor4>(m));
-  m = fmax(m, dpp_f64<kDppRowRor8>(m));
-  return fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
-}
-template <int NPER, int NT>
-__device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
-                                            int* s_exp, double* s_l) {
-  const int lane = threadIdx.x & 63;
-  double v[NT][NPER];
-  int id[NT][NPER];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = lane + 64 * i;
-      id[t][i] = e < E ? e : 0x7FFFFFFF;
-      v[t][i] = e < E ? __hip_atomic_load(logits + (size_t)tok[t] * (E + 1) + e, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                      : -__builtin_inf();
-    }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t], id[t]);
-  for (int j = 0; j < k; ++j) {
-    double m[NT];
-    int win[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) m[t] = wave_max_f64(v[t][0]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint64_t hold = __ballot(id[t][0] != 0x7FFFFFFF && v[t][0] == m[t]);
-      int wl = (int)__ffsll((long long)hold) - 1;
-      int w0 = __builtin_amdgcn_readlane(id[t][0], wl);
-      hold &= hold - 1;
-      while (hold) {  // exact tie between lanes: the lowest expert index wins
-        const int l = (int)__ffsll((long long)hold) - 1;
-        hold &= hold - 1;
-        w0 = min(w0, __builtin_amdgcn_readlane(id[t][0], l));
-      }
-      win[t] = w0;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (lane == 0) { s_exp[tok[t] * k + j] = win[t]; s_l[tok[t] * k + j] = m[t]; }
-      const bool pop = (win[t] & 63) == lane;
-#pragma unroll
-      for (int i = 0; i + 1 < NPER; ++i) {
-        v[t][i] = pop ? v[t][i + 1] : v[t][i];
-        id[t][i] = pop ? id[t][i + 1] : id[t][i];
-      }
-      v[t][NPER - 1] = pop ? -__builtin_inf() : v[t][NPER - 1];
-      id[t][NPER - 1] = pop ? 0x7FFFFFFF : id[t][NPER - 1];
-    }
-  }
-}
-
 template <int NPER>
 __device__ __forceinline__ void topk_wave(const double* __restrict__ logits, int E, int k, int T, int t0, int t1,
                                           int* s_exp, double* s_l) {
   if (t1 < T) {
     const int tok[2] = {t0, t1};
-    topk_tokens<NPER, 2>(logits, E, k, tok, s_exp, s_l);
+    topk_tokens<NPER, 2, true>(logits, E, k, tok, tok, s_exp, s_l);
   } else if (t0 < T) {
     const int tok[1] = {t0};
-    topk_tokens<NPER, 1>(logits, E, k, tok, s_exp, s_l);
+    topk_tokens<NPER, 1, true>(logits, E, k, tok, tok, s_exp, s_l);
   }
 }
 

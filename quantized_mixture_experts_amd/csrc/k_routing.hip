@@ -104,63 +104,48 @@ __global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + softmax gates.  One wave per token; lane i holds experts i, i+64, ...
-// Round j takes the largest remaining logit, ties to the lower index.
-// g_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), in fp64, stored as fp32.
-// Also writes the per-pair weights: pair_w[t*k+j] = g[t][j]; with a shared expert
+// Top-k + softmax gates.  One wave per token (the per-lane sorted candidates of
+// topk_tokens, ties to the lower index); lane j < k computes exp(l_j - l_0) and a wave
+// sum normalises them: g_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), in fp64, stored as
+// fp32.  Also the per-pair weights: pair_w[t*k+j] = g[t][j]; with a shared expert
 // pair_w[T*k+t] = 1 or sigmoid(shared logit).
 // ---------------------------------------------------------------------------
-constexpr int kMaxEPerLane = 16;  // E <= 1024
+template <int NPER>
+__device__ __forceinline__ void topk_one(const double* logits, int E, int k, int t, int* s_exp, double* s_l) {
+  const int tok[1] = {t}, slot[1] = {0};
+  topk_tokens<NPER, 1, false>(logits, E, k, tok, slot, s_exp, s_l);
+}
 
 __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* __restrict__ logits,
                                               int32_t* __restrict__ ids, float* __restrict__ pair_w,
                                               int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ int s_exp[4][16];
+  __shared__ double s_l[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // no block-wide synchronisation below
   const int E = L.E, k = L.k;
-  const double* lt = logits + (size_t)t * (E + 1);
-  double v[kMaxEPerLane];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxEPerLane; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (e < E) ? lt[e] : 0.0;
+  const int nper = (E + 63) >> 6;
+  if (nper <= 1) topk_one<1>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  else if (nper <= 2) topk_one<2>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  else if (nper <= 4) topk_one<4>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  else if (nper <= 8) topk_one<8>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  else topk_one<16>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  const double l0 = s_l[wave][0];
+  const double z = lane < k ? exp(s_l[wave][lane] - l0) : 0.0;
+  const double zs = wave_sum_f64(z);
+  if (lane < k) {
+    const float g = (float)(z / zs);
+    const int id = s_exp[wave][lane];
+    ids[t * k + lane] = id;
+    pair_w[t * k + lane] = g;
+    if (dbg_ids) dbg_ids[t * k + lane] = id;
+    if (dbg_w) dbg_w[t * k + lane] = g;
   }
-  double lsel[16];
-  int isel[16];
-  for (int j = 0; j < k; ++j) {
-    // local best: largest value, lowest index among equals (i ascending = index ascending)
-    double bv = 0.0;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxEPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u)) {
-        if (bi == 0x7FFFFFFF || v[i] > bv) { bv = v[i]; bi = e; }
-      }
-    }
-    // wave argmax with the same order
-    wave_argmax(bv, bi);
-    lsel[j] = bv;
-    isel[j] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-  }
-  if (lane == 0) {
-    double z[16], sum = 0.0;
-    for (int j = 0; j < k; ++j) { z[j] = exp(lsel[j] - lsel[0]); sum += z[j]; }
-    for (int j = 0; j < k; ++j) {
-      const float g = (float)(z[j] / sum);
-      ids[t * k + j] = isel[j];
-      pair_w[t * k + j] = g;
-      if (dbg_ids) dbg_ids[t * k + j] = isel[j];
-      if (dbg_w) dbg_w[t * k + j] = g;
-    }
-    if (L.has_shared) {
-      float s = 1.0f;
-      if (L.shared_gate_w) s = (float)(1.0 / (1.0 + exp(-lt[E])));
-      pair_w[T * k + t] = s;
-    }
+  if (L.has_shared && lane == 0) {
+    float s = 1.0f;
+    if (L.shared_gate_w) s = (float)(1.0 / (1.0 + exp(-logits[(size_t)t * (E + 1) + E])));
+    pair_w[T * k + t] = s;
   }
 }
 
@@ -181,17 +166,23 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
                                                 int32_t* __restrict__ n_groups, int32_t* __restrict__ dbg_counts,
                                                 int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
   __shared__ int hist[1024];
-  __shared__ int red[5][4];
-  __shared__ int wave_tot[4];
+  __shared__ int red[6][4];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Pr = T * k;
+  // each wave owns the contiguous pair range [wave * chunk, (wave + 1) * chunk)
+  const int chunk = ((Pr + 3) / 4 + 63) / 64 * 64;
+  const int p0 = wave * chunk, p1 = min(Pr, p0 + chunk);
   for (int i = tid; i < E; i += 256) hist[i] = 0;
   __syncthreads();
-  for (int p = tid; p < Pr; p += 256) {
-    const int id = ids[p];
+  int mine = 0;  // pairs of this wave's range routed to e
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const int id = p < p1 ? ids[p] : -1;
     if (id >= 0 && id < E) atomicAdd(&hist[id], 1);
+    mine += __popcll(__ballot(id == e));
   }
+  if (lane == 0) red[5][wave] = mine;
   __syncthreads();
   // pairs, non-empty buckets and groups below e; non-empty buckets and groups overall
   int v[5] = {0, 0, 0, 0, 0};
@@ -240,23 +231,20 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
   const int ng = (eq + kGroupPairs - 1) / kGroupPairs;
   for (int i = tid; i < ng; i += 256)
     groups[g_below + i] = make_int4(e, lt + kGroupPairs * i, min(kGroupPairs, eq - kGroupPairs * i), 0);
-  int running = 0;
-  for (int base = 0; base < Pr; base += 256) {
-    const int p = base + tid;
-    const bool flag = p < Pr && ids[p] == e;
+  // stable positions: earlier waves' matches, then this wave's in increasing p
+  int pos = lt;
+  for (int w2 = 0; w2 < wave; ++w2) pos += red[5][w2];
+  if (red[5][wave] == 0) return;
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool flag = p < p1 && ids[p] == e;
     const uint64_t m = __ballot(flag);
-    const int before = __popcll(m & ((1ull << lane) - 1ull));
-    __syncthreads();
-    if (lane == 0) wave_tot[wave] = __popcll(m);
-    __syncthreads();
-    int woff = 0;
-    for (int w = 0; w < wave; ++w) woff += wave_tot[w];
     if (flag) {
-      const int pos = lt + running + woff + before;
-      perm[pos] = p;
-      if (dbg_perm) dbg_perm[pos] = p;
+      const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+      perm[at] = p;
+      if (dbg_perm) dbg_perm[at] = p;
     }
-    running += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    pos += __popcll(m);
   }
 }
 
