@@ -28,8 +28,8 @@
 
 namespace moeq {
 
-constexpr int kPfWaves = 8;
-constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfWaves = 8;  // waves per block (eight 64-row wave tiles: 512 weight rows)
+
 constexpr int kPfRowBytes = 256;                         // one staged row chunk: 128 bf16
 constexpr int kPfPlaneBytes = kGroupPairs * kPfRowBytes;  // 16 KB per plane per buffer
 
@@ -175,8 +175,8 @@ __device__ __forceinline__ int pf_token_of_pair(int p, int T, int k) { return p 
 // Per-block state of one projection, shared by the token-tile specialisations.
 struct PfCtx {
   PackedTile tile[4];      // the wave's 4 row tiles (uniform)
-  gbyte_t* src[2];         // activation source row of this lane's two staging loads
-  int piece[2];            // byte offset of this lane's 16-byte piece in a staged row chunk
+  gbyte_t* src[4];         // activation source rows of this lane's staging loads (16/W of them)
+  int piece[4];            // byte offset of this lane's 16-byte piece in a staged row chunk
   uint8_t* xs;             // LDS activation buffers [D][NP][64 rows][256 B]
   const uint32_t* lut;     // CB4 table
   const int* s_pair;       // the group's pair ids
@@ -185,19 +185,20 @@ struct PfCtx {
   uint32_t rt_mask;
 };
 
-// Copy staged chunk s (clamped to the last one) of every group row into buffer buf:
-// this wave's two loads per plane cover rows 4u..4u+3, u = wave and wave + 8.
-template <int NP>
+// Copy staged chunk s (clamped to the last one) of every group row into buffer buf: the
+// 16 one-kilobyte loads per plane (4 rows each) are spread over the W waves, this wave
+// taking u = wave + W q, q < 16/W.
+template <int NP, int W>
 __device__ __forceinline__ void pf_stage(const PfCtx& c, int s, int buf) {
   const int sc = s < c.nks ? s : c.nks - 1;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < 16 / W; ++q) {
     int off = kPfRowBytes * sc + c.piece[q];
     off = off + 16 <= c.row_bytes ? off : 0;  // past the row end: real data, never used
 #pragma unroll
     for (int p = 0; p < NP; ++p)
       pf_load_lds_16(c.src[q] + p * c.act_plane_bytes + off,
-                     c.xs + (buf * NP + p) * kPfPlaneBytes + (c.wave + kPfWaves * q) * 1024);
+                     c.xs + (buf * NP + p) * kPfPlaneBytes + (c.wave + W * q) * 1024);
   }
 }
 
@@ -228,31 +229,31 @@ __device__ __forceinline__ void pf_pin(PfStep<2, 1>& r) {
 // s+D-1 into the buffer every wave has finished with, MFMAs, then the weights of step
 // s+D into the ring slot just consumed.  Straight-line code: every wave issues the same
 // loads at every step, so the wait is a constant.
-template <int FMT, int NP, int D, int SCL, int NTT, int U>
+template <int FMT, int NP, int D, int SCL, int NTT, int U, int W>
 __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s, f32x4_t (&acc)[4][NTT]) {
   // chunk s was issued D-1 steps before step s: after it, this wave issued the weights
   // of one step and (D-2) steps of chunk + weights
-  constexpr int kWait = (D - 1) * pf_loads_per_step<FMT, SCL>() + (D - 2) * 2 * NP;
+  constexpr int kWait = (D - 1) * pf_loads_per_step<FMT, SCL>() + (D - 2) * (16 / W) * NP;
   static_assert(kWait <= 63, "too many loads in flight for the vmcnt counter");
   __builtin_amdgcn_s_waitcnt(pf_vm_le(kWait));
   __builtin_amdgcn_s_barrier();
-  pf_stage<NP>(c, s + D - 1, (U + D - 1) % D);
+  pf_stage<NP, W>(c, s + D - 1, (U + D - 1) % D);
   pf_pin(ring[U]);
   pf_mma_step<FMT, NP, SCL, NTT>(ring[U], c.xs + U * NP * kPfPlaneBytes, s, c.nkb, c.lut, acc);
   pf_load_step<FMT, SCL>(ring[U], c.tile, s + D, c.nks, c.nkb, c.m, c.g);
 }
 
 // The last R (< D) k-steps, straight-line.
-template <int FMT, int NP, int D, int SCL, int NTT, int R>
+template <int FMT, int NP, int D, int SCL, int NTT, int R, int W>
 __device__ __forceinline__ void pf_tail(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s0, f32x4_t (&acc)[4][NTT]) {
-  if constexpr (R >= 1) pf_kstep<FMT, NP, D, SCL, NTT, 0>(c, ring, s0, acc);
-  if constexpr (R >= 2) pf_kstep<FMT, NP, D, SCL, NTT, 1>(c, ring, s0 + 1, acc);
-  if constexpr (R >= 3) pf_kstep<FMT, NP, D, SCL, NTT, 2>(c, ring, s0 + 2, acc);
+  if constexpr (R >= 1) pf_kstep<FMT, NP, D, SCL, NTT, 0, W>(c, ring, s0, acc);
+  if constexpr (R >= 2) pf_kstep<FMT, NP, D, SCL, NTT, 1, W>(c, ring, s0 + 1, acc);
+  if constexpr (R >= 3) pf_kstep<FMT, NP, D, SCL, NTT, 2, W>(c, ring, s0 + 2, acc);
   static_assert(R < 4, "tail longer than supported");
 }
 
 // Main loop and epilogue for a group with NTT live token tiles.
-template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT>
+template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT, int W>
 __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T, const Work& w, int wt, int nt) {
   f32x4_t acc[4][NTT];
 #pragma unroll
@@ -263,21 +264,21 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
   PfStep<FMT, SCL> ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    if (j < D - 1) pf_stage<NP>(c, j, j);
+    if (j < D - 1) pf_stage<NP, W>(c, j, j);
     pf_load_step<FMT, SCL>(ring[j], c.tile, j, c.nks, c.nkb, c.m, c.g);
   }
   const int nfull = c.nks / D * D;
   for (int s0 = 0; s0 < nfull; s0 += D) {
-    pf_kstep<FMT, NP, D, SCL, NTT, 0>(c, ring, s0, acc);
-    if constexpr (D > 1) pf_kstep<FMT, NP, D, SCL, NTT, (D > 1 ? 1 : 0)>(c, ring, s0 + 1, acc);
-    if constexpr (D > 2) pf_kstep<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 0)>(c, ring, s0 + 2, acc);
-    if constexpr (D > 3) pf_kstep<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 0)>(c, ring, s0 + 3, acc);
+    pf_kstep<FMT, NP, D, SCL, NTT, 0, W>(c, ring, s0, acc);
+    if constexpr (D > 1) pf_kstep<FMT, NP, D, SCL, NTT, (D > 1 ? 1 : 0), W>(c, ring, s0 + 1, acc);
+    if constexpr (D > 2) pf_kstep<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 0), W>(c, ring, s0 + 2, acc);
+    if constexpr (D > 3) pf_kstep<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 0), W>(c, ring, s0 + 3, acc);
     static_assert(D <= 4, "deeper rings need more unrolled steps");
   }
   switch (c.nks - nfull) {
-    case 1: pf_tail<FMT, NP, D, SCL, NTT, 1>(c, ring, nfull, acc); break;
-    case 2: pf_tail<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 1)>(c, ring, nfull, acc); break;
-    case 3: pf_tail<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 1)>(c, ring, nfull, acc); break;
+    case 1: pf_tail<FMT, NP, D, SCL, NTT, 1, W>(c, ring, nfull, acc); break;
+    case 2: pf_tail<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 1), W>(c, ring, nfull, acc); break;
+    case 3: pf_tail<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 1), W>(c, ring, nfull, acc); break;
     default: break;
   }
   // the trailing (never used) loads must land before the block's LDS is released
@@ -336,9 +337,9 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
 // grid = RB row blocks x max groups; blocks past RB * n_groups exit.  Block ids are
 // remapped so that the row blocks of one group run on one XCD (consecutive hardware
 // ids go to different XCDs), where they share the group's activation rows in L2.
-template <int FMT, int NP, int D, bool GATEUP, int SCL>
-__global__ __launch_bounds__(kPfThreads) void k_pf_proj(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                       size_t act_plane, int RB) {
+template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
+__global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
+                                                   size_t act_plane, int RB) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int ng = *w.n_groups;
   const int M = RB * ng;
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_proj(LayerArgs L, int T, Work
   c.nks = (c.nkb + 3) >> 2;
   c.row_bytes = 2 * K;
   c.act_plane_bytes = act_plane * 2;
-  const int wt = rb * kPfWaves + c.wave;
+  const int wt = rb * W + c.wave;
 
   c.xs = smem;
   uint32_t* lut = (uint32_t*)(smem + D * NP * kPfPlaneBytes);
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_proj(LayerArgs L, int T, Work
   __syncthreads();
 
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 4 * (c.wave + kPfWaves * q) + (lane >> 4);
+  for (int q = 0; q < 16 / W; ++q) {
+    const int row = 4 * (c.wave + W * q) + (lane >> 4);
     const int p = s_pair[row];
     const int r = GATEUP ? pf_token_of_pair(p, T, k) : p;
     c.src[q] = as_global(act) + (size_t)r * K * 2;
@@ -401,10 +402,10 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_proj(LayerArgs L, int T, Work
   }
 
   switch ((nt + 15) >> 4) {
-    case 1: pf_run<FMT, NP, D, GATEUP, SCL, 1>(c, L, T, w, wt, nt); break;
-    case 2: pf_run<FMT, NP, D, GATEUP, SCL, 2>(c, L, T, w, wt, nt); break;
-    case 3: pf_run<FMT, NP, D, GATEUP, SCL, 3>(c, L, T, w, wt, nt); break;
-    default: pf_run<FMT, NP, D, GATEUP, SCL, 4>(c, L, T, w, wt, nt); break;
+    case 1: pf_run<FMT, NP, D, GATEUP, SCL, 1, W>(c, L, T, w, wt, nt); break;
+    case 2: pf_run<FMT, NP, D, GATEUP, SCL, 2, W>(c, L, T, w, wt, nt); break;
+    case 3: pf_run<FMT, NP, D, GATEUP, SCL, 3, W>(c, L, T, w, wt, nt); break;
+    default: pf_run<FMT, NP, D, GATEUP, SCL, 4, W>(c, L, T, w, wt, nt); break;
   }
 }
 
@@ -424,30 +425,32 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
 }
 
 // ---------------------------------------------------------------------------
-template <int FMT, int NP, int D, bool GATEUP, int SCL>
+template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
 static void pf_launch(const LayerArgs& L, int T, const Work& w, const uint16_t* act, size_t act_plane, int RB,
                       int max_groups_, int stage, hipStream_t s, const Timing& tm) {
   constexpr int lds = pf_lds_bytes(NP, D);
-  auto kern = k_pf_proj<FMT, NP, D, GATEUP, SCL>;
+  auto kern = k_pf_proj<FMT, NP, D, GATEUP, SCL, W>;
   // more than 64 KB of dynamic LDS: raise the kernel's limit once per instantiation
   static const bool lds_ok =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
   (void)lds_ok;
-  MOEQ_LAUNCH(tm, stage, kern, dim3(RB * max_groups_), dim3(kPfThreads), lds, s, L, T, w, act, act_plane, RB);
+  MOEQ_LAUNCH(tm, stage, kern, dim3(RB * max_groups_), dim3(64 * W), lds, s, L, T, w, act, act_plane, RB);
 }
 
-template <int FMT, int SCL, int D>
+// Waves per block: WG for the gate/up kernel, WD for the down kernel.
+template <int FMT, int SCL, int D, int WG, int WD, int DD>
 static void pf_launch_fmt(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int mg,
                           hipStream_t s, const Timing& tm) {
-  const int rb_gu = ((L.I / 32) + kPfWaves - 1) / kPfWaves;
-  const int rb_dn = (((L.H + 63) / 64) + kPfWaves - 1) / kPfWaves;
+  const int rb_gu = ((L.I / 32) + WG - 1) / WG;
+  const int rb_dn = (((L.H + 63) / 64) + WD - 1) / WD;
   const int P = T * L.k + (L.has_shared ? T : 0);
   if (x_dtype == 1)
-    pf_launch<FMT, 1, D, true, SCL>(L, T, w, (const uint16_t*)x, 0, rb_gu, mg, kStageGateUp, s, tm);
+    pf_launch<FMT, 1, D, true, SCL, WG>(L, T, w, (const uint16_t*)x, 0, rb_gu, mg, kStageGateUp, s, tm);
   else  // three exact bf16 planes of fp32 x: at most 3 buffers fit in LDS (2 for CB4's registers)
-    pf_launch<FMT, 3, (FMT == 1 ? 3 : 2), true, SCL>(L, T, w, w.xplanes, (size_t)T * L.H, rb_gu, mg, kStageGateUp,
-                                                     s, tm);
-  pf_launch<FMT, 2, D, false, SCL>(L, T, w, w.hplanes, (size_t)P * L.I, rb_dn, mg, kStageDown, s, tm);
+    pf_launch<FMT, 3, (FMT == 1 ? 3 : 2), true, SCL, kPfWaves>(L, T, w, w.xplanes, (size_t)T * L.H,
+                                                               (L.I / 32 + kPfWaves - 1) / kPfWaves,
+                                                        mg, kStageGateUp, s, tm);
+  pf_launch<FMT, 2, DD, false, SCL, WD>(L, T, w, w.hplanes, (size_t)P * L.I, rb_dn, mg, kStageDown, s, tm);
 }
 
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
@@ -455,11 +458,13 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
   const int P = T * L.k + (L.has_shared ? T : 0);
   const int mg = max_groups(P, L.E);
   if (L.wfmt == 1) {
-    pf_launch_fmt<1, 0, 4>(L, x, x_dtype, T, w, mg, s, tm);
+    pf_launch_fmt<1, 0, 4, kPfWaves, kPfWaves, 4>(L, x, x_dtype, T, w, mg, s, tm);
   } else {
     // both K ranges must be multiples of 128 for the 8-byte scale loads
-    if (L.H % 128 == 0 && L.I % 128 == 0) pf_launch_fmt<2, 1, 3>(L, x, x_dtype, T, w, mg, s, tm);
-    else pf_launch_fmt<2, 0, 2>(L, x, x_dtype, T, w, mg, s, tm);
+    if (L.H % 128 == 0 && L.I % 128 == 0)
+      pf_launch_fmt<2, 1, 3, kPfWaves, kPfWaves, 3>(L, x, x_dtype, T, w, mg, s, tm);
+    else
+      pf_launch_fmt<2, 0, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
   }
   MOEQ_LAUNCH(tm, kStageCombine, k_pf_combine, dim3((L.H + 255) / 256, T), dim3(256), 0, s, T, L.H, L.k,
               L.has_shared, (const float*)w.o, (const float*)w.pair_w, y);

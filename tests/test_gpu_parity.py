@@ -244,3 +244,46 @@ def test_rms_rescale_within_one_bf16_ulp():
     ref = oracle.rms_rescale(y.astype(np.float64))
     diff = np.abs(out.astype(np.int32) - ref.astype(np.int32))
     assert diff.max() <= 1 and (diff == 0).mean() > 0.99
+
+
+# ---------------------------------------------------------------------------
+# 36 stacked gpt-oss-shaped layers (every expert of every layer resident, ~61 GB)
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def stacked_layers():
+    spec = synth.CONFIGS["c4"]
+    layers = [q.DeviceLayer.from_layer(synth.make_layer(spec, layer=l)) for l in range(spec.n_layers)]
+    yield spec, layers
+    del layers
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_stacked_layers_teacher_forced(stacked_layers, T):
+    """Each layer's y, RMS-rescaled on the GPU, is the next layer's x.  Sampled layers are
+    compared with the oracle fed the GPU's own input to that layer (a near-tie at one
+    layer cannot then compound), and every rescale is compared with the oracle's."""
+    spec, layers = stacked_layers
+    ws = layers[0].workspace(T)
+    xs = [_dev(synth.make_x(spec, T=T, layer=0))]
+    ys, dbgs = [], []
+    for l in range(spec.n_layers):
+        y, dbg = q.forward(layers[l], xs[l], spec.x_dtype, ws=ws, debug=True)
+        ys.append(y)
+        dbgs.append(dbg)
+        if l + 1 < spec.n_layers:
+            xs.append(q.rms_rescale(y))
+    torch.cuda.synchronize()
+    for l in range(spec.n_layers - 1):
+        got = xs[l + 1].cpu().numpy().view(np.uint16).astype(np.int32)
+        want = oracle.rms_rescale(ys[l].cpu().numpy().astype(np.float64)).astype(np.int32)
+        assert np.abs(got - want).max() <= 1, f"rescale after layer {l}"
+    for l in (0, spec.n_layers // 2, spec.n_layers - 1):
+        x_l = xs[l].cpu().numpy().view(np.uint16)
+        router = synth.make_layer(spec, layer=l, experts=[])
+        ids_ref, _ = oracle.topk_softmax(
+            oracle.router_logits(oracle.activations_f64(x_l, spec.x_dtype), router.router_w, router.router_b),
+            spec.top_k)
+        used = np.union1d(ids_ref.ravel(), dbgs[l]["ids"].cpu().numpy().ravel())
+        host = synth.make_layer(spec, layer=l, experts=used)
+        check_forward(host, x_l, spec.x_dtype, ys[l], dbgs[l], what=f"stacked layer {l}, T={T}")
