@@ -45,7 +45,7 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, wq, groups,
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, groups,
       n_groups, total;
 };
 
@@ -67,7 +67,6 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
-  o.wq = take((E + 3) * 4);
   o.groups = take((size_t)moeq::max_groups((int)P, (int)E) * 16);
   o.n_groups = take(4);
   o.total = at;
@@ -89,7 +88,6 @@ Work carve(void* ws, const Layout& lo) {
   w.o = reinterpret_cast<float*>(b + lo.o);
   w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
   w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
-  w.wq = reinterpret_cast<uint32_t*>(b + lo.wq);
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
   w.groups = reinterpret_cast<int4*>(b + lo.groups);
   w.n_groups = reinterpret_cast<int32_t*>(b + lo.n_groups);

@@ -72,7 +72,6 @@ struct Work {
   uint16_t* hplanes;   // [2][P][I] bf16 planes of the SwiGLU output (h ~= p0 + p1)
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
   uint32_t* tickets;   // [H/16] arrival counters of the decode combine
-  uint32_t* wq;        // [1 + E + 1] decode work queue: next item, then finished gate/up tiles per slot
   float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)
   struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
   int4* groups;        // prefill work groups: (expert, first bucket position, pairs <= 64, 0)
