@@ -229,11 +229,12 @@ __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, i
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
+      // every lane loads (index clamped into the row): no branch around the loads
       const int e = lane + 64 * i;
       id[t][i] = e < E ? e : 0x7FFFFFFF;
-      const double* src = logits + (size_t)tok[t] * (E + 1) + e;
-      v[t][i] = e >= E ? -__builtin_inf()
-                       : (COHERENT ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src);
+      const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
+      const double lv = COHERENT ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+      v[t][i] = e >= E ? -__builtin_inf() : lv;
     }
 #pragma unroll
   for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t], id[t]);

@@ -72,59 +72,75 @@ __device__ __forceinline__ void topk_wave(const double* __restrict__ logits, int
 }
 
 // Partial logits of one expert row for all T tokens over the columns [h0, h1), by one
-// wave: sum_h x[t][h] w[h] in fp64 (every product exact).  Weights come in chunks of 8
-// float4 per lane with every load issued before the products; tokens in tiles of 4.
-// part[t] receives the wave's sums.
+// wave: sum_h x[t][h] w[h] in fp64 (every product exact).  Branch-free: each lane loads
+// its kPer 4-column chunks of the row once per chunk pass (addresses clamped into the
+// row, values past it masked at use) together with the activation chunks of the first
+// kTB tokens (token index clamped), so a pass starts with one round trip for all its
+// loads.  part[t] receives the wave's sum for token t (summed over passes in order).
+template <int XDT>
+struct RouterX;
+template <>
+struct RouterX<0> {  // fp32 activations
+  using chunk = f32x4_t;
+  __device__ static chunk load(const void* x, size_t off) {
+    return *(const __attribute__((address_space(1))) f32x4_t*)((const float*)x + off);
+  }
+  __device__ static float get(const chunk& c, int q) { return c[q]; }
+};
+template <>
+struct RouterX<1> {  // bf16 activations
+  using chunk = uint64_t;
+  __device__ static chunk load(const void* x, size_t off) {
+    return *(const __attribute__((address_space(1))) uint64_t*)((const uint16_t*)x + off);
+  }
+  __device__ static float get(const chunk& c, int q) { return bf16_bits_to_f32((uint32_t)(c >> (16 * q)) & 0xFFFFu); }
+};
+
 template <int XDT>
 __device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
                                             int h0, int h1, double* __restrict__ part) {
+  using RX = RouterX<XDT>;
   const int lane = threadIdx.x & 63;
-  constexpr int kPer = 8;
-  constexpr int kTT = 4;
-  const int c_end = h1 / 4;
-  for (int t0 = 0; t0 < T; t0 += kTT) {
-    double acc[kTT];
+  constexpr int kPer = 3;  // a quarter of a 2880-column row in one pass
+  constexpr int kTB = 4;
+  const int c_beg = h0 / 4, c_end = h1 / 4;
+  if (c_end <= c_beg) {
+    if (lane == 0)
+      for (int t = 0; t < T; ++t) part[t] = 0.0;
+    return;
+  }
+  for (int c0 = c_beg; c0 < c_end; c0 += 64 * kPer) {
+    f32x4_t wv[kPer];
+    int cc[kPer];
 #pragma unroll
-    for (int u = 0; u < kTT; ++u) acc[u] = 0.0;
-    for (int c0 = h0 / 4; c0 < c_end; c0 += 64 * kPer) {
-      float4 wv[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = c0 + lane + 64 * i;
-        wv[i] = c < c_end ? *(const float4*)(wrow + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = c0 + lane + 64 * i;
-        if (c < c_end) {
-#pragma unroll
-          for (int u = 0; u < kTT; ++u) {
-            const int t = t0 + u;
-            if (t < T) {
-              float x0, x1, x2, x3;
-              if (XDT == 0) {
-                const float4 q = *(const float4*)((const float*)x + (size_t)t * H + 4 * c);
-                x0 = q.x; x1 = q.y; x2 = q.z; x3 = q.w;
-              } else {
-                const uint2 q = *(const uint2*)((const uint16_t*)x + (size_t)t * H + 4 * c);
-                x0 = bf16_bits_to_f32(q.x & 0xFFFFu); x1 = bf16_bits_to_f32(q.x >> 16);
-                x2 = bf16_bits_to_f32(q.y & 0xFFFFu); x3 = bf16_bits_to_f32(q.y >> 16);
-              }
-              double a = acc[u];
-              a = fma((double)wv[i].x, (double)x0, a);
-              a = fma((double)wv[i].y, (double)x1, a);
-              a = fma((double)wv[i].z, (double)x2, a);
-              a = fma((double)wv[i].w, (double)x3, a);
-              acc[u] = a;
-            }
-          }
-        }
-      }
+    for (int i = 0; i < kPer; ++i) {
+      cc[i] = min(c0 + lane + 64 * i, c_end - 1);
+      wv[i] = *(const __attribute__((address_space(1))) f32x4_t*)(wrow + 4 * cc[i]);
     }
+    typename RX::chunk xq[kTB][kPer];
 #pragma unroll
-    for (int u = 0; u < kTT; ++u) {
-      const double sum = wave_sum_f64(acc[u]);
-      if (lane == 0 && t0 + u < T) part[t0 + u] = sum;
+    for (int u = 0; u < kTB; ++u)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)min(u, T - 1) * H + 4 * cc[i]);
+    for (int t0 = 0; t0 < T; t0 += kTB) {
+#pragma unroll
+      for (int u = 0; u < kTB; ++u) {
+        double a = 0.0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const bool ok = c0 + lane + 64 * i < c_end;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a = fma(ok ? (double)wv[i][q] : 0.0, (double)RX::get(xq[u][i], q), a);
+        }
+        const double sum = wave_sum_f64(a);
+        if (lane == 0 && t0 + u < T) part[t0 + u] = c0 == c_beg ? sum : part[t0 + u] + sum;
+      }
+      if (t0 + kTB < T) {
+#pragma unroll
+        for (int u = 0; u < kTB; ++u)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)min(t0 + kTB + u, T - 1) * H + 4 * cc[i]);
+      }
     }
   }
 }
@@ -158,8 +174,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
-  __shared__ const uint8_t* s_gu[1024 + 1];
-  __shared__ const uint8_t* s_dn[1024 + 1];
   __shared__ double s_part[kRouteThreads / 64][kDecMaxTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int kWaves = kRouteThreads / 64;
@@ -182,14 +196,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       }
     }
   }
-  // expert pointer tables and zeroed counts for the route (only the elected block uses
-  // them; loading them here keeps them off its critical path)
-  for (int i = tid; i < nb; i += kRouteThreads) {
-    s_cnt[i] = 0;
-    const bool ok = i < E || L.has_shared;
-    s_gu[i] = ok ? L.gate_up[i] : nullptr;
-    s_dn[i] = ok ? L.down[i] : nullptr;
-  }
+  for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
   {
     // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns
     const int e = blockIdx.x * kRouterRows + (wave >> 2);
@@ -218,6 +225,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     return;
   }
   wait_arrivals(rr_flags, gridDim.x);
+  // thread e's expert pointers for the slot records: issued now, used at the end
+  const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
+  const uint8_t* const my_gu = L.gate_up[ie];
+  const uint8_t* const my_dn = L.down[ie];
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
@@ -295,8 +306,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       w.active[1 + a] = e;
       Slot& sl = w.slots[a];
       sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
-      sl.gate_up = s_gu[e];
-      sl.down = s_dn[e];
+      sl.gate_up = e == tid ? my_gu : L.gate_up[e];
+      sl.down = e == tid ? my_dn : L.down[e];
     }
   }
   for (int a = n_active + tid; a < max_slots; a += kRouteThreads) {

@@ -33,7 +33,49 @@ constexpr int kPfWaves = 8;  // waves per block (eight 64-row wave tiles: 512 we
 constexpr int kPfRowBytes = 256;                         // one staged row chunk: 128 bf16
 constexpr int kPfPlaneBytes = kGroupPairs * kPfRowBytes;  // 16 KB per plane per buffer
 
-__host__ __device__ constexpr int pf_lds_bytes(int np, int d) { return d * np * kPfPlaneBytes + 1024 + 256; }
+// CB4 decode table at LDS offset 0, in one of two forms:
+//  - replicated, one copy per lane: the entry for code byte b (two bf16 values) of lane
+//    l sits at byte 256 b + 4 l, so the 64 lanes of a lookup always hit 64 distinct
+//    dword slots of one 256-byte row, whatever their code bytes (no bank conflicts),
+//    and a lookup address is one byte permute of the code word; 64 KB;
+//  - a single 1 KB copy (lookups conflict by chance) where the 64 KB do not fit beside
+//    the activation buffers.
+constexpr int kPfLutReplBytes = 256 * 64 * 4;
+constexpr int kPfLdsMax = 160 * 1024;
+
+__host__ __device__ constexpr bool pf_lut_repl(int fmt, int np, int d) {
+  return fmt == 2 && kPfLutReplBytes + d * np * kPfPlaneBytes + 4 * kGroupPairs <= kPfLdsMax;
+}
+__host__ __device__ constexpr int pf_lut_bytes(int fmt, int np, int d) {
+  return fmt != 2 ? 0 : pf_lut_repl(fmt, np, d) ? kPfLutReplBytes : 1024;
+}
+// LUT, then the D x NP activation buffers, then the group's 64 pair ids.
+__host__ __device__ constexpr int pf_lds_bytes(int fmt, int np, int d) {
+  return pf_lut_bytes(fmt, np, d) + d * np * kPfPlaneBytes;
+}
+__host__ __device__ constexpr int pf_lds_total(int fmt, int np, int d) {
+  return pf_lds_bytes(fmt, np, d) + 4 * kGroupPairs;
+}
+
+__device__ __forceinline__ void pf_build_lut(uint32_t* lut, const int8_t* codebook) {
+  for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) {
+    const int b = i >> 6;
+    lut[i] = int8_to_bf16_bits(codebook[b & 15]) | (int8_to_bf16_bits(codebook[b >> 4]) << 16);
+  }
+}
+
+// Eight CB4 values (one code word) -> bf16: byte i of the code word indexes row i of the
+// table; the address is (code byte << 8) | (4 lane), assembled by v_perm_b32 from the
+// code word (high source) and the lane offset (low source).
+__device__ __forceinline__ bf16x8_t pf_cb4x8(uint32_t codes, uint32_t lane_off) {
+  u32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t addr = __builtin_amdgcn_perm(codes, lane_off, 0x0C0C0000u | ((4u + i) << 8));
+    v[i] = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)addr;
+  }
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // s_waitcnt immediate: at most n vector-memory operations of this wave outstanding.
 __host__ __device__ constexpr int pf_vm_le(int n) {
@@ -107,9 +149,9 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
 
 // Branch-free: all 4 row tiles are computed (a row tile past the matrix holds clamped
 // real rows whose results are not stored) and NTT token tiles are live.
-template <int FMT, int NP, int SCL, int NTT>
+template <int FMT, int NP, int SCL, int NTT, bool REPL>
 __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uint8_t* xb, int ks, int nkb,
-                                            const uint32_t* lut, f32x4_t (&acc)[4][NTT]) {
+                                            uint32_t lane_off, const uint32_t* lut, f32x4_t (&acc)[4][NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   if constexpr (FMT == 1) {
@@ -136,13 +178,16 @@ __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uin
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool kval = 4 * ks + j < nkb;  // a block past the row adds 0 x (finite products)
+      // a block past the row adds 0 x (finite products); with 8-byte scale loads K is a
+      // multiple of 128 and every block of a step is real
+      const bool kval = SCL == 1 || 4 * ks + j < nkb;
       {
         bf16x8_t b[4];
         float sc[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          b[rt] = cb4x8_to_bf16(r.c[rt][j], lut);
+          if constexpr (REPL) b[rt] = pf_cb4x8(r.c[rt][j], lane_off);
+          else b[rt] = cb4x8_to_bf16(r.c[rt][j], lut);
           uint32_t sb;
           if constexpr (SCL == 1) sb = (uint32_t)(r.s[rt] >> (16 * j));
           else sb = r.s[rt][j];
@@ -178,8 +223,10 @@ struct PfCtx {
   gbyte_t* src[4];         // activation source rows of this lane's staging loads (16/W of them)
   int piece[4];            // byte offset of this lane's 16-byte piece in a staged row chunk
   uint8_t* xs;             // LDS activation buffers [D][NP][64 rows][256 B]
-  const uint32_t* lut;     // CB4 table
-  const int* s_pair;       // the group's pair ids
+  uint32_t lane_off;       // 4 x lane: this lane's column of the replicated CB4 table
+  const uint32_t* lut;     // the CB4 table (LDS offset 0)
+  int start;               // the group's first bucket position
+  const int* s_pair;       // the group's pair ids in LDS (when they fit there)
   size_t act_plane_bytes;
   int nks, nkb, row_bytes, wave, g, m;
   uint32_t rt_mask;
@@ -239,7 +286,8 @@ __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring
   __builtin_amdgcn_s_barrier();
   pf_stage<NP, W>(c, s + D - 1, (U + D - 1) % D);
   pf_pin(ring[U]);
-  pf_mma_step<FMT, NP, SCL, NTT>(ring[U], c.xs + U * NP * kPfPlaneBytes, s, c.nkb, c.lut, acc);
+  pf_mma_step<FMT, NP, SCL, NTT, pf_lut_repl(FMT, NP, D)>(ring[U], c.xs + U * NP * kPfPlaneBytes, s, c.nkb,
+                                                         c.lane_off, c.lut, acc);
   pf_load_step<FMT, SCL>(ring[U], c.tile, s + D, c.nks, c.nkb, c.m, c.g);
 }
 
@@ -285,6 +333,15 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
   __builtin_amdgcn_s_waitcnt(pf_vm_le(0));
 
   const int g = c.g, m = c.m;
+  // pair ids of this lane's output slots, fetched together before the stores
+  int pid[NTT][4];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int slot = min(16 * tt + 4 * g + q, nt - 1);
+      pid[tt][q] = c.s_pair[slot];
+    }
   if (GATEUP) {
     if (c.rt_mask) {
       const int I = L.I;
@@ -298,7 +355,7 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
           for (int q = 0; q < 4; ++q) {
             const int slot = 16 * tt + 4 * g + q;
             if (slot < nt) {
-              const int p = c.s_pair[slot];
+              const int p = pid[tt][q];
               const float h = silu_f32(acc[rt][tt][q]) * acc[rt + 2][tt][q];
               const uint32_t hi = f32_to_bf16_rne(h);
               const uint32_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
@@ -320,7 +377,7 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int slot = 16 * tt + 4 * g + q;
-            if (slot < nt) w.o[(size_t)c.s_pair[slot] * H + col] = acc[rt][tt][q];
+            if (slot < nt) w.o[(size_t)pid[tt][q] * H + col] = acc[rt][tt][q];
           }
         }
       }
@@ -364,19 +421,24 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   c.act_plane_bytes = act_plane * 2;
   const int wt = rb * W + c.wave;
 
-  c.xs = smem;
-  uint32_t* lut = (uint32_t*)(smem + D * NP * kPfPlaneBytes);
-  int* s_pair = (int*)(smem + D * NP * kPfPlaneBytes + 1024);
-  c.lut = lut;
+  c.xs = smem + pf_lut_bytes(FMT, NP, D);
+  c.start = start;
+  c.lane_off = 4u * (uint32_t)lane;
+  c.lut = (const uint32_t*)smem;
+  if (FMT == 2) {
+    if constexpr (pf_lut_repl(FMT, NP, D)) pf_build_lut((uint32_t*)smem, L.codebook);
+    else build_cb4_lut((uint32_t*)smem, L.codebook);
+  }
+  int* s_pair = (int*)(smem + pf_lds_bytes(FMT, NP, D));
   c.s_pair = s_pair;
-  if (threadIdx.x < kGroupPairs) s_pair[threadIdx.x] = w.perm[start + ((int)threadIdx.x < nt ? threadIdx.x : 0)];
-  if (FMT == 2) build_cb4_lut(lut, L.codebook);
+  if (threadIdx.x < kGroupPairs)
+    s_pair[threadIdx.x] = w.perm[start + ((int)threadIdx.x < nt ? (int)threadIdx.x : 0)];
   __syncthreads();
 
 #pragma unroll
   for (int q = 0; q < 16 / W; ++q) {
     const int row = 4 * (c.wave + W * q) + (lane >> 4);
-    const int p = s_pair[row];
+    const int p = w.perm[start + (row < nt ? row : 0)];
     const int r = GATEUP ? pf_token_of_pair(p, T, k) : p;
     c.src[q] = as_global(act) + (size_t)r * K * 2;
     c.piece[q] = 16 * ((lane & 15) ^ (row & 15));
@@ -428,7 +490,8 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
 static void pf_launch(const LayerArgs& L, int T, const Work& w, const uint16_t* act, size_t act_plane, int RB,
                       int max_groups_, int stage, hipStream_t s, const Timing& tm) {
-  constexpr int lds = pf_lds_bytes(NP, D);
+  constexpr int lds = pf_lds_total(FMT, NP, D);
+  static_assert(lds <= kPfLdsMax, "LDS budget of one workgroup");
   auto kern = k_pf_proj<FMT, NP, D, GATEUP, SCL, W>;
   // more than 64 KB of dynamic LDS: raise the kernel's limit once per instantiation
   static const bool lds_ok =
