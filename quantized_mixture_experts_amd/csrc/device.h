@@ -136,34 +136,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
 }
 
-// (value, index) maximum over the wave: larger value first, lower index on ties;
-// index 0x7FFFFFFF marks an empty candidate.  Returned to every lane.
-__device__ __forceinline__ bool argmax_better(double ov, int oi, double bv, int bi) {
-  return oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-}
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(double& bv, int& bi) {
-  const double ov = dpp_f64<CTRL>(bv);
-  const int oi = dpp_i32<CTRL>(bi);
-  if (argmax_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-}
-__device__ __forceinline__ void wave_argmax(double& bv, int& bi) {
-  argmax_step<kDppRowRor1>(bv, bi);
-  argmax_step<kDppRowRor2>(bv, bi);
-  argmax_step<kDppRowRor4>(bv, bi);
-  argmax_step<kDppRowRor8>(bv, bi);
-  double v = readlane_f64(bv, 0);
-  int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const double ov = readlane_f64(bv, r);
-    const int oi = __builtin_amdgcn_readlane(bi, r);
-    if (argmax_better(ov, oi, v, i)) { v = ov; i = oi; }
-  }
-  bv = v;
-  bi = i;
-}
-
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += __builtin_bit_cast(float, dpp_i32<kDppRowRor1>(__builtin_bit_cast(int, v)));
   v += __builtin_bit_cast(float, dpp_i32<kDppRowRor2>(__builtin_bit_cast(int, v)));
@@ -190,83 +162,92 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 // (-logit, e); every round takes the wave maximum of the lanes' heads, finds the lane
 // holding it (exact ties between lanes go to the lowest expert index) and that lane
 // pops its head.  Empty candidates hold -inf and index 0x7FFFFFFF.
-__device__ __forceinline__ bool cand_before(double va, int ia, double vb, int ib) {
-  return ia != 0x7FFFFFFF && (ib == 0x7FFFFFFF || va > vb || (va == vb && ia < ib));
+// ---- top-k on 64-bit selection keys ----
+// key(v, e): the fp64 bits of v mapped to an unsigned integer of the same order (sign
+// bit flipped for v >= 0, all bits inverted for v < 0), with the low 10 bits replaced
+// by 1023 - e.  A larger key is a larger logit, and on equal upper bits the lower
+// expert index; so one unsigned maximum picks the winner, exact ties going to the lower
+// index.  Two logits that differ only in the 10 dropped bits (less than 2^-42 of their
+// magnitude) also order by index.  Key 0 marks an empty candidate (E <= 1024).
+__device__ __forceinline__ uint64_t topk_key(double v, int e) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t o = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (o & ~1023ull) | (uint64_t)(1023 - e);
 }
+__device__ __forceinline__ int topk_key_index(uint64_t key) { return 1023 - (int)(key & 1023ull); }
+// The logit a key stands for (its dropped low bits zero in the key's order).
+__device__ __forceinline__ double topk_key_value(uint64_t key) {
+  const uint64_t o = key & ~1023ull;
+  const uint64_t b = (o >> 63) ? (o & 0x7FFFFFFFFFFFFFFFull) : ~o;
+  return __builtin_bit_cast(double, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = dpp_i32<CTRL>((int)(uint32_t)v);
+  const int hi = dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t m) {
+  m = max_u64(m, dpp_u64<kDppRowRor1>(m));
+  m = max_u64(m, dpp_u64<kDppRowRor2>(m));
+  m = max_u64(m, dpp_u64<kDppRowRor4>(m));
+  m = max_u64(m, dpp_u64<kDppRowRor8>(m));
+  return max_u64(max_u64(readlane_u64(m, 0), readlane_u64(m, 16)), max_u64(readlane_u64(m, 32), readlane_u64(m, 48)));
+}
+// Descending order of a lane's candidates (odd-even transposition, static indices).
 template <int NPER>
-__device__ __forceinline__ void sort_lane(double (&v)[NPER], int (&id)[NPER]) {
-  // odd-even transposition sort (NPER passes), static indices only
+__device__ __forceinline__ void sort_lane(uint64_t (&v)[NPER]) {
 #pragma unroll
   for (int pass = 0; pass < NPER; ++pass) {
 #pragma unroll
     for (int i = pass & 1; i + 1 < NPER; i += 2) {
-      const bool sw = cand_before(v[i + 1], id[i + 1], v[i], id[i]);
-      const double tv = v[i];
-      const int ti = id[i];
-      v[i] = sw ? v[i + 1] : v[i];
-      id[i] = sw ? id[i + 1] : id[i];
-      v[i + 1] = sw ? tv : v[i + 1];
-      id[i + 1] = sw ? ti : id[i + 1];
+      const uint64_t hi = max_u64(v[i], v[i + 1]), lo = v[i] > v[i + 1] ? v[i + 1] : v[i];
+      v[i] = hi;
+      v[i + 1] = lo;
     }
   }
 }
-__device__ __forceinline__ double wave_max_f64(double m) {
-  m = fmax(m, dpp_f64<kDppRowRor1>(m));
-  m = fmax(m, dpp_f64<kDppRowRor2>(m));
-  m = fmax(m, dpp_f64<kDppRowRor4>(m));
-  m = fmax(m, dpp_f64<kDppRowRor8>(m));
-  return fmax(fmax(readlane_f64(m, 0), readlane_f64(m, 16)), fmax(readlane_f64(m, 32), readlane_f64(m, 48)));
-}
 // COHERENT: the logits were written by other blocks of the running kernel.  Token t's
-// selections go to s_exp/s_l[slot[t] * k + j] (written by lane 0).
+// selections go to s_exp/s_l[slot[t] * k + j] (written by lane 0), j = 0 .. k-1 in
+// selection order.
 template <int NPER, int NT, bool COHERENT>
 __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
                                             const int (&slot)[NT], int* s_exp, double* s_l) {
   const int lane = threadIdx.x & 63;
-  double v[NT][NPER];
-  int id[NT][NPER];
+  uint64_t v[NT][NPER];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       // every lane loads (index clamped into the row): no branch around the loads
       const int e = lane + 64 * i;
-      id[t][i] = e < E ? e : 0x7FFFFFFF;
       const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
       const double lv = COHERENT ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
-      v[t][i] = e >= E ? -__builtin_inf() : lv;
+      v[t][i] = e < E ? topk_key(lv, e) : 0ull;
     }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t], id[t]);
+  for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t]);
   for (int j = 0; j < k; ++j) {
-    double m[NT];
-    int win[NT];
+    uint64_t m[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) m[t] = wave_max_f64(v[t][0]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint64_t hold = __ballot(id[t][0] != 0x7FFFFFFF && v[t][0] == m[t]);
-      int wl = (int)__ffsll((long long)hold) - 1;
-      int w0 = __builtin_amdgcn_readlane(id[t][0], wl);
-      hold &= hold - 1;
-      while (hold) {  // exact tie between lanes: the lowest expert index wins
-        const int l = (int)__ffsll((long long)hold) - 1;
-        hold &= hold - 1;
-        w0 = min(w0, __builtin_amdgcn_readlane(id[t][0], l));
-      }
-      win[t] = w0;
-    }
+    for (int t = 0; t < NT; ++t) m[t] = wave_max_u64(v[t][0]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (lane == 0) { s_exp[slot[t] * k + j] = win[t]; s_l[slot[t] * k + j] = m[t]; }
-      const bool pop = (win[t] & 63) == lane;
-#pragma unroll
-      for (int i = 0; i + 1 < NPER; ++i) {
-        v[t][i] = pop ? v[t][i + 1] : v[t][i];
-        id[t][i] = pop ? id[t][i + 1] : id[t][i];
+      if (lane == 0) {
+        s_exp[slot[t] * k + j] = topk_key_index(m[t]);
+        s_l[slot[t] * k + j] = topk_key_value(m[t]);
       }
-      v[t][NPER - 1] = pop ? -__builtin_inf() : v[t][NPER - 1];
-      id[t][NPER - 1] = pop ? 0x7FFFFFFF : id[t][NPER - 1];
+      const bool pop = v[t][0] == m[t];  // keys are unique: exactly one lane
+#pragma unroll
+      for (int i = 0; i + 1 < NPER; ++i) v[t][i] = pop ? v[t][i + 1] : v[t][i];
+      v[t][NPER - 1] = pop ? 0ull : v[t][NPER - 1];
     }
   }
 }
