@@ -358,15 +358,16 @@ struct WeightRegs<2, KSW> {
   uint32_t s[KSW][4];  // fp16 scale bits of blocks 4ks..4ks+3
 };
 
-// Loads of one wave's k-steps ks0, ks0+4, ... of one 16-row weight tile.  Straight-line
+// Loads of one wave's k-steps ks0, ks0+stride, ... of one 16-row weight tile (stride 4:
+// the 4 waves split K; stride 1: the wave takes every k-step).  Straight-line
 // code with clamped addresses and no use of the loaded values here, so each k-step's
 // MFMAs wait only for their own loads.  Out-of-range data is never used: k-steps past
 // the row are skipped and k blocks past the row meet a zero activation operand.
 template <int FMT, int KSW>
 __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, const PackedTile& pt, int nkb, int ks0,
-                                              int nks, int m, int g) {
+                                              int nks, int m, int g, int stride = 4) {
   {
-    const int ks = ks0 + 4 * i;
+    const int ks = ks0 + stride * i;
     if constexpr (FMT == 1) {
       const int kb = 4 * ks + g;
       const int kbc = (ks < nks && kb < nkb) ? kb : 0;
@@ -388,9 +389,9 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
 
 template <int FMT, int KSW>
 __device__ __forceinline__ void prefetch_weights(WeightRegs<FMT, KSW>& r, const PackedTile& pt, int nkb, int ks0,
-                                                 int nks, int m, int g) {
+                                                 int nks, int m, int g, int stride = 4) {
 #pragma unroll
-  for (int i = 0; i < KSW; ++i) prefetch_step<FMT, KSW>(r, i, pt, nkb, ks0, nks, m, g);
+  for (int i = 0; i < KSW; ++i) prefetch_step<FMT, KSW>(r, i, pt, nkb, ks0, nks, m, g, stride);
 }
 
 // Two tiles (gate and up rows) k-step by k-step, so a k-step's MFMAs of both tiles
@@ -566,7 +567,6 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const int H = L.H, I = L.I, k = L.k;
   const int K = H, nkb = K >> 5, nks = (nkb + 3) >> 2;
   const int xstride = lds_row_stride(K);
-  const int nslots = 16 * NTT;
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const PackedTile pu = packed_tile(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x, FMT == 1 ? 1 : 2);
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
-  for (int tb = 0; tb < cnt; tb += nslots) {
+  for (int tb = 0; tb < cnt; tb += xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
     f32x4_t accg[NTT], accu[NTT];
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int slot = tb + 16 * tt + 4 * g + q;
-          if (slot < cnt) {
+          if (slot < tb + xrows) {  // this pass's pairs only
             const int p = w.perm[off + slot];
             const float h = silu_f32(v[8 * tt + q]) * v[8 * tt + 4 + q];
             const uint32_t hi = f32_to_bf16_rne(h);
@@ -653,14 +653,13 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   const int P = T * k + (L.has_shared ? T : 0);
   const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
   const int xstride = lds_row_stride(K);
-  const int nslots = 16 * NTT;
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
   const PackedTile pd = packed_tile(slot_rec->down, H, K, blockIdx.x, FMT == 1 ? 1 : 2);
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
-  for (int tb = 0; tb < cnt; tb += nslots) {
+  for (int tb = 0; tb < cnt; tb += xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
     f32x4_t acc[NTT];
@@ -699,7 +698,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int slot = tb + 16 * tt + 4 * g + q;
-          if (slot < cnt)
+          if (slot < tb + xrows)  // this pass's pairs only
             __hip_atomic_store(&w.o[(size_t)w.perm[off + slot] * H + col], v[4 * tt + q], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -719,6 +718,98 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   for (int idx = threadIdx.x; idx < T * 16; idx += 256) {
     const int t = idx >> 4;
     const int col = 16 * blockIdx.x + (idx & 15);
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float o = __hip_atomic_load(&w.o[(size_t)(t * k + j) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s = fmaf(w.pair_w[t * k + j], o, s);
+    }
+    if (L.has_shared) {
+      const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s = fmaf(w.pair_w[T * k + t], o, s);
+    }
+    y[(size_t)t * H + col] = s;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// 4'. Down projection for short rows (K = I of at most 4 k-steps of 128 columns):
+// instead of splitting K over the 4 waves, each wave owns one 16-row tile over the
+// whole K, so a block covers 64 output columns with no split-K reduction.
+// grid = (ceil(H/64), max active slots).  TICKETS: per 64 columns a ticket elects the
+// last block, which sums y in the fixed order (few active experts); otherwise o is
+// written plainly and a separate combine kernel follows (many active experts, where
+// one ticket would take an atomic per expert on a single address).
+// ---------------------------------------------------------------------------
+template <int FMT, int NTT, int KSW, bool TICKETS>
+__global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Work w, float* __restrict__ y,
+                                                          uint32_t* __restrict__ tickets, int xrows_max) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int is_last;
+  const Slot* slot_rec = w.slots + blockIdx.y;
+  const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
+  if (cnt == 0) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int H = L.H, I = L.I, k = L.k;
+  const int P = T * k + (L.has_shared ? T : 0);
+  const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
+  const int xstride = lds_row_stride(K);
+  const size_t lds_plane = (size_t)xrows_max * xstride;
+  uint32_t* lut = (uint32_t*)smem;
+  uint16_t* xs = (uint16_t*)(smem + 1024);
+  const int tile = 4 * blockIdx.x + wave;  // this wave's 16 output columns
+  const bool tile_ok = 16 * tile < H;
+  const PackedTile pd = packed_tile(slot_rec->down, H, K, tile_ok ? tile : 0, FMT == 1 ? 1 : 2);
+
+  for (int tb = 0; tb < cnt; tb += xrows_max) {
+    const int live = min(NTT, (cnt - tb + 15) / 16);
+    const int xrows = min(cnt - tb, xrows_max);
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tb > 0) __syncthreads();
+    else if (FMT == 2) build_cb4_lut(lut, L.codebook);
+    stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb, xrows,
+                             T, k);
+    WeightRegs<FMT, KSW> wd;
+    prefetch_weights<FMT, KSW>(wd, pd, nkb, 0, nks, n, g, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < KSW; ++i)
+      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, acc);
+    if (tile_ok) {
+      const int col = 16 * tile + n;
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int slot = tb + 16 * tt + 4 * g + q;
+          if (slot < tb + xrows) {  // this pass's pairs only
+            float* dst = &w.o[(size_t)w.perm[off + slot] * H + col];
+            if constexpr (TICKETS) __hip_atomic_store(dst, acc[tt][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = acc[tt][q];
+          }
+        }
+    }
+  }
+  if constexpr (!TICKETS) return;
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == (uint32_t)(n_active - 1));
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  for (int idx = threadIdx.x; idx < T * 64; idx += 256) {
+    const int t = idx >> 6;
+    const int col = 64 * blockIdx.x + (idx & 63);
+    if (col >= H) continue;
     float s = 0.f;
     for (int j = 0; j < k; ++j) {
       const float o = __hip_atomic_load(&w.o[(size_t)(t * k + j) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -762,6 +853,25 @@ static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int 
                 s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows);
 }
 
+// Active slots above which the combine runs as its own kernel instead of ticketed.
+constexpr int kTicketSlotsMax = 24;
+
+template <int FMT, int NTT, int KSW>
+static void launch_down_rows_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
+                               hipStream_t s, const Timing& tm) {
+  const int slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
+  const dim3 g2((L.H + 63) / 64, slots);
+  const size_t lds = dec_lds_bytes(L.I, 2, NTT, xrows);
+  if (slots <= kTicketSlotsMax) {
+    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, true>), g2, dim3(256), lds, s, L, T, w, y, tickets,
+                xrows);
+  } else {
+    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, false>), g2, dim3(256), lds, s, L, T, w, y, tickets,
+                xrows);
+    (void)launch_combine(L, T, w, y, s, tm);
+  }
+}
+
 template <int FMT, int NTT, int KSW>
 static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                           hipStream_t s, const Timing& tm) {
@@ -770,16 +880,39 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
               T, w, y, tickets, xrows);
 }
 
+// Rows of activations a projection block stages per pass: as many of the expert's
+// pairs as fit in kDecStageBytes of LDS (at least 1, at most T), so that several blocks
+// share a CU whatever T is; an expert with more pairs takes several passes.
+constexpr size_t kDecStageBytes = 32 * 1024;
+static int dec_rows_per_pass(int K, int NP, int T) {
+  const size_t row = (size_t)lds_row_stride(K) * 2 * NP;
+  const int cap = (int)(kDecStageBytes / row);
+  return max(1, min(T, min(cap, kDecMaxTokens)));
+}
+
 template <int FMT, int NTT>
-static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
-                                     uint32_t* tickets, hipStream_t s, const Timing& tm) {
-  const int xrows = min(T, 16 * NTT);  // an expert holds at most T pairs
+static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
+                              hipStream_t s, const Timing& tm) {
   switch (pick_ksw(L.H)) {
     case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, s, tm); break;
     case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, s, tm); break;
     case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, s, tm); break;
     case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, s, tm); break;
     default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, s, tm); break;
+  }
+}
+
+template <int FMT, int NTT>
+static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
+                            hipStream_t s, const Timing& tm) {
+  const int nks_dn = (L.I / 32 + 3) / 4;
+  if (nks_dn <= 4) {  // short rows: one 16-row tile per wave over the whole K
+    switch (nks_dn) {
+      case 1: launch_down_rows_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm); break;
+      case 2: launch_down_rows_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, s, tm); break;
+      default: launch_down_rows_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, s, tm); break;
+    }
+    return;
   }
   switch (pick_ksw(L.I)) {
     case 1: launch_down_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm); break;
@@ -788,14 +921,27 @@ static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dt
     case 6: launch_down_k<FMT, NTT, 6>(L, T, w, y, tickets, xrows, s, tm); break;
     default: launch_down_k<FMT, NTT, 8>(L, T, w, y, tickets, xrows, s, tm); break;
   }
+}
+
+// Token tiles per pass follow the rows staged per pass (16 or 32).
+template <int FMT>
+static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
+                                     uint32_t* tickets, hipStream_t s, const Timing& tm) {
+  const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T);
+  const int xd = dec_rows_per_pass(L.I, 2, T);
+  if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, s, tm);
+  else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, s, tm);
+  if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, s, tm);
+  else launch_dec_down<FMT, 2>(L, T, w, y, tickets, xd, s, tm);
   return hipGetLastError();
 }
 
 bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   if (T > kDecMaxTokens) return false;
-  const int NTT = T <= 16 ? 1 : 2;
-  const size_t g = dec_lds_bytes(L.H, x_dtype == 1 ? 1 : 3, NTT, T);
-  const size_t d = dec_lds_bytes(L.I, 2, NTT, T);
+  const int np = x_dtype == 1 ? 1 : 3;
+  const int xg = dec_rows_per_pass(L.H, np, T), xd = dec_rows_per_pass(L.I, 2, T);
+  const size_t g = dec_lds_bytes(L.H, np, xg <= 16 ? 1 : 2, xg);
+  const size_t d = dec_lds_bytes(L.I, 2, xd <= 16 ? 1 : 2, xd);
   return g <= 160 * 1024 && d <= 160 * 1024;
 }
 
@@ -814,11 +960,8 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
                 w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (T <= 16)
-    return L.wfmt == 1 ? launch_dec_experts<1, 1>(L, x, x_dtype, T, w, y, w.tickets, s, tm)
-                       : launch_dec_experts<2, 1>(L, x, x_dtype, T, w, y, w.tickets, s, tm);
-  return L.wfmt == 1 ? launch_dec_experts<1, 2>(L, x, x_dtype, T, w, y, w.tickets, s, tm)
-                     : launch_dec_experts<2, 2>(L, x, x_dtype, T, w, y, w.tickets, s, tm);
+  return L.wfmt == 1 ? launch_dec_experts<1>(L, x, x_dtype, T, w, y, w.tickets, s, tm)
+                     : launch_dec_experts<2>(L, x, x_dtype, T, w, y, w.tickets, s, tm);
 }
 
 }  // namespace moeq

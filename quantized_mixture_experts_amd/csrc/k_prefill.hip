@@ -529,6 +529,10 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
     else
       pf_launch_fmt<2, 0, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
   }
+  return launch_combine(L, T, w, y, s, tm);
+}
+
+hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, float* y, hipStream_t s, const Timing& tm) {
   MOEQ_LAUNCH(tm, kStageCombine, k_pf_combine, dim3((L.H + 255) / 256, T), dim3(256), 0, s, T, L.H, L.k,
               L.has_shared, (const float*)w.o, (const float*)w.pair_w, y);
   return hipGetLastError();

@@ -37,6 +37,8 @@ hipError_t launch_bucket(int T, int k, int E, int has_shared, const int32_t* ids
                          const Timing& tm = Timing());
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
                           hipStream_t s, const Timing& tm = Timing());
+// y[t] = sum_j g[t,j] o[t*k+j] (+ shared), fixed order, from the o rows in the workspace.
+hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, float* y, hipStream_t s, const Timing& tm);
 // Decode path (T <= 32 and the activation tiles fit in LDS).
 bool decode_path_fits(const LayerArgs& L, int T, int x_dtype);
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
