@@ -18,8 +18,9 @@ namespace moeq {
 // A = activations (tokens x k), B = router rows (k x experts); every product of a
 // bf16/fp32 activation and an fp32 weight is exact in fp64 and the matrix core sums in
 // fp64, so only the summation order differs from a plain fp64 loop.
-// Block: 32 tokens x 16 expert rows; its 4 waves split K in 16-column chunks (wave w
-// takes chunks w, w+4, ...) and are summed in wave order.  Each lane loads 4
+// Block: 32 tokens x 16 expert rows; its 8 waves (two per SIMD, so that one wave's
+// loads are in flight while the other's MFMAs run) split K in 16-column chunks (wave w
+// takes chunks w, w+8, ...) and are summed in wave order.  Each lane loads 4
 // consecutive k of its token rows and its expert row; MFMA step q pairs element q of
 // both, so a chunk's 4 steps cover its 16 columns.  Row E (with a shared-gate vector)
 // is w_sg.  Blocks of the first expert tile also write the exact 3-plane bf16 split of
@@ -27,10 +28,13 @@ namespace moeq {
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 
+constexpr int kRouterWaves = 8;
+
 template <int XDT>
-__global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __restrict__ x, int T, int erows,
-                                                     double* __restrict__ logits, uint16_t* __restrict__ xplanes) {
-  __shared__ double red[3][2][4][64];
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, const void* __restrict__ x, int T,
+                                                                  int erows, double* __restrict__ logits,
+                                                                  uint16_t* __restrict__ xplanes) {
+  __shared__ double red[kRouterWaves - 1][2][4][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, kk = lane >> 4;
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 16;
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __
   if (XDT == 0 && blockIdx.y == 0) {
     const float* xf = (const float*)x;
     const int nt = min(32, T - t0);
-    for (int idx = threadIdx.x; idx < nt * H; idx += 256) {
+    for (int idx = threadIdx.x; idx < nt * H; idx += 64 * kRouterWaves) {
       const size_t o = (size_t)t0 * H + idx;
       const float v = xf[o];
       const uint32_t p0 = f32_to_bf16_rne(v);
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __
   f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
   const int nch = H >> 4;
 #pragma unroll 4
-  for (int ch = wave; ch < nch; ch += 4) {
+  for (int ch = wave; ch < nch; ch += kRouterWaves) {
     const int k = 16 * ch + 4 * kk;
     double a0[4], a1[4], b[4];
     const float4 wv = *(const float4*)(wrow + k);
@@ -92,8 +96,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(LayerArgs L, const void* __
     const double bias = (col < L.E && L.router_b) ? (double)L.router_b[col] : 0.0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const double s0 = ((acc0[r] + red[0][0][r][lane]) + red[1][0][r][lane]) + red[2][0][r][lane];
-      const double s1 = ((acc1[r] + red[0][1][r][lane]) + red[1][1][r][lane]) + red[2][1][r][lane];
+      double s0 = acc0[r], s1 = acc1[r];
+#pragma unroll
+      for (int v = 0; v < kRouterWaves - 1; ++v) {
+        s0 += red[v][0][r][lane];
+        s1 += red[v][1][r][lane];
+      }
       const int row = 4 * r + kk;  // token within the 16-token tile
       if (col < erows) {
         if (t0 + row < T) logits[(size_t)(t0 + row) * (L.E + 1) + col] = s0 + bias;
@@ -256,9 +264,9 @@ hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, in
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
   dim3 grid((T + 31) / 32, (erows + 15) / 16);
   if (x_dtype == 0)
-    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<0>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
+    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<0>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
   else
-    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<1>, grid, dim3(256), 0, s, L, x, T, erows, w.logits, w.xplanes);
+    MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<1>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
   MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits, w.ids,
               w.pair_w, dbg_ids, dbg_w);
   return hipGetLastError();
