@@ -15,7 +15,12 @@
 //     (direct global->LDS loads; the 16-byte pieces of a row are XOR-swizzled by row so
 //     that the MFMA operand reads hit 16 distinct bank groups), D-1 chunks ahead, in D
 //     rotating buffers;
-//   - weights: each wave streams its own rows into a register ring D k-steps ahead;
+//   - weights: each wave streams its own rows' codes into a register ring D k-steps
+//     ahead; MXFP4 block scales (one 64-byte unit per row tile and k-step) are copied
+//     into LDS for the block's 32 row tiles, D k-steps at a time, by one direct
+//     global->LDS load per wave, into two alternating buffers (a byte load per lane and
+//     row tile per k-step would cost as many memory instructions as the codes);
+//   - only the activation rows of the group's live 16-row token tiles are staged;
 //   - the k loop is unrolled by D, so ring slots and buffers are compile-time indices
 //     and the wait before each step is a constant vmcnt (every wave issues the same
 //     number of loads per step; loads past the row end re-read a real block that is
@@ -49,9 +54,14 @@ __host__ __device__ constexpr bool pf_lut_repl(int fmt, int np, int d) {
 __host__ __device__ constexpr int pf_lut_bytes(int fmt, int np, int d) {
   return fmt != 2 ? 0 : pf_lut_repl(fmt, np, d) ? kPfLutReplBytes : 1024;
 }
-// LUT, then the D x NP activation buffers, then the group's 64 pair ids.
+// MXFP4 scale buffers: two groups of D k-steps; group buffer = 8 waves x 1 KB, step u
+// of the group at 2 KB u, row tile (wave w, tile rt) at 64 (4 w + rt) inside it.
+constexpr int kPfScaleGroupBytes = 8 * 1024;
+__host__ __device__ constexpr int pf_scale_lds_bytes(int fmt) { return fmt == 1 ? 2 * kPfScaleGroupBytes : 0; }
+// LUT, then the D x NP activation buffers, then the MXFP4 scale buffers, then the
+// group's 64 pair ids.
 __host__ __device__ constexpr int pf_lds_bytes(int fmt, int np, int d) {
-  return pf_lut_bytes(fmt, np, d) + d * np * kPfPlaneBytes;
+  return pf_lut_bytes(fmt, np, d) + d * np * kPfPlaneBytes + pf_scale_lds_bytes(fmt);
 }
 __host__ __device__ constexpr int pf_lds_total(int fmt, int np, int d) {
   return pf_lds_bytes(fmt, np, d) + 4 * kGroupPairs;
@@ -89,8 +99,7 @@ template <int FMT, int SCL>
 struct PfStep;
 template <int SCL>
 struct PfStep<1, SCL> {
-  u32x4_t c[4];
-  uint32_t s[4];
+  u32x4_t c[4];  // the scales are staged in LDS
 };
 template <>
 struct PfStep<2, 0> {
@@ -104,7 +113,7 @@ struct PfStep<2, 1> {
 };
 template <int FMT, int SCL>
 __host__ __device__ constexpr int pf_loads_per_step() {
-  return FMT == 1 ? 8 : (SCL ? 20 : 32);
+  return FMT == 1 ? 4 : (SCL ? 20 : 32);
 }
 
 __device__ __forceinline__ void pf_load_lds_16(gbyte_t* gptr, void* lds) {
@@ -126,7 +135,6 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
       const int kb = min(4 * kc + g, nkb - 1);
       r.c[rt] = __builtin_nontemporal_load(
           (const __attribute__((address_space(1))) u32x4_t*)(pt[rt].codes + pk_code(kb, m)));
-      r.s[rt] = pt[rt].scales[pk_scale_mx(kb, m)];
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -149,16 +157,18 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
 
 // Branch-free: all 4 row tiles are computed (a row tile past the matrix holds clamped
 // real rows whose results are not stored) and NTT token tiles are live.
+// sb (MXFP4): this lane's scale byte of row tile 0 for step ks in LDS (tile rt at +64 rt).
 template <int FMT, int NP, int SCL, int NTT, bool REPL>
 __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uint8_t* xb, int ks, int nkb,
-                                            uint32_t lane_off, const uint32_t* lut, f32x4_t (&acc)[4][NTT]) {
+                                            uint32_t lane_off, const uint32_t* lut, const uint8_t* sb,
+                                            f32x4_t (&acc)[4][NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   if constexpr (FMT == 1) {
     const bool kval = 4 * ks + g < nkb;
     float sc[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_to_f32(r.s[rt]);
+    for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_to_f32(sb[64 * rt]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8_t b[4];
@@ -227,19 +237,25 @@ struct PfCtx {
   const uint32_t* lut;     // the CB4 table (LDS offset 0)
   int start;               // the group's first bucket position
   const int* s_pair;       // the group's pair ids in LDS (when they fit there)
+  gbyte_t* ssrc;           // MXFP4: scale unit (this lane's staging tile, step 0) + 16 x chunk
+  uint8_t* sbuf;           // MXFP4: LDS scale buffers
+  int sstep;               // MXFP4: the step of a D-step group whose scales this wave stages
+  int schunk;              // MXFP4: this lane's 16-byte chunk (block g) of a scale unit
+  int soff;                // MXFP4: this lane's scale byte of its row tile 0 in a staged step
   size_t act_plane_bytes;
   int nks, nkb, row_bytes, wave, g, m;
   uint32_t rt_mask;
 };
 
-// Copy staged chunk s (clamped to the last one) of every group row into buffer buf: the
-// 16 one-kilobyte loads per plane (4 rows each) are spread over the W waves, this wave
-// taking u = wave + W q, q < 16/W.
-template <int NP, int W>
+// Copy staged chunk s (clamped to the last one) of the group's rows into buffer buf: the
+// one-kilobyte loads per plane (4 rows each) are spread over the W waves, this wave
+// taking u = wave + W q, q < NQ (16 / W loads cover all 64 rows; fewer cover the rows of
+// the live token tiles).
+template <int NP, int W, int NQ>
 __device__ __forceinline__ void pf_stage(const PfCtx& c, int s, int buf) {
   const int sc = s < c.nks ? s : c.nks - 1;
 #pragma unroll
-  for (int q = 0; q < 16 / W; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     int off = kPfRowBytes * sc + c.piece[q];
     off = off + 16 <= c.row_bytes ? off : 0;  // past the row end: real data, never used
 #pragma unroll
@@ -249,13 +265,36 @@ __device__ __forceinline__ void pf_stage(const PfCtx& c, int s, int buf) {
   }
 }
 
+// Stage the MXFP4 scales of steps s..s+D-1 (clamped to the last step) of the block's 32
+// row tiles into group buffer par: one 1 KB load per wave, wave w taking step w/2 of the
+// group (a wave past the group's steps re-reads its last step into its own slice) and
+// the 16 tiles 16 (w & 1).. of it, 4 lanes per 64-byte unit.  Chunks past a partial
+// last unit re-read chunk 0 of it (those blocks are masked at use).
+template <int D>
+__device__ __forceinline__ void pf_stage_scales(const PfCtx& c, int s, int par) {
+  const int st = min(s + c.sstep, c.nks - 1);
+  const int nb = min(4, c.nkb - 4 * st);
+  const int ch = c.schunk < nb ? c.schunk : 0;
+  pf_load_lds_16(c.ssrc + 64 * st + 16 * (ch - c.schunk), c.sbuf + par * kPfScaleGroupBytes + c.wave * 1024);
+}
+
+// The vmcnt wait at the start of the k-step in ring slot U that covers chunk s: chunk s
+// was staged D-1 steps earlier and was followed by that step's weights and by D-2 whole
+// steps (chunk + weights, plus the scale load of a slot-0 step, which precedes its chunk).
+template <int FMT, int SCL, int D, int NQNP>
+__host__ __device__ constexpr int pf_wait_count(int U) {
+  int n = pf_loads_per_step<FMT, SCL>();
+  for (int v = 2; v < D; ++v) n += NQNP + pf_loads_per_step<FMT, SCL>() + ((FMT == 1 && (U + v) % D == 0) ? 1 : 0);
+  return n;
+}
+
 // Marks a ring slot's registers as produced here: the compiler may not move their uses
 // (or its own waits for them) above this point, which keeps the uses of slot U inside
 // step U instead of hoisting them to the loop head where the later slots are in flight.
 template <int SCL>
 __device__ __forceinline__ void pf_pin(PfStep<1, SCL>& r) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(r.c[rt]), "+v"(r.s[rt]));
+  for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(r.c[rt]));
 }
 __device__ __forceinline__ void pf_pin(PfStep<2, 0>& r) {
 #pragma unroll
@@ -272,22 +311,33 @@ __device__ __forceinline__ void pf_pin(PfStep<2, 1>& r) {
   }
 }
 
-// One k-step: wait for chunk s (and this wave's weights of step s), stage chunk
-// s+D-1 into the buffer every wave has finished with, MFMAs, then the weights of step
-// s+D into the ring slot just consumed.  Straight-line code: every wave issues the same
-// loads at every step, so the wait is a constant.
+// Activation staging loads per wave per plane and k-step for NTT live token tiles.
+template <int W, int NTT>
+__host__ __device__ constexpr int pf_nq() {
+  return (4 * NTT + W - 1) / W < 16 / W ? (4 * NTT + W - 1) / W : 16 / W;
+}
+
+// One k-step (s = a multiple of D plus U): wait for chunk s, stage (in a slot-0 step) the
+// MXFP4 scales of the next D-step group and chunk s+D-1 into buffers every wave has
+// finished with, MFMAs, then the weights of step s+D into the ring slot just consumed.
+// The wait covers chunk s and every load issued before it (this wave's weights of step s
+// and the scales of step s's group); the barrier then makes every wave's staged data
+// visible and frees the buffers of step s-1.  Straight-line code: every wave issues the
+// same loads at every step, so the wait is a constant.
 template <int FMT, int NP, int D, int SCL, int NTT, int U, int W>
 __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s, f32x4_t (&acc)[4][NTT]) {
-  // chunk s was issued D-1 steps before step s: after it, this wave issued the weights
-  // of one step and (D-2) steps of chunk + weights
-  constexpr int kWait = (D - 1) * pf_loads_per_step<FMT, SCL>() + (D - 2) * (16 / W) * NP;
+  constexpr int NQ = pf_nq<W, NTT>();
+  constexpr int kWait = pf_wait_count<FMT, SCL, D, NQ * NP>(U);
   static_assert(kWait <= 63, "too many loads in flight for the vmcnt counter");
   __builtin_amdgcn_s_waitcnt(pf_vm_le(kWait));
   __builtin_amdgcn_s_barrier();
-  pf_stage<NP, W>(c, s + D - 1, (U + D - 1) % D);
+  const int grp = s / D;
+  if constexpr (FMT == 1 && U == 0) pf_stage_scales<D>(c, s + D, (grp + 1) & 1);
+  pf_stage<NP, W, NQ>(c, s + D - 1, (U + D - 1) % D);
   pf_pin(ring[U]);
+  const uint8_t* sb = c.sbuf + (grp & 1) * kPfScaleGroupBytes + U * 2048 + c.soff;
   pf_mma_step<FMT, NP, SCL, NTT, pf_lut_repl(FMT, NP, D)>(ring[U], c.xs + U * NP * kPfPlaneBytes, s, c.nkb,
-                                                         c.lane_off, c.lut, acc);
+                                                         c.lane_off, c.lut, sb, acc);
   pf_load_step<FMT, SCL>(ring[U], c.tile, s + D, c.nks, c.nkb, c.m, c.g);
 }
 
@@ -310,9 +360,10 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   PfStep<FMT, SCL> ring[D];
+  if constexpr (FMT == 1) pf_stage_scales<D>(c, 0, 0);
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    if (j < D - 1) pf_stage<NP, W>(c, j, j);
+    if (j < D - 1) pf_stage<NP, W, pf_nq<W, NTT>()>(c, j, j);
     pf_load_step<FMT, SCL>(ring[j], c.tile, j, c.nks, c.nkb, c.m, c.g);
   }
   const int nfull = c.nks / D * D;
@@ -446,21 +497,40 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
 
   const void* base = GATEUP ? L.gate_up[e] : L.down[e];
   const int rows_total = GATEUP ? 2 * I : H;
+  // row tile rt of wave tile wt: GATEUP gate rows 32wt.. (rt 0, 1) and up rows I+32wt..
+  // (rt 2, 3); down rows 64wt + 16rt..  A tile past the matrix reads tile 0 (its results
+  // are not stored).
+  auto tile_of = [&](int wtile, int rt, bool& ok) {
+    int row0;
+    if (GATEUP) {
+      ok = 32 * wtile < I;
+      row0 = (rt < 2 ? 0 : I) + 32 * wtile + 16 * (rt & 1);
+    } else {
+      row0 = 64 * wtile + 16 * rt;
+      ok = row0 < H;
+    }
+    return packed_tile(base, rows_total, K, ok ? row0 / 16 : 0, FMT == 1 ? 1 : 2);
+  };
   c.rt_mask = 0;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    int row0;
     bool ok;
-    if (GATEUP) {
-      ok = 32 * wt < I;
-      row0 = (rt < 2 ? 0 : I) + 32 * wt + 16 * (rt & 1);
-    } else {
-      row0 = 64 * wt + 16 * rt;
-      ok = row0 < H;
-    }
+    c.tile[rt] = tile_of(wt, rt, ok);
     if (ok) c.rt_mask |= 1u << rt;
-    // a row tile past the matrix reads tile 0 (its results are not stored)
-    c.tile[rt] = packed_tile(base, rows_total, K, ok ? row0 / 16 : 0, FMT == 1 ? 1 : 2);
+  }
+  if constexpr (FMT == 1) {
+    static_assert(W == 8, "the scale staging assumes 8 waves (32 row tiles) per block");
+    bool ok;
+    const int wv = 4 * (c.wave & 1) + (lane >> 4);  // the wave owning this lane's staged tile
+    c.schunk = lane & 3;
+    c.ssrc = tile_of(rb * W + wv, (lane >> 2) & 3, ok).scales + 16 * c.schunk;
+    c.sstep = min(c.wave >> 1, D - 1);
+    c.sbuf = smem + pf_lut_bytes(FMT, NP, D) + D * NP * kPfPlaneBytes;
+    c.soff = 256 * c.wave + 16 * c.g + c.m;
+  } else {
+    c.ssrc = nullptr;
+    c.sbuf = nullptr;
+    c.sstep = c.schunk = c.soff = 0;
   }
 
   switch ((nt + 15) >> 4) {
@@ -509,8 +579,8 @@ static void pf_launch_fmt(const LayerArgs& L, const void* x, int x_dtype, int T,
   const int P = T * L.k + (L.has_shared ? T : 0);
   if (x_dtype == 1)
     pf_launch<FMT, 1, D, true, SCL, WG>(L, T, w, (const uint16_t*)x, 0, rb_gu, mg, kStageGateUp, s, tm);
-  else  // three exact bf16 planes of fp32 x: at most 3 buffers fit in LDS (2 for CB4's registers)
-    pf_launch<FMT, 3, (FMT == 1 ? 3 : 2), true, SCL, kPfWaves>(L, T, w, w.xplanes, (size_t)T * L.H,
+  else  // three exact bf16 planes of fp32 x: 2 buffers fit in LDS beside the MXFP4 scales / CB4 table
+    pf_launch<FMT, 3, 2, true, SCL, kPfWaves>(L, T, w, w.xplanes, (size_t)T * L.H,
                                                                (L.I / 32 + kPfWaves - 1) / kPfWaves,
                                                         mg, kStageGateUp, s, tm);
   pf_launch<FMT, 2, DD, false, SCL, WD>(L, T, w, w.hplanes, (size_t)P * L.I, rb_dn, mg, kStageDown, s, tm);
