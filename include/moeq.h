@@ -143,7 +143,8 @@ typedef enum {
   MOE_STAGE_GATEUP = 3,   /* fused dequant + gate/up + SwiGLU */
   MOE_STAGE_DOWN = 4,     /* dequant + down projection */
   MOE_STAGE_COMBINE = 5,  /* gate-weighted combine */
-  MOE_NUM_STAGES = 6
+  MOE_STAGE_ACT_QUANT = 6,  /* fp8 activation planes (MXFP4 prefill path) */
+  MOE_NUM_STAGES = 7
 } moe_stage;
 
 /* moe_forward with per-stage timing: stage_events holds 2*MOE_NUM_STAGES hipEvent_t

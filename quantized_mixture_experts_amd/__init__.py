@@ -24,7 +24,7 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 EXPORTED = ["moe_packed_bytes", "moe_workspace_bytes", "moe_router_topk", "moe_bucket", "moe_forward",
             "moe_forward_timed", "moe_dequant", "moe_rms_rescale", "moe_status_str"]
-STAGES = ["router", "topk", "bucket", "gateup", "down", "combine"]
+STAGES = ["router", "topk", "bucket", "gateup", "down", "combine", "xquant"]
 
 
 class MoeLayerC(ctypes.Structure):

@@ -2,6 +2,7 @@
 // Validation runs entirely on the host before anything is enqueued and touches no
 // HIP API, so the error paths can be exercised without a GPU.
 #include <stddef.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "../../include/moeq.h"
@@ -62,8 +63,10 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.offsets = take((E + 2) * 4);
   o.perm = take(P * 4);
   o.active = take((E + 2) * 4);
-  o.xplanes = take(3 * (size_t)T * H * 2);
-  o.hplanes = take(2 * P * I * 2);
+  // bf16 planes (CB4 prefill, fp32 x) or fp8 planes + scales (MXFP4 prefill) share a region
+  const size_t Hp = align_up(H, 128), Ip = align_up(I, 256);
+  o.xplanes = take(std::max(3 * (size_t)T * H * 2, 3 * (size_t)T * Hp + (size_t)T));
+  o.hplanes = take(std::max(2 * P * I * 2, 3 * P * Ip + P * (Ip / 256)));
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
@@ -89,6 +92,8 @@ Work carve(void* ws, const Layout& lo) {
   w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
   w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
+  w.xq = b + lo.xplanes;
+  w.hq = b + lo.hplanes;
   w.groups = reinterpret_cast<int4*>(b + lo.groups);
   w.n_groups = reinterpret_cast<int32_t*>(b + lo.n_groups);
   w.rr_flags = reinterpret_cast<uint32_t*>(b);

@@ -73,6 +73,8 @@ struct Work {
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
   uint32_t* tickets;   // [H/16] arrival counters of the decode combine
   float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)
+  uint8_t* xq;         // MXFP4 prefill: fp8 planes [NPX][T][Hp] + [T] E8M0 row scales (aliases xplanes)
+  uint8_t* hq;         // MXFP4 prefill: fp8 planes [3][P][Ip] + [P][Ip/256] E8M0 chunk scales (aliases hplanes)
   struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
   int4* groups;        // prefill work groups: (expert, first bucket position, pairs <= 64, 0)
   int32_t* n_groups;   // [1] number of valid entries of groups

@@ -35,8 +35,14 @@ namespace moeq {
 
 constexpr int kPfWaves = 8;  // waves per block (eight 64-row wave tiles: 512 weight rows)
 
-constexpr int kPfRowBytes = 256;                         // one staged row chunk: 128 bf16
+constexpr int kPfRowBytes = 256;                         // CB4 path: one staged row chunk, 128 bf16
 constexpr int kPfPlaneBytes = kGroupPairs * kPfRowBytes;  // 16 KB per plane per buffer
+constexpr int kMxRowBytes = 128;                          // MXFP4 path: one staged row chunk, 128 fp8
+constexpr int kMxPlaneBytes = kGroupPairs * kMxRowBytes;  // 8 KB per plane per buffer
+constexpr int kMxChunkCols = 256;  // h columns per activation scale (one gate/up block's columns)
+constexpr int kMxAScaleStride = 64;  // LDS activation scales: 64 rows x up to 64 chunks (I <= 16384)
+__host__ __device__ constexpr int pf_row_bytes(int fmt) { return fmt == 1 ? kMxRowBytes : kPfRowBytes; }
+__host__ __device__ constexpr int pf_plane_bytes(int fmt) { return fmt == 1 ? kMxPlaneBytes : kPfPlaneBytes; }
 
 // CB4 decode table at LDS offset 0, in one of two forms:
 //  - replicated, one copy per lane: the entry for code byte b (two bf16 values) of lane
@@ -58,10 +64,16 @@ __host__ __device__ constexpr int pf_lut_bytes(int fmt, int np, int d) {
 // of the group at 2 KB u, row tile (wave w, tile rt) at 64 (4 w + rt) inside it.
 constexpr int kPfScaleGroupBytes = 8 * 1024;
 __host__ __device__ constexpr int pf_scale_lds_bytes(int fmt) { return fmt == 1 ? 2 * kPfScaleGroupBytes : 0; }
-// LUT, then the D x NP activation buffers, then the MXFP4 scale buffers, then the
-// group's 64 pair ids.
+// MXFP4: the rows' activation scales, then the gate/up epilogue's per-wave row maxima
+// [64 rows][8 waves] (a region of its own, so that waves still in their last k-step are
+// not disturbed)
+__host__ __device__ constexpr int pf_ascale_lds_bytes(int fmt) {
+  return fmt == 1 ? kGroupPairs * kMxAScaleStride + kGroupPairs * 8 * 4 : 0;
+}
+// LUT, then the D x NP activation buffers, then (MXFP4) the weight scale buffers and the
+// rows' activation scales, then the group's 64 pair ids.
 __host__ __device__ constexpr int pf_lds_bytes(int fmt, int np, int d) {
-  return pf_lut_bytes(fmt, np, d) + d * np * kPfPlaneBytes + pf_scale_lds_bytes(fmt);
+  return pf_lut_bytes(fmt, np, d) + d * np * pf_plane_bytes(fmt) + pf_scale_lds_bytes(fmt) + pf_ascale_lds_bytes(fmt);
 }
 __host__ __device__ constexpr int pf_lds_total(int fmt, int np, int d) {
   return pf_lds_bytes(fmt, np, d) + 4 * kGroupPairs;
@@ -157,32 +169,52 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
 
 // Branch-free: all 4 row tiles are computed (a row tile past the matrix holds clamped
 // real rows whose results are not stored) and NTT token tiles are live.
-// sb (MXFP4): this lane's scale byte of row tile 0 for step ks in LDS (tile rt at +64 rt).
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// MXFP4 A operand of v_mfma_scale_f32_16x16x128_f8f6f4 for token row `row` of a staged
+// fp8 chunk: lane 16g + m supplies columns 16g..16g+15 (bytes 0..15) and 64+16g..
+// 64+16g+15 (bytes 16..31) of its row.  The 16-byte pieces of row r sit at piece ^
+// ((r >> 1) & 7) in LDS, which spreads the 16 rows of a read over 16 bank groups.
+__device__ __forceinline__ i32x8_t pf_mx_a(const uint8_t* plane, int row, int g) {
+  const int sw = (row >> 1) & 7;
+  const uint8_t* rb = plane + row * kMxRowBytes;
+  const u32x4_t lo = *(const u32x4_t*)(rb + 16 * (g ^ sw));
+  const u32x4_t hi = *(const u32x4_t*)(rb + 16 * ((4 + g) ^ sw));
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// sb (MXFP4): this lane's weight scale byte of row tile 0 for step ks in LDS (tile rt at
+// +64 rt); ab (MXFP4): this lane's activation scale byte of token row m of the step
+// (token tile tt at +16 x kMxAScaleStride x tt).
 template <int FMT, int NP, int SCL, int NTT, bool REPL>
 __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uint8_t* xb, int ks, int nkb,
                                             uint32_t lane_off, const uint32_t* lut, const uint8_t* sb,
-                                            f32x4_t (&acc)[4][NTT]) {
+                                            const uint8_t* ab, f32x4_t (&acc)[4][NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   if constexpr (FMT == 1) {
-    const bool kval = 4 * ks + g < nkb;
-    float sc[4];
+    // Block-scaled matrix cores: A = NP fp8 e4m3 planes of the activations with one E8M0
+    // scale per row (chunk), B = the E2M1 codes exactly as stored (lane 16g + m holds
+    // block g of weight row m, which is the B operand layout) with their E8M0 scales.
+    // Columns past K meet zero activations (the planes are zero-padded), so a clamped
+    // block of a partial last step adds nothing.
+    i32x8_t bw[4];
+    int sbv[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_to_f32(sb[64 * rt]);
+    for (int rt = 0; rt < 4; ++rt) {
+      bw[rt] = i32x8_t{(int)r.c[rt][0], (int)r.c[rt][1], (int)r.c[rt][2], (int)r.c[rt][3], 0, 0, 0, 0};
+      sbv[rt] = sb[64 * rt];
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t b[4];
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int sa = ab[16 * kMxAScaleStride * tt];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) b[rt] = fp4x8_to_bf16(kval ? r.c[rt][j] : 0u, sc[rt]);
+      for (int p = 0; p < NP; ++p) {
+        const i32x8_t a = pf_mx_a(xb + p * kMxPlaneBytes, 16 * tt + m, g);
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const bf16x8_t a = *(const bf16x8_t*)(xb + p * kPfPlaneBytes + (16 * tt + m) * kPfRowBytes +
-                                                16 * ((4 * g + j) ^ m));
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[rt][tt] = mfma_bf16(a, b[rt], acc[rt][tt]);
-        }
+        for (int rt = 0; rt < 4; ++rt)
+          acc[rt][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw[rt], acc[rt][tt], 0, 4, 0, sa, 0,
+                                                                        sbv[rt]);
       }
     }
   } else {
@@ -242,6 +274,8 @@ struct PfCtx {
   int sstep;               // MXFP4: the step of a D-step group whose scales this wave stages
   int schunk;              // MXFP4: this lane's 16-byte chunk (block g) of a scale unit
   int soff;                // MXFP4: this lane's scale byte of its row tile 0 in a staged step
+  const uint8_t* ascale;   // MXFP4: LDS activation scales [64 rows][kMxAScaleStride], row m
+  float* cmax;             // MXFP4 gate/up epilogue: LDS row maxima [64 rows][8 waves]
   size_t act_plane_bytes;
   int nks, nkb, row_bytes, wave, g, m;
   uint32_t rt_mask;
@@ -251,17 +285,19 @@ struct PfCtx {
 // one-kilobyte loads per plane (4 rows each) are spread over the W waves, this wave
 // taking u = wave + W q, q < NQ (16 / W loads cover all 64 rows; fewer cover the rows of
 // the live token tiles).
-template <int NP, int W, int NQ>
+// MXFP4: fp8 rows of 128 bytes, 8 rows per 1 KB load, so every wave issues one load per
+// plane for all 64 rows.
+template <int FMT, int NP, int W, int NQ>
 __device__ __forceinline__ void pf_stage(const PfCtx& c, int s, int buf) {
   const int sc = s < c.nks ? s : c.nks - 1;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    int off = kPfRowBytes * sc + c.piece[q];
+    int off = pf_row_bytes(FMT) * sc + c.piece[q];
     off = off + 16 <= c.row_bytes ? off : 0;  // past the row end: real data, never used
 #pragma unroll
     for (int p = 0; p < NP; ++p)
       pf_load_lds_16(c.src[q] + p * c.act_plane_bytes + off,
-                     c.xs + (buf * NP + p) * kPfPlaneBytes + (c.wave + W * q) * 1024);
+                     c.xs + (buf * NP + p) * pf_plane_bytes(FMT) + (c.wave + W * q) * 1024);
   }
 }
 
@@ -311,10 +347,11 @@ __device__ __forceinline__ void pf_pin(PfStep<2, 1>& r) {
   }
 }
 
-// Activation staging loads per wave per plane and k-step for NTT live token tiles.
-template <int W, int NTT>
+// Activation staging loads per wave per plane and k-step for NTT live token tiles (CB4:
+// 4 rows per load; MXFP4: one load covers 8 rows, all 64 are staged).
+template <int FMT, int W, int NTT>
 __host__ __device__ constexpr int pf_nq() {
-  return (4 * NTT + W - 1) / W < 16 / W ? (4 * NTT + W - 1) / W : 16 / W;
+  return FMT == 1 ? 64 / 8 / W : ((4 * NTT + W - 1) / W < 16 / W ? (4 * NTT + W - 1) / W : 16 / W);
 }
 
 // One k-step (s = a multiple of D plus U): wait for chunk s, stage (in a slot-0 step) the
@@ -324,30 +361,130 @@ __host__ __device__ constexpr int pf_nq() {
 // and the scales of step s's group); the barrier then makes every wave's staged data
 // visible and frees the buffers of step s-1.  Straight-line code: every wave issues the
 // same loads at every step, so the wait is a constant.
-template <int FMT, int NP, int D, int SCL, int NTT, int U, int W>
+template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT, int U, int W>
 __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s, f32x4_t (&acc)[4][NTT]) {
-  constexpr int NQ = pf_nq<W, NTT>();
+  constexpr int NQ = pf_nq<FMT, W, NTT>();
   constexpr int kWait = pf_wait_count<FMT, SCL, D, NQ * NP>(U);
   static_assert(kWait <= 63, "too many loads in flight for the vmcnt counter");
   __builtin_amdgcn_s_waitcnt(pf_vm_le(kWait));
   __builtin_amdgcn_s_barrier();
   const int grp = s / D;
   if constexpr (FMT == 1 && U == 0) pf_stage_scales<D>(c, s + D, (grp + 1) & 1);
-  pf_stage<NP, W, NQ>(c, s + D - 1, (U + D - 1) % D);
+  pf_stage<FMT, NP, W, NQ>(c, s + D - 1, (U + D - 1) % D);
   pf_pin(ring[U]);
   const uint8_t* sb = c.sbuf + (grp & 1) * kPfScaleGroupBytes + U * 2048 + c.soff;
-  pf_mma_step<FMT, NP, SCL, NTT, pf_lut_repl(FMT, NP, D)>(ring[U], c.xs + U * NP * kPfPlaneBytes, s, c.nkb,
-                                                         c.lane_off, c.lut, sb, acc);
+  // activation scale chunk of step s: one per row for x, one per 256 columns for h
+  const uint8_t* ab = c.ascale + (GATEUP ? 0 : (s * 128) / kMxChunkCols);
+  pf_mma_step<FMT, NP, SCL, NTT, pf_lut_repl(FMT, NP, D)>(ring[U], c.xs + U * NP * pf_plane_bytes(FMT), s, c.nkb,
+                                                         c.lane_off, c.lut, sb, ab, acc);
   pf_load_step<FMT, SCL>(ring[U], c.tile, s + D, c.nks, c.nkb, c.m, c.g);
 }
 
 // The last R (< D) k-steps, straight-line.
-template <int FMT, int NP, int D, int SCL, int NTT, int R, int W>
+template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT, int R, int W>
 __device__ __forceinline__ void pf_tail(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s0, f32x4_t (&acc)[4][NTT]) {
-  if constexpr (R >= 1) pf_kstep<FMT, NP, D, SCL, NTT, 0, W>(c, ring, s0, acc);
-  if constexpr (R >= 2) pf_kstep<FMT, NP, D, SCL, NTT, 1, W>(c, ring, s0 + 1, acc);
-  if constexpr (R >= 3) pf_kstep<FMT, NP, D, SCL, NTT, 2, W>(c, ring, s0 + 2, acc);
+  if constexpr (R >= 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc);
+  if constexpr (R >= 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, s0 + 1, acc);
+  if constexpr (R >= 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 2, W>(c, ring, s0 + 2, acc);
   static_assert(R < 4, "tail longer than supported");
+}
+
+// Largest value of v over the 16 lanes of this lane's DPP row.
+__device__ __forceinline__ float pf_row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+
+// fp8 e4m3 (round to nearest even) of one value, and its value.
+__device__ __forceinline__ uint32_t pf_to_fp8(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float pf_from_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+// E8M0 exponent e of a block whose largest magnitude is amax: amax / 2^e in [128, 256),
+// so that the fp8 planes of v / 2^e stay below the e4m3 maximum (448); e = 0 for a zero
+// block.
+__device__ __forceinline__ int pf_mx_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // floor(log2) for normal amax
+  const int e = (amax < 1.17549435e-38f ? -126 : ex) - 7;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// MXFP4 gate/up epilogue: h = silu(gate) * up in registers, then h as three fp8 planes
+// with one E8M0 scale per (pair, 256-column chunk), the chunk this block computes:
+// h ~= 2^e (p0 + p1 + p2), p_i = fp8(the remainder after p0..p_{i-1}), so about 12
+// significant bits below the chunk maximum.  The bytes are assembled in LDS (the
+// staging buffers are free) and written as 16-byte rows; columns past I are zeros.
+template <int NTT, int W>
+__device__ __forceinline__ void pf_mx_h_epilogue(const PfCtx& c, const LayerArgs& L, int T, const Work& w, int wt,
+                                                 int nt, const f32x4_t (&acc)[4][NTT]) {
+  static_assert(W == 8, "row maxima are kept for 8 waves");
+  const int g = c.g, m = c.m;
+  const int I = L.I;
+  const int Ip = (I + kMxChunkCols - 1) / kMxChunkCols * kMxChunkCols;
+  const int nch = Ip / kMxChunkCols;
+  const size_t P = (size_t)T * L.k + (L.has_shared ? T : 0);
+  const int rb = wt / W;
+  uint8_t* hb = c.xs;  // [3][64 rows][256 columns], once every wave is past the k loop
+  // h of this lane: rows 16 tt + 4 g + q, columns 32 wt + 16 rt + m (rt = 0, 1);
+  // silu(a) = a / (1 + e^-a) with the hardware exp2 and reciprocal (a few ulp)
+  float hv[NTT][4][2];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float a = acc[rt][tt][q];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
+        hv[tt][q][rt] = c.rt_mask ? a * sg * acc[rt + 2][tt][q] : 0.0f;
+      }
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float r = pf_row16_max(fmaxf(fabsf(hv[tt][q][0]), fabsf(hv[tt][q][1])));
+      if (m == 0) c.cmax[(16 * tt + 4 * g + q) * 8 + c.wave] = r;
+    }
+  __syncthreads();  // row maxima complete; every wave is past its last read of the staged chunks
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 16 * tt + 4 * g + q;
+      const f32x4_t m0 = *(const f32x4_t*)(c.cmax + 8 * row);
+      const f32x4_t m1 = *(const f32x4_t*)(c.cmax + 8 * row + 4);
+      const float cm = fmaxf(fmaxf(fmaxf(m0[0], m0[1]), fmaxf(m0[2], m0[3])),
+                             fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3])));
+      const int e = pf_mx_exp(cm);
+      float v0 = ldexpf(hv[tt][q][0], -e), v1 = ldexpf(hv[tt][q][1], -e);
+      uint8_t* dst = hb + row * kMxChunkCols + 32 * c.wave + m;
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+        v0 -= f[0];
+        v1 -= f[1];
+        dst[pl * kGroupPairs * kMxChunkCols] = (uint8_t)(b & 0xFFu);
+        dst[pl * kGroupPairs * kMxChunkCols + 16] = (uint8_t)((b >> 8) & 0xFFu);
+      }
+      if (c.wave == 0 && m == 0 && row < nt)
+        w.hq[3 * P * Ip + (size_t)c.s_pair[row] * nch + rb] = (uint8_t)(e + 127);
+    }
+  __syncthreads();
+  // 3 planes x nt rows x 256 bytes, 16 bytes per thread and pass
+  for (int idx = threadIdx.x; idx < 3 * kGroupPairs * 16; idx += 64 * W) {
+    const int pl = idx / (kGroupPairs * 16), row = (idx / 16) % kGroupPairs, ch = idx % 16;
+    if (row < nt) {
+      const size_t p = (size_t)c.s_pair[row];
+      *(u32x4_t*)(w.hq + pl * P * Ip + p * Ip + (size_t)kMxChunkCols * rb + 16 * ch) =
+          *(const u32x4_t*)(hb + (pl * kGroupPairs + row) * kMxChunkCols + 16 * ch);
+    }
+  }
 }
 
 // Main loop and epilogue for a group with NTT live token tiles.
@@ -363,21 +500,21 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
   if constexpr (FMT == 1) pf_stage_scales<D>(c, 0, 0);
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    if (j < D - 1) pf_stage<NP, W, pf_nq<W, NTT>()>(c, j, j);
+    if (j < D - 1) pf_stage<FMT, NP, W, pf_nq<FMT, W, NTT>()>(c, j, j);
     pf_load_step<FMT, SCL>(ring[j], c.tile, j, c.nks, c.nkb, c.m, c.g);
   }
   const int nfull = c.nks / D * D;
   for (int s0 = 0; s0 < nfull; s0 += D) {
-    pf_kstep<FMT, NP, D, SCL, NTT, 0, W>(c, ring, s0, acc);
-    if constexpr (D > 1) pf_kstep<FMT, NP, D, SCL, NTT, (D > 1 ? 1 : 0), W>(c, ring, s0 + 1, acc);
-    if constexpr (D > 2) pf_kstep<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 0), W>(c, ring, s0 + 2, acc);
-    if constexpr (D > 3) pf_kstep<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 0), W>(c, ring, s0 + 3, acc);
+    pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc);
+    if constexpr (D > 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 1 ? 1 : 0), W>(c, ring, s0 + 1, acc);
+    if constexpr (D > 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 0), W>(c, ring, s0 + 2, acc);
+    if constexpr (D > 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 0), W>(c, ring, s0 + 3, acc);
     static_assert(D <= 4, "deeper rings need more unrolled steps");
   }
   switch (c.nks - nfull) {
-    case 1: pf_tail<FMT, NP, D, SCL, NTT, 1, W>(c, ring, nfull, acc); break;
-    case 2: pf_tail<FMT, NP, D, SCL, NTT, (D > 2 ? 2 : 1), W>(c, ring, nfull, acc); break;
-    case 3: pf_tail<FMT, NP, D, SCL, NTT, (D > 3 ? 3 : 1), W>(c, ring, nfull, acc); break;
+    case 1: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, nfull, acc); break;
+    case 2: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 1), W>(c, ring, nfull, acc); break;
+    case 3: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 1), W>(c, ring, nfull, acc); break;
     default: break;
   }
   // the trailing (never used) loads must land before the block's LDS is released
@@ -393,7 +530,9 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
       const int slot = min(16 * tt + 4 * g + q, nt - 1);
       pid[tt][q] = c.s_pair[slot];
     }
-  if (GATEUP) {
+  if constexpr (GATEUP && FMT == 1) {
+    pf_mx_h_epilogue<NTT, W>(c, L, T, w, wt, nt, acc);
+  } else if constexpr (GATEUP) {
     if (c.rt_mask) {
       const int I = L.I;
       const int P = T * L.k + (L.has_shared ? T : 0);
@@ -446,8 +585,8 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
 // remapped so that the row blocks of one group run on one XCD (consecutive hardware
 // ids go to different XCDs), where they share the group's activation rows in L2.
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
-__global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                   size_t act_plane, int RB) {
+__global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, const uint8_t* __restrict__ act,
+                                                   size_t act_plane_bytes, int RB) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int ng = *w.n_groups;
   const int M = RB * ng;
@@ -468,8 +607,11 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   const int K = GATEUP ? H : I;
   c.nkb = K >> 5;
   c.nks = (c.nkb + 3) >> 2;
-  c.row_bytes = 2 * K;
-  c.act_plane_bytes = act_plane * 2;
+  // activation row stride: bf16 rows of K (CB4); fp8 rows padded to whole k-steps (x) or
+  // whole 256-column chunks (h) (MXFP4)
+  c.row_bytes = FMT == 1 ? (GATEUP ? (H + 127) / 128 * 128 : (I + kMxChunkCols - 1) / kMxChunkCols * kMxChunkCols)
+                         : 2 * K;
+  c.act_plane_bytes = act_plane_bytes;
   const int wt = rb * W + c.wave;
 
   c.xs = smem + pf_lut_bytes(FMT, NP, D);
@@ -484,15 +626,43 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   c.s_pair = s_pair;
   if (threadIdx.x < kGroupPairs)
     s_pair[threadIdx.x] = w.perm[start + ((int)threadIdx.x < nt ? (int)threadIdx.x : 0)];
+  if constexpr (FMT == 1) {
+    // the rows' activation scales (they follow the NP planes): one per x row, one per
+    // 256-column chunk of an h row; rows past nt repeat row 0
+    uint8_t* as = smem + pf_lds_bytes(FMT, NP, D) - pf_ascale_lds_bytes(FMT);
+    c.cmax = (float*)(as + kGroupPairs * kMxAScaleStride);
+    const int nch = GATEUP ? 1 : c.row_bytes / kMxChunkCols;
+    const uint8_t* src_scales = act + NP * act_plane_bytes;
+    for (int t = threadIdx.x; t < kGroupPairs * nch; t += 64 * W) {
+      const int row = t / nch, ch = t % nch;
+      const int p = w.perm[start + (row < nt ? row : 0)];
+      as[row * kMxAScaleStride + ch] =
+          GATEUP ? src_scales[pf_token_of_pair(p, T, k)] : src_scales[(size_t)p * nch + ch];
+    }
+    c.ascale = as + c.m * kMxAScaleStride;
+  } else {
+    c.ascale = nullptr;
+    c.cmax = nullptr;
+  }
   __syncthreads();
 
-#pragma unroll
-  for (int q = 0; q < 16 / W; ++q) {
-    const int row = 4 * (c.wave + W * q) + (lane >> 4);
+  if constexpr (FMT == 1) {
+    // one 1 KB staging load per plane covers rows 8 wave .. 8 wave + 7: lane l loads
+    // row 8 wave + l / 8, the 16-byte piece that belongs at LDS piece l % 8
+    const int row = 8 * c.wave + (lane >> 3);
     const int p = w.perm[start + (row < nt ? row : 0)];
     const int r = GATEUP ? pf_token_of_pair(p, T, k) : p;
-    c.src[q] = as_global(act) + (size_t)r * K * 2;
-    c.piece[q] = 16 * ((lane & 15) ^ (row & 15));
+    c.src[0] = as_global(act) + (size_t)r * c.row_bytes;
+    c.piece[0] = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16 / W; ++q) {
+      const int row = 4 * (c.wave + W * q) + (lane >> 4);
+      const int p = w.perm[start + (row < nt ? row : 0)];
+      const int r = GATEUP ? pf_token_of_pair(p, T, k) : p;
+      c.src[q] = as_global(act) + (size_t)r * K * 2;
+      c.piece[q] = 16 * ((lane & 15) ^ (row & 15));
+    }
   }
 
   const void* base = GATEUP ? L.gate_up[e] : L.down[e];
@@ -525,7 +695,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
     c.schunk = lane & 3;
     c.ssrc = tile_of(rb * W + wv, (lane >> 2) & 3, ok).scales + 16 * c.schunk;
     c.sstep = min(c.wave >> 1, D - 1);
-    c.sbuf = smem + pf_lut_bytes(FMT, NP, D) + D * NP * kPfPlaneBytes;
+    c.sbuf = smem + pf_lut_bytes(FMT, NP, D) + D * NP * pf_plane_bytes(FMT);
     c.soff = 256 * c.wave + 16 * c.g + c.m;
   } else {
     c.ssrc = nullptr;
@@ -557,8 +727,64 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// MXFP4 path: fp8 planes of the activations x with one E8M0 scale per row.
+//   x [T][H] bf16 (XDT 1, NPX = 2: exact) or fp32 (XDT 0, NPX = 3); xq = NPX planes
+//   [T][Hp] (Hp = H rounded up to 128, zero columns past H), then T scale bytes.
+// One block per row: the row maximum, then x / 2^e split into fp8 planes as in the h
+// epilogue (2^e maps the row maximum into [128, 256)).
+// ---------------------------------------------------------------------------
+template <int XDT, int NPX>
+__global__ __launch_bounds__(256) void k_mx_xquant(const void* __restrict__ x, int T, int H, int Hp,
+                                                   uint8_t* __restrict__ xq) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  auto load4 = [&](int c, float (&v)[4]) {
+    if (XDT == 1) {
+      const uint2 q = *(const uint2*)((const uint16_t*)x + (size_t)t * H + c);
+      v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+    } else {
+      const f32x4_t q = *(const f32x4_t*)((const float*)x + (size_t)t * H + c);
+      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+    }
+  };
+  float amax = 0.0f;
+  for (int c = 4 * threadIdx.x; c < H; c += 1024) {
+    float v[4];
+    load4(c, v);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = pf_mx_exp(amax);
+  if (threadIdx.x == 0) xq[(size_t)NPX * T * Hp + t] = (uint8_t)(e + 127);
+  for (int c = 4 * threadIdx.x; c < Hp; c += 1024) {  // H % 32 == 0: a group is all in or all past
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c < H) {
+      load4(c, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = ldexpf(v[j], -e);
+    }
+#pragma unroll
+    for (int p = 0; p < NPX; ++p) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = pf_to_fp8(v[j]);
+        v[j] -= pf_from_fp8(b);
+        word |= b << (8 * j);
+      }
+      *(uint32_t*)(xq + ((size_t)p * T + t) * Hp + c) = word;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
-static void pf_launch(const LayerArgs& L, int T, const Work& w, const uint16_t* act, size_t act_plane, int RB,
+static void pf_launch(const LayerArgs& L, int T, const Work& w, const void* act, size_t act_plane_bytes, int RB,
                       int max_groups_, int stage, hipStream_t s, const Timing& tm) {
   constexpr int lds = pf_lds_total(FMT, NP, D);
   static_assert(lds <= kPfLdsMax, "LDS budget of one workgroup");
@@ -567,23 +793,43 @@ static void pf_launch(const LayerArgs& L, int T, const Work& w, const uint16_t* 
   static const bool lds_ok =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
   (void)lds_ok;
-  MOEQ_LAUNCH(tm, stage, kern, dim3(RB * max_groups_), dim3(64 * W), lds, s, L, T, w, act, act_plane, RB);
+  MOEQ_LAUNCH(tm, stage, kern, dim3(RB * max_groups_), dim3(64 * W), lds, s, L, T, w, (const uint8_t*)act,
+              act_plane_bytes, RB);
 }
 
-// Waves per block: WG for the gate/up kernel, WD for the down kernel.
-template <int FMT, int SCL, int D, int WG, int WD, int DD>
-static void pf_launch_fmt(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int mg,
+// CB4: bf16 activation planes (x itself, or three exact planes of fp32 x; h in two
+// planes).  Waves per block: WG for the gate/up kernel, WD for the down kernel.
+template <int SCL, int D, int WG, int WD, int DD>
+static void pf_launch_cb4(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int mg,
                           hipStream_t s, const Timing& tm) {
   const int rb_gu = ((L.I / 32) + WG - 1) / WG;
   const int rb_dn = (((L.H + 63) / 64) + WD - 1) / WD;
-  const int P = T * L.k + (L.has_shared ? T : 0);
+  const size_t P = (size_t)T * L.k + (L.has_shared ? T : 0);
   if (x_dtype == 1)
-    pf_launch<FMT, 1, D, true, SCL, WG>(L, T, w, (const uint16_t*)x, 0, rb_gu, mg, kStageGateUp, s, tm);
-  else  // three exact bf16 planes of fp32 x: 2 buffers fit in LDS beside the MXFP4 scales / CB4 table
-    pf_launch<FMT, 3, 2, true, SCL, kPfWaves>(L, T, w, w.xplanes, (size_t)T * L.H,
-                                                               (L.I / 32 + kPfWaves - 1) / kPfWaves,
-                                                        mg, kStageGateUp, s, tm);
-  pf_launch<FMT, 2, DD, false, SCL, WD>(L, T, w, w.hplanes, (size_t)P * L.I, rb_dn, mg, kStageDown, s, tm);
+    pf_launch<2, 1, D, true, SCL, WG>(L, T, w, x, 0, rb_gu, mg, kStageGateUp, s, tm);
+  else  // three exact bf16 planes of fp32 x: 2 buffers fit in LDS beside the table
+    pf_launch<2, 3, 2, true, SCL, kPfWaves>(L, T, w, w.xplanes, (size_t)T * L.H * 2,
+                                            (L.I / 32 + kPfWaves - 1) / kPfWaves, mg, kStageGateUp, s, tm);
+  pf_launch<2, 2, DD, false, SCL, WD>(L, T, w, w.hplanes, P * L.I * 2, rb_dn, mg, kStageDown, s, tm);
+}
+
+// MXFP4: fp8 activation planes on the block-scaled matrix cores (x: 2 planes for bf16,
+// 3 for fp32; h: 3 planes).
+static void pf_launch_mx(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int mg,
+                         hipStream_t s, const Timing& tm) {
+  const int Hp = (L.H + 127) / 128 * 128;
+  const size_t Ip = (size_t)(L.I + kMxChunkCols - 1) / kMxChunkCols * kMxChunkCols;
+  const size_t P = (size_t)T * L.k + (L.has_shared ? T : 0);
+  const int rb_gu = ((L.I / 32) + kPfWaves - 1) / kPfWaves;
+  const int rb_dn = (((L.H + 63) / 64) + kPfWaves - 1) / kPfWaves;
+  if (x_dtype == 1) {
+    MOEQ_LAUNCH(tm, kStageActQuant, (k_mx_xquant<1, 2>), dim3(T), dim3(256), 0, s, x, T, L.H, Hp, w.xq);
+    pf_launch<1, 2, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
+  } else {
+    MOEQ_LAUNCH(tm, kStageActQuant, (k_mx_xquant<0, 3>), dim3(T), dim3(256), 0, s, x, T, L.H, Hp, w.xq);
+    pf_launch<1, 3, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
+  }
+  pf_launch<1, 3, 4, false, 0, kPfWaves>(L, T, w, w.hq, P * Ip, rb_dn, mg, kStageDown, s, tm);
 }
 
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
@@ -591,13 +837,13 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
   const int P = T * L.k + (L.has_shared ? T : 0);
   const int mg = max_groups(P, L.E);
   if (L.wfmt == 1) {
-    pf_launch_fmt<1, 0, 4, kPfWaves, kPfWaves, 4>(L, x, x_dtype, T, w, mg, s, tm);
+    pf_launch_mx(L, x, x_dtype, T, w, mg, s, tm);
   } else {
     // both K ranges must be multiples of 128 for the 8-byte scale loads
     if (L.H % 128 == 0 && L.I % 128 == 0)
-      pf_launch_fmt<2, 1, 3, kPfWaves, kPfWaves, 3>(L, x, x_dtype, T, w, mg, s, tm);
+      pf_launch_cb4<1, 3, kPfWaves, kPfWaves, 3>(L, x, x_dtype, T, w, mg, s, tm);
     else
-      pf_launch_fmt<2, 0, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
+      pf_launch_cb4<0, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
   }
   return launch_combine(L, T, w, y, s, tm);
 }

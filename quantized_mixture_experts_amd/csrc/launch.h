@@ -8,7 +8,11 @@ namespace moeq {
 
 // Kernel stages of one forward call.  A stage whose work is fused into another
 // kernel on the chosen path launches nothing and leaves its events untouched.
-enum Stage { kStageRouter = 0, kStageTopk, kStageBucket, kStageGateUp, kStageDown, kStageCombine, kNumStages };
+enum Stage {
+  kStageRouter = 0, kStageTopk, kStageBucket, kStageGateUp, kStageDown, kStageCombine,
+  kStageActQuant,  // fp8 activation planes of the block-scaled (MXFP4) prefill path
+  kNumStages
+};
 
 // Optional start/stop events per stage, stamped by the dispatch packet itself
 // (hipExtLaunchKernel), i.e. the kernel's own execution interval.
