@@ -841,7 +841,7 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
   } else {
     // both K ranges must be multiples of 128 for the 8-byte scale loads
     if (L.H % 128 == 0 && L.I % 128 == 0)
-      pf_launch_cb4<1, 3, kPfWaves, kPfWaves, 3>(L, x, x_dtype, T, w, mg, s, tm);
+      pf_launch_cb4<1, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
     else
       pf_launch_cb4<0, 2, kPfWaves, kPfWaves, 2>(L, x, x_dtype, T, w, mg, s, tm);
   }
