@@ -827,9 +827,9 @@ static void pf_launch_mx(const LayerArgs& L, const void* x, int x_dtype, int T, 
     pf_launch<1, 2, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
   } else {
     MOEQ_LAUNCH(tm, kStageActQuant, (k_mx_xquant<0, 3>), dim3(T), dim3(256), 0, s, x, T, L.H, Hp, w.xq);
-    pf_launch<1, 3, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
+    pf_launch<1, 3, 3, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
   }
-  pf_launch<1, 3, 4, false, 0, kPfWaves>(L, T, w, w.hq, P * Ip, rb_dn, mg, kStageDown, s, tm);
+  pf_launch<1, 3, 3, false, 0, kPfWaves>(L, T, w, w.hq, P * Ip, rb_dn, mg, kStageDown, s, tm);
 }
 
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
