@@ -79,11 +79,20 @@ __host__ __device__ constexpr int pf_lds_total(int fmt, int np, int d) {
   return pf_lds_bytes(fmt, np, d) + 4 * kGroupPairs;
 }
 
+// Wave w writes rows b = w + 8k (k < 32) of the replicated table: the low value is
+// codebook[b & 15] = codebook[w + 8 (k & 1)], the high one codebook[b >> 4] =
+// codebook[k >> 1].  The 16 codebook values are read once (one byte per lane) and
+// broadcast with readlane, so the table costs one global load per lane.
+template <int W>
 __device__ __forceinline__ void pf_build_lut(uint32_t* lut, const int8_t* codebook) {
-  for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) {
-    const int b = i >> 6;
-    lut[i] = int8_to_bf16_bits(codebook[b & 15]) | (int8_to_bf16_bits(codebook[b >> 4]) << 16);
-  }
+  static_assert(W == 8, "rows b = wave + 8k assume 8 waves");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t bits = int8_to_bf16_bits(codebook[lane & 15]);
+  const uint32_t lo0 = __builtin_amdgcn_readlane(bits, wave), lo1 = __builtin_amdgcn_readlane(bits, wave + 8);
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    lut[(wave + 8 * k) * 64 + lane] = ((k & 1) ? lo1 : lo0) | (__builtin_amdgcn_readlane(bits, k >> 1) << 16);
 }
 
 // Eight CB4 values (one code word) -> bf16: byte i of the code word indexes row i of the
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   c.lane_off = 4u * (uint32_t)lane;
   c.lut = (const uint32_t*)smem;
   if (FMT == 2) {
-    if constexpr (pf_lut_repl(FMT, NP, D)) pf_build_lut((uint32_t*)smem, L.codebook);
+    if constexpr (pf_lut_repl(FMT, NP, D)) pf_build_lut<W>((uint32_t*)smem, L.codebook);
     else build_cb4_lut((uint32_t*)smem, L.codebook);
   }
   int* s_pair = (int*)(smem + pf_lds_bytes(FMT, NP, D));
