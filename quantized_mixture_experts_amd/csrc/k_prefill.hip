@@ -729,8 +729,20 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
   const int t = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= H) return;
+  // the k (<= 16) routed rows, 8 loads in flight (clamped, in bounds), summed in order
   float s = 0.f;
-  for (int j = 0; j < k; ++j) s = fmaf(pair_w[t * k + j], o[(size_t)(t * k + j) * H + n], s);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float ov[8], wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, k - 1);
+      ov[u] = o[(size_t)(t * k + j) * H + n];
+      wv[u] = pair_w[t * k + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k) s = fmaf(wv[u], ov[u], s);
+  }
   if (has_shared) s = fmaf(pair_w[T * k + t], o[(size_t)(T * k + t) * H + n], s);
   y[(size_t)t * H + n] = s;
 }

@@ -167,34 +167,56 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
 // with no grid-wide scan.  perm[offsets[e] + r] = the r-th pair (increasing p) with
 // id_p = e, by ballot compaction.  The result is deterministic.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_shared,
+// Each of the 16 waves scans its own contiguous range of pairs, 8 loads in flight per
+// lane (the ids are read in two passes, histogram and placement).
+constexpr int kBucketWaves = 16;
+constexpr int kBucketBatch = 8;
+
+// ids of pairs base + 64 u + lane (u < kBucketBatch), -1 past the wave's range end p1
+// (loads clamped to the last pair, so every load is in bounds).
+__device__ __forceinline__ void bucket_load(const int32_t* __restrict__ ids, int base, int p1, int Pr,
+                                            int (&id)[kBucketBatch]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kBucketBatch; ++u) {
+    const int p = base + 64 * u + lane;
+    const int v = ids[min(p, Pr - 1)];
+    id[u] = p < p1 ? v : -1;
+  }
+}
+
+__global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(int T, int k, int E, int has_shared,
                                                 const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                 int32_t* __restrict__ active, int4* __restrict__ groups,
                                                 int32_t* __restrict__ n_groups, int32_t* __restrict__ dbg_counts,
                                                 int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
+  constexpr int NT = 64 * kBucketWaves;
   __shared__ int hist[1024];
-  __shared__ int red[6][4];
+  __shared__ int red[6][kBucketWaves];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Pr = T * k;
   // each wave owns the contiguous pair range [wave * chunk, (wave + 1) * chunk)
-  const int chunk = ((Pr + 3) / 4 + 63) / 64 * 64;
+  const int chunk = ((Pr + kBucketWaves - 1) / kBucketWaves + 63) / 64 * 64;
   const int p0 = wave * chunk, p1 = min(Pr, p0 + chunk);
-  for (int i = tid; i < E; i += 256) hist[i] = 0;
+  for (int i = tid; i < E; i += NT) hist[i] = 0;
   __syncthreads();
   int mine = 0;  // pairs of this wave's range routed to e
-  for (int base = p0; base < p1; base += 64) {
-    const int p = base + lane;
-    const int id = p < p1 ? ids[p] : -1;
-    if (id >= 0 && id < E) atomicAdd(&hist[id], 1);
-    mine += __popcll(__ballot(id == e));
+  for (int base = p0; base < p1; base += 64 * kBucketBatch) {
+    int id[kBucketBatch];
+    bucket_load(ids, base, p1, Pr, id);
+#pragma unroll
+    for (int u = 0; u < kBucketBatch; ++u) {
+      if (id[u] >= 0 && id[u] < E) atomicAdd(&hist[id[u]], 1);
+      mine += __popcll(__ballot(id[u] == e));
+    }
   }
   if (lane == 0) red[5][wave] = mine;
   __syncthreads();
   // pairs, non-empty buckets and groups below e; non-empty buckets and groups overall
   int v[5] = {0, 0, 0, 0, 0};
-  for (int i = tid; i < E; i += 256) {
+  for (int i = tid; i < E; i += NT) {
     const int c = hist[i], ng = (c + kGroupPairs - 1) / kGroupPairs;
     if (i < e) { v[0] += c; v[1] += c > 0; v[2] += ng; }
     v[3] += c > 0;
@@ -207,7 +229,12 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
   }
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 5; ++q) v[q] = red[q][0] + red[q][1] + red[q][2] + red[q][3];
+  for (int q = 0; q < 5; ++q) {
+    int acc = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kBucketWaves; ++w2) acc += red[q][w2];
+    v[q] = acc;
+  }
   const int lt = v[0], below = v[1], g_below = v[2], total = v[3], g_total = v[4];
   if (e == E) {
     const int cnt = has_shared ? T : 0;
@@ -220,9 +247,9 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
       if (dbg_counts) dbg_counts[E] = cnt;
       if (dbg_offsets) { dbg_offsets[E] = Pr; dbg_offsets[E + 1] = Pr + cnt; }
     }
-    for (int i = tid; i < ngs; i += 256)
+    for (int i = tid; i < ngs; i += NT)
       groups[g_total + i] = make_int4(E, Pr + kGroupPairs * i, min(kGroupPairs, cnt - kGroupPairs * i), 0);
-    for (int t = tid; t < cnt; t += 256) {
+    for (int t = tid; t < cnt; t += NT) {
       perm[Pr + t] = Pr + t;
       if (dbg_perm) dbg_perm[Pr + t] = Pr + t;
     }
@@ -237,22 +264,27 @@ __global__ __launch_bounds__(256) void k_bucket(int T, int k, int E, int has_sha
   }
   if (eq == 0) return;
   const int ng = (eq + kGroupPairs - 1) / kGroupPairs;
-  for (int i = tid; i < ng; i += 256)
+  for (int i = tid; i < ng; i += NT)
     groups[g_below + i] = make_int4(e, lt + kGroupPairs * i, min(kGroupPairs, eq - kGroupPairs * i), 0);
   // stable positions: earlier waves' matches, then this wave's in increasing p
   int pos = lt;
   for (int w2 = 0; w2 < wave; ++w2) pos += red[5][w2];
   if (red[5][wave] == 0) return;
-  for (int base = p0; base < p1; base += 64) {
-    const int p = base + lane;
-    const bool flag = p < p1 && ids[p] == e;
-    const uint64_t m = __ballot(flag);
-    if (flag) {
-      const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
-      perm[at] = p;
-      if (dbg_perm) dbg_perm[at] = p;
+  for (int base = p0; base < p1; base += 64 * kBucketBatch) {
+    int id[kBucketBatch];
+    bucket_load(ids, base, p1, Pr, id);
+#pragma unroll
+    for (int u = 0; u < kBucketBatch; ++u) {
+      const bool flag = id[u] == e;
+      const uint64_t m = __ballot(flag);
+      if (flag) {
+        const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+        const int p = base + 64 * u + lane;
+        perm[at] = p;
+        if (dbg_perm) dbg_perm[at] = p;
+      }
+      pos += __popcll(m);
     }
-    pos += __popcll(m);
   }
 }
 
@@ -275,8 +307,8 @@ hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, in
 hipError_t launch_bucket(int T, int k, int E, int has_shared, const int32_t* ids, const Work& w,
                          int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s,
                          const Timing& tm) {
-  MOEQ_LAUNCH(tm, kStageBucket, k_bucket, dim3(E + 1), dim3(256), 0, s, T, k, E, has_shared, ids, w.counts,
-              w.offsets, w.perm, w.active, w.groups, w.n_groups, dbg_counts, dbg_offsets, dbg_perm);
+  MOEQ_LAUNCH(tm, kStageBucket, k_bucket, dim3(E + 1), dim3(64 * kBucketWaves), 0, s, T, k, E, has_shared, ids,
+              w.counts, w.offsets, w.perm, w.active, w.groups, w.n_groups, dbg_counts, dbg_offsets, dbg_perm);
   return hipGetLastError();
 }
 
