@@ -174,6 +174,27 @@ def test_forward_shared_gate_and_fp32_inputs(xd):
     check_forward(layer, x, spec.x_dtype, y, dbg, what="shared gate")
 
 
+@pytest.mark.parametrize("xd", [synth.X_F32, synth.X_BF16])
+def test_mxfp4_grouped_activation_planes(xd):
+    """The block-scaled MXFP4 grouped path (fp8 activation planes: two for bf16 x, three
+    for fp32 x, one E8M0 scale per row; h in three planes per 256-column chunk) with a
+    ragged K (H = 160), h chunks padded past I = 96, a shared gate, an all-zero token and
+    tokens holding one entry 2^12 times the rest of the row (the row scale then leaves
+    the small entries fewer bits)."""
+    spec = synth.small_spec("mxplanes", 40, 160, 96, 12, 3, synth.WFMT_MXFP4, has_shared=1, x_dtype=xd,
+                            bias="normal", seed=321)
+    layer = synth.make_layer(spec, shared_gate=True)
+    x = synth.make_x(spec).copy()
+    x[0] = 0
+    for t, col in ((1, 0), (2, 77), (3, 159)):
+        if xd == synth.X_F32:
+            x[t, col] *= 4096.0
+        else:  # a bf16 value times 2^12: the exponent field plus 12 (exact)
+            x[t, col] = np.uint16(int(x[t, col]) + (12 << 7))
+    layer, x, dl, y, dbg = _run(spec, layer=layer, x=x, path=2)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"mxfp4 planes xd={xd}")
+
+
 def test_forward_deterministic_and_batch_invariant():
     spec = synth.CONFIGS["c3"]
     layer, x, dl, y, dbg = _run(spec)
