@@ -56,7 +56,7 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   Layout o{};
   size_t at = kHeaderBytes;  // the fixed header (synchronisation words) comes first
   auto take = [&](size_t bytes) { size_t r = at; at = align_up(at + bytes, kAlign); return r; };
-  o.logits = take((size_t)T * (E + 1) * 8);
+  o.logits = take((size_t)moeq::router_splits(T, (int)H) * T * (E + 1) * 8);  // K-split partial logits
   o.ids = take((size_t)T * k * 4);
   o.pair_w = take(P * 4);
   o.counts = take((E + 1) * 4);

@@ -219,11 +219,16 @@ __device__ __forceinline__ void sort_lane(uint64_t (&v)[NPER]) {
 // COHERENT: the logits were written by other blocks of the running kernel.  Token t's
 // selections go to s_exp/s_l[slot[t] * k + j] (written by lane 0), j = 0 .. k-1 in
 // selection order.
-template <int NPER, int NT, bool COHERENT>
+// The logits may come as nsplit <= MAXS partial sums (a K-split router), split z at
+// logits + z * split_stride; every split is loaded before any is added (clamped split
+// index: no branch around the loads), and they are added in z order.
+template <int NPER, int NT, bool COHERENT, int MAXS = 1>
 __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
-                                            const int (&slot)[NT], int* s_exp, double* s_l) {
+                                            const int (&slot)[NT], int* s_exp, double* s_l, int nsplit = 1,
+                                            size_t split_stride = 0) {
   const int lane = threadIdx.x & 63;
   uint64_t v[NT][NPER];
+  double part[NT][NPER][MAXS];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -231,7 +236,20 @@ __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, i
       // every lane loads (index clamped into the row): no branch around the loads
       const int e = lane + 64 * i;
       const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
-      const double lv = COHERENT ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+#pragma unroll
+      for (int z = 0; z < MAXS; ++z) {
+        const double* sz = src + (size_t)min(z, nsplit - 1) * split_stride;
+        part[t][i][z] = COHERENT ? __hip_atomic_load(sz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sz;
+      }
+    }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      double lv = part[t][i][0];
+#pragma unroll
+      for (int z = 1; z < MAXS; ++z) lv = z < nsplit ? lv + part[t][i][z] : lv;
       v[t][i] = e < E ? topk_key(lv, e) : 0ull;
     }
 #pragma unroll

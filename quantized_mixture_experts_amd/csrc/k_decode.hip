@@ -163,6 +163,80 @@ __device__ __forceinline__ void wait_arrivals(uint32_t* __restrict__ flags, int 
   }
 }
 
+// Routing after top-k (s_exp[p] = the expert of pair p for p < P, s_cnt zeroed): LDS
+// histogram, scan and stable ranks -> counts, offsets, perm, the active list and one slot
+// record per active expert.  Every thread of the block takes part.
+__device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots,
+                                               const int* s_exp, int* s_cnt, int* s_incl, const uint8_t* my_gu,
+                                               const uint8_t* my_dn, int32_t* __restrict__ dbg_counts,
+                                               int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = L.E, k = L.k;
+  const int nb = E + 1;
+  const int Pr = T * k;
+  const int P = Pr + (L.has_shared ? T : 0);
+  for (int p = tid; p < P; p += kRouteThreads) atomicAdd(&s_cnt[s_exp[p]], 1);
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < nb; base += 64) {
+      const int i = base + lane;
+      const int c = i < nb ? s_cnt[i] : 0;
+      int x = c | ((c > 0 ? 1 : 0) << 16);
+      // inclusive scan: DPP row shifts inside 16-lane rows, then the row totals
+      x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+      x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+      x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+      x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+      const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+      const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+      const int row = lane >> 4;
+      x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+      x += carry;
+      if (i < nb) s_incl[i] = x;
+      carry += r0 + r1 + r2 + r3;
+    }
+  }
+  __syncthreads();
+  const int n_active = s_incl[nb - 1] >> 16;
+  for (int e = tid; e < nb; e += kRouteThreads) {
+    const int c = s_cnt[e];
+    const int off = (s_incl[e] & 0xFFFF) - c;
+    w.counts[e] = c;
+    w.offsets[e] = off;
+    if (dbg_counts) dbg_counts[e] = c;
+    if (dbg_offsets) dbg_offsets[e] = off;
+    if (c > 0) {
+      const int a = (s_incl[e] >> 16) - 1;
+      w.active[1 + a] = e;
+      Slot& sl = w.slots[a];
+      sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
+      sl.gate_up = e == tid ? my_gu : L.gate_up[e];
+      sl.down = e == tid ? my_dn : L.down[e];
+    }
+  }
+  for (int a = n_active + tid; a < max_slots; a += kRouteThreads) {
+    Slot& sl = w.slots[a];
+    sl.e = 0; sl.cnt = 0; sl.off = 0; sl.n_active = n_active;
+    sl.gate_up = nullptr;
+    sl.down = nullptr;
+  }
+  if (tid == 0) {
+    w.offsets[nb] = P;
+    if (dbg_offsets) dbg_offsets[nb] = P;
+    w.active[0] = n_active;
+  }
+  for (int p = tid; p < P; p += kRouteThreads) {
+    const int e = s_exp[p];
+    int r = 0;
+    for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
+    const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
+    w.perm[pos] = p;
+    if (dbg_perm) dbg_perm[pos] = p;
+    if (r < kSlotRows) w.slots[(s_incl[e] >> 16) - 1].rows[r] = p;
+  }
+}
+
 template <int XDT>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
@@ -270,66 +344,31 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   __syncthreads();
-  for (int p = tid; p < P; p += kRouteThreads) atomicAdd(&s_cnt[s_exp[p]], 1);
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, my_gu, my_dn, dbg_counts, dbg_offsets, dbg_perm);
+}
+
+
+// Decode routing when the logits, ids and gates come from the matrix-core router and the
+// per-token top-k kernel (larger T): the combine tickets, then the route of one block.
+__global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T, Work w, int max_slots, int ntickets,
+                                                             int32_t* __restrict__ dbg_counts,
+                                                             int32_t* __restrict__ dbg_offsets,
+                                                             int32_t* __restrict__ dbg_perm) {
+  __shared__ int s_exp[kMaxPairsDec];
+  __shared__ int s_cnt[1024 + 1];
+  __shared__ int s_incl[1024 + 1];
+  const int tid = threadIdx.x;
+  const int E = L.E, nb = E + 1;
+  const int Pr = T * L.k;
+  const int P = Pr + (L.has_shared ? T : 0);
+  for (int i = tid; i < ntickets; i += kRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
+  for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
+  const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
+  const uint8_t* const my_gu = L.gate_up[ie];
+  const uint8_t* const my_dn = L.down[ie];
+  for (int p = tid; p < P; p += kRouteThreads) s_exp[p] = p < Pr ? w.ids[p] : E;
   __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < nb; base += 64) {
-      const int i = base + lane;
-      const int c = i < nb ? s_cnt[i] : 0;
-      int x = c | ((c > 0 ? 1 : 0) << 16);
-      // inclusive scan: DPP row shifts inside 16-lane rows, then the row totals
-      x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-      x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-      x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-      x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-      const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
-      const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
-      const int row = lane >> 4;
-      x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-      x += carry;
-      if (i < nb) s_incl[i] = x;
-      carry += r0 + r1 + r2 + r3;
-    }
-  }
-  __syncthreads();
-  const int n_active = s_incl[nb - 1] >> 16;
-  for (int e = tid; e < nb; e += kRouteThreads) {
-    const int c = s_cnt[e];
-    const int off = (s_incl[e] & 0xFFFF) - c;
-    w.counts[e] = c;
-    w.offsets[e] = off;
-    if (dbg_counts) dbg_counts[e] = c;
-    if (dbg_offsets) dbg_offsets[e] = off;
-    if (c > 0) {
-      const int a = (s_incl[e] >> 16) - 1;
-      w.active[1 + a] = e;
-      Slot& sl = w.slots[a];
-      sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
-      sl.gate_up = e == tid ? my_gu : L.gate_up[e];
-      sl.down = e == tid ? my_dn : L.down[e];
-    }
-  }
-  for (int a = n_active + tid; a < max_slots; a += kRouteThreads) {
-    Slot& sl = w.slots[a];
-    sl.e = 0; sl.cnt = 0; sl.off = 0; sl.n_active = n_active;
-    sl.gate_up = nullptr;
-    sl.down = nullptr;
-  }
-  if (tid == 0) {
-    w.offsets[nb] = P;
-    if (dbg_offsets) dbg_offsets[nb] = P;
-    w.active[0] = n_active;
-  }
-  for (int p = tid; p < P; p += kRouteThreads) {
-    const int e = s_exp[p];
-    int r = 0;
-    for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
-    const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
-    w.perm[pos] = p;
-    if (dbg_perm) dbg_perm[pos] = p;
-    if (r < kSlotRows) w.slots[(s_incl[e] >> 16) - 1].rows[r] = p;
-  }
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, my_gu, my_dn, dbg_counts, dbg_offsets, dbg_perm);
 }
 
 // ---------------------------------------------------------------------------
@@ -945,6 +984,11 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   return g <= 160 * 1024 && d <= 160 * 1024;
 }
 
+// From this many tokens the decode path routes with three kernels (matrix-core router,
+// per-token top-k, route) instead of the single router/route kernel, whose fp64
+// reductions and one-CU top-k grow with T.
+constexpr int kDecSplitRouteT = 8;
+
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
                          int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts, int32_t* dbg_offsets,
                          int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
@@ -952,7 +996,13 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const int ntickets = L.H / 16;
   const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
   const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
-  if (x_dtype == 0)
+  if (T >= kDecSplitRouteT) {
+    // the fp64 matrix-core router and one wave per token for the top-k, then the route
+    hipError_t e = launch_router_topk(L, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
+    if (e != hipSuccess) return e;
+    MOEQ_LAUNCH(tm, kStageBucket, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, w, max_slots, ntickets,
+                dbg_counts, dbg_offsets, dbg_perm);
+  } else if (x_dtype == 0)
     MOEQ_LAUNCH(tm, kStageRouter, k_dec_rr<0>, grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w, max_slots,
                 w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   else

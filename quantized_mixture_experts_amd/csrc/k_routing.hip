@@ -39,8 +39,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
   const int i = lane & 15, kk = lane >> 4;
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 16;
   const int H = L.H;
+  const int z = blockIdx.z, nsplit = gridDim.z;  // this block's share of the 16-column chunks
 
-  if (XDT == 0 && blockIdx.y == 0) {
+  if (XDT == 0 && blockIdx.y == 0 && z == 0) {
     const float* xf = (const float*)x;
     const int nt = min(32, T - t0);
     for (int idx = threadIdx.x; idx < nt * H; idx += 64 * kRouterWaves) {
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
   const float* wrow = e < L.E ? L.router_w + (size_t)e * H : (e < erows ? L.shared_gate_w : L.router_w);
   f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
   const int nch = H >> 4;
+  const int ch_beg = z * nch / nsplit, ch_end = (z + 1) * nch / nsplit;
 #pragma unroll 4
-  for (int ch = wave; ch < nch; ch += kRouterWaves) {
+  for (int ch = ch_beg + wave; ch < ch_end; ch += kRouterWaves) {
     const int k = 16 * ch + 4 * kk;
     double a0[4], a1[4], b[4];
     const float4 wv = *(const float4*)(wrow + k);
@@ -93,7 +95,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
   __syncthreads();
   if (wave == 0) {
     const int col = e0 + i;  // expert of this lane's outputs
-    const double bias = (col < L.E && L.router_b) ? (double)L.router_b[col] : 0.0;
+    const double bias = (z == 0 && col < L.E && L.router_b) ? (double)L.router_b[col] : 0.0;
+    double* out = logits + (size_t)z * T * (L.E + 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       double s0 = acc0[r], s1 = acc1[r];
@@ -104,8 +107,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
       }
       const int row = 4 * r + kk;  // token within the 16-token tile
       if (col < erows) {
-        if (t0 + row < T) logits[(size_t)(t0 + row) * (L.E + 1) + col] = s0 + bias;
-        if (t0 + 16 + row < T) logits[(size_t)(t0 + 16 + row) * (L.E + 1) + col] = s1 + bias;
+        if (t0 + row < T) out[(size_t)(t0 + row) * (L.E + 1) + col] = s0 + bias;
+        if (t0 + 16 + row < T) out[(size_t)(t0 + 16 + row) * (L.E + 1) + col] = s1 + bias;
       }
     }
   }
@@ -119,12 +122,14 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
 // pair_w[T*k+t] = 1 or sigmoid(shared logit).
 // ---------------------------------------------------------------------------
 template <int NPER>
-__device__ __forceinline__ void topk_one(const double* logits, int E, int k, int t, int* s_exp, double* s_l) {
+__device__ __forceinline__ void topk_one(const double* logits, int E, int k, int t, int* s_exp, double* s_l,
+                                         int nsplit, size_t split_stride) {
   const int tok[1] = {t}, slot[1] = {0};
-  topk_tokens<NPER, 1, false>(logits, E, k, tok, slot, s_exp, s_l);
+  if (nsplit == 1) topk_tokens<NPER, 1, false, 1>(logits, E, k, tok, slot, s_exp, s_l);
+  else topk_tokens<NPER, 1, false, kRouterMaxSplits>(logits, E, k, tok, slot, s_exp, s_l, nsplit, split_stride);
 }
 
-__global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* __restrict__ logits,
+__global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* __restrict__ logits, int nsplit,
                                               int32_t* __restrict__ ids, float* __restrict__ pair_w,
                                               int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w) {
   __shared__ int s_exp[4][16];
@@ -133,12 +138,13 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // no block-wide synchronisation below
   const int E = L.E, k = L.k;
+  const size_t sstride = (size_t)T * (E + 1);
   const int nper = (E + 63) >> 6;
-  if (nper <= 1) topk_one<1>(logits, E, k, t, s_exp[wave], s_l[wave]);
-  else if (nper <= 2) topk_one<2>(logits, E, k, t, s_exp[wave], s_l[wave]);
-  else if (nper <= 4) topk_one<4>(logits, E, k, t, s_exp[wave], s_l[wave]);
-  else if (nper <= 8) topk_one<8>(logits, E, k, t, s_exp[wave], s_l[wave]);
-  else topk_one<16>(logits, E, k, t, s_exp[wave], s_l[wave]);
+  if (nper <= 1) topk_one<1>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
+  else if (nper <= 2) topk_one<2>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
+  else if (nper <= 4) topk_one<4>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
+  else if (nper <= 8) topk_one<8>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
+  else topk_one<16>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
   const double l0 = s_l[wave][0];
   const double z = lane < k ? exp(s_l[wave][lane] - l0) : 0.0;
   const double zs = wave_sum_f64(z);
@@ -152,7 +158,15 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
   }
   if (L.has_shared && lane == 0) {
     float s = 1.0f;
-    if (L.shared_gate_w) s = (float)(1.0 / (1.0 + exp(-logits[(size_t)t * (E + 1) + E])));
+    if (L.shared_gate_w) {
+      double pz[kRouterMaxSplits];  // every split loaded first (clamped index), added in order
+#pragma unroll
+      for (int z = 0; z < kRouterMaxSplits; ++z) pz[z] = logits[(size_t)min(z, nsplit - 1) * sstride + (size_t)t * (E + 1) + E];
+      double ls = pz[0];
+#pragma unroll
+      for (int z = 1; z < kRouterMaxSplits; ++z) ls = z < nsplit ? ls + pz[z] : ls;
+      s = (float)(1.0 / (1.0 + exp(-ls)));
+    }
     pair_w[T * k + t] = s;
   }
 }
@@ -294,13 +308,14 @@ __global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(int T, int k, int 
 hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
                               int32_t* dbg_ids, float* dbg_w, hipStream_t s, const Timing& tm) {
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
-  dim3 grid((T + 31) / 32, (erows + 15) / 16);
+  const int nsplit = router_splits(T, L.H);
+  dim3 grid((T + 31) / 32, (erows + 15) / 16, nsplit);
   if (x_dtype == 0)
     MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<0>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
   else
     MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<1>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
-  MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits, w.ids,
-              w.pair_w, dbg_ids, dbg_w);
+  MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits, nsplit,
+              w.ids, w.pair_w, dbg_ids, dbg_w);
   return hipGetLastError();
 }
 

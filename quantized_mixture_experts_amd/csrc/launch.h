@@ -33,6 +33,16 @@ struct Timing {
       hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                \
   } while (0)
 
+// K-split of the matrix-core router for small batches (up to 32 tokens fill one token
+// tile, so the expert tiles alone would leave most CUs idle): each split writes partial
+// logits [T][E+1] at logits + z * T * (E + 1), summed in z order by the top-k.
+constexpr int kRouterMaxSplits = 8;  // the top-k loads at most this many partial sums
+inline int router_splits(int T, int H) {
+  if (T > 32) return 1;
+  const int nch = H / 16;  // 16-column chunks
+  return nch >= kRouterMaxSplits * 16 ? kRouterMaxSplits : (nch >= 4 * 16 ? 4 : 1);
+}
+
 hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
                               int32_t* dbg_ids, float* dbg_w, hipStream_t s,
                               const Timing& tm = Timing());
