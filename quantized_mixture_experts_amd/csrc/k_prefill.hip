@@ -3,8 +3,8 @@
 // Work unit: a group = up to 64 consecutive bucket positions of one expert (the
 // bucketing kernel lists them in bucket order).  A block of 8 waves covers 512 weight
 // rows of that expert for the group's pairs; every wave owns a 64-row x 64-pair tile
-// (4 x 4 tiles of v_mfma_f32_16x16x32_bf16) over the whole K range, so there is no
-// split-K reduction.  In the fused gate/up kernel a wave holds 32 gate rows and the 32
+// (4 x 4 MFMA tiles of 16 x 16) over the whole K range, so there is no split-K
+// reduction.  In the fused gate/up kernel a wave holds 32 gate rows and the 32
 // matching up rows, so SwiGLU is applied in registers.  Each selected expert's rows
 // are read from HBM once per group (once in total when it has at most 64 pairs), the
 // grouping the NInfer Qwen3.8-Flash-Next page describes for its MoE execution (pairs
@@ -20,14 +20,17 @@
 //     into LDS for the block's 32 row tiles, D k-steps at a time, by one direct
 //     global->LDS load per wave, into two alternating buffers (a byte load per lane and
 //     row tile per k-step would cost as many memory instructions as the codes);
-//   - only the activation rows of the group's live 16-row token tiles are staged;
+//   - only the activation rows of the group's live 16-row token tiles are staged (CB4);
 //   - the k loop is unrolled by D, so ring slots and buffers are compile-time indices
 //     and the wait before each step is a constant vmcnt (every wave issues the same
 //     number of loads per step; loads past the row end re-read a real block that is
 //     then masked, so nothing outside the matrices is touched).
-// Operands as in the decode kernels: A = activation rows (bf16 planes, exact), B =
-// decoded weights (MXFP4 with its E8M0 scale folded in, exact; CB4 codebook values,
-// with the fp16 block scale applied to each 32-column block's fp32 MFMA result).
+// Operands:
+//   - CB4 (v_mfma_f32_16x16x32_bf16): A = activation rows as bf16 planes (exact), B =
+//     codebook values from the LDS table (exact in bf16), the fp16 block scale applied
+//     to each 32-column block's fp32 MFMA result;
+//   - MXFP4 (v_mfma_scale_f32_16x16x128_f8f6f4): A = the activations as fp8 e4m3 planes
+//     with E8M0 scales, B = the stored E2M1 codes and their E8M0 scales as they are.
 #include "device.h"
 #include "launch.h"
 
