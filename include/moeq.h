@@ -108,7 +108,7 @@ size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols);
 
 /* [host] Workspace bytes moe_forward / moe_router_topk / moe_bucket need for up
  * to T_max tokens (0 if the descriptor is invalid).  The workspace is scratch
- * except for its first 2048 bytes, which hold synchronisation words: they must be
+ * except for its first 18432 bytes, which hold synchronisation words: they must be
  * zero before the workspace's first use (e.g. hipMemset once after allocation),
  * and every completed call leaves them zero.  Everything past them is rewritten
  * by every call. */

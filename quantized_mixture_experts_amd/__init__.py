@@ -147,7 +147,7 @@ class DeviceLayer:
         n = self.workspace_bytes(T)
         if n == 0 and T > 0:
             raise MoeError(MOE_ERR_INVALID_ARG, "moe_workspace_bytes")
-        return torch.zeros(max(n, 2048), dtype=torch.uint8, device=self.router_w.device)
+        return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.router_w.device)
 
 
 def router_topk(L: DeviceLayer, x, x_dtype: int, ws=None, stream=None):

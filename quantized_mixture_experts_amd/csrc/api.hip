@@ -17,8 +17,9 @@ using moeq::Work;
 constexpr size_t kAlign = 256;
 // Workspace header at offset 0 whatever T is: words that must read zero when a call
 // starts (each call leaves them zero): the decode router's arrival flags, one word
-// per router block (at most (1024 + 1 + 3) / 4 = 257 blocks).
-constexpr size_t kHeaderBytes = 2048;
+// per router block (at most (1024 + 1 + 3) / 4 = 257 blocks), then its logit mailbox
+// (moeq::kDecMailboxWords 64-bit words at byte 2048).
+constexpr size_t kHeaderBytes = 2048 + 8 * moeq::kDecMailboxWords;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -97,6 +98,7 @@ Work carve(void* ws, const Layout& lo) {
   w.groups = reinterpret_cast<int4*>(b + lo.groups);
   w.n_groups = reinterpret_cast<int32_t*>(b + lo.n_groups);
   w.rr_flags = reinterpret_cast<uint32_t*>(b);
+  w.rr_mbox = reinterpret_cast<uint64_t*>(b + 2048);
   return w;
 }
 

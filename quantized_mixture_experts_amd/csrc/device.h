@@ -80,7 +80,12 @@ struct Work {
   int32_t* n_groups;   // [1] number of valid entries of groups
   uint32_t* rr_flags;  // decode router arrival flags, one per block: in the workspace's fixed
                        // header, zero between calls
+  uint64_t* rr_mbox;   // decode router logit mailbox [T][E+1] (T (E+1) <= kDecMailboxWords): in
+                       // the fixed header, zero between calls; a logit l is posted as ~bits(l)
 };
+// Words of the decode router's logit mailbox.  ~bits(l) is never 0: that needs the
+// all-ones NaN, which fp64 arithmetic on fp32/bf16 data does not produce.
+constexpr int kDecMailboxWords = 2048;
 
 // Pairs per prefill work group (four 16-row MFMA token tiles).
 constexpr int kGroupPairs = 64;
@@ -222,26 +227,59 @@ __device__ __forceinline__ void sort_lane(uint64_t (&v)[NPER]) {
 // The logits may come as nsplit <= MAXS partial sums (a K-split router), split z at
 // logits + z * split_stride; every split is loaded before any is added (clamped split
 // index: no branch around the loads), and they are added in z order.
-template <int NPER, int NT, bool COHERENT, int MAXS = 1>
+//
+// MBOX: the logits are posted as ~bits in a zeroed mailbox by other blocks (logits is
+// then the mailbox): the wave polls its entries (bounded) until none reads 0, decodes
+// them and clears them for the next call.
+template <int NPER, int NT, bool COHERENT, int MAXS = 1, bool MBOX = false>
 __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
                                             const int (&slot)[NT], int* s_exp, double* s_l, int nsplit = 1,
                                             size_t split_stride = 0) {
   const int lane = threadIdx.x & 63;
   uint64_t v[NT][NPER];
   double part[NT][NPER][MAXS];
+  if constexpr (MBOX) {
+    static_assert(MAXS == 1, "the mailbox holds whole logits");
+    uint64_t raw[NT][NPER];
+    for (uint32_t spins = 0;; ++spins) {
+      bool missing = false;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      // every lane loads (index clamped into the row): no branch around the loads
-      const int e = lane + 64 * i;
-      const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
-#pragma unroll
-      for (int z = 0; z < MAXS; ++z) {
-        const double* sz = src + (size_t)min(z, nsplit - 1) * split_stride;
-        part[t][i][z] = COHERENT ? __hip_atomic_load(sz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sz;
-      }
+        for (int i = 0; i < NPER; ++i) {
+          const int e = lane + 64 * i;
+          uint64_t* src = (uint64_t*)(logits + (size_t)tok[t] * (E + 1) + min(e, E - 1));
+          raw[t][i] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          missing |= e < E && raw[t][i] == 0ull;
+        }
+      if (__ballot(missing) == 0ull || spins > (1u << 22)) break;
+      __builtin_amdgcn_s_sleep(1);
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = lane + 64 * i;
+        part[t][i][0] = __builtin_bit_cast(double, ~raw[t][i]);
+        if (e < E)
+          __hip_atomic_store((uint64_t*)(logits + (size_t)tok[t] * (E + 1) + e), 0ull, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        // every lane loads (index clamped into the row): no branch around the loads
+        const int e = lane + 64 * i;
+        const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
+#pragma unroll
+        for (int z = 0; z < MAXS; ++z) {
+          const double* sz = src + (size_t)min(z, nsplit - 1) * split_stride;
+          part[t][i][z] = COHERENT ? __hip_atomic_load(sz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sz;
+        }
+      }
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll

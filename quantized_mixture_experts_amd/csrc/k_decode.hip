@@ -59,15 +59,15 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
-template <int NPER>
+template <int NPER, bool MBOX>
 __device__ __forceinline__ void topk_wave(const double* __restrict__ logits, int E, int k, int T, int t0, int t1,
                                           int* s_exp, double* s_l) {
   if (t1 < T) {
     const int tok[2] = {t0, t1};
-    topk_tokens<NPER, 2, true>(logits, E, k, tok, tok, s_exp, s_l);
+    topk_tokens<NPER, 2, true, 1, MBOX>(logits, E, k, tok, tok, s_exp, s_l);
   } else if (t0 < T) {
     const int tok[1] = {t0};
-    topk_tokens<NPER, 1, true>(logits, E, k, tok, tok, s_exp, s_l);
+    topk_tokens<NPER, 1, true, 1, MBOX>(logits, E, k, tok, tok, s_exp, s_l);
   }
 }
 
@@ -237,7 +237,10 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   }
 }
 
-template <int XDT>
+// MBOX (T (E+1) <= kDecMailboxWords): the logits go through the mailbox in the
+// workspace header and block 0 polls them directly (no arrival flags, one round trip
+// fewer); otherwise through w.logits and the arrival flags.
+template <int XDT, bool MBOX>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
                                                           int ntickets, int32_t* __restrict__ dbg_ids,
@@ -286,19 +289,27 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       if (er < erows) {
         double v = ((s_part[4 * r][t] + s_part[4 * r + 1][t]) + s_part[4 * r + 2][t]) + s_part[4 * r + 3][t];
         if (er < E && L.router_b) v += (double)L.router_b[er];
-        __hip_atomic_store(w.logits + (size_t)t * (E + 1) + er, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (MBOX)
+          __hip_atomic_store(w.rr_mbox + (size_t)t * (E + 1) + er, ~__builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          __hip_atomic_store(w.logits + (size_t)t * (E + 1) + er, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  // arrival: this block's logits are written through and complete before its flag
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (blockIdx.x != 0) {
-    if (tid == 0) __hip_atomic_store(rr_flags + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
+  if (MBOX) {
+    if (blockIdx.x != 0) return;
+  } else {
+    // arrival: this block's logits are written through and complete before its flag
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blockIdx.x != 0) {
+      if (tid == 0) __hip_atomic_store(rr_flags + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    wait_arrivals(rr_flags, gridDim.x);
   }
-  wait_arrivals(rr_flags, gridDim.x);
   // thread e's expert pointers for the slot records: issued now, used at the end
   const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
   const uint8_t* const my_gu = L.gate_up[ie];
@@ -308,16 +319,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
 
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  const double* logits = w.logits;
+  const double* logits = MBOX ? (const double*)w.rr_mbox : w.logits;
   // top-k: wave w takes tokens w and w + 16 (T <= 32), side by side
   {
     const int t0 = wave, t1 = wave + kWaves;
     const int nper = (E + 63) >> 6;
-    if (nper <= 1) topk_wave<1>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 2) topk_wave<2>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 4) topk_wave<4>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 8) topk_wave<8>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else topk_wave<16>(logits, E, k, T, t0, t1, s_exp, s_l);
+    if (nper <= 1) topk_wave<1, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 2) topk_wave<2, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 4) topk_wave<4, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else if (nper <= 8) topk_wave<8, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
+    else topk_wave<16, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
     for (int t = t0; t < T && t <= t1; t += kWaves) {
       const double l0 = s_l[t * k];
       const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
@@ -334,8 +345,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       if (L.has_shared && lane == 0) {
         double sg = 1.0;
         if (L.shared_gate_w) {
-          const double ls =
-              __hip_atomic_load(logits + (size_t)t * (E + 1) + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          double ls;
+          if (MBOX) {  // poll the posted shared-gate logit (bounded), then clear it
+            uint64_t* src = w.rr_mbox + (size_t)t * (E + 1) + E;
+            uint64_t raw = 0;
+            for (uint32_t spins = 0; spins <= (1u << 22); ++spins) {
+              raw = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (raw != 0ull) break;
+              __builtin_amdgcn_s_sleep(1);
+            }
+            __hip_atomic_store(src, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ls = __builtin_bit_cast(double, ~raw);
+          } else {
+            ls = __hip_atomic_load(logits + (size_t)t * (E + 1) + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
           sg = 1.0 / (1.0 + exp(-ls));
         }
         w.pair_w[Pr + t] = (float)sg;
@@ -1002,12 +1025,21 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
     if (e != hipSuccess) return e;
     MOEQ_LAUNCH(tm, kStageBucket, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, w, max_slots, ntickets,
                 dbg_counts, dbg_offsets, dbg_perm);
-  } else if (x_dtype == 0)
-    MOEQ_LAUNCH(tm, kStageRouter, k_dec_rr<0>, grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w, max_slots,
-                w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-  else
-    MOEQ_LAUNCH(tm, kStageRouter, k_dec_rr<1>, grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w, max_slots,
-                w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+  } else {
+    const bool mbox = T * (L.E + 1) <= kDecMailboxWords;
+    if (x_dtype == 0 && mbox)
+      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else if (x_dtype == 0)
+      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else if (mbox)
+      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else
+      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return L.wfmt == 1 ? launch_dec_experts<1>(L, x, x_dtype, T, w, y, w.tickets, s, tm)
