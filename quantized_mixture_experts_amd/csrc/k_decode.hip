@@ -694,6 +694,38 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   }
 }
 
+// y[t][col0 .. col0+ncols) = sum_j g[t,j] o[t*k+j] (+ shared), j ascending then the shared
+// expert: the fixed-order combine of the block that arrives last at a column tile.
+// The o rows are read at device scope (written through by the other blocks), the k
+// routed ones 8 at a time (clamped loads, in bounds).
+__device__ __forceinline__ void dec_combine_cols(const LayerArgs& L, int T, const Work& w, float* __restrict__ y,
+                                                 int col0, int ncols) {
+  const int H = L.H, k = L.k;
+  for (int idx = threadIdx.x; idx < T * ncols; idx += blockDim.x) {
+    const int t = idx / ncols;
+    const int col = col0 + idx % ncols;
+    if (col >= H) continue;
+    float s = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float ov[8], wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, k - 1);
+        ov[u] = __hip_atomic_load(&w.o[(size_t)(t * k + j) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wv[u] = w.pair_w[t * k + j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) s = fmaf(wv[u], ov[u], s);
+    }
+    if (L.has_shared) {
+      const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s = fmaf(w.pair_w[T * k + t], o, s);
+    }
+    y[(size_t)t * H + col] = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 4. Down projection + combine.  grid = (H/16, max active slots), 4 waves split K=I.
 // Each block writes o_p[16 cols] for its expert's pairs; the last block to arrive at
@@ -777,20 +809,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  for (int idx = threadIdx.x; idx < T * 16; idx += 256) {
-    const int t = idx >> 4;
-    const int col = 16 * blockIdx.x + (idx & 15);
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float o = __hip_atomic_load(&w.o[(size_t)(t * k + j) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s = fmaf(w.pair_w[t * k + j], o, s);
-    }
-    if (L.has_shared) {
-      const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s = fmaf(w.pair_w[T * k + t], o, s);
-    }
-    y[(size_t)t * H + col] = s;
-  }
+  dec_combine_cols(L, T, w, y, 16 * blockIdx.x, 16);
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -868,21 +887,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  for (int idx = threadIdx.x; idx < T * 64; idx += 256) {
-    const int t = idx >> 6;
-    const int col = 64 * blockIdx.x + (idx & 63);
-    if (col >= H) continue;
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float o = __hip_atomic_load(&w.o[(size_t)(t * k + j) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s = fmaf(w.pair_w[t * k + j], o, s);
-    }
-    if (L.has_shared) {
-      const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s = fmaf(w.pair_w[T * k + t], o, s);
-    }
-    y[(size_t)t * H + col] = s;
-  }
+  dec_combine_cols(L, T, w, y, 64 * blockIdx.x, 64);
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
