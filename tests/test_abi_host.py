@@ -125,3 +125,15 @@ def test_status_strings(L):
 def test_workspace_grows_with_tokens(L):
     lay = layer()
     assert ws_bytes(L, lay, 0) < ws_bytes(L, lay, 1) < ws_bytes(L, lay, 1024)
+
+
+def test_workspace_covers_header_and_fp8_planes(L):
+    """The fixed header (arrival flags + the decode router's logit mailbox: 18,432 bytes)
+    comes first, and the activation regions also hold the MXFP4 prefill's fp8 planes,
+    which exceed the bf16 planes for small H and I (rows padded to 128 / 256 columns)."""
+    T = 64
+    lay = layer(hidden=32, inter=32, n_experts=8, top_k=2, wfmt=q.WFMT_MXFP4, codebook=None, has_shared=1)
+    P = T * 2 + T
+    need = ws_bytes(L, lay, T)
+    assert need >= 18432 + (3 * T * 128 + T) + (3 * P * 256 + P)
+    assert ws_bytes(L, layer(), 1) >= 18432
