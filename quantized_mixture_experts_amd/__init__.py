@@ -231,7 +231,10 @@ class HipEvents:
     def elapsed_ms(self, i: int, j: int) -> Optional[float]:
         ms = ctypes.c_float()
         r = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j])
-        return ms.value if r == 0 else None
+        if r != 0:  # a stage that launched nothing: clear the error the query left behind
+            self.hip.hipGetLastError()
+            return None
+        return ms.value
 
     def __del__(self):
         try:
