@@ -195,6 +195,22 @@ def test_mxfp4_grouped_activation_planes(xd):
     check_forward(layer, x, spec.x_dtype, y, dbg, what=f"mxfp4 planes xd={xd}")
 
 
+@pytest.mark.parametrize("H,I,k,shared,wfmt,xd", [
+    (512, 4096, 4, 0, synth.WFMT_MXFP4, synth.X_BF16),   # K = I over several k-step chunks per wave
+    (384, 768, 2, 1, synth.WFMT_MXFP4, synth.X_F32),     # 3 slots, fp32 x planes, ragged last k-step group
+    (256, 1024, 4, 1, synth.WFMT_CB4, synth.X_F32),      # codebook weights, shared gate
+    (256, 1024, 8, 1, synth.WFMT_CB4, synth.X_BF16),     # 9 slots
+])
+def test_one_token_long_rows(H, I, k, shared, wfmt, xd):
+    """One token with long down rows (the split-K down kernel and its ticketed combine)
+    over several slot counts, both weight formats and both activation types."""
+    spec = synth.small_spec(f"t1_{H}_{I}_{k}", 1, H, I, 24, k, wfmt, has_shared=shared, x_dtype=xd,
+                            bias="normal", seed=7 * I + k)
+    layer = synth.make_layer(spec, shared_gate=bool(shared))
+    layer, x, dl, y, dbg = _run(spec, layer=layer)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"one token H={H} I={I} k={k}")
+
+
 def test_forward_deterministic_and_batch_invariant():
     spec = synth.CONFIGS["c3"]
     layer, x, dl, y, dbg = _run(spec)
