@@ -211,6 +211,26 @@ def test_one_token_long_rows(H, I, k, shared, wfmt, xd):
     check_forward(layer, x, spec.x_dtype, y, dbg, what=f"one token H={H} I={I} k={k}")
 
 
+@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("T,H,I,E,k,wfmt,shared,xd", [
+    (5, 128, 64, 1024, 16, synth.WFMT_MXFP4, 1, synth.X_BF16),   # most experts, largest top-k
+    (40, 128, 64, 1024, 16, synth.WFMT_CB4, 1, synth.X_F32),
+    (3, 16384, 64, 4, 2, synth.WFMT_CB4, 0, synth.X_BF16),       # largest H: 128 k-steps of gate/up
+    (3, 64, 16384, 4, 2, synth.WFMT_MXFP4, 1, synth.X_F32),      # largest I: 128 k-steps of down
+    (64, 16384, 64, 4, 2, synth.WFMT_MXFP4, 1, synth.X_BF16),
+    (64, 64, 16384, 4, 2, synth.WFMT_MXFP4, 0, synth.X_F32),     # 64 h scale chunks, the LDS table's size
+    (64, 64, 16384, 4, 2, synth.WFMT_CB4, 1, synth.X_BF16),
+])
+def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
+    """The library's largest supported experts count, top-k, hidden and intermediate
+    sizes, on the automatic path (decode kernels up to 32 tokens) and the grouped one."""
+    spec = synth.small_spec(f"lim{T}_{H}_{I}_{E}", T, H, I, E, k, wfmt, has_shared=shared, x_dtype=xd,
+                            bias="normal", seed=T + H + I + E)
+    layer = synth.make_layer(spec, shared_gate=bool(shared))
+    layer, x, dl, y, dbg = _run(spec, layer=layer, path=path)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"limits T={T} H={H} I={I} E={E} k={k} path={path}")
+
+
 def test_forward_deterministic_and_batch_invariant():
     spec = synth.CONFIGS["c3"]
     layer, x, dl, y, dbg = _run(spec)
