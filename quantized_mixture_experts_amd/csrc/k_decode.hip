@@ -243,7 +243,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
 template <int XDT, bool MBOX>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
-                                                          int ntickets, int32_t* __restrict__ dbg_ids,
+                                                          int ntickets, int nzero_o, int32_t* __restrict__ dbg_ids,
                                                           float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
                                                           int32_t* __restrict__ dbg_offsets,
                                                           int32_t* __restrict__ dbg_perm) {
@@ -259,6 +259,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
 
   if (blockIdx.x == 0) {
     for (int i = tid; i < ntickets; i += kRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
+    // the o mailbox of the one-token combine (nzero_o words, 0 = not posted)
+    for (int i = tid; i < nzero_o; i += kRouteThreads) reinterpret_cast<uint32_t*>(w.o)[i] = 0u;
     if (XDT == 0) {  // exact 3-plane bf16 split of fp32 x for the projections
       const float* xf = (const float*)x;
       for (int idx = tid; idx < T * H; idx += kRouteThreads) {
@@ -733,7 +735,17 @@ __device__ __forceinline__ void dec_combine_cols(const LayerArgs& L, int T, cons
 // travel as write-through stores and a relaxed device-scope ticket counts arrivals,
 // so no full L2 write-back is needed.
 // ---------------------------------------------------------------------------
-template <int FMT, int NTT, int KSW>
+// Pairs of one token: top-k routed ones plus the shared one.
+constexpr int kMaxPairsT1 = 17;
+
+// o posted to the one-token mailbox as ~bits(o): never 0 (the all-ones NaN is replaced
+// by another NaN), so 0 marks an entry not yet written.
+__device__ __forceinline__ uint32_t omb_encode(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return ~(b == 0xFFFFFFFFu ? 0xFFC00000u : b);
+}
+
+template <int FMT, int NTT, int KSW, bool OMB>
 __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
                                                      uint32_t* __restrict__ tickets, int xrows_max) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -785,6 +797,43 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * tt + q] = acc[tt][q];
     reduce4<4 * NTT>(v, (float*)(smem + 1024));
+    if constexpr (OMB) {
+      // One token (one pair per slot, one pass): the block of the last active slot sums
+      // the column tile over all pairs in the fixed order, reading the other slots' o
+      // from the mailbox; the others only post theirs.  The launch admits this only when
+      // the whole grid is resident at once, so the posts it waits for always come.
+      if (wave == 0 && g == 0) {
+        const int col = 16 * blockIdx.x + n;
+        const int p_own = w.perm[off];
+        uint32_t* omb = reinterpret_cast<uint32_t*>(w.o);
+        if ((int)blockIdx.y != n_active - 1) {
+          __hip_atomic_store(&omb[(size_t)p_own * H + col], omb_encode(v[0]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
+          uint32_t e[kMaxPairsT1];
+          for (uint32_t spins = 0; spins <= (1u << 22); ++spins) {
+            bool miss = false;
+#pragma unroll
+            for (int u = 0; u < kMaxPairsT1; ++u) {
+              const int p = min(u, P1 - 1);
+              e[u] = p == p_own ? omb_encode(v[0])
+                                : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+              miss |= e[u] == 0u;
+            }
+            if (!miss) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+          float sum = 0.f;
+#pragma unroll
+          for (int u = 0; u < kMaxPairsT1; ++u)
+            if (u < P1) sum = fmaf(w.pair_w[u], __uint_as_float(~e[u]), sum);
+          y[col] = sum;
+        }
+      }
+      return;
+    }
     if (wave == 0) {
       const int col = 16 * blockIdx.x + n;
 #pragma unroll
@@ -941,10 +990,56 @@ static void launch_down_rows_k(const LayerArgs& L, int T, const Work& w, float* 
 
 template <int FMT, int NTT, int KSW>
 static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
-                          hipStream_t s, const Timing& tm) {
+                          bool omb, hipStream_t s, const Timing& tm) {
   const dim3 g2(L.H / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
-  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW>), g2, dim3(256), dec_lds_bytes(L.I, 2, NTT, xrows), s, L,
-              T, w, y, tickets, xrows);
+  if constexpr (NTT == 1) {
+    if (omb) {
+      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), g2, dim3(256), dec_lds_bytes(L.I, 2, 1, xrows), s,
+                  L, T, w, y, tickets, xrows);
+      return;
+    }
+  }
+  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), g2, dim3(256), dec_lds_bytes(L.I, 2, NTT, xrows),
+              s, L, T, w, y, tickets, xrows);
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int FMT, int KSW>
+static bool down_grid_resident(const LayerArgs& L, int nslots, size_t lds) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_dec_down<FMT, 1, KSW, true>, 256, lds) !=
+      hipSuccess)
+    return false;
+  return (long)(L.H / 16) * nslots <= (long)device_cus() * per_cu;
+}
+
+// The one-token mailbox combine of the split-K down kernel: one token, long down rows,
+// and a grid that is resident at once (so the block that waits never waits for a block
+// that has not started).
+template <int FMT>
+static bool use_down_mailbox(const LayerArgs& L, int T) {
+  if (T != 1 || (L.I / 32 + 3) / 4 <= 4) return false;
+  const int nslots = min(L.k, L.E) + (L.has_shared ? 1 : 0);
+  const size_t lds = dec_lds_bytes(L.I, 2, 1, 1);  // one token: one staged row
+  switch (pick_ksw(L.I)) {
+    case 1: return down_grid_resident<FMT, 1>(L, nslots, lds);
+    case 2: return down_grid_resident<FMT, 2>(L, nslots, lds);
+    case 4: return down_grid_resident<FMT, 4>(L, nslots, lds);
+    case 6: return down_grid_resident<FMT, 6>(L, nslots, lds);
+    default: return down_grid_resident<FMT, 8>(L, nslots, lds);
+  }
 }
 
 // Rows of activations a projection block stages per pass: as many of the expert's
@@ -971,7 +1066,7 @@ static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, in
 
 template <int FMT, int NTT>
 static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
-                            hipStream_t s, const Timing& tm) {
+                            bool omb, hipStream_t s, const Timing& tm) {
   const int nks_dn = (L.I / 32 + 3) / 4;
   if (nks_dn <= 4) {  // short rows: one 16-row tile per wave over the whole K
     switch (nks_dn) {
@@ -982,24 +1077,24 @@ static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, 
     return;
   }
   switch (pick_ksw(L.I)) {
-    case 1: launch_down_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm); break;
-    case 2: launch_down_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, s, tm); break;
-    case 4: launch_down_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, s, tm); break;
-    case 6: launch_down_k<FMT, NTT, 6>(L, T, w, y, tickets, xrows, s, tm); break;
-    default: launch_down_k<FMT, NTT, 8>(L, T, w, y, tickets, xrows, s, tm); break;
+    case 1: launch_down_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, omb, s, tm); break;
+    case 2: launch_down_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, omb, s, tm); break;
+    case 4: launch_down_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, omb, s, tm); break;
+    case 6: launch_down_k<FMT, NTT, 6>(L, T, w, y, tickets, xrows, omb, s, tm); break;
+    default: launch_down_k<FMT, NTT, 8>(L, T, w, y, tickets, xrows, omb, s, tm); break;
   }
 }
 
 // Token tiles per pass follow the rows staged per pass (16 or 32).
 template <int FMT>
 static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
-                                     uint32_t* tickets, hipStream_t s, const Timing& tm) {
+                                     uint32_t* tickets, bool omb, hipStream_t s, const Timing& tm) {
   const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T);
   const int xd = dec_rows_per_pass(L.I, 2, T);
   if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, s, tm);
   else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, s, tm);
-  if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, s, tm);
-  else launch_dec_down<FMT, 2>(L, T, w, y, tickets, xd, s, tm);
+  if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, omb, s, tm);
+  else launch_dec_down<FMT, 2>(L, T, w, y, tickets, xd, false, s, tm);
   return hipGetLastError();
 }
 
@@ -1024,6 +1119,8 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const int ntickets = L.H / 16;
   const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
   const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
+  const bool omb = L.wfmt == 1 ? use_down_mailbox<1>(L, T) : use_down_mailbox<2>(L, T);
+  const int nzero_o = omb ? (L.k + (L.has_shared ? 1 : 0)) * L.H : 0;  // T == 1
   if (T >= kDecSplitRouteT) {
     // the fp64 matrix-core router and one wave per token for the top-k, then the route
     hipError_t e = launch_router_topk(L, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
@@ -1034,21 +1131,21 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
     const bool mbox = T * (L.E + 1) <= kDecMailboxWords;
     if (x_dtype == 0 && mbox)
       MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
     else if (x_dtype == 0)
       MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
     else if (mbox)
       MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
     else
       MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return L.wfmt == 1 ? launch_dec_experts<1>(L, x, x_dtype, T, w, y, w.tickets, s, tm)
-                     : launch_dec_experts<2>(L, x, x_dtype, T, w, y, w.tickets, s, tm);
+  return L.wfmt == 1 ? launch_dec_experts<1>(L, x, x_dtype, T, w, y, w.tickets, omb, s, tm)
+                     : launch_dec_experts<2>(L, x, x_dtype, T, w, y, w.tickets, omb, s, tm);
 }
 
 }  // namespace moeq
