@@ -120,11 +120,16 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
     typename RX::chunk xq[kTB][kPer];
 #pragma unroll
     for (int u = 0; u < kTB; ++u)
+      if (u < T) {  // uniform; the block's loads share one CU's address unit
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)min(u, T - 1) * H + 4 * cc[i]);
+        for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)u * H + 4 * cc[i]);
+      }
     for (int t0 = 0; t0 < T; t0 += kTB) {
 #pragma unroll
       for (int u = 0; u < kTB; ++u) {
+        // token slots past T are skipped (uniform): the waves of a SIMD run their fp64
+        // sums one after another, so dead slots would lengthen every block
+        if (t0 + u >= T) break;
         double a = 0.0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -135,12 +140,12 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
         const double sum = wave_sum_f64(a);
         if (lane == 0 && t0 + u < T) part[t0 + u] = c0 == c_beg ? sum : part[t0 + u] + sum;
       }
-      if (t0 + kTB < T) {
 #pragma unroll
-        for (int u = 0; u < kTB; ++u)
+      for (int u = 0; u < kTB; ++u)
+        if (t0 + kTB + u < T) {
 #pragma unroll
-          for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)min(t0 + kTB + u, T - 1) * H + 4 * cc[i]);
-      }
+          for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)(t0 + kTB + u) * H + 4 * cc[i]);
+        }
     }
   }
 }
@@ -277,6 +282,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   }
   for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
   {
+    // the bias of the logit this thread finishes (if any), loaded before the sums
+    double bias = 0.0;
+    if (tid < kRouterRows * T) {
+      const int er = blockIdx.x * kRouterRows + tid / T;
+      if (er < E && L.router_b) bias = (double)L.router_b[er];
+    }
     // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns
     const int e = blockIdx.x * kRouterRows + (wave >> 2);
     const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       const int er = blockIdx.x * kRouterRows + r;
       if (er < erows) {
         double v = ((s_part[4 * r][t] + s_part[4 * r + 1][t]) + s_part[4 * r + 2][t]) + s_part[4 * r + 3][t];
-        if (er < E && L.router_b) v += (double)L.router_b[er];
+        if (er < E && L.router_b) v += bias;
         if (MBOX)
           __hip_atomic_store(w.rr_mbox + (size_t)t * (E + 1) + er, ~__builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
