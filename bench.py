@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+RMS_EPS = 1e-6  # eps of the RMS rescale between the stacked layers
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_gateup.json")
 CSRC = os.path.join(ROOT, "quantized_mixture_experts_amd", "csrc")
 
@@ -103,22 +104,27 @@ class Workload:
         self.forwards_per_step = nl if self.stacked else 1
         self.steps_per_graph = 1 if self.stacked else nl
 
-    def _chain(self, s, fn):
-        """Enqueue step s; fn(layer_index, x, y) enqueues one layer forward."""
+    def _chain(self, s, fn, fn_rms=None):
+        """Enqueue step s; fn(layer_index, x, y) enqueues one layer forward.  Stacked:
+        layer l > 0 takes the RMS rescale of y_{l-1}, through fn_rms(l, y_prev, y) (the
+        rescale inside the layer call) when given, else as a separate rescale and fn."""
         q = self.q
         if self.stacked:
-            x = self.xs[0]
-            for l in range(self.nl):
-                fn(l, x, self.ys[l])
-                if l + 1 < self.nl:
-                    q.rms_rescale(self.ys[l], out=self.xs[l + 1])
+            fn(0, self.xs[0], self.ys[0])
+            for l in range(1, self.nl):
+                if fn_rms is not None:
+                    fn_rms(l, self.ys[l - 1], self.ys[l])
+                else:
+                    q.rms_rescale(self.ys[l - 1], out=self.xs[l])
+                    fn(l, self.xs[l], self.ys[l])
         else:
             l = s % self.nl
             fn(l, self.xs[l], self.ys[0])
 
     def step(self, s):
         q, xd = self.q, self.spec.x_dtype
-        self._chain(s, lambda l, x, y: q.forward(self.layers[l], x, xd, y=y, ws=self.ws))
+        self._chain(s, lambda l, x, y: q.forward(self.layers[l], x, xd, y=y, ws=self.ws),
+                    lambda l, yp, y: q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws))
 
     def step_timed(self, s, events, ev0):
         q, xd, NS = self.q, self.spec.x_dtype, len(self.q.STAGES)
@@ -127,7 +133,11 @@ class Workload:
         def fn(l, x, y):
             q.forward_timed(self.layers[l], x, xd, y, self.ws, events.slice(ctr[0], 2 * NS))
             ctr[0] += 2 * NS
-        self._chain(s, fn)
+
+        def fn_rms(l, yp, y):
+            q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws, events=events.slice(ctr[0], 2 * NS))
+            ctr[0] += 2 * NS
+        self._chain(s, fn, fn_rms)
 
     def distinct_experts(self):
         """Distinct routed experts of every forward of one rotation (for the byte counts)."""

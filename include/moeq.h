@@ -164,9 +164,30 @@ int moe_dequant(int32_t wfmt, const void *packed, const int8_t *codebook, int32_
                 int32_t cols, float *out, void *stream);
 
 /* Helper between stacked layers (not part of the layer):
- * x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y[t][n]^2 + eps)), bf16 bits. */
+ * x_next[t][n] = bf16_rne(y[t][n] * r_t), bf16 bits, where
+ * r_t = the fp32 reciprocal of sqrt(mean_n y[t][n]^2 + eps).
+ * The result is within one bf16 step of rounding the exact quotient. */
 int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_next_bf16,
                     void *stream);
+
+/* The whole layer on the RMS rescale of the previous layer's output.
+ * x = the bf16 values moe_rms_rescale(y_prev, T, H, eps) writes; then moe_forward of x as
+ * MOE_BF16, with the same routing, kernels and y bits.
+ * The rescale is folded into the router kernel, which also writes x for the projections.
+ * The Neural Server technical page's router kernels likewise hand on the normalized
+ * hidden state with the expert ids and weights ("How one token and one prompt are
+ * processed", step 2).  Below 8 tokens on the decode kernels this saves the separate
+ * rescale launch; otherwise the rescale kernel runs first.
+ * Arguments:
+ *   y_prev        [T][H] fp32, 16-byte aligned, must not be y;
+ *   eps           >= 0;
+ *   path          as for moe_forward;
+ *   stage_events  as for moe_forward_timed, or NULL.
+ * Workspace: moe_workspace_bytes(L, T).  Errors as for moe_forward;
+ * MOE_ERR_INVALID_ARG also for eps < 0 or NaN, or y_prev == y. */
+int moe_forward_rms(const moe_layer *L, const float *y_prev, float eps, int32_t T, float *y,
+                    void *ws, size_t ws_bytes, void *stream, int32_t path,
+                    void *const *stage_events);
 
 /* [host] Static description of a status code. */
 const char *moe_status_str(int status);

@@ -47,7 +47,7 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, o, tickets, slots, groups,
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, xr, o, tickets, slots, groups,
       n_groups, total;
 };
 
@@ -68,6 +68,7 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   const size_t Hp = align_up(H, 128), Ip = align_up(I, 256);
   o.xplanes = take(std::max(3 * (size_t)T * H * 2, 3 * (size_t)T * Hp + (size_t)T));
   o.hplanes = take(std::max(2 * P * I * 2, 3 * P * Ip + P * (Ip / 256)));
+  o.xr = take((size_t)T * H * 2);  // bf16 x of a rescaled-input call (not shared with the planes)
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
@@ -90,6 +91,7 @@ Work carve(void* ws, const Layout& lo) {
   w.xplanes = reinterpret_cast<uint16_t*>(b + lo.xplanes);
   w.hplanes = reinterpret_cast<uint16_t*>(b + lo.hplanes);
   w.o = reinterpret_cast<float*>(b + lo.o);
+  w.xr = reinterpret_cast<uint16_t*>(b + lo.xr);
   w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
   w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
@@ -123,14 +125,19 @@ int check_ws(const moe_layer* L, int32_t T, void* ws, size_t ws_bytes) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// x_dtype kRmsInput: x is the previous layer's fp32 y and the layer's input is
+// bf16(y / sqrt(mean(y^2) + eps)) per token, as moe_rms_rescale computes it.
+constexpr int32_t kRmsInput = 2;
+
 int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
                         size_t ws_bytes, void* stream, int32_t path, int32_t* dbg_ids, float* dbg_w,
-                        int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, const moeq::Timing& tm) {
+                        int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, const moeq::Timing& tm,
+                        float eps = 0.0f) {
   int st = validate_layer(L);
   if (st) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != kRmsInput) return MOE_ERR_INVALID_ARG;
   if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !y) return MOE_ERR_INVALID_ARG;
@@ -142,12 +149,18 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Work w = carve(ws, layout_for(L, T));
   const LayerArgs a = args_of(L);
-  const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype);
+  const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype == kRmsInput ? MOE_BF16 : x_dtype);
   if (path == MOE_PATH_DECODE && !dec_ok) return MOE_ERR_UNSUPPORTED;
   if (path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && dec_ok))
-    return hip_status(moeq::launch_decode(a, x, x_dtype, T, w, y, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm,
-                                          s, tm));
-  hipError_t e = moeq::launch_router_topk(a, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
+    return hip_status(moeq::launch_decode(a, x, x_dtype, T, w, y, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                                          dbg_perm, s, tm));
+  hipError_t e = hipSuccess;
+  if (x_dtype == kRmsInput) {  // the rescale first, then the grouped path on its bf16 output
+    e = moeq::launch_rms_rescale(static_cast<const float*>(x), T, a.H, eps, w.xr, s);
+    x = w.xr;
+    x_dtype = MOE_BF16;
+  }
+  if (e == hipSuccess) e = moeq::launch_router_topk(a, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
   if (e == hipSuccess)
     e = moeq::launch_bucket(T, a.k, a.E, a.has_shared, w.ids, w, dbg_counts, dbg_offsets, dbg_perm, s, tm);
   if (e == hipSuccess) e = moeq::launch_experts(a, x, x_dtype, T, w, y, s, tm);
@@ -205,16 +218,28 @@ int moe_bucket(const moe_layer* L, const int32_t* topk_ids, int32_t T, int32_t* 
 int moe_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
                 size_t ws_bytes, void* stream, int32_t path, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
                 int32_t* dbg_offsets, int32_t* dbg_perm) {
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   return forward_impl(L, x, x_dtype, T, y, ws, ws_bytes, stream, path, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                       dbg_perm, moeq::Timing());
 }
 
 int moe_forward_timed(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
                       size_t ws_bytes, void* stream, int32_t path, void* const* stage_events) {
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   moeq::Timing tm;
   tm.ev = stage_events;
   return forward_impl(L, x, x_dtype, T, y, ws, ws_bytes, stream, path, nullptr, nullptr, nullptr, nullptr,
                       nullptr, tm);
+}
+
+int moe_forward_rms(const moe_layer* L, const float* y_prev, float eps, int32_t T, float* y, void* ws,
+                    size_t ws_bytes, void* stream, int32_t path, void* const* stage_events) {
+  if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && y_prev == y) return MOE_ERR_INVALID_ARG;
+  moeq::Timing tm;
+  tm.ev = stage_events;
+  return forward_impl(L, y_prev, kRmsInput, T, y, ws, ws_bytes, stream, path, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, tm, eps);
 }
 
 int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,

@@ -70,6 +70,7 @@ struct Work {
   int32_t* active;     // [E + 2]  active[0] = number of active experts, then their ids ascending
   uint16_t* xplanes;   // [3][T][H] bf16 planes of fp32 activations (x = p0 + p1 + p2)
   uint16_t* hplanes;   // [2][P][I] bf16 planes of the SwiGLU output (h ~= p0 + p1)
+  uint16_t* xr;        // [T][H] bf16 RMS rescale of the previous layer's y (rescaled-input calls)
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
   uint32_t* tickets;   // [H/16] arrival counters of the decode combine
   float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)

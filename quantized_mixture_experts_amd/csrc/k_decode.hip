@@ -20,6 +20,10 @@
 
 namespace moeq {
 
+// From this many tokens the decode path routes with three kernels (matrix-core router,
+// per-token top-k, route) instead of the single router/route kernel, whose fp64
+// reductions and one-CU top-k grow with T.
+constexpr int kDecSplitRouteT = 8;
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
 // operations of this wave are outstanding, leaving the other counters alone.
@@ -96,10 +100,26 @@ struct RouterX<1> {  // bf16 activations
   __device__ static float get(const chunk& c, int q) { return bf16_bits_to_f32((uint32_t)(c >> (16 * q)) & 0xFFFFu); }
 };
 
+// Activation chunk of token u at column c.  XDT 2: x is the previous layer's fp32 y and
+// the chunk is bf16(y * inv[u]), the RMS rescale computed on the fly (inv in LDS).
+template <int XDT>
+__device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(const void* x, int u, int H, int c,
+                                                                                 const float* d) {
+  if constexpr (XDT == 2) {
+    const f32x4_t v = RouterX<0>::load(x, (size_t)u * H + c);
+    uint64_t r = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r |= (uint64_t)f32_to_bf16_rne(v[q] * d[u]) << (16 * q);
+    return r;
+  } else {
+    return RouterX<XDT>::load(x, (size_t)u * H + c);
+  }
+}
+
 template <int XDT>
 __device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
-                                            int h0, int h1, double* __restrict__ part) {
-  using RX = RouterX<XDT>;
+                                            int h0, int h1, double* __restrict__ part, const float* d) {
+  using RX = RouterX<XDT == 2 ? 1 : XDT>;
   const int lane = threadIdx.x & 63;
   constexpr int kPer = 3;  // a quarter of a 2880-column row in one pass
   constexpr int kTB = 4;
@@ -122,7 +142,7 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
     for (int u = 0; u < kTB; ++u)
       if (u < T) {  // uniform; the block's loads share one CU's address unit
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)u * H + 4 * cc[i]);
+        for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, u, H, 4 * cc[i], d);
       }
     for (int t0 = 0; t0 < T; t0 += kTB) {
 #pragma unroll
@@ -144,7 +164,7 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
       for (int u = 0; u < kTB; ++u)
         if (t0 + kTB + u < T) {
 #pragma unroll
-          for (int i = 0; i < kPer; ++i) xq[u][i] = RX::load(x, (size_t)(t0 + kTB + u) * H + 4 * cc[i]);
+          for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, t0 + kTB + u, H, 4 * cc[i], d);
         }
     }
   }
@@ -248,7 +268,8 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
 template <int XDT, bool MBOX>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
-                                                          int ntickets, int nzero_o, int32_t* __restrict__ dbg_ids,
+                                                          int ntickets, int nzero_o, float eps,
+                                                          int32_t* __restrict__ dbg_ids,
                                                           float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
                                                           int32_t* __restrict__ dbg_offsets,
                                                           int32_t* __restrict__ dbg_perm) {
@@ -281,6 +302,28 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
+  __shared__ float s_d[kDecSplitRouteT];  // XDT 2: each token's 1 / sqrt(mean(y^2) + eps)
+  if constexpr (XDT == 2) {
+    // With the rescale kernel's exact arithmetic: thread i of a 256-thread group sums
+    // y[n]^2 for n = i, i + 256, ... (fmaf in that order), its 4 wave sums are added in
+    // wave order and divided by H, and the scale is 1 / sqrt(that + eps).  Group g of the
+    // block's four takes tokens g, g + 4.
+    __shared__ float s_ms[kDecSplitRouteT][4];
+    const int grp = wave >> 2, i = tid & 255;
+    for (int t = grp; t < T; t += kWaves / 4) {
+      const float* yt = (const float*)x + (size_t)t * H;
+      float sq = 0.f;
+      for (int n = i; n < H; n += 256) sq = fmaf(yt[n], yt[n], sq);
+      sq = wave_sum_f32(sq);
+      if (lane == 0) s_ms[t][wave & 3] = sq;
+    }
+    __syncthreads();
+    if (tid < T) s_d[tid] = 1.0f / sqrtf((s_ms[tid][0] + s_ms[tid][1] + s_ms[tid][2] + s_ms[tid][3]) / (float)H + eps);
+    __syncthreads();
+    if (blockIdx.x == 0)  // the bf16 x of the projections
+      for (int idx = tid; idx < T * H; idx += kRouteThreads)
+        w.xr[idx] = (uint16_t)f32_to_bf16_rne(((const float*)x)[idx] * s_d[idx / H]);
+  }
   {
     // the bias of the logit this thread finishes (if any), loaded before the sums
     double bias = 0.0;
@@ -293,7 +336,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
     if (e < erows) {
       const float* wrow = e < E ? L.router_w + (size_t)e * H : L.shared_gate_w;
-      router_part<XDT>(wrow, x, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave]);
+      router_part<XDT>(wrow, x, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave], s_d);
     }
     __syncthreads();
     if (tid < kRouterRows * T) {
@@ -1118,45 +1161,60 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   return g <= 160 * 1024 && d <= 160 * 1024;
 }
 
-// From this many tokens the decode path routes with three kernels (matrix-core router,
-// per-token top-k, route) instead of the single router/route kernel, whose fp64
-// reductions and one-CU top-k grow with T.
-constexpr int kDecSplitRouteT = 8;
+template <int XDT>
+static void launch_rr(const LayerArgs& L, const void* x, int T, int erows, const Work& w, int max_slots, int ntickets,
+                      int nzero_o, float eps, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
+                      int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
+  const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
+  if (T * (L.E + 1) <= kDecMailboxWords)
+    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+  else
+    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+}
 
-hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
+hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y, float eps,
                          int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts, int32_t* dbg_offsets,
                          int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
   const int ntickets = L.H / 16;
   const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
   const bool omb = L.wfmt == 1 ? use_down_mailbox<1>(L, T) : use_down_mailbox<2>(L, T);
   const int nzero_o = omb ? (L.k + (L.has_shared ? 1 : 0)) * L.H : 0;  // T == 1
+  // x_dtype 2: x is the previous layer's fp32 y, and the layer takes its bf16 RMS rescale
+  // in w.xr.  For one token the router kernel rescales on the fly and writes w.xr (one
+  // launch fewer: stacked decode 1.141 -> 1.072 ms); for more tokens, whose rows every
+  // router block would rescale again, the rescale kernel runs first (at T = 4 the folded
+  // form was 3 % slower).
+  if (x_dtype == 2 && T > 1) {
+    hipError_t e = launch_rms_rescale((const float*)x, T, L.H, eps, w.xr, s);
+    if (e != hipSuccess) return e;
+    x = w.xr;
+    x_dtype = 1;
+  }
+  const void* xp = x_dtype == 2 ? (const void*)w.xr : x;
+  const int xdp = x_dtype == 2 ? 1 : x_dtype;
   if (T >= kDecSplitRouteT) {
     // the fp64 matrix-core router and one wave per token for the top-k, then the route
-    hipError_t e = launch_router_topk(L, x, x_dtype, T, w, dbg_ids, dbg_w, s, tm);
+    hipError_t e = launch_router_topk(L, xp, xdp, T, w, dbg_ids, dbg_w, s, tm);
     if (e != hipSuccess) return e;
     MOEQ_LAUNCH(tm, kStageBucket, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, w, max_slots, ntickets,
                 dbg_counts, dbg_offsets, dbg_perm);
+  } else if (x_dtype == 0) {
+    launch_rr<0>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                 dbg_perm, s, tm);
+  } else if (x_dtype == 1) {
+    launch_rr<1>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                 dbg_perm, s, tm);
   } else {
-    const bool mbox = T * (L.E + 1) <= kDecMailboxWords;
-    if (x_dtype == 0 && mbox)
-      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    else if (x_dtype == 0)
-      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<0, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    else if (mbox)
-      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    else
-      MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<1, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                  max_slots, w.rr_flags, ntickets, nzero_o, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    launch_rr<2>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                 dbg_perm, s, tm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return L.wfmt == 1 ? launch_dec_experts<1>(L, x, x_dtype, T, w, y, w.tickets, omb, s, tm)
-                     : launch_dec_experts<2>(L, x, x_dtype, T, w, y, w.tickets, omb, s, tm);
+  return L.wfmt == 1 ? launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm)
+                     : launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
 }
 
 }  // namespace moeq

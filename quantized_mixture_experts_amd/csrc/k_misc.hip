@@ -54,9 +54,9 @@ __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y
   s = wave_sum_f32(s);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
-  const float ms = (part[0] + part[1] + part[2] + part[3]) / (float)H;
-  const float d = sqrtf(ms + eps);
-  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(yt[n] / d);
+  // scaled by the rounded reciprocal of the divisor (within one bf16 step of the quotient)
+  const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)H + eps);
+  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(yt[n] * inv);
 }
 
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,

@@ -53,9 +53,10 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
                           hipStream_t s, const Timing& tm = Timing());
 // y[t] = sum_j g[t,j] o[t*k+j] (+ shared), fixed order, from the o rows in the workspace.
 hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, float* y, hipStream_t s, const Timing& tm);
-// Decode path (T <= 32 and the activation tiles fit in LDS).
+// Decode path (T <= 32 and the activation tiles fit in LDS).  x_dtype 2: x is the previous
+// layer's fp32 y and the layer's input is its bf16 RMS rescale with eps (written to w.xr).
 bool decode_path_fits(const LayerArgs& L, int T, int x_dtype);
-hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
+hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y, float eps,
                          int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts, int32_t* dbg_offsets,
                          int32_t* dbg_perm, hipStream_t s, const Timing& tm);
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,

@@ -83,6 +83,7 @@ def test_forward_rejects_bad_calls(L):
     assert f(x=None) == q.MOE_ERR_INVALID_ARG
     assert f(y=None) == q.MOE_ERR_INVALID_ARG
     assert f(dt=5) == q.MOE_ERR_INVALID_ARG
+    assert f(dt=2) == q.MOE_ERR_INVALID_ARG  # the rescaled-input mode only through moe_forward_rms
     assert f(T=-1) == q.MOE_ERR_INVALID_ARG
     assert f(T=1 << 20) == q.MOE_ERR_UNSUPPORTED
     assert f(path=9) == q.MOE_ERR_INVALID_ARG
@@ -92,6 +93,22 @@ def test_forward_rejects_bad_calls(L):
     assert f(n=need - 1) == q.MOE_ERR_WORKSPACE
     assert f(ws=FAKE + 16) == q.MOE_ERR_ALIGNMENT
     assert f(T=0) == q.MOE_OK     # nothing is enqueued for zero tokens
+
+
+def test_forward_rms_rejects_bad_calls(L):
+    lay = layer()
+    need = ws_bytes(L, lay, 4)
+    Y = FAKE + 256
+    f = lambda yp=FAKE, eps=1e-6, T=4, y=Y, ws=FAKE, n=need, path=0: L.moe_forward_rms(
+        ctypes.byref(lay), yp, eps, T, y, ws, n, None, path, None)
+    assert f(eps=-1.0) == q.MOE_ERR_INVALID_ARG
+    assert f(eps=float("nan")) == q.MOE_ERR_INVALID_ARG
+    assert f(y=FAKE) == q.MOE_ERR_INVALID_ARG          # y_prev may not be y
+    assert f(yp=None) == q.MOE_ERR_INVALID_ARG
+    assert f(yp=FAKE + 8) == q.MOE_ERR_ALIGNMENT
+    assert f(path=9) == q.MOE_ERR_INVALID_ARG
+    assert f(n=need - 1) == q.MOE_ERR_WORKSPACE
+    assert f(T=0) == q.MOE_OK
 
 
 def test_router_and_bucket_validation(L):

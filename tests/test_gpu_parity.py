@@ -231,6 +231,27 @@ def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
     check_forward(layer, x, spec.x_dtype, y, dbg, what=f"limits T={T} H={H} I={I} E={E} k={k} path={path}")
 
 
+@pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
+@pytest.mark.parametrize("T,path", [(1, 0), (4, 0), (7, 0), (9, 0), (40, 0), (4, 2)])
+def test_forward_rms_equals_rescale_then_forward(wfmt, T, path):
+    """moe_forward_rms (the rescale folded into the router kernel below 8 decode tokens,
+    the rescale kernel first otherwise) gives the bits of moe_rms_rescale followed by
+    moe_forward on the same path; that two-step result is checked against the oracle."""
+    spec = synth.small_spec(f"rms{T}", T, 512, 1024, 16, 4, wfmt, has_shared=1, x_dtype=synth.X_BF16,
+                            bias="normal", seed=40 + T)
+    layer = synth.make_layer(spec, shared_gate=True)
+    dl = q.DeviceLayer.from_layer(layer)
+    rng = np.random.default_rng(900 + T)
+    y_prev = _dev((rng.standard_normal((T, 512)) * rng.uniform(0.1, 20.0, (T, 1))).astype(np.float32))
+    x = q.rms_rescale(y_prev)
+    y2, dbg = q.forward(dl, x, synth.X_BF16, path=path, debug=True)
+    y1 = q.forward_rms(dl, y_prev, 1e-6, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    xb = x.cpu().numpy().view(np.uint16)
+    check_forward(layer, xb, synth.X_BF16, y2, dbg, what=f"rms T={T} path={path}")
+
+
 def test_forward_deterministic_and_batch_invariant():
     spec = synth.CONFIGS["c3"]
     layer, x, dl, y, dbg = _run(spec)
