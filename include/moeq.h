@@ -173,20 +173,24 @@ int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_nex
 /* The whole layer on the RMS rescale of the previous layer's output.
  * x = the bf16 values moe_rms_rescale(y_prev, T, H, eps) writes; then moe_forward of x as
  * MOE_BF16, with the same routing, kernels and y bits.
- * The rescale is folded into the router kernel, which also writes x for the projections.
- * The Neural Server technical page's router kernels likewise hand on the normalized
- * hidden state with the expert ids and weights ("How one token and one prompt are
- * processed", step 2).  Below 8 tokens on the decode kernels this saves the separate
- * rescale launch; otherwise the rescale kernel runs first.
+ * residual = 1: y = y_prev + that layer output (the pre-norm block's residual add,
+ * added in fp32 after the fixed-order combine); residual = 0: y = the layer output.
+ * For one token on the decode kernels the rescale is folded into the router kernel, which
+ * also writes x for the projections, saving the separate rescale launch.  The router
+ * kernels of "How Neural runs a 120-billion-parameter model on one gaming PC" likewise
+ * hand on the normalized hidden state with the expert ids and weights (section "How one
+ * token and one prompt are processed", step 2).
+ * Otherwise the rescale kernel runs first.
  * Arguments:
  *   y_prev        [T][H] fp32, 16-byte aligned, must not be y;
  *   eps           >= 0;
+ *   residual      0 or 1;
  *   path          as for moe_forward;
  *   stage_events  as for moe_forward_timed, or NULL.
  * Workspace: moe_workspace_bytes(L, T).  Errors as for moe_forward;
- * MOE_ERR_INVALID_ARG also for eps < 0 or NaN, or y_prev == y. */
-int moe_forward_rms(const moe_layer *L, const float *y_prev, float eps, int32_t T, float *y,
-                    void *ws, size_t ws_bytes, void *stream, int32_t path,
+ * MOE_ERR_INVALID_ARG also for eps < 0 or NaN, residual not 0 or 1, or y_prev == y. */
+int moe_forward_rms(const moe_layer *L, const float *y_prev, float eps, int32_t residual, int32_t T,
+                    float *y, void *ws, size_t ws_bytes, void *stream, int32_t path,
                     void *const *stage_events);
 
 /* [host] Static description of a status code. */

@@ -59,7 +59,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.argtypes = [ctypes.POINTER(MoeLayerC), vp, i32, i32, vp, vp, sz, vp, i32, vp]
         L.moe_dequant.argtypes = [i32, vp, vp, i32, i32, vp, vp]
         L.moe_rms_rescale.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
-        L.moe_forward_rms.argtypes = [ctypes.POINTER(MoeLayerC), vp, ctypes.c_float, i32, vp, vp, sz, vp, i32, vp]
+        L.moe_forward_rms.argtypes = [ctypes.POINTER(MoeLayerC), vp, ctypes.c_float, i32, i32, vp, vp, sz, vp, i32,
+                                      vp]
         L.moe_status_str.argtypes, L.moe_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         for f in ["moe_router_topk", "moe_bucket", "moe_forward", "moe_forward_timed", "moe_dequant",
                   "moe_rms_rescale", "moe_forward_rms"]:
@@ -254,16 +255,17 @@ def dequant(wfmt: int, packed, rows: int, cols: int, codebook=None, stream=None)
 
 
 def forward_rms(L: DeviceLayer, y_prev, eps: float = 1e-6, y=None, ws=None, path: int = PATH_AUTO, events=None,
-                stream=None):
+                residual: bool = False, stream=None):
     """moe_forward_rms: the layer on the bf16 RMS rescale of the previous layer's fp32
-    output y_prev [T][H] (the values rms_rescale(y_prev, eps) gives).  `events`: None or
-    2 * len(STAGES) hipEvent_t handles (see HipEvents)."""
+    output y_prev [T][H] (the values rms_rescale(y_prev, eps) gives); residual=True adds
+    y_prev to the result.  `events`: None or 2 * len(STAGES) hipEvent_t handles (see
+    HipEvents)."""
     import torch
     T = y_prev.shape[0]
     ws = L.workspace(T) if ws is None else ws
     y = torch.empty((T, L.hidden), dtype=torch.float32, device=y_prev.device) if y is None else y
-    _check(lib().moe_forward_rms(ctypes.byref(L.c), y_prev.data_ptr(), eps, T, y.data_ptr(), ws.data_ptr(),
-                                 ws.numel(), _stream(stream), path, events), "moe_forward_rms")
+    _check(lib().moe_forward_rms(ctypes.byref(L.c), y_prev.data_ptr(), eps, int(residual), T, y.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream(stream), path, events), "moe_forward_rms")
     return y
 
 

@@ -81,6 +81,7 @@ Layout layout_for(const moe_layer* L, int32_t T) {
 Work carve(void* ws, const Layout& lo) {
   uint8_t* b = static_cast<uint8_t*>(ws);
   Work w;
+  w.resid = nullptr;
   w.logits = reinterpret_cast<double*>(b + lo.logits);
   w.ids = reinterpret_cast<int32_t*>(b + lo.ids);
   w.pair_w = reinterpret_cast<float*>(b + lo.pair_w);
@@ -132,7 +133,7 @@ constexpr int32_t kRmsInput = 2;
 int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,
                         size_t ws_bytes, void* stream, int32_t path, int32_t* dbg_ids, float* dbg_w,
                         int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, const moeq::Timing& tm,
-                        float eps = 0.0f) {
+                        float eps = 0.0f, bool residual = false) {
   int st = validate_layer(L);
   if (st) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -147,7 +148,8 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
     return MOE_ERR_ALIGNMENT;
   if ((st = check_ws(L, T, ws, ws_bytes))) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Work w = carve(ws, layout_for(L, T));
+  Work w = carve(ws, layout_for(L, T));
+  w.resid = residual ? static_cast<const float*>(x) : nullptr;  // pre-norm block: y_prev + layer
   const LayerArgs a = args_of(L);
   const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype == kRmsInput ? MOE_BF16 : x_dtype);
   if (path == MOE_PATH_DECODE && !dec_ok) return MOE_ERR_UNSUPPORTED;
@@ -232,14 +234,14 @@ int moe_forward_timed(const moe_layer* L, const void* x, int32_t x_dtype, int32_
                       nullptr, tm);
 }
 
-int moe_forward_rms(const moe_layer* L, const float* y_prev, float eps, int32_t T, float* y, void* ws,
-                    size_t ws_bytes, void* stream, int32_t path, void* const* stage_events) {
-  if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+int moe_forward_rms(const moe_layer* L, const float* y_prev, float eps, int32_t residual, int32_t T, float* y,
+                    void* ws, size_t ws_bytes, void* stream, int32_t path, void* const* stage_events) {
+  if (!(eps >= 0.0f) || (residual != 0 && residual != 1)) return MOE_ERR_INVALID_ARG;
   if (T > 0 && y_prev == y) return MOE_ERR_INVALID_ARG;
   moeq::Timing tm;
   tm.ev = stage_events;
   return forward_impl(L, y_prev, kRmsInput, T, y, ws, ws_bytes, stream, path, nullptr, nullptr, nullptr, nullptr,
-                      nullptr, tm, eps);
+                      nullptr, tm, eps, residual == 1);
 }
 
 int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,

@@ -71,6 +71,7 @@ struct Work {
   uint16_t* xplanes;   // [3][T][H] bf16 planes of fp32 activations (x = p0 + p1 + p2)
   uint16_t* hplanes;   // [2][P][I] bf16 planes of the SwiGLU output (h ~= p0 + p1)
   uint16_t* xr;        // [T][H] bf16 RMS rescale of the previous layer's y (rescaled-input calls)
+  const float* resid;  // [T][H] fp32 added to y after the combine, or null
   float* o;            // [P][H]  expert outputs (down projection, before the gate)
   uint32_t* tickets;   // [H/16] arrival counters of the decode combine
   float* hf32;         // [P][I] SwiGLU output of the decode path (aliases hplanes)

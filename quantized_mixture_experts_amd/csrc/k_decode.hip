@@ -778,7 +778,7 @@ __device__ __forceinline__ void dec_combine_cols(const LayerArgs& L, int T, cons
       const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s = fmaf(w.pair_w[T * k + t], o, s);
     }
-    y[(size_t)t * H + col] = s;
+    y[(size_t)t * H + col] = w.resid ? w.resid[(size_t)t * H + col] + s : s;
   }
 }
 
@@ -865,6 +865,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
                              __HIP_MEMORY_SCOPE_AGENT);
         } else {
           const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
+          const float rv = w.resid ? w.resid[col] : 0.f;  // loaded before the wait
           uint32_t e[kMaxPairsT1];
           for (uint32_t spins = 0; spins <= (1u << 22); ++spins) {
             bool miss = false;
@@ -883,7 +884,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 #pragma unroll
           for (int u = 0; u < kMaxPairsT1; ++u)
             if (u < P1) sum = fmaf(w.pair_w[u], __uint_as_float(~e[u]), sum);
-          y[col] = sum;
+          y[col] = w.resid ? rv + sum : sum;
         }
       }
       return;

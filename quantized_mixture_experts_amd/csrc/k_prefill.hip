@@ -725,10 +725,12 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
 
 // ---------------------------------------------------------------------------
 // Combine: y[t][n] = sum_j pair_w[t*k+j] * o[t*k+j][n] (+ pair_w[T*k+t] * o[T*k+t][n]),
-// j ascending and the shared expert last, a fixed order for every run.
+// j ascending and the shared expert last, a fixed order for every run; resid[t][n] is
+// added to the finished sum when given.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has_shared, const float* __restrict__ o,
-                                                    const float* __restrict__ pair_w, float* __restrict__ y) {
+                                                    const float* __restrict__ pair_w, const float* __restrict__ resid,
+                                                    float* __restrict__ y) {
   const int t = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= H) return;
@@ -747,7 +749,7 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
       if (j0 + u < k) s = fmaf(wv[u], ov[u], s);
   }
   if (has_shared) s = fmaf(pair_w[T * k + t], o[(size_t)(T * k + t) * H + n], s);
-  y[(size_t)t * H + n] = s;
+  y[(size_t)t * H + n] = resid ? resid[(size_t)t * H + n] + s : s;
 }
 
 // ---------------------------------------------------------------------------
@@ -874,7 +876,7 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
 
 hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, float* y, hipStream_t s, const Timing& tm) {
   MOEQ_LAUNCH(tm, kStageCombine, k_pf_combine, dim3((L.H + 255) / 256, T), dim3(256), 0, s, T, L.H, L.k,
-              L.has_shared, (const float*)w.o, (const float*)w.pair_w, y);
+              L.has_shared, (const float*)w.o, (const float*)w.pair_w, w.resid, y);
   return hipGetLastError();
 }
 

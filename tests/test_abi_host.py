@@ -99,9 +99,10 @@ def test_forward_rms_rejects_bad_calls(L):
     lay = layer()
     need = ws_bytes(L, lay, 4)
     Y = FAKE + 256
-    f = lambda yp=FAKE, eps=1e-6, T=4, y=Y, ws=FAKE, n=need, path=0: L.moe_forward_rms(
-        ctypes.byref(lay), yp, eps, T, y, ws, n, None, path, None)
+    f = lambda yp=FAKE, eps=1e-6, res=0, T=4, y=Y, ws=FAKE, n=need, path=0: L.moe_forward_rms(
+        ctypes.byref(lay), yp, eps, res, T, y, ws, n, None, path, None)
     assert f(eps=-1.0) == q.MOE_ERR_INVALID_ARG
+    assert f(res=2) == q.MOE_ERR_INVALID_ARG
     assert f(eps=float("nan")) == q.MOE_ERR_INVALID_ARG
     assert f(y=FAKE) == q.MOE_ERR_INVALID_ARG          # y_prev may not be y
     assert f(yp=None) == q.MOE_ERR_INVALID_ARG

@@ -234,9 +234,10 @@ def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T,path", [(1, 0), (4, 0), (7, 0), (9, 0), (40, 0), (4, 2)])
 def test_forward_rms_equals_rescale_then_forward(wfmt, T, path):
-    """moe_forward_rms (the rescale folded into the router kernel below 8 decode tokens,
+    """moe_forward_rms (the rescale folded into the router kernel for one decode token,
     the rescale kernel first otherwise) gives the bits of moe_rms_rescale followed by
-    moe_forward on the same path; that two-step result is checked against the oracle."""
+    moe_forward on the same path, and with the residual add y_prev plus those bits; the
+    two-step result is checked against the oracle."""
     spec = synth.small_spec(f"rms{T}", T, 512, 1024, 16, 4, wfmt, has_shared=1, x_dtype=synth.X_BF16,
                             bias="normal", seed=40 + T)
     layer = synth.make_layer(spec, shared_gate=True)
@@ -246,8 +247,10 @@ def test_forward_rms_equals_rescale_then_forward(wfmt, T, path):
     x = q.rms_rescale(y_prev)
     y2, dbg = q.forward(dl, x, synth.X_BF16, path=path, debug=True)
     y1 = q.forward_rms(dl, y_prev, 1e-6, path=path)
+    y3 = q.forward_rms(dl, y_prev, 1e-6, path=path, residual=True)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+    assert torch.equal(y3, y_prev + y1)  # the residual add follows the finished combine, in fp32
     xb = x.cpu().numpy().view(np.uint16)
     check_forward(layer, xb, synth.X_BF16, y2, dbg, what=f"rms T={T} path={path}")
 
