@@ -51,7 +51,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
-    ap.add_argument("--tokens", type=int, default=None, help="override T (the stacked config runs T=1 and T=4)")
+    ap.add_argument("--tokens", type=int, default=None, help="override T (the stacked config runs T=1 and T=4; "
+                    "the verify config with T=136 is the batched verify round of 8 requests x 17 tokens)")
+    ap.add_argument("--path", choices=["auto", "decode", "prefill"], default="auto",
+                    help="kernel path (auto: decode kernels up to 32 tokens)")
     ap.add_argument("--layers", type=int, default=None, help="distinct layer instances in the rotation")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,6 +85,7 @@ class Workload:
         import synth
         self.q, self.spec = q, spec
         self.T = args.tokens or spec.T
+        self.path = {"auto": q.PATH_AUTO, "decode": q.PATH_DECODE, "prefill": q.PATH_PREFILL}[args.path]
         self.stacked = spec.n_layers > 1
         if self.stacked:
             nl = spec.n_layers
@@ -123,19 +127,20 @@ class Workload:
 
     def step(self, s):
         q, xd = self.q, self.spec.x_dtype
-        self._chain(s, lambda l, x, y: q.forward(self.layers[l], x, xd, y=y, ws=self.ws),
-                    lambda l, yp, y: q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws))
+        self._chain(s, lambda l, x, y: q.forward(self.layers[l], x, xd, y=y, ws=self.ws, path=self.path),
+                    lambda l, yp, y: q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws, path=self.path))
 
     def step_timed(self, s, events, ev0):
         q, xd, NS = self.q, self.spec.x_dtype, len(self.q.STAGES)
         ctr = [ev0]
 
         def fn(l, x, y):
-            q.forward_timed(self.layers[l], x, xd, y, self.ws, events.slice(ctr[0], 2 * NS))
+            q.forward_timed(self.layers[l], x, xd, y, self.ws, events.slice(ctr[0], 2 * NS), path=self.path)
             ctr[0] += 2 * NS
 
         def fn_rms(l, yp, y):
-            q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws, events=events.slice(ctr[0], 2 * NS))
+            q.forward_rms(self.layers[l], yp, RMS_EPS, y=y, ws=self.ws, events=events.slice(ctr[0], 2 * NS),
+                          path=self.path)
             ctr[0] += 2 * NS
         self._chain(s, fn, fn_rms)
 
@@ -264,7 +269,8 @@ def main():
 
     fmt = "MXFP4" if spec.weights.wfmt == synth.WFMT_MXFP4 else "4-bit codebook"
     workload = (f"{args.config}: {spec.name}, T={T}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
-                f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers" if wl.stacked else ""))
+                f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers" if wl.stacked else "")
+                + (f", {args.path} kernels forced" if args.path != "auto" else ""))
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),

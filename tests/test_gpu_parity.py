@@ -129,13 +129,16 @@ def test_forward_decode_configs(cfg):
 SWEEP_T = [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
 
 
-@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("path", [0, 1, 2])
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T", SWEEP_T)
 def test_forward_token_sweep(wfmt, T, path):
     """Every tile threshold of the token dimension (16-row MFMA tiles, 4 tiles per pass),
     with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4.  path 0
-    picks the decode kernels up to 32 tokens; path 2 forces the grouped kernels."""
+    picks the decode kernels up to 10 (MXFP4) or 22 (CB4) tokens; path 1 forces them
+    (up to 32 tokens); path 2 forces the grouped kernels."""
+    if path == 1 and T > 32:
+        pytest.skip("the decode kernels take at most 32 tokens")
     H = 160 if wfmt == synth.WFMT_MXFP4 else 256
     spec = synth.small_spec(f"sweep{T}", T, H, 96, 12, 3, wfmt, has_shared=1, x_dtype=synth.X_BF16,
                             bias="normal", seed=100 + T)
@@ -300,10 +303,13 @@ def test_forward_zero_tokens_is_noop():
     assert y.shape == (0, spec.hidden)
 
 
-@pytest.mark.parametrize("cfg", ["c5a", "c5b"])
-def test_forward_prefill_full_size_sampled(cfg):
-    """T = 1024 at full shape: routing and bucketing compared in full, y on sampled tokens."""
-    spec = synth.CONFIGS[cfg]
+@pytest.mark.parametrize("cfg,T", [("c5a", None), ("c5b", None), ("c3", 136)])
+def test_forward_prefill_full_size_sampled(cfg, T):
+    """Full shapes on the grouped path: the two prefill chunks (T = 1024) and the batched
+    verify round (the verify layer with 8 requests x 17 tokens, T = 136); routing and
+    bucketing compared in full, y on sampled tokens."""
+    import dataclasses
+    spec = synth.CONFIGS[cfg] if T is None else dataclasses.replace(synth.CONFIGS[cfg], T=T)
     layer, x, dl, y, dbg = _run(spec)
     x64 = oracle.activations_f64(x, spec.x_dtype)
     l = oracle.router_logits(x64, layer.router_w, layer.router_b)
@@ -313,7 +319,8 @@ def test_forward_prefill_full_size_sampled(cfg):
     c, o, p, _ = oracle.bucket(ids_ref, spec.n_experts, spec.has_shared)
     assert np.array_equal(dbg["counts"].cpu().numpy(), c)
     assert np.array_equal(dbg["perm"].cpu().numpy(), p)
-    sample = np.array([0, 1, 255, 511, 512, 777, 1022, 1023])
+    n = spec.T
+    sample = np.unique(np.array([0, 1, n // 4 - 1, n // 2 - 1, n // 2, 3 * n // 4, n - 2, n - 1]))
     ref = oracle.moe_forward(layer, x[sample], spec.x_dtype)
     check_forward(layer, x, spec.x_dtype, y, dbg, ref=ref, tokens=sample, what=cfg)
 
