@@ -176,8 +176,8 @@ int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_nex
  * MOE_BF16, with the same routing, kernels and y bits.
  * residual = 1: y = y_prev + that layer output (the pre-norm block's residual add,
  * added in fp32 after the fixed-order combine); residual = 0: y = the layer output.
- * For one token on the decode kernels the rescale is folded into the router kernel, which
- * also writes x for the projections, saving the separate rescale launch.  The router
+ * Below 8 tokens on the decode kernels (and T*H <= 24576) the rescale is folded into the
+ * router kernel, which also writes x for the projections, saving the separate launch.  The router
  * kernels of "How Neural runs a 120-billion-parameter model on one gaming PC" likewise
  * hand on the normalized hidden state with the expert ids and weights (section "How one
  * token and one prompt are processed", step 2).

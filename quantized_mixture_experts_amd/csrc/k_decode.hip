@@ -24,6 +24,9 @@ namespace moeq {
 // per-token top-k, route) instead of the single router/route kernel, whose fp64
 // reductions and one-CU top-k grow with T.
 constexpr int kDecSplitRouteT = 8;
+// bf16 elements of the rescaled rows a router block keeps in LDS when it folds the RMS
+// rescale in (T * H at most: 48 KB)
+constexpr int kRmsFoldElems = 24576;
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
 // operations of this wave are outstanding, leaving the other counters alone.
@@ -100,17 +103,12 @@ struct RouterX<1> {  // bf16 activations
   __device__ static float get(const chunk& c, int q) { return bf16_bits_to_f32((uint32_t)(c >> (16 * q)) & 0xFFFFu); }
 };
 
-// Activation chunk of token u at column c.  XDT 2: x is the previous layer's fp32 y and
-// the chunk is bf16(y * inv[u]), the RMS rescale computed on the fly (inv in LDS).
+// Activation chunk of token u at column c.  XDT 2: x is the block's LDS copy of the bf16
+// RMS rescale of the previous layer's y.
 template <int XDT>
-__device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(const void* x, int u, int H, int c,
-                                                                                 const float* d) {
+__device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(const void* x, int u, int H, int c) {
   if constexpr (XDT == 2) {
-    const f32x4_t v = RouterX<0>::load(x, (size_t)u * H + c);
-    uint64_t r = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r |= (uint64_t)f32_to_bf16_rne(v[q] * d[u]) << (16 * q);
-    return r;
+    return *(const uint64_t*)((const uint16_t*)x + (size_t)u * H + c);
   } else {
     return RouterX<XDT>::load(x, (size_t)u * H + c);
   }
@@ -118,7 +116,7 @@ __device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(
 
 template <int XDT>
 __device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
-                                            int h0, int h1, double* __restrict__ part, const float* d) {
+                                            int h0, int h1, double* __restrict__ part) {
   using RX = RouterX<XDT == 2 ? 1 : XDT>;
   const int lane = threadIdx.x & 63;
   constexpr int kPer = 3;  // a quarter of a 2880-column row in one pass
@@ -142,7 +140,7 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
     for (int u = 0; u < kTB; ++u)
       if (u < T) {  // uniform; the block's loads share one CU's address unit
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, u, H, 4 * cc[i], d);
+        for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, u, H, 4 * cc[i]);
       }
     for (int t0 = 0; t0 < T; t0 += kTB) {
 #pragma unroll
@@ -164,7 +162,7 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
       for (int u = 0; u < kTB; ++u)
         if (t0 + kTB + u < T) {
 #pragma unroll
-          for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, t0 + kTB + u, H, 4 * cc[i], d);
+          for (int i = 0; i < kPer; ++i) xq[u][i] = router_x<XDT>(x, t0 + kTB + u, H, 4 * cc[i]);
         }
     }
   }
@@ -302,8 +300,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
-  __shared__ float s_d[kDecSplitRouteT];  // XDT 2: each token's 1 / sqrt(mean(y^2) + eps)
+  const void* xr = x;  // the router's activations (XDT 2: the block's LDS copy of the rescale)
   if constexpr (XDT == 2) {
+    __shared__ float s_d[kDecSplitRouteT];  // each token's 1 / sqrt(mean(y^2) + eps)
+    __shared__ __align__(16) uint16_t s_x[kRmsFoldElems];
     // With the rescale kernel's exact arithmetic: thread i of a 256-thread group sums
     // y[n]^2 for n = i, i + 256, ... (fmaf in that order), its 4 wave sums are added in
     // wave order and divided by H, and the scale is 1 / sqrt(that + eps).  Group g of the
@@ -320,9 +320,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     __syncthreads();
     if (tid < T) s_d[tid] = 1.0f / sqrtf((s_ms[tid][0] + s_ms[tid][1] + s_ms[tid][2] + s_ms[tid][3]) / (float)H + eps);
     __syncthreads();
-    if (blockIdx.x == 0)  // the bf16 x of the projections
-      for (int idx = tid; idx < T * H; idx += kRouteThreads)
-        w.xr[idx] = (uint16_t)f32_to_bf16_rne(((const float*)x)[idx] * s_d[idx / H]);
+    // the rescaled rows once per block into LDS (block 0 also writes them for the projections)
+    for (int idx = tid; idx < T * H; idx += kRouteThreads) {
+      const uint16_t v = (uint16_t)f32_to_bf16_rne(((const float*)x)[idx] * s_d[idx / H]);
+      s_x[idx] = v;
+      if (blockIdx.x == 0) w.xr[idx] = v;
+    }
+    __syncthreads();
+    xr = s_x;
   }
   {
     // the bias of the logit this thread finishes (if any), loaded before the sums
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
     if (e < erows) {
       const float* wrow = e < E ? L.router_w + (size_t)e * H : L.shared_gate_w;
-      router_part<XDT>(wrow, x, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave], s_d);
+      router_part<XDT>(wrow, xr, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave]);
     }
     __syncthreads();
     if (tid < kRouterRows * T) {
@@ -1184,11 +1189,9 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const bool omb = L.wfmt == 1 ? use_down_mailbox<1>(L, T) : use_down_mailbox<2>(L, T);
   const int nzero_o = omb ? (L.k + (L.has_shared ? 1 : 0)) * L.H : 0;  // T == 1
   // x_dtype 2: x is the previous layer's fp32 y, and the layer takes its bf16 RMS rescale
-  // in w.xr.  For one token the router kernel rescales on the fly and writes w.xr (one
-  // launch fewer: stacked decode 1.141 -> 1.072 ms); for more tokens, whose rows every
-  // router block would rescale again, the rescale kernel runs first (at T = 4 the folded
-  // form was 3 % slower).
-  if (x_dtype == 2 && T > 1) {
+  // in w.xr.  Below the split, when the rows fit the router block's LDS copy, the router
+  // kernel rescales them (one launch fewer); otherwise the rescale kernel runs first.
+  if (x_dtype == 2 && (T >= kDecSplitRouteT || T * L.H > kRmsFoldElems)) {
     hipError_t e = launch_rms_rescale((const float*)x, T, L.H, eps, w.xr, s);
     if (e != hipSuccess) return e;
     x = w.xr;

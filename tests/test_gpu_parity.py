@@ -237,7 +237,7 @@ def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T,path", [(1, 0), (4, 0), (7, 0), (9, 0), (40, 0), (4, 2)])
 def test_forward_rms_equals_rescale_then_forward(wfmt, T, path):
-    """moe_forward_rms (the rescale folded into the router kernel for one decode token,
+    """moe_forward_rms (the rescale folded into the router kernel below 8 decode tokens,
     the rescale kernel first otherwise) gives the bits of moe_rms_rescale followed by
     moe_forward on the same path, and with the residual add y_prev plus those bits; the
     two-step result is checked against the oracle."""
