@@ -217,6 +217,8 @@ def test_one_token_long_rows(H, I, k, shared, wfmt, xd):
 @pytest.mark.parametrize("path", [0, 2])
 @pytest.mark.parametrize("T,H,I,E,k,wfmt,shared,xd", [
     (5, 128, 64, 1024, 16, synth.WFMT_MXFP4, 1, synth.X_BF16),   # most experts, largest top-k
+    (1, 128, 64, 1024, 16, synth.WFMT_MXFP4, 1, synth.X_BF16),   # the logit mailbox with 16 candidates a lane
+    (2, 128, 64, 300, 8, synth.WFMT_CB4, 0, synth.X_F32),        # the mailbox with 5 candidates a lane
     (40, 128, 64, 1024, 16, synth.WFMT_CB4, 1, synth.X_F32),
     (3, 16384, 64, 4, 2, synth.WFMT_CB4, 0, synth.X_BF16),       # largest H: 128 k-steps of gate/up
     (3, 64, 16384, 4, 2, synth.WFMT_MXFP4, 1, synth.X_F32),      # largest I: 128 k-steps of down
