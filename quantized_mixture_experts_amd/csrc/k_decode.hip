@@ -680,11 +680,15 @@ __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
 // ---------------------------------------------------------------------------
 template <int FMT, int NP, int NTT, int KSW>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                       size_t act_plane, int xrows_max) {
+                                                       size_t act_plane, int xrows_max, int nslots) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const Slot* slot_rec = w.slots + blockIdx.y;
+  // grid.y = passes x slots, pass-major: block row y takes pass y / nslots of slot
+  // y % nslots (rows xrows_max (y / nslots) ..), so an expert with more pairs than one
+  // pass stages runs its passes side by side; rows past a slot's pairs exit at once
+  const Slot* slot_rec = w.slots + blockIdx.y % nslots;
   const int cnt = slot_rec->cnt, off = slot_rec->off;
-  if (cnt == 0) return;
+  const int tb0 = (int)(blockIdx.y / nslots) * xrows_max;
+  if (tb0 >= cnt) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
@@ -697,7 +701,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const PackedTile pu = packed_tile(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x, FMT == 1 ? 1 : 2);
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
-  for (int tb = 0; tb < cnt; tb += xrows_max) {
+  for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
     f32x4_t accg[NTT], accu[NTT];
@@ -706,7 +710,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
     for (int ch = 0; ch < nchunks; ++ch) {
       const int ks0 = ch * 4 * KSW + wave;
       if (ch == 0) {
-        if (tb > 0) __syncthreads();  // the previous pass finished with the LDS tile
+        if (tb > tb0) __syncthreads();  // the previous pass finished with the LDS tile
         else if (FMT == 2) build_cb4_lut(lut, L.codebook);
         stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, slot_rec, w.perm + off, tb, xrows, T,
                                  k);
@@ -933,12 +937,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 // ---------------------------------------------------------------------------
 template <int FMT, int NTT, int KSW, bool TICKETS>
 __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Work w, float* __restrict__ y,
-                                                          uint32_t* __restrict__ tickets, int xrows_max) {
+                                                          uint32_t* __restrict__ tickets, int xrows_max, int nslots) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int is_last;
-  const Slot* slot_rec = w.slots + blockIdx.y;
+  // without tickets, grid.y = passes x slots, pass-major as in the gate/up kernel (the
+  // ticketed form counts one arrival per slot, so it keeps one row per slot)
+  const Slot* slot_rec = w.slots + blockIdx.y % nslots;
   const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
-  if (cnt == 0) return;
+  const int tb0 = (int)(blockIdx.y / nslots) * xrows_max;
+  if (tb0 >= cnt) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
@@ -952,13 +959,13 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   const bool tile_ok = 16 * tile < H;
   const PackedTile pd = packed_tile(slot_rec->down, H, K, tile_ok ? tile : 0, FMT == 1 ? 1 : 2);
 
-  for (int tb = 0; tb < cnt; tb += xrows_max) {
+  for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
     f32x4_t acc[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (tb > 0) __syncthreads();
+    if (tb > tb0) __syncthreads();
     else if (FMT == 2) build_cb4_lut(lut, L.codebook);
     stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb, xrows,
                              T, k);
@@ -1020,13 +1027,15 @@ static int pick_ksw(int K) {
 template <int FMT, int NTT, int KSW>
 static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
                             hipStream_t s, const Timing& tm) {
-  const dim3 g1(L.I / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
+  const int nslots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
+  const int npass = (T + xrows - 1) / xrows;  // a slot holds at most T pairs
+  const dim3 g1(L.I / 16, nslots * npass);
   if (x_dtype == 1)
     MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 1, NTT, xrows),
-                s, L, T, w, (const uint16_t*)x, (size_t)0, xrows);
+                s, L, T, w, (const uint16_t*)x, (size_t)0, xrows, nslots);
   else
     MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 3, NTT, xrows),
-                s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows);
+                s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows, nslots);
 }
 
 // Active slots above which the combine runs as its own kernel instead of ticketed.
@@ -1036,14 +1045,14 @@ template <int FMT, int NTT, int KSW>
 static void launch_down_rows_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                                hipStream_t s, const Timing& tm) {
   const int slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const dim3 g2((L.H + 63) / 64, slots);
   const size_t lds = dec_lds_bytes(L.I, 2, NTT, xrows);
   if (slots <= kTicketSlotsMax) {
-    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, true>), g2, dim3(256), lds, s, L, T, w, y, tickets,
-                xrows);
+    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, true>), dim3((L.H + 63) / 64, slots), dim3(256), lds,
+                s, L, T, w, y, tickets, xrows, slots);
   } else {
-    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, false>), g2, dim3(256), lds, s, L, T, w, y, tickets,
-                xrows);
+    const int npass = (T + xrows - 1) / xrows;  // a slot holds at most T pairs
+    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, false>), dim3((L.H + 63) / 64, slots * npass),
+                dim3(256), lds, s, L, T, w, y, tickets, xrows, slots);
     (void)launch_combine(L, T, w, y, s, tm);
   }
 }
