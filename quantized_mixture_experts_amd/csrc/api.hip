@@ -30,11 +30,11 @@ constexpr int32_t kMaxTopK = 16;
 constexpr int32_t kMaxTokens = 1 << 16;
 // MOE_PATH_AUTO takes the decode kernels up to this many tokens, where they measured
 // faster than the grouped ones on MI355X.  gpt-oss MXFP4 shape (E 128, top-4, H = I = 2880):
-// T = 8 decode 89.7 against grouped 97.4 us, T = 12 116.8 against 104.7 us.  CB4
-// verify shape (E 256, top-8, H 2048, I 512): T = 20 81.0 against 91.0 us, T = 24 93.2
-// against 91.5 us.
+// T = 8 decode 89.7 against grouped 97.4 us, T = 12 116.9 against 105.9 us.  CB4
+// verify shape (E 256, top-8, H 2048, I 512, Zipf routing): T = 24 80.3 against 92.1 us,
+// T = 32 94.3 against 92.8 us.
 constexpr int32_t kAutoDecodeTokensMx = 10;
-constexpr int32_t kAutoDecodeTokensCb4 = 22;
+constexpr int32_t kAutoDecodeTokensCb4 = 30;
 
 int validate_layer(const moe_layer* L) {
   if (!L) return MOE_ERR_INVALID_ARG;
