@@ -682,12 +682,14 @@ template <int FMT, int NP, int NTT, int KSW>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
                                                        size_t act_plane, int xrows_max, int nslots) {
   extern __shared__ __align__(16) uint8_t smem[];
-  // grid.y = passes x slots, pass-major: block row y takes pass y / nslots of slot
-  // y % nslots (rows xrows_max (y / nslots) ..), so an expert with more pairs than one
-  // pass stages runs its passes side by side; rows past a slot's pairs exit at once
-  const Slot* slot_rec = w.slots + blockIdx.y % nslots;
+  // grid.y = slots x passes, slot-major: block row y takes pass y % npass of slot
+  // y / npass (rows xrows_max (y % npass) ..), so an expert with more pairs than one pass
+  // stages runs its passes side by side on adjacent rows, dispatched together with its
+  // first pass; rows past a slot's pairs exit at once
+  const int npass = (int)gridDim.y / nslots;
+  const Slot* slot_rec = w.slots + blockIdx.y / npass;
   const int cnt = slot_rec->cnt, off = slot_rec->off;
-  const int tb0 = (int)(blockIdx.y / nslots) * xrows_max;
+  const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
   if (tb0 >= cnt) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -940,11 +942,12 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
                                                           uint32_t* __restrict__ tickets, int xrows_max, int nslots) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int is_last;
-  // without tickets, grid.y = passes x slots, pass-major as in the gate/up kernel (the
+  // without tickets, grid.y = slots x passes, slot-major as in the gate/up kernel (the
   // ticketed form counts one arrival per slot, so it keeps one row per slot)
-  const Slot* slot_rec = w.slots + blockIdx.y % nslots;
+  const int npass = (int)gridDim.y / nslots;
+  const Slot* slot_rec = w.slots + blockIdx.y / npass;
   const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
-  const int tb0 = (int)(blockIdx.y / nslots) * xrows_max;
+  const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
   if (tb0 >= cnt) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
