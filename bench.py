@@ -1,21 +1,25 @@
 """Benchmark of the routed MoE layer on one MI355X.
 
-Workload (default): the gpt-oss-120B-shaped decode layer, T = 1 token, H = 2880,
-I = 2880, E = 128 experts, top-4, MXFP4 experts (13,219,200 B each), bf16
-activations, router bias ~ N(0, 0.5).  One step = one whole layer forward (router,
-top-k, bucketing, fused gate/up + SwiGLU, down, combine) on one token.
+Workload (default): 36 stacked gpt-oss-120B-shaped MoE layers (H = 2880, I = 2880,
+E = 128 experts, top-4, MXFP4 experts of 13,219,200 B, about 61 GB of experts resident
+in HBM), bf16 activations, router bias ~ N(0, 0.5).  One step = one token batch through
+all 36 layers: layer 0 takes x, every later layer takes the fp64 RMS rescale of the
+previous layer's fp32 output (inside the layer call).  T = 1 gives `value`; T = 4 is
+reported beside it.  Every layer's experts are distinct, so each step reads its experts
+from HBM (1.96 GB per token at T = 1), not from the 256 MB Infinity Cache.
 
-Steps rotate over a bank of independently seeded layer instances resident in HBM,
-each with its own input token, so that a step's experts were last touched several
-hundred MB of traffic earlier and are read from HBM rather than from the 256 MB
-Infinity Cache.
+Other workloads (--config): the single decode layer (c2), the verify window (c3), the
+tiny layer (c1) and the two 1,024-token prefill chunks (c5a, c5b).  Single-layer steps
+rotate over several independently seeded layer instances resident in HBM for the same
+reason.
 
 Prints one JSON line.  `roofline` covers the dominant kernel (the fused gate/up +
-SwiGLU, about 2/3 of the layer's bytes): algorithmic bytes per launch (the packed
-gate/up matrices of the distinct selected experts plus the activations) over the
-kernel's average execution time, stamped by the kernel's dispatch packet on its own
-stream during the timed steps.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+SwiGLU, about 2/3 of the layer's bytes): algorithmic bytes per launch (the packed gate/up
+matrices of the distinct selected experts plus the activations) over the kernel's
+average execution time, stamped by its dispatch packet on its own stream.
+`step_roofline` is the whole step's algorithmic bytes over the step time.  Every
+fraction is also given against the streaming-read probe's measured bandwidth.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -31,9 +35,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), TFLOP/s (prefill), 1 GPU"
 HBM_PEAK_GBS = 8000.0
-RMS_EPS = 1e-6  # eps of the RMS rescale between the stacked layers
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_gateup.json")
+BF16_PEAK_TFLOPS = 2500.0
+RMS_EPS = 1e-6  # eps of the RMS rescale between the stacked layers (passed as fp32)
 CSRC = os.path.join(ROOT, "quantized_mixture_experts_amd", "csrc")
+PROBE_BYTES = 4 << 30
+PROBE_BLOCKS = 4096
+
+
+def traffic_file(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{config}_gateup.json")
 
 
 def kernel_source_hash() -> str:
@@ -48,22 +58,25 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--tokens", type=int, default=None, help="override T (the stacked config runs T=1 and T=4; "
                     "the verify config with T=136 is the batched verify round of 8 requests x 17 tokens)")
     ap.add_argument("--path", choices=["auto", "decode", "prefill"], default="auto",
-                    help="kernel path (auto: decode kernels up to 32 tokens)")
+                    help="kernel path (auto: decode kernels for small batches)")
     ap.add_argument("--layers", type=int, default=None, help="distinct layer instances in the rotation")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget (wall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="eager steps only (no graph), then a plain 1 GiB device copy that calibrates the "
                          "HBM byte counters; meant to run under rocprofv3 --pmc")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs of a --counters run into the stored "
                          "per-launch HBM traffic of the gate/up kernel")
+    ap.add_argument("--traffic-kernel", default="k_dec_gateup",
+                    help="substring of the kernel name whose counters --traffic-from averages")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -77,14 +90,12 @@ COPY_BYTES = 1 << 30
 
 
 class Workload:
-    """Resident layer instances and inputs of one config, and what one step enqueues."""
+    """Resident layer instances of one config, and what one step enqueues for T tokens."""
 
     def __init__(self, args, spec, dev):
-        import torch
         import quantized_mixture_experts_amd as q
         import synth
-        self.q, self.spec = q, spec
-        self.T = args.tokens or spec.T
+        self.q, self.spec, self.dev = q, spec, dev
         self.path = {"auto": q.PATH_AUTO, "decode": q.PATH_DECODE, "prefill": q.PATH_PREFILL}[args.path]
         self.stacked = spec.n_layers > 1
         if self.stacked:
@@ -93,34 +104,38 @@ class Workload:
             nl = args.layers or {"c1": 4, "c2": 16, "c3": 16, "c5a": 4, "c5b": 4}[args.config]
         self.nl = nl
         t0 = time.time()
-        self.layers, self.xs = [], []
+        self.layers = []
         for l in range(nl):
             host = synth.make_layer(spec, layer=l)
             self.layers.append(q.DeviceLayer.from_layer(host, device=dev))
             del host
-            self.xs.append(torch.from_numpy(synth.make_x(spec, T=self.T, layer=l)).to(dev))
             log(args, f"layer instance {l + 1}/{nl} resident ({time.time() - t0:.1f} s)")
-        self.ws = self.layers[0].workspace(self.T)
-        H = spec.hidden
-        # stacked: y_l feeds x_{l+1} through the RMS rescale; single layers share one y
-        self.ys = [torch.empty((self.T, H), dtype=torch.float32, device=dev)
-                   for _ in range(nl if self.stacked else 1)]
         self.forwards_per_step = nl if self.stacked else 1
-        self.steps_per_graph = 1 if self.stacked else nl
+        self.set_tokens(spec.T)
 
-    def _chain(self, s, fn, fn_rms=None):
-        """Enqueue step s; fn(layer_index, x, y) enqueues one layer forward.  Stacked:
-        layer l > 0 takes the RMS rescale of y_{l-1}, through fn_rms(l, y_prev, y) (the
-        rescale inside the layer call) when given, else as a separate rescale and fn."""
-        q = self.q
+    def set_tokens(self, T):
+        import torch
+        import synth
+        self.T = T
+        self.xs = [torch.from_numpy(synth.make_x(self.spec, T=T, layer=l)).to(self.dev)
+                   for l in range(1 if self.stacked else self.nl)]
+        self.ws = self.layers[0].workspace(T)
+        H = self.spec.hidden
+        # stacked: y_l feeds layer l+1 through the RMS rescale; single layers share one y
+        self.ys = [torch.empty((T, H), dtype=torch.float32, device=self.dev)
+                   for _ in range(self.nl if self.stacked else 1)]
+
+    def graph_count(self):
+        """Graphs to capture: one whole step (stacked) or one per layer instance."""
+        return 1 if self.stacked else self.nl
+
+    def _chain(self, s, fn, fn_rms):
+        """Enqueue step s: fn(l, x, y) enqueues a layer forward on x, fn_rms(l, y_prev, y)
+        one on the RMS rescale of y_prev (stacked layers 1..)."""
         if self.stacked:
             fn(0, self.xs[0], self.ys[0])
             for l in range(1, self.nl):
-                if fn_rms is not None:
-                    fn_rms(l, self.ys[l - 1], self.ys[l])
-                else:
-                    q.rms_rescale(self.ys[l - 1], out=self.xs[l])
-                    fn(l, self.xs[l], self.ys[l])
+                fn_rms(l, self.ys[l - 1], self.ys[l])
         else:
             l = s % self.nl
             fn(l, self.xs[l], self.ys[0])
@@ -148,12 +163,177 @@ class Workload:
         """Distinct routed experts of every forward of one rotation (for the byte counts)."""
         import numpy as np
         out = []
-        for s in range(self.steps_per_graph):
+        for s in range(self.graph_count()):
             def fn(l, x, y):
                 _, dbg = self.q.forward(self.layers[l], x, self.spec.x_dtype, y=y, ws=self.ws, debug=True)
                 out.append(len(np.unique(dbg["ids"].cpu().numpy())))
-            self._chain(s, fn)
+
+            def fn_rms(l, yp, y):
+                xr = self.q.rms_rescale(yp, RMS_EPS)
+                fn(l, xr, y)
+            self._chain(s, fn, fn_rms)
         return out
+
+
+def pct(vals, p):
+    v = sorted(vals)
+    i = min(len(v) - 1, max(0, int(round(p / 100.0 * (len(v) - 1)))))
+    return v[i]
+
+
+def measure(args, wl, T, probe_gbs):
+    """Graph-replayed timing of K steps at T tokens, then the per-kernel durations of an
+    eager pass of the same K steps."""
+    import torch
+    import quantized_mixture_experts_amd as q
+    import synth
+    spec = wl.spec
+    wl.set_tokens(T)
+    H, I, E, k, sh = spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared
+    distinct = wl.distinct_experts()  # one entry per forward of a rotation
+    torch.cuda.synchronize()
+    gu_bytes = q.packed_bytes(spec.weights.wfmt, 2 * I, H)
+    dn_bytes = q.packed_bytes(spec.weights.wfmt, H, I)
+    xb = 4 if spec.x_dtype == synth.X_F32 else 2
+
+    def fwd_bytes(d):
+        router = E * H * 4 + (E * 4 if spec.bias != "none" else 0)
+        return (d + sh) * (gu_bytes + dn_bytes) + router + T * H * xb + T * H * 4
+
+    P = T * k + T * sh
+    fwd_flops = 2 * T * E * H + P * 6 * H * I
+
+    K, W = args.steps, args.warmup
+    ng = wl.graph_count()
+    for s in range(W):
+        wl.step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in range(ng):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step(s)
+        graphs.append(g)
+    for s in range(max(W, ng)):
+        graphs[s % ng].replay()
+    torch.cuda.synchronize()
+    # ---- the timed region: K graph-replayed steps, an event between consecutive steps ----
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record()
+    for s in range(K):
+        graphs[s % ng].replay()
+        evs[s + 1].record()
+    torch.cuda.synchronize()
+    total_ms = evs[0].elapsed_time(evs[K])
+    step_ms = [evs[s].elapsed_time(evs[s + 1]) for s in range(K)]
+    ms_per_step = total_ms / K
+    del graphs
+
+    # ---- kernel durations: the same K steps launched eagerly, each kernel carrying its own
+    # start/stop events (stamped by its dispatch packet on the layer's stream) ----
+    NS = len(q.STAGES)
+    fps = wl.forwards_per_step
+    events = q.HipEvents(2 * NS * fps * K)
+    ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ee0.record()
+    for s in range(K):
+        wl.step_timed(s, events, 2 * NS * fps * s)
+    ee1.record()
+    torch.cuda.synchronize()
+    eager_ms_per_step = ee0.elapsed_time(ee1) / K
+    stage_ms, moe_ms_per_step = {}, 0.0
+    for st, name in enumerate(q.STAGES):
+        vals = []
+        for s in range(K):
+            for f in range(fps):
+                b = 2 * NS * (fps * s + f) + 2 * st
+                v = events.elapsed_ms(b, b + 1)
+                if v is not None:
+                    vals.append(v)
+        if vals:
+            stage_ms[name] = sum(vals) / len(vals)
+            moe_ms_per_step += stage_ms[name] * fps
+    del events
+
+    gu_ms = stage_ms.get("gateup")
+    gu_b = sum((d + sh) * gu_bytes + T * H * xb for d in distinct) / len(distinct)
+    achieved = gu_b / (gu_ms * 1e-3) / 1e9 if gu_ms else None
+    step_bytes = sum(fwd_bytes(d) for d in distinct) / len(distinct) * fps
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = T * K / (total_ms * 1e-3)
+
+    traffic = None
+    tf = traffic_file(args.config)
+    if os.path.exists(tf):
+        tr = json.load(open(tf))
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("tokens") == T:
+            traffic = tr.get("bytes_per_launch")
+
+    def frac(a, p):
+        return round(a / p, 4) if (a and p) else None
+
+    return {
+        "value": round(tokens_per_s, 2),
+        "T": T,
+        "ms_per_step": round(ms_per_step, 6),
+        "step_ms_p10_p50_p90": [round(pct(step_ms, p), 6) for p in (10, 50, 90)],
+        "eager_ms_per_step": round(eager_ms_per_step, 6),
+        "moe_kernels_ms_per_step": round(moe_ms_per_step, 6),
+        "moe_us_per_token": round(ms_per_step * 1e3 / T, 3),
+        "hbm_gbs": round(step_gbs, 1),
+        "tflops": round(fwd_flops * fps / (ms_per_step * 1e-3) / 1e12, 3),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "distinct_experts_per_forward": round(sum(distinct) / len(distinct), 2),
+        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "roofline": {
+            "kernel": "gateup (fused dequant + gate/up + SwiGLU)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": frac(achieved, HBM_PEAK_GBS),
+            "traffic": traffic,
+            "bytes_per_launch": int(gu_b),
+            "avg_us": round(gu_ms * 1e3, 2) if gu_ms else None,
+            "probe_gbs": probe_gbs,
+            "frac_of_probe": frac(achieved, probe_gbs),
+        },
+        "step_roofline": {
+            "bound": "hbm",
+            "achieved": round(step_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": frac(step_gbs, HBM_PEAK_GBS),
+            "frac_of_probe": frac(step_gbs, probe_gbs),
+            "roofline_us_per_step": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3),
+        },
+    }
+
+
+def hbm_probe(args, dev):
+    """Streaming read of 4 GiB with 16-byte loads (the library's probe kernel): the best of
+    five timed passes, GB/s."""
+    import torch
+    import quantized_mixture_experts_amd as q
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    out = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=dev)
+    q.hbm_read_probe(buf, out, PROBE_BLOCKS)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q.hbm_read_probe(buf, out, PROBE_BLOCKS)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf, out
+    torch.cuda.empty_cache()
+    gbs = PROBE_BYTES / (best * 1e-3) / 1e9
+    log(args, f"streaming-read probe: {gbs:.0f} GB/s")
+    return round(gbs, 1)
 
 
 def main():
@@ -173,13 +353,15 @@ def main():
     q.lib()
     dev = torch.device("cuda:0")
     spec = synth.CONFIGS[args.config]
+    probe_gbs = None if (args.no_probe or args.counters) else hbm_probe(args, dev)
     wl = Workload(args, spec, dev)
-    T, H, I, E, k = wl.T, spec.hidden, spec.inter, spec.n_experts, spec.top_k
-    sh = spec.has_shared
-    distinct = wl.distinct_experts()  # one entry per forward of a rotation
-    torch.cuda.synchronize()
+    stacked = spec.n_layers > 1
+    Ts = [args.tokens] if args.tokens else ([1, 4] if stacked else [spec.T])
 
     if args.counters:
+        T = Ts[0]
+        wl.set_tokens(T)
+        distinct = wl.distinct_experts()
         for s in range(max(args.steps, 1)):
             wl.step(s)
         torch.cuda.synchronize()
@@ -189,96 +371,34 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"counters_run": args.config, "steps": args.steps, "copy_bytes": COPY_BYTES,
-                          "gateup_bytes_per_launch": gateup_bytes_avg(spec, T, distinct),
-                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        gu = q.packed_bytes(spec.weights.wfmt, 2 * spec.inter, spec.hidden)
+        xb = 4 if spec.x_dtype == synth.X_F32 else 2
+        gub = sum((d + spec.has_shared) * gu + T * spec.hidden * xb for d in distinct) / len(distinct)
+        print(json.dumps({"counters_run": args.config, "tokens": T, "steps": args.steps, "copy_bytes": COPY_BYTES,
+                          "gateup_bytes_per_launch": gub, "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
 
-    gu_bytes = q.packed_bytes(spec.weights.wfmt, 2 * I, H)
-    dn_bytes = q.packed_bytes(spec.weights.wfmt, H, I)
-    xb = 4 if spec.x_dtype == synth.X_F32 else 2
-
-    def fwd_bytes(d):
-        router = E * H * 4 + (E * 4 if spec.bias != "none" else 0)
-        return (d + sh) * (gu_bytes + dn_bytes) + router + T * H * xb + T * H * 4
-
-    def fwd_flops():
-        P = T * k + T * sh
-        return 2 * T * E * H + P * 6 * H * I
-
-    # ---- the timed region: HIP-graph replays of whole steps --------------------------
-    K, W = args.steps, args.warmup
-    spg = wl.steps_per_graph
-    K = max(spg, (K // spg) * spg)
-    NS = len(q.STAGES)
-    for s in range(W):
-        wl.step(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for s in range(spg):
-            wl.step(s)
-    for _ in range(max(1, W // spg)):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K // spg):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    ms_per_step = total_ms / K
-
-    # ---- kernel durations: the same K steps launched eagerly, each kernel carrying its
-    # own start/stop events (stamped by its dispatch packet on the layer's stream) -------
-    fps = wl.forwards_per_step
-    events = q.HipEvents(2 * NS * fps * K)
-    ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ee0.record()
-    for s in range(K):
-        wl.step_timed(s, events, 2 * NS * fps * s)
-    ee1.record()
-    torch.cuda.synchronize()
-    eager_ms_per_step = ee0.elapsed_time(ee1) / K
-
-    # per-forward stage durations; forward f of step s is rotation entry (s % spg) * fps + f
-    stage_ms, moe_ms_per_step = {}, 0.0
-    for st, name in enumerate(q.STAGES):
-        vals = []
-        for s in range(K):
-            for f in range(fps):
-                b = 2 * NS * (fps * s + f) + 2 * st
-                v = events.elapsed_ms(b, b + 1)
-                if v is not None:
-                    vals.append(v)
-        if vals:
-            stage_ms[name] = sum(vals) / len(vals)
-            moe_ms_per_step += stage_ms[name] * fps
-    gu_ms = stage_ms.get("gateup")
-    gu_b = gateup_bytes_avg(spec, T, distinct)
-    achieved = gu_b / (gu_ms * 1e-3) / 1e9 if gu_ms else None
-    sb = sum(fwd_bytes(d) for d in distinct) / len(distinct) * fps
-    tokens_per_s = T * K / (total_ms * 1e-3)
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("config") == args.config:
-            traffic = tr.get("bytes_per_launch")
+    runs = []
+    for T in Ts:
+        r = measure(args, wl, T, probe_gbs)
+        log(args, f"T={T}: {r['value']} tokens/s, {r['ms_per_step']} ms per step")
+        runs.append(r)
+    main_run = runs[0]
 
     fmt = "MXFP4" if spec.weights.wfmt == synth.WFMT_MXFP4 else "4-bit codebook"
-    workload = (f"{args.config}: {spec.name}, T={T}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
-                f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers" if wl.stacked else "")
+    H, I, E, k, sh = spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared
+    workload = (f"{args.config}: {spec.name}, T={main_run['T']}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
+                f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers (RMS rescale between)"
+                                             if stacked else "")
                 + (f", {args.path} kernels forced" if args.path != "auto" else ""))
     result = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 2),
+        "value": main_run["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_run["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -287,44 +407,24 @@ def main():
         "config": {
             "workload": workload,
             "layer_instances": wl.nl,
-            "global_batch": T,
+            "global_batch": main_run["T"],
         },
-        "timing": "HIP-graph replay of whole steps; kernel durations from an eager pass of the same steps",
-        "eager_ms_per_step": round(eager_ms_per_step, 6),
-        "moe_kernels_ms_per_step": round(moe_ms_per_step, 6),
-        "layer_hbm_gbs": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
-        "algorithmic_bytes_per_step": int(sb),
-        "tflops": round(fwd_flops() * fps / (ms_per_step * 1e-3) / 1e12, 3),
-        "stage_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
-        "roofline": {
-            "kernel": "gateup (fused dequant + gate/up + SwiGLU)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1) if achieved else None,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-            "traffic": traffic,
-            "bytes_per_launch": int(gu_b),
-            "avg_us": round(gu_ms * 1e3, 2) if gu_ms else None,
-        },
-        "cpu_baseline": None,
+        "timing": "HIP-graph replay of whole steps, an event between consecutive steps; kernel durations "
+                  "from an eager pass of the same steps with dispatch-stamped events",
     }
-
-    # ---- CPU oracle on a bounded sample -------------------------------------------
+    for key in ("step_ms_p10_p50_p90", "eager_ms_per_step", "moe_kernels_ms_per_step", "moe_us_per_token",
+                "hbm_gbs", "tflops", "algorithmic_bytes_per_step", "distinct_experts_per_forward", "stage_us",
+                "roofline", "step_roofline"):
+        result[key] = main_run[key]
+    if len(runs) > 1:
+        result["other_batches"] = {f"T={r['T']}": r for r in runs[1:]}
+    result["hbm_probe_gbs"] = probe_gbs
+    result["cpu_baseline"] = None
+    del wl
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, spec, T, wl.nl, wl.stacked)
-
+        result["cpu_baseline"] = cpu_baseline(args, spec, main_run["T"], stacked)
     print(json.dumps(result), flush=True)
-
-
-def gateup_bytes_avg(spec, T, distinct):
-    """Algorithmic bytes of one gate/up launch: the packed gate/up matrices of the distinct
-    selected experts (plus the shared one) and the activations, averaged over launches."""
-    import quantized_mixture_experts_amd as q
-    import synth
-    gu = q.packed_bytes(spec.weights.wfmt, 2 * spec.inter, spec.hidden)
-    xb = 4 if spec.x_dtype == synth.X_F32 else 2
-    return sum((d + spec.has_shared) * gu + T * spec.hidden * xb for d in distinct) / len(distinct)
 
 
 def _counter_rows(path):
@@ -363,9 +463,9 @@ def write_traffic(args):
     wcopy, _ = copy_kib(write)
     f_scale = COPY_BYTES / (fcopy * 1024.0)
     w_scale = COPY_BYTES / (wcopy * 1024.0)
-    gu = [n for n in fetch if "gateup" in n]
+    gu = [n for n in fetch if args.traffic_kernel in n]
     if not gu:
-        raise SystemExit("no gate/up kernel in the counter CSV")
+        raise SystemExit(f"no kernel named like {args.traffic_kernel!r} in the counter CSV")
     per_kernel = {}
     for n in gu:
         fv, wv = fetch[n], write.get(n, [0.0])
@@ -378,8 +478,10 @@ def write_traffic(args):
     meta_path = os.path.join(os.path.dirname(os.path.abspath(args.traffic_from[0])), "counters_run.json")
     if os.path.exists(meta_path):
         meta = json.load(open(meta_path))
+    config = meta.get("counters_run", "c4")
     out = {
-        "config": meta.get("counters_run", "c2"),
+        "config": config,
+        "tokens": meta.get("tokens"),
         "kernel_source_hash": meta["kernel_source_hash"] if "kernel_source_hash" in meta else kernel_source_hash(),
         "bytes_per_launch": int(round(fb + wb)),
         "fetch_bytes_per_launch": int(round(fb)),
@@ -389,46 +491,67 @@ def write_traffic(args):
                         "fetch_scale": f_scale, "write_scale": w_scale},
         "kernels": per_kernel,
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(config), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(args, spec, T, nl, stacked):
-    """The oracle as it stands, on a bounded sample of the same workload: whole layers of
-    independently seeded instances (each with its own input rows) until the time budget
-    is spent.  For the stacked config one token's step is 36 layers, so the rate is the
-    sampled per-layer time times the depth."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, spec, T, stacked):
+    """The oracle as it stands, on a bounded sample of the same workload: independent
+    layer forwards of T tokens (seeded layer instances, each with its own input rows; for
+    the stacked config each forward is one layer of the 36, teacher-forced), one per
+    worker thread on every core the job may use, until about the time budget is spent.
+    The stacked config's rate is the per-layer rate divided by the depth."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    spent, layers_used = 0.0, 0
-    for l in range(max(nl, 64)):
+    cores = min(16, len(os.sched_getaffinity(0)))
+
+    def item(l):
         x = synth.make_x(spec, T=T, layer=l)
         router_only = synth.make_layer(spec, layer=l, experts=[])
         x64 = oracle.activations_f64(x, spec.x_dtype)
         ids, _ = oracle.topk_softmax(oracle.router_logits(x64, router_only.router_w, router_only.router_b),
                                      spec.top_k)
-        layer = synth.make_layer(spec, layer=l, experts=np.unique(ids))
-        t0 = time.perf_counter()
+        return synth.make_layer(spec, layer=l, experts=np.unique(ids)), x
+
+    def run(it):
+        layer, x = it
         oracle.moe_forward(layer, x, spec.x_dtype)
-        spent += time.perf_counter() - t0
-        layers_used += 1
-        log(args, f"cpu oracle: {layers_used} layer forwards of {T} tokens in {spent:.1f} s")
-        if spent >= args.cpu_seconds:
-            break
+
+    # one forward alone sizes the sample: rounds of one forward per core
+    first = item(0)
+    t0 = time.perf_counter()
+    run(first)
+    t_one = time.perf_counter() - t0
+    rounds = max(1, int(round(args.cpu_seconds / max(t_one, 1e-3))))
+    n_items = rounds * cores
+    items = [item(l) for l in range(1, n_items + 1)]
+    with ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(run, items))
+        wall = time.perf_counter() - t0
+    log(args, f"cpu oracle: {n_items} layer forwards of {T} token(s) on {cores} threads in {wall:.1f} s "
+              f"(one alone {t_one:.1f} s)")
     depth = spec.n_layers if stacked else 1
-    tokens_per_s = T * layers_used / spent / depth
-    what = (f"{layers_used} forwards of {T} token(s) through seeded instances of the layer"
-            + (f", scaled by the {depth}-layer depth" if stacked else "")
-            + f"; fp64 numpy oracle, {spent:.1f} s of oracle time")
-    return {"value": round(tokens_per_s, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": what}
+    tokens_per_s = T * n_items / wall / depth
+    what = (f"{n_items} independent forwards of {T} token(s) through seeded instances of one layer, one per "
+            f"worker thread, {wall:.1f} s wall" + (f"; per-layer rate divided by the {depth}-layer depth"
+                                                   if stacked else "")
+            + "; fp64 numpy oracle")
+    return {"value": round(tokens_per_s, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": what, "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0))}
 
 
 if __name__ == "__main__":

@@ -28,10 +28,21 @@
  *   y[t]    = sum_j g[t,j] * o_(t*k+j) + s_t * o_(T*k+t)   (j ascending, shared last)
  *   s_t     = 1, or sigmoid(shared_gate_w . x[t]) when shared_gate_w != NULL
  *
- * Packed matrix [N rows][K cols] (K a multiple of 32), blocks of 32 along a row:
- *   code plane at byte 0: N*K/2 bytes row-major; byte j of a block holds element
- *     2j in its low nibble and element 2j+1 in its high nibble;
- *   scale plane at byte round_up(N*K/2, 256): N*K/32 scales, row-major;
+ * Packed matrix [N rows][K cols] (N a multiple of 16, K a multiple of 32), blocks of
+ * 32 consecutive values along a row, nkb = K/32 blocks per row.  Within a block, code
+ * byte j holds element 2j in its low nibble and element 2j+1 in its high nibble.
+ * The matrix is a code plane followed by a scale plane, both stored tile-major: rows
+ * form tiles of 16 (tile t = rows 16t .. 16t+15, row m = row % 16) and a row's blocks
+ * form steps of 4 (step s = blocks 4s .. 4s+3; the last step holds r = nkb - 4s < 4
+ * blocks when nkb % 4 != 0; block b = 4s + g):
+ *   code plane at byte 0, N*K/2 bytes: the 16 code bytes of block (row 16t+m, 4s+g)
+ *     start at byte t*8*K + 1024*s + (16*g + m)*16, so one tile's step is one
+ *     contiguous run of 256*r bytes;
+ *   scale plane at byte S = round_up(N*K/2, 256), N*nkb scales: the scale of block
+ *     (row 16t+m, 4s+g) is entry t*16*nkb + 64*s + i of the plane, where
+ *       MXFP4: i = 16*g + m, entries are bytes (byte S + entry);
+ *       CB4:   i = m*r + g, entries are little-endian fp16 (bytes S + 2*entry, +1);
+ *   moe_packed_bytes gives S + N*nkb (MXFP4) or S + 2*N*nkb (CB4).
  *   MXFP4: code = FP4 E2M1, scale = E8M0 byte u, element = e2m1 * 2^(u-127)
  *     (OCP Microscaling v1.0; the Neural page names MXFP4 experts, "What it runs
  *     on and what it runs": 13,219,200 bytes per gpt-oss-120B expert, which this
@@ -55,9 +66,14 @@
  *   - A launch failure returns MOE_ERR_HIP; faults during execution surface at
  *     the caller's next synchronisation, as with any stream API.
  *   - No C++ exception crosses the ABI and nothing is printed.  The library is
- *     reentrant; it has no global mutable state.
+ *     reentrant: it keeps no state between calls besides the caller's workspace.
  *   - Calls that share a workspace must not overlap in time (same stream, or
  *     ordered by events).
+ *   - No GPU block ever waits for another block: where a kernel needs results of
+ *     other blocks of the same launch, each block checks once, after its own results
+ *     have landed, and the block that finds them all complete does the dependent work.
+ *     Results therefore do not depend on which blocks the GPU runs at the same time
+ *     (other streams or processes may hold any share of the compute units).
  */
 #ifndef MOEQ_H
 #define MOEQ_H
@@ -103,8 +119,9 @@ typedef struct {
   const float *shared_gate_w;  /* [H] fp32, or NULL (shared weight 1); ignored without a shared expert */
 } moe_layer;
 
-/* [host] Bytes of one packed matrix; 0 if cols is not a positive multiple of 32
- * or rows <= 0 or the format is unknown. */
+/* [host] Bytes of one packed matrix [rows][cols] in the layout above; 0 if cols is not
+ * a positive multiple of 32, rows is not a positive multiple of 16, or the format is
+ * unknown. */
 size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols);
 
 /* [host] Workspace bytes moe_forward / moe_router_topk / moe_bucket need for up
@@ -158,16 +175,24 @@ int moe_forward_timed(const moe_layer *L, const void *x, int32_t x_dtype, int32_
                       void *ws, size_t ws_bytes, void *stream, int32_t path,
                       void *const *stage_events);
 
-/* Test export: decode one packed matrix to fp32 out [rows][cols], bit-exact
- * (every element is exactly representable in fp32 for MXFP4 scales u <= 252
- * and every finite fp16 scale).  codebook: CB4 [16] int8, NULL for MXFP4. */
+/* Test export: decode one packed matrix (layout above) to fp32 out [rows][cols],
+ * bit-exact (every element is exactly representable in fp32 for MXFP4 scales
+ * u <= 252 and every finite fp16 scale).  codebook: CB4 [16] int8, NULL for MXFP4.
+ * Errors: MOE_ERR_INVALID_ARG for an unknown format, rows not a positive multiple of
+ * 16, cols not a positive multiple of 32, NULL packed/out, or a CB4 call without a
+ * codebook; MOE_ERR_UNSUPPORTED above 2^34 elements; MOE_ERR_ALIGNMENT for packed or
+ * out not 16-byte aligned. */
 int moe_dequant(int32_t wfmt, const void *packed, const int8_t *codebook, int32_t rows,
                 int32_t cols, float *out, void *stream);
 
 /* Helper between stacked layers (not part of the layer):
- * x_next[t][n] = bf16_rne(y[t][n] * r_t), bf16 bits, where
- * r_t = the fp32 reciprocal of sqrt(mean_n y[t][n]^2 + eps).
- * The result is within one bf16 step of rounding the exact quotient. */
+ * x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y[t][n]^2 + eps)), bf16 bits.
+ * The sum of squares (exact squares, summed in a fixed order), the mean, the square
+ * root and the quotient are fp64 (the square root and quotient correctly rounded), and
+ * the fp64 quotient is rounded once to bf16 (nearest, ties to even).  y is [T][H] fp32;
+ * eps >= 0 (converted exactly to fp64); results of magnitude below 2^-126 (the bf16
+ * normal range) are outside this definition.  Errors: MOE_ERR_INVALID_ARG for T < 0,
+ * H <= 0, eps < 0 or NaN, or a NULL pointer with T > 0. */
 int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_next_bf16,
                     void *stream);
 
@@ -193,6 +218,14 @@ int moe_rms_rescale(const float *y, int32_t T, int32_t H, float eps, void *x_nex
 int moe_forward_rms(const moe_layer *L, const float *y_prev, float eps, int32_t residual, int32_t T,
                     float *y, void *ws, size_t ws_bytes, void *stream, int32_t path,
                     void *const *stage_events);
+
+/* Measurement helper (not part of the layer): reads `bytes` (a multiple of 16) of buf
+ * with 16-byte nontemporal loads, grid-stride over `blocks` blocks of 256 threads, and
+ * writes one word per block to out[blocks] (the xor of what it read).  Timing it gives
+ * the HBM read bandwidth a plain stream achieves on this GPU.  Errors:
+ * MOE_ERR_INVALID_ARG for NULL pointers, bytes 0 or not a multiple of 16, blocks
+ * outside 1 .. 2^20; MOE_ERR_ALIGNMENT for buf not 16-byte or out not 4-byte aligned. */
+int moe_hbm_read_probe(const void *buf, size_t bytes, uint32_t *out, int32_t blocks, void *stream);
 
 /* [host] Static description of a status code. */
 const char *moe_status_str(int status);

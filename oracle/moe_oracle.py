@@ -249,10 +249,12 @@ def expert_ffn(w_gate_up: np.ndarray, w_down: np.ndarray, X: np.ndarray):
     return h, h @ w_down.T
 
 
-def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = False):
+def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = False, map_fn=map):
     """The whole layer for the tokens in x.  When `ids`/`gates` are given, routing is
     taken from them (steps after routing only).  Returns a dict with y [T][H] fp64 and
-    every intermediate the GPU library exposes."""
+    every intermediate the GPU library exposes.  The experts' products are independent
+    of each other; `map_fn` evaluates them (the builtin map: one after another; a thread
+    pool's map gives the same values)."""
     H, I, E, k = layer.hidden, layer.inter, layer.n_experts, layer.top_k
     x64 = activations_f64(x, x_dtype)
     T = x64.shape[0]
@@ -264,16 +266,19 @@ def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = Fal
     s = shared_weights(x64, layer.shared_gate_w) if layer.has_shared else None
     counts, offsets, perm, inv = bucket(ids, E, layer.has_shared)
     P = perm.shape[0]
-    o = np.zeros((P, H))
-    h_all = np.zeros((P, I)) if want_h else None
-    for e in range(E + layer.has_shared):
+
+    def one_expert(e):
         pairs = perm[offsets[e]:offsets[e + 1]]
-        if pairs.size == 0:
-            continue
         tokens = np.where(pairs < T * k, pairs // k, pairs - T * k)
         wgu = dequant(layer.wfmt, layer.gate_up[e], layer.codebook, 2 * I, H)
         wd = dequant(layer.wfmt, layer.down[e], layer.codebook, H, I)
         h, oe = expert_ffn(wgu, wd, x64[tokens])
+        return pairs, h, oe
+
+    o = np.zeros((P, H))
+    h_all = np.zeros((P, I)) if want_h else None
+    used = [e for e in range(E + layer.has_shared) if counts[e] > 0]
+    for pairs, h, oe in map_fn(one_expert, used):
         o[pairs] = oe
         if want_h:
             h_all[pairs] = h
@@ -287,12 +292,20 @@ def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = Fal
                 offsets=offsets, perm=perm, inv=inv, h=h_all, o=o)
 
 
-def rms_rescale(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
-    """Input of the next stacked layer: y / sqrt(mean(y^2) + eps) per token, rounded to
-    bfloat16 (nearest, ties to even).  Returns uint16 bits."""
+# eps of the rescale as the library receives it: an fp32 number (1e-6 rounded to fp32)
+RMS_EPS = float(np.float32(1e-6))
+
+
+def rms_quotient(y: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """y / sqrt(mean(y^2) + eps) per token (row), in float64."""
     y = np.asarray(y, dtype=np.float64)
-    r = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
-    return round_to_bf16_bits(r)
+    return y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+
+
+def rms_rescale(y: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """Input of the next stacked layer: the fp64 quotient y / sqrt(mean(y^2) + eps) per
+    token, rounded to bfloat16 (nearest, ties to even).  Returns uint16 bits."""
+    return round_to_bf16_bits(rms_quotient(y, eps))
 
 
 def round_to_bf16_bits(v: np.ndarray) -> np.ndarray:

@@ -23,7 +23,8 @@ DT_F32, DT_BF16 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 EXPORTED = ["moe_packed_bytes", "moe_workspace_bytes", "moe_router_topk", "moe_bucket", "moe_forward",
-            "moe_forward_timed", "moe_dequant", "moe_rms_rescale", "moe_forward_rms", "moe_status_str"]
+            "moe_forward_timed", "moe_dequant", "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe",
+            "moe_status_str"]
 STAGES = ["router", "topk", "bucket", "gateup", "down", "combine", "xquant"]
 
 
@@ -61,9 +62,10 @@ def lib() -> ctypes.CDLL:
         L.moe_rms_rescale.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_forward_rms.argtypes = [ctypes.POINTER(MoeLayerC), vp, ctypes.c_float, i32, i32, vp, vp, sz, vp, i32,
                                       vp]
+        L.moe_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
         L.moe_status_str.argtypes, L.moe_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         for f in ["moe_router_topk", "moe_bucket", "moe_forward", "moe_forward_timed", "moe_dequant",
-                  "moe_rms_rescale", "moe_forward_rms"]:
+                  "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe"]:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -275,3 +277,10 @@ def rms_rescale(y, eps: float = 1e-6, out=None, stream=None):
     out = torch.empty((T, H), dtype=torch.int16, device=y.device) if out is None else out
     _check(lib().moe_rms_rescale(y.data_ptr(), T, H, eps, out.data_ptr(), _stream(stream)), "moe_rms_rescale")
     return out
+
+
+def hbm_read_probe(buf, out, blocks: int, stream=None):
+    """moe_hbm_read_probe: stream-read every byte of the device tensor buf (one word per
+    block written to out, a device int32 tensor of at least `blocks` entries)."""
+    _check(lib().moe_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(), blocks,
+                                    _stream(stream)), "moe_hbm_read_probe")

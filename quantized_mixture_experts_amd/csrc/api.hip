@@ -272,6 +272,12 @@ int moe_rms_rescale(const float* y, int32_t T, int32_t H, float eps, void* x_nex
                                              static_cast<hipStream_t>(stream)));
 }
 
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream) {
+  if (!buf || !out || bytes == 0 || bytes % 16 || blocks <= 0 || blocks > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(buf) || !aligned4(out)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moeq::launch_read_probe(buf, bytes, out, blocks, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

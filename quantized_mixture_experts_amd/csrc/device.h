@@ -116,6 +116,36 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Round-to-nearest-even fp64 -> bf16 bits, for finite v that is 0 or of magnitude in the
+// bf16 normal range: the fraction is rounded at bf16's last kept bit (bit 45 of the fp64
+// fraction) on the integer bits, and the result, having 8 significant bits, converts to
+// fp32 exactly.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+  constexpr uint64_t kDrop = (1ull << 45) - 1;  // fraction bits below bf16's seventh
+  uint64_t b = __builtin_bit_cast(uint64_t, v);
+  b = (b + (kDrop >> 1) + ((b >> 45) & 1ull)) & ~kDrop;
+  return __float_as_uint((float)__builtin_bit_cast(double, b)) >> 16;
+}
+
+// ---- RMS rescale between stacked layers: x = bf16_rne(y / sqrt(mean(y^2) + eps)) ----
+// One thread's share of a row's sum of squares, n = i, i + 256, ... (fp64: every square
+// of an fp32 value is exact; the sum rounds in this order).  A row is summed by 256
+// threads (4 waves), the wave sums added in wave order; the rescale kernel and the
+// router kernel that folds the rescale in both use exactly these steps.
+__device__ __forceinline__ double rms_partial(const float* __restrict__ yt, int H, int i) {
+  double s = 0.0;
+  for (int n = i; n < H; n += 256) {
+    const double v = (double)yt[n];
+    s = fma(v, v, s);
+  }
+  return s;
+}
+__device__ __forceinline__ double rms_divisor(double s0, double s1, double s2, double s3, int H, float eps) {
+  return sqrt((((s0 + s1) + s2) + s3) / (double)H + (double)eps);
+}
+// the fp64 quotient (correctly rounded), then rounded to bf16
+__device__ __forceinline__ uint16_t rms_apply(float y, double d) { return (uint16_t)f64_to_bf16_rne((double)y / d); }
+
 // ---- cross-lane helpers on DPP row rotations (a few cycles each) plus readlane ----
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v) {
@@ -223,74 +253,20 @@ __device__ __forceinline__ void sort_lane(uint64_t (&v)[NPER]) {
     }
   }
 }
-// COHERENT: the logits were written by other blocks of the running kernel.  Token t's
-// selections go to s_exp/s_l[slot[t] * k + j] (written by lane 0), j = 0 .. k-1 in
-// selection order.
-// The logits may come as nsplit <= MAXS partial sums (a K-split router), split z at
-// logits + z * split_stride; every split is loaded before any is added (clamped split
-// index: no branch around the loads), and they are added in z order.
-//
-// MBOX: the logits are posted as ~bits in a zeroed mailbox by other blocks (logits is
-// then the mailbox): the wave polls its entries (bounded) until none reads 0, decodes
-// them and clears them for the next call.
-template <int NPER, int NT, bool COHERENT, int MAXS = 1, bool MBOX = false>
-__device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
-                                            const int (&slot)[NT], int* s_exp, double* s_l, int nsplit = 1,
-                                            size_t split_stride = 0) {
+// Selection of the top k of NT tokens from each lane's candidate logits lv[t][i] (expert
+// e = lane + 64 i; entries with e >= E are ignored).  Token t's selections go to
+// s_exp/s_l[slot[t] * k + j] (written by lane 0), j = 0 .. k-1 in selection order.
+template <int NPER, int NT>
+__device__ __forceinline__ void topk_select(const double (&lv)[NT][NPER], int E, int k, const int (&slot)[NT],
+                                            int* s_exp, double* s_l) {
   const int lane = threadIdx.x & 63;
   uint64_t v[NT][NPER];
-  double part[NT][NPER][MAXS];
-  if constexpr (MBOX) {
-    static_assert(MAXS == 1, "the mailbox holds whole logits");
-    uint64_t raw[NT][NPER];
-    for (uint32_t spins = 0;; ++spins) {
-      bool missing = false;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          const int e = lane + 64 * i;
-          uint64_t* src = (uint64_t*)(logits + (size_t)tok[t] * (E + 1) + min(e, E - 1));
-          raw[t][i] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          missing |= e < E && raw[t][i] == 0ull;
-        }
-      if (__ballot(missing) == 0ull || spins > (1u << 22)) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) {
-        const int e = lane + 64 * i;
-        part[t][i][0] = __builtin_bit_cast(double, ~raw[t][i]);
-        if (e < E)
-          __hip_atomic_store((uint64_t*)(logits + (size_t)tok[t] * (E + 1) + e), 0ull, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-  } else {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) {
-        // every lane loads (index clamped into the row): no branch around the loads
-        const int e = lane + 64 * i;
-        const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
-#pragma unroll
-        for (int z = 0; z < MAXS; ++z) {
-          const double* sz = src + (size_t)min(z, nsplit - 1) * split_stride;
-          part[t][i][z] = COHERENT ? __hip_atomic_load(sz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sz;
-        }
-      }
-  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       const int e = lane + 64 * i;
-      double lv = part[t][i][0];
-#pragma unroll
-      for (int z = 1; z < MAXS; ++z) lv = z < nsplit ? lv + part[t][i][z] : lv;
-      v[t][i] = e < E ? topk_key(lv, e) : 0ull;
+      v[t][i] = e < E ? topk_key(lv[t][i], e) : 0ull;
     }
 #pragma unroll
   for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t]);
@@ -310,6 +286,42 @@ __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, i
       v[t][NPER - 1] = pop ? 0ull : v[t][NPER - 1];
     }
   }
+}
+
+// Top-k of NT tokens whose logits are in memory ([T][E + 1] rows).  COHERENT: they were
+// written by other blocks of the running kernel (device-scope loads).
+// The logits may come as nsplit <= MAXS partial sums (a K-split router), split z at
+// logits + z * split_stride; every split is loaded before any is added (clamped split
+// index: no branch around the loads), and they are added in z order.
+template <int NPER, int NT, bool COHERENT, int MAXS = 1>
+__device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, int E, int k, const int (&tok)[NT],
+                                            const int (&slot)[NT], int* s_exp, double* s_l, int nsplit = 1,
+                                            size_t split_stride = 0) {
+  const int lane = threadIdx.x & 63;
+  double part[NT][NPER][MAXS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      // every lane loads (index clamped into the row): no branch around the loads
+      const int e = lane + 64 * i;
+      const double* src = logits + (size_t)tok[t] * (E + 1) + min(e, E - 1);
+#pragma unroll
+      for (int z = 0; z < MAXS; ++z) {
+        const double* sz = src + (size_t)min(z, nsplit - 1) * split_stride;
+        part[t][i][z] = COHERENT ? __hip_atomic_load(sz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sz;
+      }
+    }
+  double lv[NT][NPER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      lv[t][i] = part[t][i][0];
+#pragma unroll
+      for (int z = 1; z < MAXS; ++z) lv[t][i] = z < nsplit ? lv[t][i] + part[t][i][z] : lv[t][i];
+    }
+  topk_select<NPER, NT>(lv, E, k, slot, s_exp, s_l);
 }
 
 // E8M0 byte -> fp32 2^(u-127) (u = 0 gives the subnormal 2^-127).

@@ -1,20 +1,26 @@
 // Decode path (few tokens per call, e.g. a draft/verify window of up to 17 tokens):
-//   1. k_dec_rr:       router logits (4 expert rows per block), then block 0, once
-//                      every block has arrived, does the top-k + gates, the stable
-//                      bucketing of the pairs and the active-expert slot records;
-//                      block 0 also clears the per-tile arrival counters of step 3.
+//   1. k_dec_rr:       router logits (4 expert rows per block); every block posts its
+//                      logits and then checks once whether all of them are there; the
+//                      block that sees them all does the top-k + gates, the stable
+//                      bucketing of the pairs and the active-expert slot records, and
+//                      clears the per-tile arrival counters of step 3.
 //   2. k_dec_gateup:   fused dequant + gate/up + SwiGLU per (16-row tile, active expert).
 //   3. k_dec_down:     dequant + down per (16-row tile, active expert); the last block
 //                      to finish a tile sums the gate-weighted expert outputs of that
 //                      tile in a fixed order (routed j ascending, then shared), so no
 //                      float atomics and a run-to-run identical result (NInfer
-//                      Qwen3.8-Flash-Next page, MoE execution notes: one token's down
-//                      runs over all its experts and the weighted sum must not depend
-//                      on the order experts finish in).
+//                      Qwen3.8-Flash-Next page, MoE execution notes: a token's down
+//                      projection runs over all of its experts, and the weighted sum is
+//                      formed so that it does not depend on which expert finishes first).
 // Each selected expert's weights are streamed from HBM exactly once per call, for all
-// of its tokens (same page: one pass over each selected expert's rows for all of its
-// tokens).  Weight loads for a wave's whole K range are issued before the first MFMA
-// so that a wave keeps its full share of HBM requests in flight.
+// of its tokens (same page and notes: the pairs are grouped by expert so that an
+// expert's rows are read in one pass).  Weight loads for a wave's whole K range are
+// issued before the first MFMA so that a wave keeps its full share of HBM requests in
+// flight.
+// No block ever waits for another: a block that needs the results of others checks
+// once, after its own results have landed, and leaves the work to a later block when
+// something is missing.  The last block to check sees everything, so the work is always
+// done, whatever blocks the GPU keeps resident together.
 #include "device.h"
 #include "launch.h"
 
@@ -33,7 +39,11 @@ constexpr int kRmsFoldElems = 24576;
 constexpr int waitcnt_vm_le(int n) {
   return (n > 63 ? 63 : n) & 15 | (7 << 4) | (15 << 8) | (((n > 63 ? 63 : n) >> 4) << 14);
 }
-// vector-memory instructions one prefetch_step issues per 16-row tile
+// vector-memory instructions one prefetch_step issues per 16-row tile: MXFP4 one 16-byte
+// code load and one scale byte; CB4 four code dwords and four fp16 scales.  The waits
+// after the staging loads count on exactly these: no two of them can be merged into one
+// instruction, since each address is clamped separately (min / select on the block
+// index), so the compiler cannot prove two of them adjacent.
 template <int FMT>
 constexpr int loads_per_step() { return FMT == 1 ? 2 : 8; }
 constexpr int kDecMaxTokens = 32;  // two 16-slot MFMA token tiles
@@ -66,15 +76,80 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
-template <int NPER, bool MBOX>
+// Top-k of the tokens a wave takes (t0, and t1 when below T) from the logit mailbox,
+// where the blocks of this kernel post each logit l as ~bits(l) (0: not posted yet).
+// Every wave of the block loads its tokens' entries once (and lane 0 the shared-gate
+// logit, column E, when want_sg); if any is missing the block leaves the routing to a
+// later block and false is returned, uniformly over the block.  Otherwise the entries are
+// cleared for the next call and the selections written: s_exp/s_l[t * k + j], and the
+// shared-gate logit to s_sg[t].  Every wave of the block calls this (one barrier each).
+template <int NPER>
+__device__ __forceinline__ bool topk_mbox(uint64_t* __restrict__ mbox, int E, int k, int T, int t0, int t1,
+                                          bool want_sg, int* s_flag, int* s_exp, double* s_l, double* s_sg) {
+  const int lane = threadIdx.x & 63;
+  const int nt = t1 < T ? 2 : (t0 < T ? 1 : 0);  // wave-uniform
+  const int tok[2] = {t0, t1};
+  uint64_t raw[2][NPER], sgr[2] = {1ull, 1ull};
+  bool missing = false;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t < nt) {
+      const uint64_t* row = mbox + (size_t)tok[t] * (E + 1);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = lane + 64 * i;
+        raw[t][i] = __hip_atomic_load(row + min(e, E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        missing |= e < E && raw[t][i] == 0ull;
+      }
+      if (want_sg && lane == 0) {
+        sgr[t] = __hip_atomic_load(row + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        missing |= sgr[t] == 0ull;
+      }
+    }
+  }
+  if (__ballot(missing) != 0ull && lane == 0) *s_flag = 1;
+  __syncthreads();
+  if (*s_flag) return false;
+  double lv[2][NPER];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t < nt) {
+      uint64_t* row = mbox + (size_t)tok[t] * (E + 1);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = lane + 64 * i;
+        lv[t][i] = __builtin_bit_cast(double, ~raw[t][i]);
+        if (e < E) __hip_atomic_store(row + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (want_sg && lane == 0) {
+        __hip_atomic_store(row + E, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_sg[tok[t]] = __builtin_bit_cast(double, ~sgr[t]);
+      }
+    }
+  }
+  if (nt == 2) {
+    topk_select<NPER, 2>(lv, E, k, tok, s_exp, s_l);
+  } else if (nt == 1) {
+    double lw[1][NPER];
+    const int tk[1] = {t0};
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) lw[0][i] = lv[0][i];
+    topk_select<NPER, 1>(lw, E, k, tk, s_exp, s_l);
+  }
+  return true;
+}
+
+// Top-k of the tokens a wave takes from the logits in memory (written by other blocks of
+// this kernel and known to be complete).
+template <int NPER>
 __device__ __forceinline__ void topk_wave(const double* __restrict__ logits, int E, int k, int T, int t0, int t1,
                                           int* s_exp, double* s_l) {
   if (t1 < T) {
     const int tok[2] = {t0, t1};
-    topk_tokens<NPER, 2, true, 1, MBOX>(logits, E, k, tok, tok, s_exp, s_l);
+    topk_tokens<NPER, 2, true>(logits, E, k, tok, tok, s_exp, s_l);
   } else if (t0 < T) {
     const int tok[1] = {t0};
-    topk_tokens<NPER, 1, true, 1, MBOX>(logits, E, k, tok, tok, s_exp, s_l);
+    topk_tokens<NPER, 1, true>(logits, E, k, tok, tok, s_exp, s_l);
   }
 }
 
@@ -168,24 +243,6 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
   }
 }
 
-// Bounded wait of block 0 for the arrival flags of blocks 1..n-1 (all blocks of this
-// small grid are resident together, so the flags arrive; the bound only guarantees an
-// exit).  The flags are then cleared for the next call.
-__device__ __forceinline__ void wait_arrivals(uint32_t* __restrict__ flags, int n) {
-  if (threadIdx.x < 64) {
-    for (int base = 1; base < n; base += 64) {
-      const int b = base + (int)threadIdx.x;
-      uint32_t spins = 0;
-      while (true) {
-        const uint32_t f = b < n ? __hip_atomic_load(flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
-        if (__ballot(f == 0u) == 0ull || ++spins > (1u << 24)) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (b < n) __hip_atomic_store(flags + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
 // Routing after top-k (s_exp[p] = the expert of pair p for p < P, s_cnt zeroed): LDS
 // histogram, scan and stable ranks -> counts, offsets, perm, the active list and one slot
 // record per active expert.  Every thread of the block takes part.
@@ -260,9 +317,12 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   }
 }
 
-// MBOX (T (E+1) <= kDecMailboxWords): the logits go through the mailbox in the
-// workspace header and block 0 polls them directly (no arrival flags, one round trip
-// fewer); otherwise through w.logits and the arrival flags.
+// MBOX (T (E+1) <= kDecMailboxWords): the logits go through the mailbox in the workspace
+// header as ~bits(l), so a posted entry is its own arrival mark; otherwise through
+// w.logits, each block raising its arrival flag (header word blockIdx) once they have
+// landed.  Either way each block then checks once whether everything has arrived, and a
+// block that sees it all routes (more than one may: they write the same values), clearing
+// the mailbox entries or flags so that the header reads zero again after the call.
 template <int XDT, bool MBOX>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
@@ -276,11 +336,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
   __shared__ double s_part[kRouteThreads / 64][kDecMaxTokens];
+  __shared__ double s_sg[kDecMaxTokens];  // shared-gate logits read from the mailbox
+  __shared__ int s_flag;                // something this block needs has not arrived
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int kWaves = kRouteThreads / 64;
   const int E = L.E, k = L.k, H = L.H;
   const int nb = E + 1;
 
+  if (tid == 0) s_flag = 0;
   if (blockIdx.x == 0) {
     for (int i = tid; i < ntickets; i += kRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
     // the o mailbox of the one-token combine (nzero_o words, 0 = not posted)
@@ -302,27 +365,23 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
   const void* xr = x;  // the router's activations (XDT 2: the block's LDS copy of the rescale)
   if constexpr (XDT == 2) {
-    __shared__ float s_d[kDecSplitRouteT];  // each token's 1 / sqrt(mean(y^2) + eps)
+    __shared__ double s_d[kDecSplitRouteT];  // each token's sqrt(mean(y^2) + eps)
     __shared__ __align__(16) uint16_t s_x[kRmsFoldElems];
-    // With the rescale kernel's exact arithmetic: thread i of a 256-thread group sums
-    // y[n]^2 for n = i, i + 256, ... (fmaf in that order), its 4 wave sums are added in
-    // wave order and divided by H, and the scale is 1 / sqrt(that + eps).  Group g of the
-    // block's four takes tokens g, g + 4.
-    __shared__ float s_ms[kDecSplitRouteT][4];
+    // With the rescale kernel's exact arithmetic (rms_partial over 256 threads, the 4 wave
+    // sums in wave order, rms_divisor, rms_apply).  Group g of the block's four 256-thread
+    // groups takes tokens g, g + 4.
+    __shared__ double s_ms[kDecSplitRouteT][4];
     const int grp = wave >> 2, i = tid & 255;
     for (int t = grp; t < T; t += kWaves / 4) {
-      const float* yt = (const float*)x + (size_t)t * H;
-      float sq = 0.f;
-      for (int n = i; n < H; n += 256) sq = fmaf(yt[n], yt[n], sq);
-      sq = wave_sum_f32(sq);
+      const double sq = wave_sum_f64(rms_partial((const float*)x + (size_t)t * H, H, i));
       if (lane == 0) s_ms[t][wave & 3] = sq;
     }
     __syncthreads();
-    if (tid < T) s_d[tid] = 1.0f / sqrtf((s_ms[tid][0] + s_ms[tid][1] + s_ms[tid][2] + s_ms[tid][3]) / (float)H + eps);
+    if (tid < T) s_d[tid] = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
     __syncthreads();
     // the rescaled rows once per block into LDS (block 0 also writes them for the projections)
     for (int idx = tid; idx < T * H; idx += kRouteThreads) {
-      const uint16_t v = (uint16_t)f32_to_bf16_rne(((const float*)x)[idx] * s_d[idx / H]);
+      const uint16_t v = rms_apply(((const float*)x)[idx], s_d[idx / H]);
       s_x[idx] = v;
       if (blockIdx.x == 0) w.xr[idx] = v;
     }
@@ -358,38 +417,54 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       }
     }
   }
-  if (MBOX) {
-    if (blockIdx.x != 0) return;
-  } else {
-    // arrival: this block's logits are written through and complete before its flag
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (blockIdx.x != 0) {
-      if (tid == 0) __hip_atomic_store(rr_flags + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
+  // This block's posts have landed (acknowledged) before any of its checks is issued, so the
+  // block whose check comes last sees every post.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (!MBOX) {
+    if (wave == 0) {
+      if (lane == 0) __hip_atomic_store(rr_flags + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      bool missing = false;
+      for (int b = lane; b < (int)gridDim.x; b += 64)
+        missing |= __hip_atomic_load(rr_flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+      if (__ballot(missing) != 0ull && lane == 0) s_flag = 1;
     }
-    wait_arrivals(rr_flags, gridDim.x);
+    __syncthreads();
+    if (s_flag) return;
+    for (int b = tid; b < (int)gridDim.x; b += kRouteThreads)
+      __hip_atomic_store(rr_flags + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // thread e's expert pointers for the slot records: issued now, used at the end
   const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
   const uint8_t* const my_gu = L.gate_up[ie];
   const uint8_t* const my_dn = L.down[ie];
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
   const int Pr = T * k;
-  const int P = Pr + (L.has_shared ? T : 0);
-  const double* logits = MBOX ? (const double*)w.rr_mbox : w.logits;
+  const bool want_sg = L.has_shared && L.shared_gate_w;
   // top-k: wave w takes tokens w and w + 16 (T <= 32), side by side
   {
     const int t0 = wave, t1 = wave + kWaves;
     const int nper = (E + 63) >> 6;
-    if (nper <= 1) topk_wave<1, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 2) topk_wave<2, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 4) topk_wave<4, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else if (nper <= 8) topk_wave<8, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
-    else topk_wave<16, MBOX>(logits, E, k, T, t0, t1, s_exp, s_l);
+    if (MBOX) {
+      bool ok;
+      if (nper <= 1) ok = topk_mbox<1>(w.rr_mbox, E, k, T, t0, t1, want_sg, &s_flag, s_exp, s_l, s_sg);
+      else if (nper <= 2) ok = topk_mbox<2>(w.rr_mbox, E, k, T, t0, t1, want_sg, &s_flag, s_exp, s_l, s_sg);
+      else if (nper <= 4) ok = topk_mbox<4>(w.rr_mbox, E, k, T, t0, t1, want_sg, &s_flag, s_exp, s_l, s_sg);
+      else if (nper <= 8) ok = topk_mbox<8>(w.rr_mbox, E, k, T, t0, t1, want_sg, &s_flag, s_exp, s_l, s_sg);
+      else ok = topk_mbox<16>(w.rr_mbox, E, k, T, t0, t1, want_sg, &s_flag, s_exp, s_l, s_sg);
+      if (!ok) return;  // block-uniform: a later block routes
+    } else {
+      if (nper <= 1) topk_wave<1>(w.logits, E, k, T, t0, t1, s_exp, s_l);
+      else if (nper <= 2) topk_wave<2>(w.logits, E, k, T, t0, t1, s_exp, s_l);
+      else if (nper <= 4) topk_wave<4>(w.logits, E, k, T, t0, t1, s_exp, s_l);
+      else if (nper <= 8) topk_wave<8>(w.logits, E, k, T, t0, t1, s_exp, s_l);
+      else topk_wave<16>(w.logits, E, k, T, t0, t1, s_exp, s_l);
+    }
     for (int t = t0; t < T && t <= t1; t += kWaves) {
       const double l0 = s_l[t * k];
       const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
@@ -405,21 +480,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       }
       if (L.has_shared && lane == 0) {
         double sg = 1.0;
-        if (L.shared_gate_w) {
-          double ls;
-          if (MBOX) {  // poll the posted shared-gate logit (bounded), then clear it
-            uint64_t* src = w.rr_mbox + (size_t)t * (E + 1) + E;
-            uint64_t raw = 0;
-            for (uint32_t spins = 0; spins <= (1u << 22); ++spins) {
-              raw = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if (raw != 0ull) break;
-              __builtin_amdgcn_s_sleep(1);
-            }
-            __hip_atomic_store(src, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ls = __builtin_bit_cast(double, ~raw);
-          } else {
-            ls = __hip_atomic_load(logits + (size_t)t * (E + 1) + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+        if (want_sg) {
+          const double ls = MBOX ? s_sg[t]
+                                 : __hip_atomic_load(w.logits + (size_t)t * (E + 1) + E, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
           sg = 1.0 / (1.0 + exp(-ls));
         }
         w.pair_w[Pr + t] = (float)sg;
@@ -622,7 +686,7 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds) {
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr),
                "v"((const __attribute__((address_space(1))) void*)gptr)
-               : "memory");
+               : "memory", "m0");
 }
 
 template <int NP, bool BY_TOKEN>
@@ -863,34 +927,32 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
       for (int q = 0; q < 4; ++q) v[4 * tt + q] = acc[tt][q];
     reduce4<4 * NTT>(v, (float*)(smem + 1024));
     if constexpr (OMB) {
-      // One token (one pair per slot, one pass): the block of the last active slot sums
-      // the column tile over all pairs in the fixed order, reading the other slots' o
-      // from the mailbox; the others only post theirs.  The launch admits this only when
-      // the whole grid is resident at once, so the posts it waits for always come.
+      // One token (one pair per slot, one pass): every slot's block posts its 16 o values to
+      // the mailbox (zeroed by the router kernel) and, once they have landed, reads the
+      // other pairs' entries once; a block that finds them all sums the column tile over
+      // the pairs in the fixed order and writes y (more than one may: the same values).
+      // The block whose read comes last finds them all.
       if (wave == 0 && g == 0) {
         const int col = 16 * blockIdx.x + n;
         const int p_own = w.perm[off];
         uint32_t* omb = reinterpret_cast<uint32_t*>(w.o);
-        if ((int)blockIdx.y != n_active - 1) {
-          __hip_atomic_store(&omb[(size_t)p_own * H + col], omb_encode(v[0]), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
-          const float rv = w.resid ? w.resid[col] : 0.f;  // loaded before the wait
-          uint32_t e[kMaxPairsT1];
-          for (uint32_t spins = 0; spins <= (1u << 22); ++spins) {
-            bool miss = false;
+        const uint32_t mine = omb_encode(v[0]);
+        const float rv = w.resid ? w.resid[col] : 0.f;
+        __hip_atomic_store(&omb[(size_t)p_own * H + col], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
+        uint32_t e[kMaxPairsT1];
+        bool miss = false;
 #pragma unroll
-            for (int u = 0; u < kMaxPairsT1; ++u) {
-              const int p = min(u, P1 - 1);
-              e[u] = p == p_own ? omb_encode(v[0])
-                                : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-              miss |= e[u] == 0u;
-            }
-            if (!miss) break;
-            __builtin_amdgcn_s_sleep(1);
-          }
+        for (int u = 0; u < kMaxPairsT1; ++u) {
+          const int p = min(u, P1 - 1);
+          e[u] = p == p_own ? mine
+                            : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          miss |= e[u] == 0u;
+        }
+        if (!miss) {
           float sum = 0.f;
 #pragma unroll
           for (int u = 0; u < kMaxPairsT1; ++u)
@@ -1075,44 +1137,9 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
               s, L, T, w, y, tickets, xrows);
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
-template <int FMT, int KSW>
-static bool down_grid_resident(const LayerArgs& L, int nslots, size_t lds) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_dec_down<FMT, 1, KSW, true>, 256, lds) !=
-      hipSuccess)
-    return false;
-  return (long)(L.H / 16) * nslots <= (long)device_cus() * per_cu;
-}
-
-// The one-token mailbox combine of the split-K down kernel: one token, long down rows,
-// and a grid that is resident at once (so the block that waits never waits for a block
-// that has not started).
-template <int FMT>
-static bool use_down_mailbox(const LayerArgs& L, int T) {
-  if (T != 1 || (L.I / 32 + 3) / 4 <= 4) return false;
-  const int nslots = min(L.k, L.E) + (L.has_shared ? 1 : 0);
-  const size_t lds = dec_lds_bytes(L.I, 2, 1, 1);  // one token: one staged row
-  switch (pick_ksw(L.I)) {
-    case 1: return down_grid_resident<FMT, 1>(L, nslots, lds);
-    case 2: return down_grid_resident<FMT, 2>(L, nslots, lds);
-    case 4: return down_grid_resident<FMT, 4>(L, nslots, lds);
-    case 6: return down_grid_resident<FMT, 6>(L, nslots, lds);
-    default: return down_grid_resident<FMT, 8>(L, nslots, lds);
-  }
-}
+// The one-token mailbox combine of the split-K down kernel: one token and long down rows
+// (no block waits for another, so any grid size works).
+static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I / 32 + 3) / 4 > 4; }
 
 // Rows of activations a projection block stages per pass: as many of the expert's
 // pairs as fit in kDecStageBytes of LDS (at least 1, at most T), so that several blocks
@@ -1198,7 +1225,7 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
   const int ntickets = L.H / 16;
   const int max_slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const bool omb = L.wfmt == 1 ? use_down_mailbox<1>(L, T) : use_down_mailbox<2>(L, T);
+  const bool omb = use_down_mailbox(L, T);
   const int nzero_o = omb ? (L.k + (L.has_shared ? 1 : 0)) * L.H : 0;  // T == 1
   // x_dtype 2: x is the previous layer's fp32 y, and the layer takes its bf16 RMS rescale
   // in w.xr.  Below the split, when the rows fit the router block's LDS copy, the router

@@ -43,20 +43,54 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   }
 }
 
-// x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y^2 + eps)); one block per token.
+// x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y^2 + eps)); one block of 256 threads per
+// token.  The sum of squares, the mean, the square root and the quotient are fp64 (the
+// quotient correctly rounded), then rounded once to bf16.
 __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y, int H, float eps,
                                                      uint16_t* __restrict__ out) {
-  __shared__ float part[4];
+  __shared__ double part[4];
   const int t = blockIdx.x;
   const float* yt = y + (size_t)t * H;
-  float s = 0.f;
-  for (int n = threadIdx.x; n < H; n += 256) s = fmaf(yt[n], yt[n], s);
-  s = wave_sum_f32(s);
+  const double s = wave_sum_f64(rms_partial(yt, H, threadIdx.x));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
-  // scaled by the rounded reciprocal of the divisor (within one bf16 step of the quotient)
-  const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)H + eps);
-  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(yt[n] * inv);
+  const double d = rms_divisor(part[0], part[1], part[2], part[3], H, eps);
+  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = rms_apply(yt[n], d);
+}
+
+// Streaming-read probe: every lane reads 16-byte chunks, grid-stride, with nontemporal
+// loads, and each block writes the xor of what it read (so the loads are not dropped).
+// It measures the HBM read bandwidth a plain stream achieves, the reference point the
+// layer's kernels are compared with besides the specification's peak.
+__global__ __launch_bounds__(256) void k_read_probe(const u32x4_t* __restrict__ src, size_t n16,
+                                                    uint32_t* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(src + i));
+    const u32x4_t b = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(src + i + stride));
+    const u32x4_t c =
+        __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(src + i + 2 * stride));
+    const u32x4_t d =
+        __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(src + i + 3 * stride));
+    acc ^= (a[0] ^ a[1] ^ a[2] ^ a[3]) ^ (b[0] ^ b[1] ^ b[2] ^ b[3]) ^ (c[0] ^ c[1] ^ c[2] ^ c[3]) ^
+           (d[0] ^ d[1] ^ d[2] ^ d[3]);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t a = src[i];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  __shared__ uint32_t part[4];
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(256), 0, s, (const u32x4_t*)buf, bytes / 16, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,

@@ -143,7 +143,7 @@ __host__ __device__ constexpr int pf_loads_per_step() {
 __device__ __forceinline__ void pf_load_lds_16(gbyte_t* gptr, void* lds) {
   const uint32_t lds_addr =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr) : "memory", "m0");
 }
 
 // Loads of k-step ks (clamped to the last step: such registers are never used).  A block

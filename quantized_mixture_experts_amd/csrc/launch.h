@@ -62,5 +62,6 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,
                           float* out, hipStream_t s);
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* out, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
 
 }  // namespace moeq

@@ -75,3 +75,31 @@ def check_forward(layer, x, x_dtype, y_gpu, dbg, ref=None, tokens=None, what="")
         alt = oracle.moe_forward(layer, x[sel], x_dtype, ids=ids_gpu[sel], gates=gates_gpu[sel].astype(np.float64))
         yr[excused] = alt["y"][excused]
     return assert_y_close(yg, yr, what), len(excused)
+
+
+MIDPOINT_REL = 2.0 ** -40
+
+
+def bf16_near_midpoint(q: np.ndarray, rel: float = MIDPOINT_REL) -> np.ndarray:
+    """True where the fp64 value q lies within rel * |q| of a point midway between two
+    adjacent bfloat16 values: there the rounding direction depends on the last bits of
+    the fp64 evaluation (its summation order), not on the definition."""
+    q = np.asarray(q, dtype=np.float64)
+    m, _ = np.frexp(q)                    # q = m * 2^e, 0.5 <= |m| < 1
+    scaled = np.abs(m) * 256.0            # bf16 keeps 8 significant bits
+    frac = scaled - np.floor(scaled)
+    return np.abs(frac - 0.5) <= rel * scaled
+
+
+def assert_rescale_exact(got_bits: np.ndarray, y: np.ndarray, what: str = "") -> int:
+    """The GPU's bf16 RMS rescale of y equals the oracle's bit for bit, except where the
+    oracle's fp64 quotient sits within 2^-40 of a bf16 rounding midpoint (there the
+    two may round apart by one step).  Returns the number of excused elements."""
+    y = np.asarray(y, dtype=np.float64)
+    want = oracle.rms_rescale(y).astype(np.int32)
+    got = np.asarray(got_bits).view(np.uint16).astype(np.int32)
+    near = bf16_near_midpoint(oracle.rms_quotient(y))
+    diff = got != want
+    bad = diff & ~(near & (np.abs(got - want) <= 1))
+    assert not bad.any(), f"{what}: {int(bad.sum())} rescaled values differ from the oracle's"
+    return int(near.sum())

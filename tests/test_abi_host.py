@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import quantized_mixture_experts_amd as q
@@ -155,3 +156,62 @@ def test_workspace_covers_header_and_fp8_planes(L):
     need = ws_bytes(L, lay, T)
     assert need >= 18432 + (3 * T * 128 + T) + (3 * P * 256 + P)
     assert ws_bytes(L, layer(), 1) >= 18432
+
+
+# ---------------------------------------------------------------------------
+# The header's storage definition, followed literally, gives the bytes the generator and
+# the test encoder write (so a caller packing by the header feeds the kernels correctly).
+# ---------------------------------------------------------------------------
+HEADER_FORMULAS = [
+    "start at byte t*8*K + 1024*s + (16*g + m)*16",
+    "entry t*16*nkb + 64*s + i of the plane",
+    "MXFP4: i = 16*g + m, entries are bytes (byte S + entry)",
+    "CB4:   i = m*r + g, entries are little-endian fp16 (bytes S + 2*entry, +1)",
+    "scale plane at byte S = round_up(N*K/2, 256)",
+]
+
+
+def _pack_by_header(wfmt, codes, scales):
+    """Element by element, as include/moeq.h states the layout."""
+    N, K = codes.shape
+    nkb = K // 32
+    S = (N * K // 2 + 255) // 256 * 256
+    out = bytearray(S + N * nkb * (1 if wfmt == q.WFMT_MXFP4 else 2))
+    for row in range(N):
+        t, m = row // 16, row % 16
+        for b in range(nkb):
+            s, g = b // 4, b % 4
+            r = min(4, nkb - 4 * s)
+            base = t * 8 * K + 1024 * s + (16 * g + m) * 16
+            for j in range(16):   # byte j: element 2j low nibble, 2j+1 high nibble
+                out[base + j] = int(codes[row, 32 * b + 2 * j]) | (int(codes[row, 32 * b + 2 * j + 1]) << 4)
+            i = 16 * g + m if wfmt == q.WFMT_MXFP4 else m * r + g
+            entry = t * 16 * nkb + 64 * s + i
+            v = int(scales[row, b])
+            if wfmt == q.WFMT_MXFP4:
+                out[S + entry] = v
+            else:
+                out[S + 2 * entry], out[S + 2 * entry + 1] = v & 0xFF, v >> 8
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("wfmt", [q.WFMT_MXFP4, q.WFMT_CB4])
+@pytest.mark.parametrize("N,K", [(16, 32), (32, 160), (48, 256)])
+def test_header_layout_matches_encoders(wfmt, N, K):
+    import numpy as np_
+    import packing
+    import synth
+    text = " ".join(open(HEADER).read().split())
+    for f in HEADER_FORMULAS:
+        assert " ".join(f.split()) in text, f"header no longer states: {f}"
+    rng = np_.random.default_rng(N + K + wfmt)
+    codes = rng.integers(0, 16, (N, K), dtype=np_.uint8)
+    if wfmt == q.WFMT_MXFP4:
+        scales = rng.integers(118, 125, (N, K // 32)).astype(np_.uint8)
+    else:
+        scales = rng.uniform(0.01, 0.05, (N, K // 32)).astype(np_.float16).view(np_.uint16)
+    got = _pack_by_header(wfmt, codes, scales)
+    assert got.size == q.packed_bytes(wfmt, N, K)
+    assert np_.array_equal(got, packing.pack(wfmt, codes, scales))
+    code_rows = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np_.uint8)
+    assert np_.array_equal(got, synth.to_tile_major(code_rows, scales, wfmt))

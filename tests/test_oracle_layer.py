@@ -220,3 +220,23 @@ def test_rms_rescale_closed_forms():
     out = oracle.rms_rescale(np.array([[3.0, 4.0]]), eps=0.0)
     want = synth.f32_to_bf16_bits(np.array([3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], dtype=np.float32))
     assert np.array_equal(out[0], want)
+    # eps is added to the mean, inside the square root: a row of c with c^2 == eps gives
+    # c / sqrt(2 c^2) = 1/sqrt(2) = 0.70710..., whose nearest bf16 is 0x3F35 (0.70703125)
+    c = np.sqrt(oracle.RMS_EPS)
+    assert np.all(oracle.rms_rescale(np.full((1, 64), c)) == 0x3F35)
+    # a half-way case: 1 + 2^-8 lies midway between bf16 1.0 and 1.0078125 and rounds to even
+    q = oracle.rms_quotient(np.array([[1.0 + 2.0 ** -8, 1.0 - 2.0 ** -8]]), eps=0.0)
+    assert abs(q[0, 0] - (1.0 + 2.0 ** -8) / np.sqrt(1.0 + 2.0 ** -16)) < 1e-15
+
+
+def test_forward_expert_map_on_threads_gives_the_same_values():
+    """The per-expert products are independent: evaluating them on a thread pool gives
+    the values of the one-after-another evaluation, bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+    spec = synth.small_spec("map", 9, 128, 64, 8, 3, synth.WFMT_CB4, has_shared=1, bias="normal")
+    layer = synth.make_layer(spec, shared_gate=True)
+    x = synth.make_x(spec)
+    r1 = oracle.moe_forward(layer, x, spec.x_dtype)
+    with ThreadPoolExecutor(4) as ex:
+        r2 = oracle.moe_forward(layer, x, spec.x_dtype, map_fn=ex.map)
+    assert np.array_equal(r1["y"], r2["y"]) and np.array_equal(r1["o"], r2["o"])
