@@ -125,8 +125,8 @@ class Workload:
         self.ys = [torch.empty((T, H), dtype=torch.float32, device=self.dev)
                    for _ in range(self.nl if self.stacked else 1)]
 
-    def graph_count(self):
-        """Graphs to capture: one whole step (stacked) or one per layer instance."""
+    def rotation(self):
+        """Steps after which the inputs repeat: one (stacked) or one per layer instance."""
         return 1 if self.stacked else self.nl
 
     def _chain(self, s, fn, fn_rms):
@@ -163,7 +163,7 @@ class Workload:
         """Distinct routed experts of every forward of one rotation (for the byte counts)."""
         import numpy as np
         out = []
-        for s in range(self.graph_count()):
+        for s in range(self.rotation()):
             def fn(l, x, y):
                 _, dbg = self.q.forward(self.layers[l], x, self.spec.x_dtype, y=y, ws=self.ws, debug=True)
                 out.append(len(np.unique(dbg["ids"].cpu().numpy())))
@@ -204,28 +204,34 @@ def measure(args, wl, T, probe_gbs):
     fwd_flops = 2 * T * E * H + P * 6 * H * I
 
     K, W = args.steps, args.warmup
-    ng = wl.graph_count()
     for s in range(W):
         wl.step(s)
     torch.cuda.synchronize()
-    graphs = []
-    for s in range(ng):
+    # one graph per chunk of steps: the stacked config's step is 108 kernels (a graph per
+    # step); single-layer steps are a few kernels, so a graph holds the whole rotation over
+    # the layer instances (plus a graph of the remaining steps, so exactly K steps run)
+    per = 1 if wl.stacked else wl.nl
+    chunks = [per] * (K // per) + ([K % per] if K % per else [])
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            wl.step(s)
-        graphs.append(g)
-    for s in range(max(W, ng)):
-        graphs[s % ng].replay()
+            for s in range(n):
+                wl.step(s)
+        return g
+    graphs = {n: capture(n) for n in sorted(set(chunks))}
+    for _ in range(max(1, W // per)):
+        graphs[per].replay()
     torch.cuda.synchronize()
-    # ---- the timed region: K graph-replayed steps, an event between consecutive steps ----
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    # ---- the timed region: K graph-replayed steps, an event between consecutive chunks ----
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(chunks) + 1)]
     evs[0].record()
-    for s in range(K):
-        graphs[s % ng].replay()
-        evs[s + 1].record()
+    for i, n in enumerate(chunks):
+        graphs[n].replay()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    total_ms = evs[0].elapsed_time(evs[K])
-    step_ms = [evs[s].elapsed_time(evs[s + 1]) for s in range(K)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) / n for i, n in enumerate(chunks)]
     ms_per_step = total_ms / K
     del graphs
 
@@ -409,8 +415,10 @@ def main():
             "layer_instances": wl.nl,
             "global_batch": main_run["T"],
         },
-        "timing": "HIP-graph replay of whole steps, an event between consecutive steps; kernel durations "
-                  "from an eager pass of the same steps with dispatch-stamped events",
+        "timing": "HIP-graph replay of whole steps (stacked: one graph per step; single layers: one graph "
+                  "per rotation over the layer instances), an event between consecutive graphs; p10/p50/p90 "
+                  "over graphs; kernel durations from an eager pass of the same steps with dispatch-stamped "
+                  "events",
     }
     for key in ("step_ms_p10_p50_p90", "eager_ms_per_step", "moe_kernels_ms_per_step", "moe_us_per_token",
                 "hbm_gbs", "tflops", "algorithmic_bytes_per_step", "distinct_experts_per_forward", "stage_us",
