@@ -66,7 +66,8 @@
  *   - A launch failure returns MOE_ERR_HIP; faults during execution surface at
  *     the caller's next synchronisation, as with any stream API.
  *   - No C++ exception crosses the ABI and nothing is printed.  The library is
- *     reentrant: it keeps no state between calls besides the caller's workspace.
+ *     reentrant: it keeps no state between calls besides the caller's workspace
+ *     (and, for moe_forward_noalloc, its per-device scratch array and its address).
  *   - Calls that share a workspace must not overlap in time (same stream, or
  *     ordered by events).
  *   - No GPU block ever waits for another block: where a kernel needs results of
@@ -152,6 +153,25 @@ int moe_bucket(const moe_layer *L, const int32_t *topk_ids, int32_t T, int32_t *
 int moe_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *y,
                 void *ws, size_t ws_bytes, void *stream, int32_t path, int32_t *dbg_ids,
                 float *dbg_w, int32_t *dbg_counts, int32_t *dbg_offsets, int32_t *dbg_perm);
+
+/* Bytes of the scratch array moe_forward_noalloc uses on each device (32 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* moe_forward for callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * the same y bits, with the workspace taken from a scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on (from the
+ * device's first call until the process ends).  Calls nothing that allocates.
+ * Arguments and errors as for moe_forward (no debug outputs), plus MOE_ERR_WORKSPACE
+ * when moe_workspace_bytes(L, T) exceeds MOE_NOALLOC_SCRATCH_BYTES (decode batches of
+ * every shape here fit; prefill chunks of a few hundred tokens do) and MOE_ERR_HIP when
+ * the scratch's address cannot be obtained.  The first call on a device also enqueues a
+ * clear of the scratch's synchronisation header on `stream`.
+ * All calls on one device share the one array: calls that overlap in time on the same
+ * device (different streams, threads or processes sharing the device's code object)
+ * race and give undefined results; serialise them (one stream, or events). */
+int moe_forward_noalloc(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *y, void *stream,
+                        int32_t path);
 
 /* Stages of one forward call, for moe_forward_timed. */
 typedef enum {

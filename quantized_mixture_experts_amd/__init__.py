@@ -24,7 +24,7 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 EXPORTED = ["moe_packed_bytes", "moe_workspace_bytes", "moe_router_topk", "moe_bucket", "moe_forward",
             "moe_forward_timed", "moe_dequant", "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe",
-            "moe_status_str"]
+            "moe_forward_noalloc", "moe_status_str"]
 STAGES = ["router", "topk", "bucket", "gateup", "down", "combine", "xquant"]
 
 
@@ -63,9 +63,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_rms.argtypes = [ctypes.POINTER(MoeLayerC), vp, ctypes.c_float, i32, i32, vp, vp, sz, vp, i32,
                                       vp]
         L.moe_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
+        L.moe_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerC), vp, i32, i32, vp, vp, i32]
         L.moe_status_str.argtypes, L.moe_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         for f in ["moe_router_topk", "moe_bucket", "moe_forward", "moe_forward_timed", "moe_dequant",
-                  "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe"]:
+                  "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe", "moe_forward_noalloc"]:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,6 +201,17 @@ def forward(L: DeviceLayer, x, x_dtype: int, y=None, ws=None, path: int = PATH_A
     if debug:
         dbg["perm"] = dbg["perm"][:T * L.top_k + T * L.has_shared]
         return y, dbg
+    return y
+
+
+def forward_noalloc(L: DeviceLayer, x, x_dtype: int, y=None, path: int = PATH_AUTO, stream=None):
+    """moe_forward_noalloc: y [T][H] fp32, with the library's per-device scratch array as the
+    workspace (no workspace argument; nothing is allocated by the library)."""
+    import torch
+    T = x.shape[0]
+    y = torch.empty((T, L.hidden), dtype=torch.float32, device=x.device) if y is None else y
+    _check(lib().moe_forward_noalloc(ctypes.byref(L.c), x.data_ptr(), x_dtype, T, y.data_ptr(), _stream(stream),
+                                     path), "moe_forward_noalloc")
     return y
 
 

@@ -3,6 +3,7 @@
 // HIP API, so the error paths can be exercised without a GPU.
 #include <stddef.h>
 #include <algorithm>
+#include <atomic>
 #include <stdint.h>
 
 #include "../../include/moeq.h"
@@ -177,6 +178,45 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
   return hip_status(e);
 }
 
+// ---- scratch of moe_forward_noalloc -------------------------------------------------
+// The workspace of the no-allocation entry point: one array per device the library runs
+// on, zero-filled when the code object is loaded and held until the process ends.  Host
+// code never uses the array's name as an address (on the host it only names the symbol):
+// the device address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device below.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Clears the scratch's synchronisation header (a kernel, not a memset, so that a caller
+// may capture the first call in a graph).
+__global__ void k_clear_words(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address (set up on the device's first call: the symbol's
+// address and a clear of the header on `s`); nullptr on a HIP error.
+void* device_scratch(hipStream_t s, hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !ptr) return nullptr;
+  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(ptr),
+                     (int)(kHeaderBytes / 4));
+  *err = hipGetLastError();
+  if (*err != hipSuccess) return nullptr;
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +271,22 @@ int moe_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, f
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   return forward_impl(L, x, x_dtype, T, y, ws, ws_bytes, stream, path, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                       dbg_perm, moeq::Timing());
+}
+
+int moe_forward_noalloc(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* stream,
+                        int32_t path) {
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  int st = validate_layer(L);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (layout_for(L, T).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* ws = device_scratch(static_cast<hipStream_t>(stream), &e);
+  if (!ws) return MOE_ERR_HIP;
+  return forward_impl(L, x, x_dtype, T, y, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, path, nullptr, nullptr, nullptr,
+                      nullptr, nullptr, moeq::Timing());
 }
 
 int moe_forward_timed(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y, void* ws,

@@ -215,3 +215,13 @@ def test_header_layout_matches_encoders(wfmt, N, K):
     assert np_.array_equal(got, packing.pack(wfmt, codes, scales))
     code_rows = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np_.uint8)
     assert np_.array_equal(got, synth.to_tile_major(code_rows, scales, wfmt))
+
+
+def test_noalloc_validates_before_touching_the_gpu(L):
+    """moe_forward_noalloc checks its arguments and the scratch size on the host first."""
+    lay = layer(hidden=2880, inter=2880, n_experts=128, top_k=4, wfmt=q.WFMT_MXFP4, codebook=None)
+    assert ws_bytes(L, lay, 1024) > 32 << 20
+    assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, q.DT_BF16, 1024, FAKE, None, 0) == q.MOE_ERR_WORKSPACE
+    assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, 7, 1, FAKE, None, 0) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, q.DT_BF16, -1, FAKE, None, 0) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, q.DT_BF16, 0, None, None, 0) == q.MOE_OK
