@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--path", choices=["auto", "decode", "prefill"], default="auto",
                     help="kernel path (auto: decode kernels for small batches)")
     ap.add_argument("--layers", type=int, default=None, help="distinct layer instances in the rotation")
+    ap.add_argument("--packed-scales", action="store_true",
+                    help="MXFP4 workloads: the same experts in the packed scale store (a base E8M0 byte per row "
+                         "and a 4-bit delta per block)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget (wall)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -359,6 +362,8 @@ def main():
     q.lib()
     dev = torch.device("cuda:0")
     spec = synth.CONFIGS[args.config]
+    if args.packed_scales:
+        spec = synth.with_packed_scales(spec)
     probe_gbs = None if (args.no_probe or args.counters) else hbm_probe(args, dev)
     wl = Workload(args, spec, dev)
     stacked = spec.n_layers > 1
@@ -391,7 +396,8 @@ def main():
         runs.append(r)
     main_run = runs[0]
 
-    fmt = "MXFP4" if spec.weights.wfmt == synth.WFMT_MXFP4 else "4-bit codebook"
+    fmt = {synth.WFMT_MXFP4: "MXFP4", synth.WFMT_CB4: "4-bit codebook",
+           synth.WFMT_MXFP4_PS: "MXFP4 (packed scale store)"}[spec.weights.wfmt]
     H, I, E, k, sh = spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared
     workload = (f"{args.config}: {spec.name}, T={main_run['T']}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
                 f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers (RMS rescale between)"

@@ -50,6 +50,14 @@
  *   CB4: code = index into a 16-entry int8 codebook, scale = IEEE fp16 bits,
  *     element = fp16 * codebook[index]; 18 bytes per 32 values (NInfer page,
  *     n-gram table paragraph: 1,440 bytes for 16 rows of 160 IQ4_NL values).
+ *   MXFP4_PS (the packed scale store of "How Neural runs a 120-billion-parameter model
+ *     on one gaming PC", section "What it runs on and what it runs": 12,839,040 bytes per
+ *     gpt-oss-120B expert, code bytes kept and scale rows re-encoded, with bit-identical
+ *     outputs): the MXFP4 code plane, then at byte S the N row bases (byte S + row) and
+ *     then N*nkb/2 bytes of 4-bit deltas: the delta of the block whose MXFP4 scale is
+ *     entry i of the scale plane is nibble i, byte S + N + i/2, low nibble for even i.
+ *     The block's E8M0 byte is base(row) + delta; everything else is MXFP4.
+ *     moe_packed_bytes gives S + N + N*nkb/2.
  *   Expert e's gate_up matrix is [2I][H] (rows 0..I-1 gate, I..2I-1 up); its
  *   down matrix is [H][I].
  *
@@ -95,7 +103,7 @@ typedef enum {
   MOE_ERR_HIP = -5           /* a HIP launch failed */
 } moe_status;
 
-typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2 } moe_wfmt;
+typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2, MOE_WFMT_MXFP4_PS = 3 } moe_wfmt;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Path selection for moe_forward: AUTO picks the decode kernels for small batches
@@ -116,7 +124,7 @@ typedef struct {
   const float *router_b;       /* [E] fp32, or NULL */
   const void *const *gate_up;  /* device array of E+has_shared device pointers -> packed [2I][H] */
   const void *const *down;     /* device array of E+has_shared device pointers -> packed [H][I] */
-  const int8_t *codebook;      /* CB4: [16] int8; MXFP4: must be NULL */
+  const int8_t *codebook;      /* CB4: [16] int8; MXFP4 and MXFP4_PS: must be NULL */
   const float *shared_gate_w;  /* [H] fp32, or NULL (shared weight 1); ignored without a shared expert */
 } moe_layer;
 
@@ -197,7 +205,7 @@ int moe_forward_timed(const moe_layer *L, const void *x, int32_t x_dtype, int32_
 
 /* Test export: decode one packed matrix (layout above) to fp32 out [rows][cols],
  * bit-exact (every element is exactly representable in fp32 for MXFP4 scales
- * u <= 252 and every finite fp16 scale).  codebook: CB4 [16] int8, NULL for MXFP4.
+ * u <= 252 and every finite fp16 scale).  codebook: CB4 [16] int8, NULL otherwise.
  * Errors: MOE_ERR_INVALID_ARG for an unknown format, rows not a positive multiple of
  * 16, cols not a positive multiple of 32, NULL packed/out, or a CB4 call without a
  * codebook; MOE_ERR_UNSUPPORTED above 2^34 elements; MOE_ERR_ALIGNMENT for packed or

@@ -63,6 +63,7 @@ import numpy as np
 
 WFMT_MXFP4 = 1
 WFMT_CB4 = 2
+WFMT_MXFP4_PS = 3   # MXFP4 codes with the packed scale store (one base byte per row + 4-bit deltas)
 X_F32 = 0
 X_BF16 = 1
 
@@ -108,12 +109,16 @@ def bf16_value(bits):
 
 
 def packed_size(wfmt: int, rows: int, cols: int) -> int:
-    """Bytes of one packed matrix: code plane, padded to 256 bytes, then the scale plane."""
+    """Bytes of one packed matrix: code plane, padded to 256 bytes, then the scale plane
+    (MXFP4: a byte per block; CB4: two bytes per block; packed scale store: a byte per row
+    plus half a byte per block)."""
     if cols % 32 or rows % 16:
         raise ValueError("rows must be a multiple of 16 and cols a multiple of 32")
     code_bytes = rows * cols // 2
     scale_off = (code_bytes + 255) // 256 * 256
     nblocks = rows * cols // 32
+    if wfmt == WFMT_MXFP4_PS:
+        return scale_off + rows + nblocks // 2
     return scale_off + nblocks * (1 if wfmt == WFMT_MXFP4 else 2)
 
 
@@ -136,13 +141,36 @@ def storage_index(wfmt: int, rows: int, cols: int):
     return code_off, scale_idx
 
 
+def packed_scale_store_exponents(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """E8M0 byte of every block [rows][cols/32] of a matrix in the packed scale store.
+
+    The store keeps the MXFP4 code plane and replaces the scale plane by one base byte per
+    row followed by one 4-bit delta per block, each block's E8M0 byte being base + delta
+    ("How Neural runs a 120-billion-parameter model on one gaming PC", section "What it
+    runs on and what it runs": 12,839,040 bytes per expert in the packed-scale store
+    against 13,219,200 raw; section "Correctness": the packed store re-encodes the scale
+    rows and outputs are bit-identical).  The page gives the byte count and the identity;
+    the placement is this reading's: at the raw store's scale-plane offset S, the bases
+    as N bytes in row order, then the deltas, one nibble per block, at nibble index equal
+    to the block's index in the raw MXFP4 scale plane (storage_index), byte S + N + i // 2,
+    low nibble for even i."""
+    code_bytes = rows * cols // 2
+    S = (code_bytes + 255) // 256 * 256
+    nkb = cols // 32
+    _, idx = storage_index(WFMT_MXFP4, rows, cols)
+    base = packed[S:S + rows].astype(np.int64)
+    dbytes = packed[S + rows:S + rows + rows * nkb // 2].astype(np.int64)
+    delta = np.where(idx % 2 == 0, dbytes[idx // 2] & 0xF, dbytes[idx // 2] >> 4)
+    return base[:, None] + delta
+
+
 def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np.ndarray:
     """Dense fp64 [rows][cols] from one packed matrix (every element exact in fp64)."""
     packed = np.asarray(packed, dtype=np.uint8)
     code_bytes = rows * cols // 2
     scale_off = (code_bytes + 255) // 256 * 256
     nblocks = rows * cols // 32
-    code_off, scale_idx = storage_index(wfmt, rows, cols)
+    code_off, scale_idx = storage_index(WFMT_MXFP4 if wfmt == WFMT_MXFP4_PS else wfmt, rows, cols)
     # the 16 code bytes of every block, in block order: [rows][cols/32][16]
     blk = packed[code_off[:, :, None] + np.arange(16)[None, None, :]].astype(np.int64)
     nib = np.empty((rows, cols // 32, 32), dtype=np.int64)
@@ -150,6 +178,9 @@ def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np
     nib[:, :, 1::2] = blk >> 4    # element 2j+1: high nibble
     if wfmt == WFMT_MXFP4:
         scales = e8m0_value(packed[scale_off:scale_off + nblocks][scale_idx])
+        vals = e2m1_value(nib)
+    elif wfmt == WFMT_MXFP4_PS:
+        scales = e8m0_value(packed_scale_store_exponents(packed, rows, cols))
         vals = e2m1_value(nib)
     elif wfmt == WFMT_CB4:
         sbits = packed[scale_off:scale_off + 2 * nblocks].view("<u2")[scale_idx]

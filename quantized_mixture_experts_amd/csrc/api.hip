@@ -43,11 +43,12 @@ int validate_layer(const moe_layer* L) {
   if (L->hidden % 32 || L->inter % 32) return MOE_ERR_INVALID_ARG;
   if (L->hidden > kMaxDim || L->inter > kMaxDim || L->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (L->top_k > L->n_experts || L->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
-  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_CB4) return MOE_ERR_INVALID_ARG;
+  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_CB4 && L->wfmt != MOE_WFMT_MXFP4_PS)
+    return MOE_ERR_INVALID_ARG;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (!L->router_w || !L->gate_up || !L->down) return MOE_ERR_INVALID_ARG;
   if (L->wfmt == MOE_WFMT_CB4 && !L->codebook) return MOE_ERR_INVALID_ARG;
-  if (L->wfmt == MOE_WFMT_MXFP4 && L->codebook) return MOE_ERR_INVALID_ARG;
+  if (L->wfmt != MOE_WFMT_CB4 && L->codebook) return MOE_ERR_INVALID_ARG;
   if (!aligned16(L->router_w) || (L->router_b && !aligned4(L->router_b))) return MOE_ERR_ALIGNMENT;
   if (L->has_shared && L->shared_gate_w && !aligned16(L->shared_gate_w)) return MOE_ERR_ALIGNMENT;
   if (!aligned16(L->gate_up) || !aligned16(L->down)) return MOE_ERR_ALIGNMENT;
@@ -161,7 +162,7 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
   const LayerArgs a = args_of(L);
   const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype == kRmsInput ? MOE_BF16 : x_dtype);
   if (path == MOE_PATH_DECODE && !dec_ok) return MOE_ERR_UNSUPPORTED;
-  const int32_t auto_max = a.wfmt == MOE_WFMT_MXFP4 ? kAutoDecodeTokensMx : kAutoDecodeTokensCb4;
+  const int32_t auto_max = a.wfmt == MOE_WFMT_CB4 ? kAutoDecodeTokensCb4 : kAutoDecodeTokensMx;
   if (path == MOE_PATH_DECODE || (path == MOE_PATH_AUTO && dec_ok && T <= auto_max))
     return hip_status(moeq::launch_decode(a, x, x_dtype, T, w, y, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                                           dbg_perm, s, tm));
@@ -223,9 +224,10 @@ extern "C" {
 
 size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return 0;
-  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return 0;
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS) return 0;
   const size_t code = (size_t)rows * cols / 2;
   const size_t nblk = (size_t)rows * cols / 32;
+  if (wfmt == MOE_WFMT_MXFP4_PS) return align_up(code, 256) + (size_t)rows + nblk / 2;
   return align_up(code, 256) + nblk * (wfmt == MOE_WFMT_MXFP4 ? 1 : 2);
 }
 
@@ -310,7 +312,7 @@ int moe_forward_rms(const moe_layer* L, const float* y_prev, float eps, int32_t 
 
 int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,
                 void* stream) {
-  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4) return MOE_ERR_INVALID_ARG;
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS) return MOE_ERR_INVALID_ARG;
   if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return MOE_ERR_INVALID_ARG;
   if ((size_t)rows * (size_t)cols > ((size_t)1 << 34)) return MOE_ERR_UNSUPPORTED;
   if (!packed || !out) return MOE_ERR_INVALID_ARG;

@@ -26,21 +26,37 @@ __device__ __forceinline__ gbyte_t* as_global(const void* p) { return (gbyte_t*)
 // round_up(N*K/2, 256); scale unit (t, s) starts at index t*16*nkb + 64s and holds MXFP4
 // (g, m) at 16g + m, CB4 (m, g) at m*r + g (fp16, so 8 contiguous bytes per row and step).
 // Keeping a 16-row step contiguous lets DRAM serve it from one open page.
+// Packed scale store (format 3, MXFP4 codes): the scale plane is replaced, at the same
+// offset S, by N base bytes in row order and then one 4-bit delta per block at the nibble
+// whose index is the block's MXFP4 scale index (low nibble first); a block's E8M0 byte is
+// base(row) + delta.  A tile's deltas start at byte S + N + t*8*nkb.
 struct PackedTile {
   gbyte_t* codes;   // code unit (t, 0)
-  gbyte_t* scales;  // scale unit (t, 0), bytes
+  gbyte_t* scales;  // scale unit (t, 0), bytes (format 3: the tile's first delta byte)
+  gbyte_t* bases;   // format 3: the base bytes of the tile's 16 rows
 };
-__device__ __forceinline__ PackedTile packed_tile(const void* base, int N, int K, int t, int scale_bytes) {
+// Formats: 1 MXFP4, 2 CB4, 3 MXFP4 with the packed scale store.
+__host__ __device__ constexpr bool fmt_is_mx(int fmt) { return fmt != 2; }
+template <int FMT>
+__device__ __forceinline__ PackedTile packed_tile(const void* base, int N, int K, int t) {
   const size_t soff = ((size_t)N * K / 2 + 255) / 256 * 256;
   gbyte_t* b = as_global(base);
-  return {b + (size_t)t * 8 * K, b + soff + (size_t)t * 16 * (K / 32) * scale_bytes};
+  if constexpr (FMT == 3)
+    return {b + (size_t)t * 8 * K, b + soff + N + (size_t)t * 8 * (K / 32), b + soff + 16 * (size_t)t};
+  return {b + (size_t)t * 8 * K, b + soff + (size_t)t * 16 * (K / 32) * (FMT == 1 ? 1 : 2), nullptr};
 }
 // block kb (< nkb) of row m of a tile: byte offset of its 16 code bytes in the tile
 __device__ __forceinline__ uint32_t pk_code(int kb, int m) {
   return (uint32_t)(kb >> 2) * 1024u + (uint32_t)(((kb & 3) * 16 + m) * 16);
 }
-// its scale's index within the tile's scales (MXFP4 bytes / CB4 fp16 entries)
+// its scale's index within the tile's scales (MXFP4 bytes / CB4 fp16 entries; in the
+// packed scale store, the index of its delta nibble)
 __device__ __forceinline__ uint32_t pk_scale_mx(int kb, int m) { return (uint32_t)(kb >> 2) * 64u + (kb & 3) * 16 + m; }
+// E8M0 byte of a block in the packed scale store: the row's base plus the delta nibble
+// (dbyte = the byte holding it, m = the row within its tile: even rows in the low nibble)
+__device__ __forceinline__ uint32_t ps_e8m0(uint32_t base, uint32_t dbyte, int m) {
+  return base + ((dbyte >> ((m & 1) * 4)) & 15u);
+}
 __device__ __forceinline__ uint32_t pk_scale_cb(int kb, int m, int nkb) {
   const int s = kb >> 2, r = min(4, nkb - 4 * s);
   return (uint32_t)s * 64u + (uint32_t)(m * r + (kb & 3));

@@ -40,12 +40,13 @@ constexpr int waitcnt_vm_le(int n) {
   return (n > 63 ? 63 : n) & 15 | (7 << 4) | (15 << 8) | (((n > 63 ? 63 : n) >> 4) << 14);
 }
 // vector-memory instructions one prefetch_step issues per 16-row tile: MXFP4 one 16-byte
-// code load and one scale byte; CB4 four code dwords and four fp16 scales.  The waits
+// code load and one scale byte (the packed scale store: one delta byte); CB4 four code
+// dwords and four fp16 scales.  The waits
 // after the staging loads count on exactly these: no two of them can be merged into one
 // instruction, since each address is clamped separately (min / select on the block
 // index), so the compiler cannot prove two of them adjacent.
 template <int FMT>
-constexpr int loads_per_step() { return FMT == 1 ? 2 : 8; }
+constexpr int loads_per_step() { return fmt_is_mx(FMT) ? 2 : 8; }
 constexpr int kDecMaxTokens = 32;  // two 16-slot MFMA token tiles
 
 __device__ __forceinline__ int dec_token_of_pair(int p, int T, int k) { return p < T * k ? p / k : p - T * k; }
@@ -540,6 +541,11 @@ struct WeightRegs<1, KSW> {
   uint32_t s[KSW];
 };
 template <int KSW>
+struct WeightRegs<3, KSW> {  // the packed scale store: s holds the byte with the delta nibble
+  u32x4_t c[KSW];
+  uint32_t s[KSW];
+};
+template <int KSW>
 struct WeightRegs<2, KSW> {
   uint32_t c[KSW][4];
   uint32_t s[KSW][4];  // fp16 scale bits of blocks 4ks..4ks+3
@@ -555,12 +561,12 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
                                               int nks, int m, int g, int stride = 4) {
   {
     const int ks = ks0 + stride * i;
-    if constexpr (FMT == 1) {
+    if constexpr (fmt_is_mx(FMT)) {
       const int kb = 4 * ks + g;
       const int kbc = (ks < nks && kb < nkb) ? kb : 0;
       r.c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(pt.codes +
                                                                                              pk_code(kbc, m)));
-      r.s[i] = pt.scales[pk_scale_mx(kbc, m)];
+      r.s[i] = pt.scales[FMT == 3 ? pk_scale_mx(kbc, m) >> 1 : pk_scale_mx(kbc, m)];
     } else {
       const int ksc = ks < nks ? ks : 0;
 #pragma unroll
@@ -595,18 +601,19 @@ __device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, cons
 }
 
 // acc[tt] += A(token tile tt, planes) x B(weights of k-step i) for one weight matrix.
+// sbase: the packed scale store's base byte of this lane's weight row (format 3 only).
 // xrows = activation rows staged in LDS.  Branch-free: the activation operand is zero
 // for slots >= xrows, for k-steps past the row (ks >= nks) and for 32-blocks past it,
 // so those MFMAs add exact zeros (the weights they meet are clamped real blocks).
 template <int FMT, int NP, int NTT, int KSW>
 __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, int ks, int nks, int nkb,
                                           const uint16_t* xs, int xstride, size_t plane_stride, int live, int xrows,
-                                          const uint32_t* lut, f32x4_t (&acc)[NTT]) {
+                                          const uint32_t* lut, uint32_t sbase, f32x4_t (&acc)[NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const bool ksv = ks < nks;
-  if constexpr (FMT == 1) {
-    const float sc = e8m0_to_f32(r.s[i]);
+  if constexpr (fmt_is_mx(FMT)) {
+    const float sc = e8m0_to_f32(FMT == 3 ? ps_e8m0(sbase, r.s[i], m) : r.s[i]);
     const bool kval = ksv && (4 * ks + g < nkb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -763,8 +770,10 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-  const PackedTile pg = packed_tile(slot_rec->gate_up, 2 * I, K, blockIdx.x, FMT == 1 ? 1 : 2);
-  const PackedTile pu = packed_tile(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x, FMT == 1 ? 1 : 2);
+  const PackedTile pg = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, blockIdx.x);
+  const PackedTile pu = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x);
+  // the packed scale store's row bases, loaded before the staging loads (not counted below)
+  const uint32_t bg = FMT == 3 ? (uint32_t)pg.bases[n] : 0u, bu = FMT == 3 ? (uint32_t)pu.bases[n] : 0u;
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
@@ -792,8 +801,8 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, accg);
-        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, accu);
+        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bg, accg);
+        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bu, accu);
       }
     }
     // split-K reduction (fixed wave order), SwiGLU, two bf16 planes of h
@@ -891,7 +900,8 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
-  const PackedTile pd = packed_tile(slot_rec->down, H, K, blockIdx.x, FMT == 1 ? 1 : 2);
+  const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, blockIdx.x);
+  const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += xrows_max) {
@@ -917,7 +927,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, acc);
+        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc);
       }
     }
     float v[4 * NTT];
@@ -1022,7 +1032,8 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   uint16_t* xs = (uint16_t*)(smem + 1024);
   const int tile = 4 * blockIdx.x + wave;  // this wave's 16 output columns
   const bool tile_ok = 16 * tile < H;
-  const PackedTile pd = packed_tile(slot_rec->down, H, K, tile_ok ? tile : 0, FMT == 1 ? 1 : 2);
+  const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, tile_ok ? tile : 0);
+  const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
 
   for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
@@ -1040,7 +1051,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
-      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, acc);
+      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc);
     if (tile_ok) {
       const int col = 16 * tile + n;
 #pragma unroll
@@ -1256,8 +1267,11 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return L.wfmt == 1 ? launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm)
-                     : launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+  switch (L.wfmt) {
+    case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+    case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+    default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+  }
 }
 
 }  // namespace moeq

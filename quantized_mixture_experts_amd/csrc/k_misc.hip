@@ -19,11 +19,12 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   if (blk >= (size_t)rows * nkb) return;
   const int row = (int)(blk / nkb), kb = (int)(blk % nkb);
   const int m = row & 15;
-  const PackedTile pt = packed_tile(packed, rows, cols, row >> 4, FMT == 1 ? 1 : 2);
+  const PackedTile pt = packed_tile<FMT>(packed, rows, cols, row >> 4);
   const u32x4_t c = *(const __attribute__((address_space(1))) u32x4_t*)(pt.codes + pk_code(kb, m));
   float* dst = out + blk * 32;
-  if (FMT == 1) {
-    const float s = e8m0_to_f32(pt.scales[pk_scale_mx(kb, m)]);
+  if (fmt_is_mx(FMT)) {
+    const float s = e8m0_to_f32(FMT == 3 ? ps_e8m0(pt.bases[m], pt.scales[pk_scale_mx(kb, m) >> 1], m)
+                                         : pt.scales[pk_scale_mx(kb, m)]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bf16x8_t v = fp4x8_to_bf16(c[q], s);
@@ -99,6 +100,8 @@ hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codeboo
   const dim3 grid((unsigned)((nblk + 255) / 256));
   if (wfmt == 1)
     hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
+  else if (wfmt == 3)
+    hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
   else
     hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
   return hipGetLastError();

@@ -44,8 +44,8 @@ constexpr int kMxRowBytes = 128;                          // MXFP4 path: one sta
 constexpr int kMxPlaneBytes = kGroupPairs * kMxRowBytes;  // 8 KB per plane per buffer
 constexpr int kMxChunkCols = 256;  // h columns per activation scale (one gate/up block's columns)
 constexpr int kMxAScaleStride = 64;  // LDS activation scales: 64 rows x up to 64 chunks (I <= 16384)
-__host__ __device__ constexpr int pf_row_bytes(int fmt) { return fmt == 1 ? kMxRowBytes : kPfRowBytes; }
-__host__ __device__ constexpr int pf_plane_bytes(int fmt) { return fmt == 1 ? kMxPlaneBytes : kPfPlaneBytes; }
+__host__ __device__ constexpr int pf_row_bytes(int fmt) { return fmt_is_mx(fmt) ? kMxRowBytes : kPfRowBytes; }
+__host__ __device__ constexpr int pf_plane_bytes(int fmt) { return fmt_is_mx(fmt) ? kMxPlaneBytes : kPfPlaneBytes; }
 
 // CB4 decode table at LDS offset 0, in one of two forms:
 //  - replicated, one copy per lane: the entry for code byte b (two bf16 values) of lane
@@ -66,12 +66,12 @@ __host__ __device__ constexpr int pf_lut_bytes(int fmt, int np, int d) {
 // MXFP4 scale buffers: two groups of D k-steps; group buffer = 8 waves x 1 KB, step u
 // of the group at 2 KB u, row tile (wave w, tile rt) at 64 (4 w + rt) inside it.
 constexpr int kPfScaleGroupBytes = 8 * 1024;
-__host__ __device__ constexpr int pf_scale_lds_bytes(int fmt) { return fmt == 1 ? 2 * kPfScaleGroupBytes : 0; }
+__host__ __device__ constexpr int pf_scale_lds_bytes(int fmt) { return fmt_is_mx(fmt) ? 2 * kPfScaleGroupBytes : 0; }
 // MXFP4: the rows' activation scales, then the gate/up epilogue's per-wave row maxima
 // [64 rows][8 waves] (a region of its own, so that waves still in their last k-step are
 // not disturbed)
 __host__ __device__ constexpr int pf_ascale_lds_bytes(int fmt) {
-  return fmt == 1 ? kGroupPairs * kMxAScaleStride + kGroupPairs * 8 * 4 : 0;
+  return fmt_is_mx(fmt) ? kGroupPairs * kMxAScaleStride + kGroupPairs * 8 * 4 : 0;
 }
 // LUT, then the D x NP activation buffers, then (MXFP4) the weight scale buffers and the
 // rows' activation scales, then the group's 64 pair ids.
@@ -122,6 +122,10 @@ __host__ __device__ constexpr int pf_vm_le(int n) {
 template <int FMT, int SCL>
 struct PfStep;
 template <int SCL>
+struct PfStep<3, SCL> {  // the packed scale store: the scales are staged in LDS as for MXFP4
+  u32x4_t c[4];
+};
+template <int SCL>
 struct PfStep<1, SCL> {
   u32x4_t c[4];  // the scales are staged in LDS
 };
@@ -137,7 +141,7 @@ struct PfStep<2, 1> {
 };
 template <int FMT, int SCL>
 __host__ __device__ constexpr int pf_loads_per_step() {
-  return FMT == 1 ? 4 : (SCL ? 20 : 32);
+  return fmt_is_mx(FMT) ? 4 : (SCL ? 20 : 32);
 }
 
 __device__ __forceinline__ void pf_load_lds_16(gbyte_t* gptr, void* lds) {
@@ -155,7 +159,7 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
   const int kc = ks < nks ? ks : nks - 1;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    if constexpr (FMT == 1) {
+    if constexpr (fmt_is_mx(FMT)) {
       const int kb = min(4 * kc + g, nkb - 1);
       r.c[rt] = __builtin_nontemporal_load(
           (const __attribute__((address_space(1))) u32x4_t*)(pt[rt].codes + pk_code(kb, m)));
@@ -204,7 +208,7 @@ __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uin
                                             const uint8_t* ab, f32x4_t (&acc)[4][NTT]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  if constexpr (FMT == 1) {
+  if constexpr (fmt_is_mx(FMT)) {
     // Block-scaled matrix cores: A = NP fp8 e4m3 planes of the activations with one E8M0
     // scale per row (chunk), B = the E2M1 codes exactly as stored (lane 16g + m holds
     // block g of weight row m, which is the B operand layout) with their E8M0 scales.
@@ -286,6 +290,8 @@ struct PfCtx {
   int sstep;               // MXFP4: the step of a D-step group whose scales this wave stages
   int schunk;              // MXFP4: this lane's 16-byte chunk (block g) of a scale unit
   int soff;                // MXFP4: this lane's scale byte of its row tile 0 in a staged step
+  gbyte_t* dsrc;           // packed scale store: this lane's 8 delta bytes (chunk) of its staging tile, step 0
+  u32x4_t sbase;           // packed scale store: the base bytes of the 16 rows of this lane's staging tile
   const uint8_t* ascale;   // MXFP4: LDS activation scales [64 rows][kMxAScaleStride], row m
   float* cmax;             // MXFP4 gate/up epilogue: LDS row maxima [64 rows][8 waves]
   size_t act_plane_bytes;
@@ -326,13 +332,38 @@ __device__ __forceinline__ void pf_stage_scales(const PfCtx& c, int s, int par) 
   pf_load_lds_16(c.ssrc + 64 * st + 16 * (ch - c.schunk), c.sbuf + par * kPfScaleGroupBytes + c.wave * 1024);
 }
 
+// Packed scale store: the lane's 16 deltas (rows 0..15 of block `schunk` of its staging
+// tile) for the steps pf_stage_scales would stage, one 8-byte register load in place of
+// the direct load (so the per-step load counts are the same) ...
+__device__ __forceinline__ uint64_t pf_load_deltas(const PfCtx& c, int s) {
+  const int st = min(s + c.sstep, c.nks - 1);
+  const int nb = min(4, c.nkb - 4 * st);
+  const int ch = c.schunk < nb ? c.schunk : 0;
+  return *(const __attribute__((address_space(1))) uint64_t*)(c.dsrc + 32 * st + 8 * (ch - c.schunk));
+}
+// ... and, once they are needed, the 16 E8M0 bytes (row base + delta nibble j for row j)
+// written where the direct load would have put them; the LDS write is complete before
+// the next step's barrier.
+__device__ __forceinline__ void pf_put_scales(const PfCtx& c, uint64_t d, int par) {
+  const int lane = threadIdx.x & 63;
+  u32x4_t v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t n = (uint32_t)(d >> (16 * q)) & 0xFFFFu;
+    const uint32_t x = (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) | ((n & 0xF000u) << 12);
+    v[q] = c.sbase[q] + x;  // base + delta <= 255 in every byte: no carries between bytes
+  }
+  *(u32x4_t*)(c.sbuf + par * kPfScaleGroupBytes + c.wave * 1024 + 16 * lane) = v;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters untouched
+}
+
 // The vmcnt wait at the start of the k-step in ring slot U that covers chunk s: chunk s
 // was staged D-1 steps earlier and was followed by that step's weights and by D-2 whole
 // steps (chunk + weights, plus the scale load of a slot-0 step, which precedes its chunk).
 template <int FMT, int SCL, int D, int NQNP>
 __host__ __device__ constexpr int pf_wait_count(int U) {
   int n = pf_loads_per_step<FMT, SCL>();
-  for (int v = 2; v < D; ++v) n += NQNP + pf_loads_per_step<FMT, SCL>() + ((FMT == 1 && (U + v) % D == 0) ? 1 : 0);
+  for (int v = 2; v < D; ++v) n += NQNP + pf_loads_per_step<FMT, SCL>() + ((fmt_is_mx(FMT) && (U + v) % D == 0) ? 1 : 0);
   return n;
 }
 
@@ -341,6 +372,11 @@ __host__ __device__ constexpr int pf_wait_count(int U) {
 // step U instead of hoisting them to the loop head where the later slots are in flight.
 template <int SCL>
 __device__ __forceinline__ void pf_pin(PfStep<1, SCL>& r) {
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(r.c[rt]));
+}
+template <int SCL>
+__device__ __forceinline__ void pf_pin(PfStep<3, SCL>& r) {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(r.c[rt]));
 }
@@ -363,7 +399,7 @@ __device__ __forceinline__ void pf_pin(PfStep<2, 1>& r) {
 // 4 rows per load; MXFP4: one load covers 8 rows, all 64 are staged).
 template <int FMT, int W, int NTT>
 __host__ __device__ constexpr int pf_nq() {
-  return FMT == 1 ? 64 / 8 / W : ((4 * NTT + W - 1) / W < 16 / W ? (4 * NTT + W - 1) / W : 16 / W);
+  return fmt_is_mx(FMT) ? 64 / 8 / W : ((4 * NTT + W - 1) / W < 16 / W ? (4 * NTT + W - 1) / W : 16 / W);
 }
 
 // One k-step (s = a multiple of D plus U): wait for chunk s, stage (in a slot-0 step) the
@@ -374,7 +410,8 @@ __host__ __device__ constexpr int pf_nq() {
 // visible and frees the buffers of step s-1.  Straight-line code: every wave issues the
 // same loads at every step, so the wait is a constant.
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT, int U, int W>
-__device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s, f32x4_t (&acc)[4][NTT]) {
+__device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s, f32x4_t (&acc)[4][NTT],
+                                         uint64_t& pend) {
   constexpr int NQ = pf_nq<FMT, W, NTT>();
   constexpr int kWait = pf_wait_count<FMT, SCL, D, NQ * NP>(U);
   static_assert(kWait <= 63, "too many loads in flight for the vmcnt counter");
@@ -382,6 +419,7 @@ __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring
   __builtin_amdgcn_s_barrier();
   const int grp = s / D;
   if constexpr (FMT == 1 && U == 0) pf_stage_scales<D>(c, s + D, (grp + 1) & 1);
+  if constexpr (FMT == 3 && U == 0) pend = pf_load_deltas(c, s + D);
   pf_stage<FMT, NP, W, NQ>(c, s + D - 1, (U + D - 1) % D);
   pf_pin(ring[U]);
   const uint8_t* sb = c.sbuf + (grp & 1) * kPfScaleGroupBytes + U * 2048 + c.soff;
@@ -390,14 +428,17 @@ __device__ __forceinline__ void pf_kstep(const PfCtx& c, PfStep<FMT, SCL> (&ring
   pf_mma_step<FMT, NP, SCL, NTT, pf_lut_repl(FMT, NP, D)>(ring[U], c.xs + U * NP * pf_plane_bytes(FMT), s, c.nkb,
                                                          c.lane_off, c.lut, sb, ab, acc);
   pf_load_step<FMT, SCL>(ring[U], c.tile, s + D, c.nks, c.nkb, c.m, c.g);
+  // the next group's scales, in the buffer every wave finished with at this group's start
+  if constexpr (FMT == 3 && U == D - 1) pf_put_scales(c, pend, (grp + 1) & 1);
 }
 
 // The last R (< D) k-steps, straight-line.
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int NTT, int R, int W>
-__device__ __forceinline__ void pf_tail(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s0, f32x4_t (&acc)[4][NTT]) {
-  if constexpr (R >= 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc);
-  if constexpr (R >= 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, s0 + 1, acc);
-  if constexpr (R >= 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 2, W>(c, ring, s0 + 2, acc);
+__device__ __forceinline__ void pf_tail(const PfCtx& c, PfStep<FMT, SCL> (&ring)[D], int s0, f32x4_t (&acc)[4][NTT],
+                                        uint64_t& pend) {
+  if constexpr (R >= 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc, pend);
+  if constexpr (R >= 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, s0 + 1, acc, pend);
+  if constexpr (R >= 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 2, W>(c, ring, s0 + 2, acc, pend);
   static_assert(R < 4, "tail longer than supported");
 }
 
@@ -509,7 +550,9 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   PfStep<FMT, SCL> ring[D];
+  uint64_t pend = 0;  // packed scale store: the next group's deltas, between its load and its use
   if constexpr (FMT == 1) pf_stage_scales<D>(c, 0, 0);
+  if constexpr (FMT == 3) pf_put_scales(c, pf_load_deltas(c, 0), 0);
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     if (j < D - 1) pf_stage<FMT, NP, W, pf_nq<FMT, W, NTT>()>(c, j, j);
@@ -517,16 +560,16 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
   }
   const int nfull = c.nks / D * D;
   for (int s0 = 0; s0 < nfull; s0 += D) {
-    pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc);
-    if constexpr (D > 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 1 ? 1 : 0), W>(c, ring, s0 + 1, acc);
-    if constexpr (D > 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 0), W>(c, ring, s0 + 2, acc);
-    if constexpr (D > 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 0), W>(c, ring, s0 + 3, acc);
+    pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, 0, W>(c, ring, s0, acc, pend);
+    if constexpr (D > 1) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 1 ? 1 : 0), W>(c, ring, s0 + 1, acc, pend);
+    if constexpr (D > 2) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 0), W>(c, ring, s0 + 2, acc, pend);
+    if constexpr (D > 3) pf_kstep<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 0), W>(c, ring, s0 + 3, acc, pend);
     static_assert(D <= 4, "deeper rings need more unrolled steps");
   }
   switch (c.nks - nfull) {
-    case 1: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, nfull, acc); break;
-    case 2: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 1), W>(c, ring, nfull, acc); break;
-    case 3: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 1), W>(c, ring, nfull, acc); break;
+    case 1: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, 1, W>(c, ring, nfull, acc, pend); break;
+    case 2: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 2 ? 2 : 1), W>(c, ring, nfull, acc, pend); break;
+    case 3: pf_tail<FMT, NP, D, GATEUP, SCL, NTT, (D > 3 ? 3 : 1), W>(c, ring, nfull, acc, pend); break;
     default: break;
   }
   // the trailing (never used) loads must land before the block's LDS is released
@@ -542,7 +585,7 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
       const int slot = min(16 * tt + 4 * g + q, nt - 1);
       pid[tt][q] = c.s_pair[slot];
     }
-  if constexpr (GATEUP && FMT == 1) {
+  if constexpr (GATEUP && fmt_is_mx(FMT)) {
     pf_mx_h_epilogue<NTT, W>(c, L, T, w, wt, nt, acc);
   } else if constexpr (GATEUP) {
     if (c.rt_mask) {
@@ -621,7 +664,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   c.nks = (c.nkb + 3) >> 2;
   // activation row stride: bf16 rows of K (CB4); fp8 rows padded to whole k-steps (x) or
   // whole 256-column chunks (h) (MXFP4)
-  c.row_bytes = FMT == 1 ? (GATEUP ? (H + 127) / 128 * 128 : (I + kMxChunkCols - 1) / kMxChunkCols * kMxChunkCols)
+  c.row_bytes = fmt_is_mx(FMT) ? (GATEUP ? (H + 127) / 128 * 128 : (I + kMxChunkCols - 1) / kMxChunkCols * kMxChunkCols)
                          : 2 * K;
   c.act_plane_bytes = act_plane_bytes;
   const int wt = rb * W + c.wave;
@@ -638,7 +681,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   c.s_pair = s_pair;
   if (threadIdx.x < kGroupPairs)
     s_pair[threadIdx.x] = w.perm[start + ((int)threadIdx.x < nt ? (int)threadIdx.x : 0)];
-  if constexpr (FMT == 1) {
+  if constexpr (fmt_is_mx(FMT)) {
     // the rows' activation scales (they follow the NP planes): one per x row, one per
     // 256-column chunk of an h row; rows past nt repeat row 0
     uint8_t* as = smem + pf_lds_bytes(FMT, NP, D) - pf_ascale_lds_bytes(FMT);
@@ -658,7 +701,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
   }
   __syncthreads();
 
-  if constexpr (FMT == 1) {
+  if constexpr (fmt_is_mx(FMT)) {
     // one 1 KB staging load per plane covers rows 8 wave .. 8 wave + 7: lane l loads
     // row 8 wave + l / 8, the 16-byte piece that belongs at LDS piece l % 8
     const int row = 8 * c.wave + (lane >> 3);
@@ -691,7 +734,7 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
       row0 = 64 * wtile + 16 * rt;
       ok = row0 < H;
     }
-    return packed_tile(base, rows_total, K, ok ? row0 / 16 : 0, FMT == 1 ? 1 : 2);
+    return packed_tile<FMT>(base, rows_total, K, ok ? row0 / 16 : 0);
   };
   c.rt_mask = 0;
 #pragma unroll
@@ -700,15 +743,20 @@ __global__ __launch_bounds__(64 * W) void k_pf_proj(LayerArgs L, int T, Work w, 
     c.tile[rt] = tile_of(wt, rt, ok);
     if (ok) c.rt_mask |= 1u << rt;
   }
-  if constexpr (FMT == 1) {
+  if constexpr (fmt_is_mx(FMT)) {
     static_assert(W == 8, "the scale staging assumes 8 waves (32 row tiles) per block");
     bool ok;
     const int wv = 4 * (c.wave & 1) + (lane >> 4);  // the wave owning this lane's staged tile
     c.schunk = lane & 3;
-    c.ssrc = tile_of(rb * W + wv, (lane >> 2) & 3, ok).scales + 16 * c.schunk;
+    const PackedTile st = tile_of(rb * W + wv, (lane >> 2) & 3, ok);
+    c.ssrc = st.scales + 16 * c.schunk;
     c.sstep = min(c.wave >> 1, D - 1);
     c.sbuf = smem + pf_lut_bytes(FMT, NP, D) + D * NP * pf_plane_bytes(FMT);
     c.soff = 256 * c.wave + 16 * c.g + c.m;
+    if constexpr (FMT == 3) {
+      c.dsrc = st.scales + 8 * c.schunk;
+      c.sbase = *(const __attribute__((address_space(1))) u32x4_t*)st.bases;
+    }
   } else {
     c.ssrc = nullptr;
     c.sbuf = nullptr;
@@ -839,8 +887,9 @@ static void pf_launch_cb4(const LayerArgs& L, const void* x, int x_dtype, int T,
   pf_launch<2, 2, DD, false, SCL, WD>(L, T, w, w.hplanes, P * L.I * 2, rb_dn, mg, kStageDown, s, tm);
 }
 
-// MXFP4: fp8 activation planes on the block-scaled matrix cores (x: 2 planes for bf16,
-// 3 for fp32; h: 3 planes).
+// MXFP4 (FMT 1) and its packed scale store (FMT 3): fp8 activation planes on the
+// block-scaled matrix cores (x: 2 planes for bf16, 3 for fp32; h: 3 planes).
+template <int FMT>
 static void pf_launch_mx(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int mg,
                          hipStream_t s, const Timing& tm) {
   const int Hp = (L.H + 127) / 128 * 128;
@@ -850,12 +899,12 @@ static void pf_launch_mx(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const int rb_dn = (((L.H + 63) / 64) + kPfWaves - 1) / kPfWaves;
   if (x_dtype == 1) {
     MOEQ_LAUNCH(tm, kStageActQuant, (k_mx_xquant<1, 2>), dim3(T), dim3(256), 0, s, x, T, L.H, Hp, w.xq);
-    pf_launch<1, 2, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
+    pf_launch<FMT, 2, 4, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
   } else {
     MOEQ_LAUNCH(tm, kStageActQuant, (k_mx_xquant<0, 3>), dim3(T), dim3(256), 0, s, x, T, L.H, Hp, w.xq);
-    pf_launch<1, 3, 3, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
+    pf_launch<FMT, 3, 3, true, 0, kPfWaves>(L, T, w, w.xq, (size_t)T * Hp, rb_gu, mg, kStageGateUp, s, tm);
   }
-  pf_launch<1, 3, 3, false, 0, kPfWaves>(L, T, w, w.hq, P * Ip, rb_dn, mg, kStageDown, s, tm);
+  pf_launch<FMT, 3, 3, false, 0, kPfWaves>(L, T, w, w.hq, P * Ip, rb_dn, mg, kStageDown, s, tm);
 }
 
 hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
@@ -863,7 +912,9 @@ hipError_t launch_experts(const LayerArgs& L, const void* x, int x_dtype, int T,
   const int P = T * L.k + (L.has_shared ? T : 0);
   const int mg = max_groups(P, L.E);
   if (L.wfmt == 1) {
-    pf_launch_mx(L, x, x_dtype, T, w, mg, s, tm);
+    pf_launch_mx<1>(L, x, x_dtype, T, w, mg, s, tm);
+  } else if (L.wfmt == 3) {
+    pf_launch_mx<3>(L, x, x_dtype, T, w, mg, s, tm);
   } else {
     // both K ranges must be multiples of 128 for the 8-byte scale loads
     if (L.H % 128 == 0 && L.I % 128 == 0)

@@ -39,6 +39,7 @@ import numpy as np
 
 WFMT_MXFP4 = 1
 WFMT_CB4 = 2
+WFMT_MXFP4_PS = 3   # MXFP4 codes with the packed scale store
 X_F32 = 0
 X_BF16 = 1
 
@@ -58,6 +59,8 @@ def scale_plane_offset(rows: int, cols: int) -> int:
 
 def packed_nbytes(wfmt: int, rows: int, cols: int) -> int:
     nblk = rows * cols // 32
+    if wfmt == WFMT_MXFP4_PS:
+        return scale_plane_offset(rows, cols) + rows + nblk // 2
     return scale_plane_offset(rows, cols) + nblk * (1 if wfmt == WFMT_MXFP4 else 2)
 
 
@@ -133,6 +136,28 @@ def to_tile_major(code_rows: np.ndarray, scale_rows: np.ndarray, wfmt: int) -> n
     return out
 
 
+def to_packed_scale_store(code_rows: np.ndarray, e8m0_rows: np.ndarray) -> np.ndarray:
+    """MXFP4 codes [N][K/2] and E8M0 bytes [N][K/32] in the packed scale store: the raw
+    store's code plane, then at the scale-plane offset one base byte per row (the row's
+    smallest E8M0 byte) and one 4-bit delta per block (E8M0 - base), the delta of block
+    (row, b) at the nibble whose index is the block's entry in the raw tile-major scale
+    plane (low nibble first).  Rows whose E8M0 bytes span more than 15 are refused."""
+    N, nkb = e8m0_rows.shape
+    e = e8m0_rows.astype(np.int64)
+    base = e.min(axis=1)
+    delta = e - base[:, None]
+    if delta.max(initial=0) > 15:
+        raise ValueError("a row's E8M0 bytes span more than 15: not representable in the packed scale store")
+    raw = to_tile_major(code_rows, delta.astype(np.uint8), WFMT_MXFP4)  # deltas in the raw scale order
+    off = scale_plane_offset(N, nkb * 32)
+    d = raw[off:off + N * nkb]
+    out = np.zeros(packed_nbytes(WFMT_MXFP4_PS, N, nkb * 32), dtype=np.uint8)
+    out[:off] = raw[:off]
+    out[off:off + N] = base.astype(np.uint8)
+    out[off + N:] = (d[0::2] | (d[1::2] << 4)).astype(np.uint8)
+    return out
+
+
 def make_packed(spec: WeightSpec, rows: int, cols: int, seed_key: Sequence[int],
                 codes_tid: int, scales_tid: int) -> np.ndarray:
     """One packed matrix [rows][cols].  The code bytes (row-major, both nibbles uniform) and
@@ -141,10 +166,12 @@ def make_packed(spec: WeightSpec, rows: int, cols: int, seed_key: Sequence[int],
     nblk = rows * cols // 32
     code_rows = random_bytes(_rng(*seed_key, codes_tid), rows * cols // 2).reshape(rows, cols // 2)
     srng = _rng(*seed_key, scales_tid)
-    if spec.wfmt == WFMT_MXFP4:
+    if spec.wfmt in (WFMT_MXFP4, WFMT_MXFP4_PS):
         sc = srng.integers(spec.e8m0_lo, spec.e8m0_hi + 1, size=nblk, dtype=np.uint8)
     else:
         sc = srng.uniform(spec.scale_lo, spec.scale_hi, size=nblk).astype(np.float16).view(np.uint16)
+    if spec.wfmt == WFMT_MXFP4_PS:  # the same draws as the raw MXFP4 store, re-encoded
+        return to_packed_scale_store(code_rows, sc.reshape(rows, cols // 32))
     return to_tile_major(code_rows, sc.reshape(rows, cols // 32), spec.wfmt)
 
 
@@ -271,3 +298,11 @@ def small_spec(name: str, T: int, hidden: int, inter: int, n_experts: int, top_k
     return LayerSpec(name, T=T, hidden=hidden, inter=inter, n_experts=n_experts, top_k=top_k,
                      has_shared=has_shared, weights=w, x_dtype=x_dtype, router_std=router_std,
                      bias=bias, bias_std=bias_std, seed=seed)
+
+
+def with_packed_scales(spec: LayerSpec) -> LayerSpec:
+    """The same MXFP4 layer (same seeds, so the same codes and E8M0 values) stored in the
+    packed scale store."""
+    assert spec.weights.wfmt == WFMT_MXFP4
+    w = dataclasses.replace(spec.weights, wfmt=WFMT_MXFP4_PS)
+    return dataclasses.replace(spec, name=spec.name + "_packed_scales", weights=w)

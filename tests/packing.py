@@ -9,7 +9,7 @@ MXFP4 (g, m) at 16g + m, CB4 (m, g) at m*r + g.
 """
 import numpy as np
 
-MXFP4, CB4 = 1, 2
+MXFP4, CB4, MXFP4_PS = 1, 2, 3
 
 
 def pack(wfmt, codes, scales):
@@ -36,4 +36,31 @@ def pack(wfmt, codes, scales):
             unit = t * 16 * nblk + 64 * s
             splane[unit + (16 * g + m if wfmt == MXFP4 else m * r + g)] = sc[row, b]
     out[scale_off:] = splane.astype("<u2" if wfmt == CB4 else np.uint8).view(np.uint8)
+    return out
+
+
+def pack_scale_store(codes, e8m0):
+    """The packed scale store of MXFP4 codes [rows][cols] and E8M0 bytes [rows][cols/32],
+    block by block: the raw code plane, then at the scale-plane offset the row bases
+    (smallest E8M0 byte of the row), then per block the nibble base-relative exponent at
+    nibble index = the block's raw scale index (low nibble first)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    nblk = cols // 32
+    e8m0 = np.asarray(e8m0).reshape(rows, nblk).astype(int)
+    raw = pack(MXFP4, codes, np.zeros((rows, nblk), dtype=np.uint8))
+    scale_off = (rows * cols // 2 + 255) // 256 * 256
+    out = np.zeros(scale_off + rows + rows * nblk // 2, dtype=np.uint8)
+    out[:scale_off] = raw[:scale_off]
+    for row in range(rows):
+        base = min(e8m0[row])
+        out[scale_off + row] = base
+        t, m = divmod(row, 16)
+        for b in range(nblk):
+            s, g = divmod(b, 4)
+            i = t * 16 * nblk + 64 * s + 16 * g + m
+            d = e8m0[row, b] - base
+            assert 0 <= d <= 15
+            at = scale_off + rows + i // 2
+            out[at] |= (d if i % 2 == 0 else d << 4)
     return out

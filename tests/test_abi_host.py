@@ -39,7 +39,7 @@ def test_packed_bytes(L):
     assert q.packed_bytes(q.WFMT_MXFP4, 5760, 2880) + q.packed_bytes(q.WFMT_MXFP4, 2880, 2880) == 13_219_200
     assert q.packed_bytes(q.WFMT_CB4, 16, 160) == 1440
     assert q.packed_bytes(q.WFMT_CB4, 16, 100) == 0
-    assert q.packed_bytes(3, 16, 64) == 0
+    assert q.packed_bytes(99, 16, 64) == 0
     assert q.packed_bytes(q.WFMT_MXFP4, 0, 64) == 0
     assert q.packed_bytes(q.WFMT_MXFP4, 8, 64) == 0   # rows come in tiles of 16
 
@@ -225,3 +225,16 @@ def test_noalloc_validates_before_touching_the_gpu(L):
     assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, 7, 1, FAKE, None, 0) == q.MOE_ERR_INVALID_ARG
     assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, q.DT_BF16, -1, FAKE, None, 0) == q.MOE_ERR_INVALID_ARG
     assert L.moe_forward_noalloc(ctypes.byref(lay), FAKE, q.DT_BF16, 0, None, None, 0) == q.MOE_OK
+
+
+def test_packed_scale_store_bytes_and_validation(L):
+    """The packed scale store: the page's 12,839,040 bytes per gpt-oss-120B expert, and
+    like MXFP4 it takes no codebook."""
+    ps = q.WFMT_MXFP4_PS
+    assert q.packed_bytes(ps, 5760, 2880) + q.packed_bytes(ps, 2880, 2880) == 12_839_040
+    assert q.packed_bytes(ps, 16, 96) == 768 + 16 + 16 * 3 // 2
+    assert q.packed_bytes(ps, 8, 64) == 0
+    lay = layer(wfmt=ps, codebook=FAKE)
+    assert ws_bytes(L, lay, 4) == 0
+    lay = layer(wfmt=ps, codebook=None)
+    assert ws_bytes(L, lay, 4) > 0

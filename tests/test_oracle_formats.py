@@ -119,14 +119,69 @@ def test_packed_sizes_match_page_figures():
     assert synth.packed_nbytes(synth.WFMT_MXFP4, 2 * I, H) + synth.packed_nbytes(synth.WFMT_MXFP4, H, I) == expert
 
 
-def test_packed_scale_store_reading_size():
-    """The page's packed-scale store size is reproduced by one byte per row plus a
-    4-bit delta per block (a reading of the page, used only as a size check)."""
+def test_packed_scale_store_size_is_the_pages():
+    """One gpt-oss-120B expert in the packed scale store (gate/up [5760][2880] plus down
+    [2880][2880]) takes exactly the 12,839,040 bytes the page prints, in the oracle's and
+    the generator's size functions alike."""
     g = json.load(open(os.path.join(GOLDEN, "page_byte_counts.json")))
-    rows = 2 * 2880 + 2880
-    blocks = rows * 2880 // 32
-    codes = rows * 2880 // 2
-    assert codes + blocks // 2 + rows == g["mxfp4_packed_scale_expert_bytes"]["value"]
+    H = I = 2880
+    want = g["mxfp4_packed_scale_expert_bytes"]["value"]
+    assert oracle.packed_size(oracle.WFMT_MXFP4_PS, 2 * I, H) + oracle.packed_size(oracle.WFMT_MXFP4_PS, H, I) == want
+    assert synth.packed_nbytes(synth.WFMT_MXFP4_PS, 2 * I, H) + synth.packed_nbytes(synth.WFMT_MXFP4_PS, H, I) == want
+    # one byte per row plus half a byte per 32-value block, on top of the raw code bytes
+    rows = 2 * I + H
+    assert rows * H // 2 + rows + rows * (H // 32) // 2 == want
+
+
+def test_packed_scale_store_hand_encoded_tile():
+    """16 rows x 64 columns (2 blocks per row), every code 2 (E2M1 1.0) except code 11
+    (-1.5) in element 0 of each row; row m has base byte 110 + m and deltas (m % 4, 15).
+    The bytes are placed by hand: bases at the scale offset, then block b of row m's
+    delta at nibble 16 b + m (low nibble first)."""
+    rows, cols = 16, 64
+    S = (rows * cols // 2 + 255) // 256 * 256          # 512
+    buf = np.zeros(S + rows + rows * 2 // 2, dtype=np.uint8)
+    for m in range(rows):
+        for b in range(2):
+            at = (16 * b + m) * 16                      # one tile, one step: block b of row m
+            buf[at:at + 16] = 0x22
+        buf[(16 * 0 + m) * 16] = 0x2B                   # element 0 -> code 11, element 1 -> code 2
+        buf[S + m] = 110 + m
+    for m in range(rows):
+        for b, d in ((0, m % 4), (1, 15)):
+            i = 16 * b + m
+            buf[S + rows + i // 2] |= d if i % 2 == 0 else d << 4
+    assert buf.size == oracle.packed_size(oracle.WFMT_MXFP4_PS, rows, cols)
+    w = oracle.dequant(oracle.WFMT_MXFP4_PS, buf, None, rows, cols)
+    for m in range(rows):
+        s0 = 2.0 ** (110 + m + m % 4 - 127)
+        s1 = 2.0 ** (110 + m + 15 - 127)
+        assert w[m, 0] == -1.5 * s0 and np.all(w[m, 1:32] == s0)
+        assert np.all(w[m, 32:] == s1)
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 32), (32, 160), (48, 512)])
+def test_packed_scale_store_decodes_like_the_raw_store(rows, cols):
+    """The page's claim of bit-identical outputs: the same codes and E8M0 values give the
+    same dense matrix from the raw and the packed store (E8M0 spans up to 15 per row)."""
+    rng = np.random.default_rng(rows + cols)
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
+    lo = rng.integers(100, 140, (rows, 1))
+    e8 = (lo + rng.integers(0, 16, (rows, cols // 32))).astype(np.uint8)
+    raw = packing.pack(packing.MXFP4, codes, e8)
+    ps = packing.pack_scale_store(codes, e8)
+    code_rows = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(ps, synth.to_packed_scale_store(code_rows, e8))
+    assert np.array_equal(oracle.dequant(oracle.WFMT_MXFP4, raw, None, rows, cols),
+                          oracle.dequant(oracle.WFMT_MXFP4_PS, ps, None, rows, cols))
+
+
+def test_packed_scale_store_refuses_wide_rows():
+    code_rows = np.zeros((16, 32), dtype=np.uint8)
+    e8 = np.full((16, 2), 120, dtype=np.uint8)
+    e8[3, 1] = 136                                      # span 16 in row 3
+    with pytest.raises(ValueError):
+        synth.to_packed_scale_store(code_rows, e8)
 
 
 @pytest.mark.parametrize("wfmt", [oracle.WFMT_MXFP4, oracle.WFMT_CB4])
