@@ -235,10 +235,35 @@ def shared_weights(x64: np.ndarray, shared_gate_w) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-z))
 
 
+def omit_marginal(ids: np.ndarray, gates: np.ndarray, tau: float):
+    """Marginal-expert omission ("Nebula" page, "Benchmark results": a 10% threshold for
+    omitting marginal experts).  The page gives the threshold, not what happens to the
+    remaining weights; the reading taken: a routed pair whose softmax gate is below tau is
+    left out (the first, largest one never is), and the kept gates are renormalised to sum
+    to 1.  Omitted pairs get id -1 and gate 0.  tau = 0 keeps every pair unchanged."""
+    ids = np.array(ids, dtype=np.int32, copy=True)
+    gates = np.array(gates, dtype=np.float64, copy=True)
+    if tau <= 0.0:
+        return ids, gates
+    T, k = ids.shape
+    for t in range(T):
+        keep = [j == 0 or gates[t, j] >= tau for j in range(k)]
+        total = sum(gates[t, j] for j in range(k) if keep[j])
+        for j in range(k):
+            if keep[j]:
+                gates[t, j] = gates[t, j] / total
+            else:
+                ids[t, j] = -1
+                gates[t, j] = 0.0
+    return ids, gates
+
+
 def bucket(ids: np.ndarray, n_experts: int, has_shared: int):
     """Counting sort of pairs p = t*k + j by expert (stable: increasing p in a bucket).
-    Shared-expert pairs p = T*k + t form bucket E.  Returns counts [E+1],
-    offsets [E+2] (exclusive prefix sums), perm (bucketed pair ids), inv (perm^-1)."""
+    Shared-expert pairs p = T*k + t form bucket E; pairs with id -1 (omitted) are in no
+    bucket.  Returns counts [E+1], offsets [E+2] (exclusive prefix sums; offsets[E+1] =
+    the pairs placed), perm (the placed pair ids in bucket order), inv (position of each
+    pair in perm, -1 for an omitted pair)."""
     T, k = ids.shape
     expert_of = list(int(e) for e in ids.reshape(-1))
     if has_shared:
@@ -246,18 +271,21 @@ def bucket(ids: np.ndarray, n_experts: int, has_shared: int):
     P = len(expert_of)
     counts = np.zeros(n_experts + 1, dtype=np.int32)
     for e in expert_of:
-        counts[e] += 1
+        if e >= 0:
+            counts[e] += 1
     offsets = np.zeros(n_experts + 2, dtype=np.int32)
     for e in range(n_experts + 1):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = offsets[:n_experts + 1].copy()
-    perm = np.empty(P, dtype=np.int32)
+    perm = np.empty(offsets[n_experts + 1], dtype=np.int32)
     for p in range(P):
         e = expert_of[p]
+        if e < 0:
+            continue
         perm[fill[e]] = p
         fill[e] += 1
-    inv = np.empty(P, dtype=np.int32)
-    for i in range(P):
+    inv = np.full(P, -1, dtype=np.int32)
+    for i in range(perm.shape[0]):
         inv[perm[i]] = i
     return counts, offsets, perm, inv
 
@@ -280,23 +308,26 @@ def expert_ffn(w_gate_up: np.ndarray, w_down: np.ndarray, X: np.ndarray):
     return h, h @ w_down.T
 
 
-def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = False, map_fn=map):
+def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = False, map_fn=map,
+                omit_below: float = 0.0):
     """The whole layer for the tokens in x.  When `ids`/`gates` are given, routing is
-    taken from them (steps after routing only).  Returns a dict with y [T][H] fp64 and
-    every intermediate the GPU library exposes.  The experts' products are independent
-    of each other; `map_fn` evaluates them (the builtin map: one after another; a thread
-    pool's map gives the same values)."""
+    taken from them (steps after routing only; an id of -1 is an omitted pair).
+    omit_below > 0 applies the marginal-expert omission to the computed routing.
+    Returns a dict with y [T][H] fp64 and every intermediate the GPU library exposes.
+    The experts' products are independent of each other; `map_fn` evaluates them (the
+    builtin map: one after another; a thread pool's map gives the same values)."""
     H, I, E, k = layer.hidden, layer.inter, layer.n_experts, layer.top_k
     x64 = activations_f64(x, x_dtype)
     T = x64.shape[0]
     logits = router_logits(x64, layer.router_w, layer.router_b)
     if ids is None:
         ids, gates = topk_softmax(logits, k)
+        ids, gates = omit_marginal(ids, gates, omit_below)
     ids = np.asarray(ids, dtype=np.int32).reshape(T, k)
     gates = np.asarray(gates, dtype=np.float64).reshape(T, k)
     s = shared_weights(x64, layer.shared_gate_w) if layer.has_shared else None
     counts, offsets, perm, inv = bucket(ids, E, layer.has_shared)
-    P = perm.shape[0]
+    P = T * k + (T if layer.has_shared else 0)   # every pair id (omitted ones keep zero rows)
 
     def one_expert(e):
         pairs = perm[offsets[e]:offsets[e + 1]]
@@ -316,7 +347,8 @@ def moe_forward(layer, x, x_dtype: int, ids=None, gates=None, want_h: bool = Fal
     y = np.zeros((T, H))
     for t in range(T):
         for j in range(k):
-            y[t] += gates[t, j] * o[t * k + j]
+            if ids[t, j] >= 0:
+                y[t] += gates[t, j] * o[t * k + j]
         if layer.has_shared:
             y[t] += s[t] * o[T * k + t]
     return dict(y=y, logits=logits, ids=ids, gates=gates, shared_w=s, counts=counts,

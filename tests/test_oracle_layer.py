@@ -240,3 +240,34 @@ def test_forward_expert_map_on_threads_gives_the_same_values():
     with ThreadPoolExecutor(4) as ex:
         r2 = oracle.moe_forward(layer, x, spec.x_dtype, map_fn=ex.map)
     assert np.array_equal(r1["y"], r2["y"]) and np.array_equal(r1["o"], r2["o"])
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_omission_dense_masked_evaluation(case):
+    """With omission the layer is the dense masked evaluation whose mask holds the
+    renormalised gates of the kept pairs (a different algorithm: no bucketing)."""
+    spec, layer, x = _mk(case, seed=33)
+    tau = 0.9 / spec.top_k
+    r = oracle.moe_forward(layer, x, spec.x_dtype, omit_below=tau)
+    x64 = oracle.activations_f64(x, spec.x_dtype)
+    ids, g = oracle.topk_softmax(oracle.router_logits(x64, layer.router_w, layer.router_b), spec.top_k)
+    T, E, I, H = x.shape[0], spec.n_experts, spec.inter, spec.hidden
+    y = np.zeros((T, H))
+    for t in range(T):
+        keep = [j for j in range(spec.top_k) if j == 0 or g[t, j] >= tau]
+        tot = sum(g[t, j] for j in keep)
+        for j in keep:
+            e = ids[t, j]
+            wgu = oracle.dequant(layer.wfmt, layer.gate_up[e], layer.codebook, 2 * I, H)
+            wd = oracle.dequant(layer.wfmt, layer.down[e], layer.codebook, H, I)
+            a = x64[t] @ wgu.T
+            y[t] += g[t, j] / tot * (((a[:I] / (1 + np.exp(-a[:I]))) * a[I:]) @ wd.T)
+    if layer.has_shared:
+        wgu = oracle.dequant(layer.wfmt, layer.gate_up[E], layer.codebook, 2 * I, H)
+        wd = oracle.dequant(layer.wfmt, layer.down[E], layer.codebook, H, I)
+        a = x64 @ wgu.T
+        sw = np.ones(T) if layer.shared_gate_w is None else \
+            1 / (1 + np.exp(-(x64 @ layer.shared_gate_w.astype(np.float64))))
+        y += sw[:, None] * (((a[:, :I] / (1 + np.exp(-a[:, :I]))) * a[:, I:]) @ wd.T)
+    assert (r["ids"] == -1).any(), "the case should omit some pairs"
+    assert np.abs(r["y"] - y).max() <= 1e-12 * np.abs(y).max()

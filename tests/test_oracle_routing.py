@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 
 def _brute_topk(l, k):
@@ -149,3 +150,71 @@ def test_shared_gate_weights():
     s = oracle.shared_weights(x, w)
     assert np.allclose(s, [0.5, 0.5, 1 / (1 + np.exp(1.75))], rtol=1e-15)
     assert np.all(oracle.shared_weights(x, None) == 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Marginal-expert omission ("Nebula" page, "Benchmark results": a 10% threshold)
+# ---------------------------------------------------------------------------
+def test_omission_hand_worked_row():
+    """Logits 0, -1, -2, -3, -5 with k = 4: gates e^-j / (1 + e^-1 + e^-2 + e^-3), i.e.
+    0.6439, 0.2369, 0.0871, 0.0321; at 10 % the last two go and the kept ones become
+    1 / (1 + e^-1) and e^-1 / (1 + e^-1)."""
+    l = np.array([[0.0, -1.0, -2.0, -3.0, -5.0]])
+    ids, g = oracle.topk_softmax(l, 4)
+    assert np.array_equal(ids[0], [0, 1, 2, 3])
+    s = 1 + np.exp(-1) + np.exp(-2) + np.exp(-3)
+    assert np.allclose(g[0], [1 / s, np.exp(-1) / s, np.exp(-2) / s, np.exp(-3) / s], rtol=1e-15, atol=0)
+    ids2, g2 = oracle.omit_marginal(ids, g, 0.1)
+    assert np.array_equal(ids2[0], [0, 1, -1, -1])
+    assert np.allclose(g2[0], [1 / (1 + np.exp(-1)), np.exp(-1) / (1 + np.exp(-1)), 0, 0], rtol=1e-15, atol=0)
+
+
+def test_omission_zero_threshold_keeps_everything():
+    rng = np.random.default_rng(5)
+    l = rng.normal(size=(20, 16))
+    ids, g = oracle.topk_softmax(l, 6)
+    ids2, g2 = oracle.omit_marginal(ids, g, 0.0)
+    assert np.array_equal(ids2, ids) and np.array_equal(g2, g)
+
+
+def test_omission_definition_brute_force():
+    """On random rows: a pair is omitted exactly when its gate is below tau and it is not
+    the first; every kept pair keeps its expert; kept gates sum to 1 and keep their
+    ratios (renormalised by the kept total)."""
+    rng = np.random.default_rng(6)
+    for tau in (0.05, 0.1, 0.2, 0.5):
+        l = rng.normal(scale=2.0, size=(40, 24))
+        ids, g = oracle.topk_softmax(l, 8)
+        ids2, g2 = oracle.omit_marginal(ids, g, tau)
+        for t in range(40):
+            kept = [j for j in range(8) if j == 0 or g[t, j] >= tau]
+            assert all(ids2[t, j] == (ids[t, j] if j in kept else -1) for j in range(8))
+            assert abs(g2[t].sum() - 1.0) < 1e-15
+            tot = sum(g[t, j] for j in kept)
+            assert all(abs(g2[t, j] - g[t, j] / tot) < 1e-16 for j in kept)
+            assert all(g2[t, j] == 0.0 for j in range(8) if j not in kept)
+
+
+def test_omission_threshold_one_is_top1_routing():
+    """tau = 1 keeps only the first pair (its gate is below 1 whenever k > 1 and the
+    logits are finite) with weight 1: the layer equals the same layer routed top-1."""
+    import copy
+    spec = synth.small_spec("om1", 6, 64, 32, 6, 3, synth.WFMT_CB4, has_shared=1, bias="normal", seed=13)
+    layer = synth.make_layer(spec)
+    x = synth.make_x(spec)
+    r = oracle.moe_forward(layer, x, spec.x_dtype, omit_below=1.0)
+    l1 = copy.copy(layer)
+    l1.spec = copy.copy(layer.spec)
+    l1.spec.top_k = 1
+    r1 = oracle.moe_forward(l1, x, spec.x_dtype)
+    assert np.array_equal(r["ids"][:, 0], r1["ids"][:, 0]) and np.all(r["ids"][:, 1:] == -1)
+    assert np.array_equal(r["y"], r1["y"])
+
+
+def test_omission_bucketing_leaves_omitted_pairs_out():
+    ids = np.array([[3, -1, 0], [3, 1, -1]], dtype=np.int32)
+    counts, offsets, perm, inv = oracle.bucket(ids, 4, 1)
+    assert list(counts) == [1, 1, 0, 2, 2]
+    assert list(offsets) == [0, 1, 2, 2, 4, 6]
+    assert list(perm) == [2, 4, 0, 3, 6, 7]
+    assert list(inv) == [2, -1, 0, 3, 1, -1, 4, 5]
