@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--path", choices=["auto", "decode", "prefill"], default="auto",
                     help="kernel path (auto: decode kernels for small batches)")
     ap.add_argument("--layers", type=int, default=None, help="distinct layer instances in the rotation")
+    ap.add_argument("--omit", type=float, default=0.0,
+                    help="marginal-expert omission threshold (routed pairs with a gate below it are left out; "
+                         "0: off)")
     ap.add_argument("--packed-scales", action="store_true",
                     help="MXFP4 workloads: the same experts in the packed scale store (a base E8M0 byte per row "
                          "and a 4-bit delta per block)")
@@ -110,7 +113,7 @@ class Workload:
         self.layers = []
         for l in range(nl):
             host = synth.make_layer(spec, layer=l)
-            self.layers.append(q.DeviceLayer.from_layer(host, device=dev))
+            self.layers.append(q.DeviceLayer.from_layer(host, device=dev, omit_below=args.omit))
             del host
             log(args, f"layer instance {l + 1}/{nl} resident ({time.time() - t0:.1f} s)")
         self.forwards_per_step = nl if self.stacked else 1
@@ -169,7 +172,8 @@ class Workload:
         for s in range(self.rotation()):
             def fn(l, x, y):
                 _, dbg = self.q.forward(self.layers[l], x, self.spec.x_dtype, y=y, ws=self.ws, debug=True)
-                out.append(len(np.unique(dbg["ids"].cpu().numpy())))
+                ids = dbg["ids"].cpu().numpy()
+                out.append(len(np.unique(ids[ids >= 0])))  # -1: an omitted pair
 
             def fn_rms(l, yp, y):
                 xr = self.q.rms_rescale(yp, RMS_EPS)
@@ -402,7 +406,8 @@ def main():
     workload = (f"{args.config}: {spec.name}, T={main_run['T']}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
                 f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers (RMS rescale between)"
                                              if stacked else "")
-                + (f", {args.path} kernels forced" if args.path != "auto" else ""))
+                + (f", {args.path} kernels forced" if args.path != "auto" else "")
+                + (f", marginal experts omitted below a gate of {args.omit}" if args.omit > 0 else ""))
     result = {
         "metric": METRIC,
         "value": main_run["value"],

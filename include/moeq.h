@@ -126,7 +126,16 @@ typedef struct {
   const void *const *down;     /* device array of E+has_shared device pointers -> packed [H][I] */
   const int8_t *codebook;      /* CB4: [16] int8; MXFP4 and MXFP4_PS: must be NULL */
   const float *shared_gate_w;  /* [H] fp32, or NULL (shared weight 1); ignored without a shared expert */
+  float omit_below;            /* marginal-expert omission threshold tau in [0, 1]; 0: off (below) */
 } moe_layer;
+
+/* Marginal-expert omission ("Nebula" page, "Benchmark results": a 10% threshold for
+ * omitting marginal experts; the renormalisation is this library's reading).  With
+ * omit_below = tau > 0, after the top-k softmax a routed pair j > 0 whose gate
+ * g[t,j] < tau (compared in fp64) is omitted: it reports expert id -1 and weight 0, is in
+ * no bucket and contributes nothing; the kept gates are renormalised to sum to 1,
+ * g'[t,j] = exp(l_j - l_0) / sum over kept j' of exp(l_j' - l_0).  The first (largest)
+ * pair is always kept; the shared expert is never omitted.  tau = 0 changes nothing. */
 
 /* [host] Bytes of one packed matrix [rows][cols] in the layout above; 0 if cols is not
  * a positive multiple of 32, rows is not a positive multiple of 16, or the format is
@@ -142,16 +151,17 @@ size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols);
 size_t moe_workspace_bytes(const moe_layer *L, int32_t T_max);
 
 /* Router logits, top-k and softmax gates for T tokens of x ([T][H], dtype
- * x_dtype).  Writes topk_ids [T][k] int32 and topk_w [T][k] fp32. */
+ * x_dtype).  Writes topk_ids [T][k] int32 and topk_w [T][k] fp32 (with omission:
+ * id -1 and weight 0 for an omitted pair). */
 int moe_router_topk(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T,
                     int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
                     void *stream);
 
 /* Stable counting sort of the pairs p = t*k + j by expert (increasing p inside
  * a bucket); with a shared expert, pairs T*k + t form bucket E.
- * counts [E+1], offsets [E+2] (exclusive prefix sums, offsets[E+1] = #pairs),
- * perm [T*k + T*has_shared] (pair ids in bucket order).  Every topk_ids value
- * must lie in [0, E). */
+ * counts [E+1], offsets [E+2] (exclusive prefix sums, offsets[E+1] = the pairs placed),
+ * perm [T*k + T*has_shared] (pair ids in bucket order, then -1 past offsets[E+1]).
+ * Every topk_ids value must lie in [0, E) or be -1 (an omitted pair: in no bucket). */
 int moe_bucket(const moe_layer *L, const int32_t *topk_ids, int32_t T, int32_t *counts,
                int32_t *offsets, int32_t *perm, void *ws, size_t ws_bytes, void *stream);
 

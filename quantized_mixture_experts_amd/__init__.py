@@ -32,7 +32,8 @@ class MoeLayerC(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("has_shared", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p), ("gate_up", ctypes.c_void_p),
-                ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p), ("shared_gate_w", ctypes.c_void_p)]
+                ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p), ("shared_gate_w", ctypes.c_void_p),
+                ("omit_below", ctypes.c_float)]
 
 
 class MoeError(RuntimeError):
@@ -102,7 +103,7 @@ class DeviceLayer:
 
     def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, wfmt: int, has_shared: int,
                  router_w, router_b, gate_up: Sequence[np.ndarray], down: Sequence[np.ndarray],
-                 codebook=None, shared_gate_w=None, device="cuda"):
+                 codebook=None, shared_gate_w=None, device="cuda", omit_below: float = 0.0):
         import torch
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.wfmt, self.has_shared = wfmt, has_shared
@@ -133,14 +134,23 @@ class DeviceLayer:
         self.expert_stride, self.gu_offset, self.dn_offset = stride, 0, a_gu
         self.c = MoeLayerC(hidden, inter, n_experts, top_k, wfmt, has_shared, _ptr(self.router_w),
                            _ptr(self.router_b), _ptr(self.gate_up_ptrs), _ptr(self.down_ptrs), _ptr(self.codebook),
-                           _ptr(self.shared_gate_w))
+                           _ptr(self.shared_gate_w), omit_below)
+
+    @property
+    def omit_below(self) -> float:
+        """Marginal-expert omission threshold of the descriptor (0: off)."""
+        return self.c.omit_below
+
+    @omit_below.setter
+    def omit_below(self, tau: float):
+        self.c.omit_below = tau
 
     @classmethod
-    def from_layer(cls, layer, device="cuda"):
+    def from_layer(cls, layer, device="cuda", omit_below: float = 0.0):
         """From a host layer object with the generator's attribute names."""
         return cls(layer.hidden, layer.inter, layer.n_experts, layer.top_k, layer.wfmt, layer.has_shared,
                    layer.router_w, layer.router_b, layer.gate_up, layer.down, layer.codebook,
-                   layer.shared_gate_w, device)
+                   layer.shared_gate_w, device, omit_below)
 
     def workspace_bytes(self, T: int) -> int:
         return lib().moe_workspace_bytes(ctypes.byref(self.c), T)

@@ -52,6 +52,7 @@ int validate_layer(const moe_layer* L) {
   if (!aligned16(L->router_w) || (L->router_b && !aligned4(L->router_b))) return MOE_ERR_ALIGNMENT;
   if (L->has_shared && L->shared_gate_w && !aligned16(L->shared_gate_w)) return MOE_ERR_ALIGNMENT;
   if (!aligned16(L->gate_up) || !aligned16(L->down)) return MOE_ERR_ALIGNMENT;
+  if (!(L->omit_below >= 0.0f && L->omit_below <= 1.0f)) return MOE_ERR_INVALID_ARG;  // NaN fails too
   return MOE_OK;
 }
 
@@ -118,6 +119,7 @@ LayerArgs args_of(const moe_layer* L) {
   LayerArgs a;
   a.H = L->hidden; a.I = L->inter; a.E = L->n_experts; a.k = L->top_k;
   a.wfmt = L->wfmt; a.has_shared = L->has_shared;
+  a.omit_below = L->omit_below;
   a.router_w = L->router_w; a.router_b = L->router_b;
   a.gate_up = reinterpret_cast<const uint8_t* const*>(L->gate_up);
   a.down = reinterpret_cast<const uint8_t* const*>(L->down);

@@ -65,6 +65,7 @@ __device__ __forceinline__ uint32_t pk_scale_cb(int kb, int m, int nkb) {
 // Layer descriptor as the kernels see it (copied by value into kernel arguments).
 struct LayerArgs {
   int H, I, E, k, wfmt, has_shared;
+  float omit_below;  // marginal-expert omission threshold (0: every routed pair kept)
   const float* router_w;
   const float* router_b;
   const uint8_t* const* gate_up;
@@ -210,6 +211,25 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   v += dpp_i32<kDppRowRor8>(v);
   return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
          __builtin_amdgcn_readlane(v, 48);
+}
+
+// Softmax gate of routed pair j = lane (< k) of one token: lj its logit, l0 the token's
+// largest: g_j = exp(lj - l0) / sum_j' exp(l_j' - l0) in fp64.  With omit_below > 0
+// (uniform) a pair j > 0 whose g_j is below omit_below (decided in fp64) is omitted: it
+// gets gate 0 and false is returned; the kept gates are renormalised over the kept pairs,
+// exp(lj - l0) / sum over kept.  Every lane of the wave calls this.
+__device__ __forceinline__ bool pair_gate(double lj, double l0, int k, float omit_below, float* g) {
+  const int lane = threadIdx.x & 63;
+  const double z = lane < k ? exp(lj - l0) : 0.0;
+  const double zs = wave_sum_f64(z);
+  bool keep = lane < k;
+  double zk = zs;
+  if (omit_below > 0.0f) {
+    keep = keep && (lane == 0 || z / zs >= (double)omit_below);
+    zk = wave_sum_f64(keep ? z : 0.0);
+  }
+  *g = keep ? (float)(z / zk) : 0.0f;
+  return keep;
 }
 
 // ---- top-k of NT tokens per wave (NT = 1 or 2, processed side by side) -------------------

@@ -256,7 +256,8 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   const int nb = E + 1;
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  for (int p = tid; p < P; p += kRouteThreads) atomicAdd(&s_cnt[s_exp[p]], 1);
+  for (int p = tid; p < P; p += kRouteThreads)
+    if (s_exp[p] >= 0) atomicAdd(&s_cnt[s_exp[p]], 1);  // expert -1: an omitted pair
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -280,6 +281,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   }
   __syncthreads();
   const int n_active = s_incl[nb - 1] >> 16;
+  const int placed = s_incl[nb - 1] & 0xFFFF;  // pairs in the buckets (omitted ones are not)
   for (int e = tid; e < nb; e += kRouteThreads) {
     const int c = s_cnt[e];
     const int off = (s_incl[e] & 0xFFFF) - c;
@@ -303,12 +305,17 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     sl.down = nullptr;
   }
   if (tid == 0) {
-    w.offsets[nb] = P;
-    if (dbg_offsets) dbg_offsets[nb] = P;
+    w.offsets[nb] = placed;
+    if (dbg_offsets) dbg_offsets[nb] = placed;
     w.active[0] = n_active;
+  }
+  for (int i = placed + tid; i < P; i += kRouteThreads) {  // past the placed pairs
+    w.perm[i] = -1;
+    if (dbg_perm) dbg_perm[i] = -1;
   }
   for (int p = tid; p < P; p += kRouteThreads) {
     const int e = s_exp[p];
+    if (e < 0) continue;
     int r = 0;
     for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
     const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
@@ -467,13 +474,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       else topk_wave<16>(w.logits, E, k, T, t0, t1, s_exp, s_l);
     }
     for (int t = t0; t < T && t <= t1; t += kWaves) {
-      const double l0 = s_l[t * k];
-      const double z = lane < k ? exp(s_l[t * k + lane] - l0) : 0.0;
-      const double zs = wave_sum_f64(z);
+      float gte;
+      const bool keep = pair_gate(s_l[t * k + min(lane, k - 1)], s_l[t * k], k, L.omit_below, &gte);
       if (lane < k) {
         const int p = t * k + lane;
-        const float gte = (float)(z / zs);
-        const int id = s_exp[p];
+        const int id = keep ? s_exp[p] : -1;  // an omitted pair is in no bucket
+        s_exp[p] = id;
         w.ids[p] = id;
         w.pair_w[p] = gte;
         if (dbg_ids) dbg_ids[p] = id;
@@ -856,7 +862,7 @@ __device__ __forceinline__ void dec_combine_cols(const LayerArgs& L, int T, cons
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (j0 + u < k) s = fmaf(wv[u], ov[u], s);
+        if (j0 + u < k && wv[u] != 0.0f) s = fmaf(wv[u], ov[u], s);  // weight 0: omitted, o not written
     }
     if (L.has_shared) {
       const float o = __hip_atomic_load(&w.o[(size_t)(T * k + t) * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -954,19 +960,21 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
         uint32_t e[kMaxPairsT1];
+        float pw[kMaxPairsT1];
         bool miss = false;
 #pragma unroll
         for (int u = 0; u < kMaxPairsT1; ++u) {
           const int p = min(u, P1 - 1);
+          pw[u] = w.pair_w[p];
           e[u] = p == p_own ? mine
                             : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          miss |= e[u] == 0u;
+          miss |= e[u] == 0u && pw[u] != 0.0f;  // an omitted pair (weight 0) posts nothing
         }
         if (!miss) {
           float sum = 0.f;
 #pragma unroll
           for (int u = 0; u < kMaxPairsT1; ++u)
-            if (u < P1) sum = fmaf(w.pair_w[u], __uint_as_float(~e[u]), sum);
+            if (u < P1 && pw[u] != 0.0f) sum = fmaf(pw[u], __uint_as_float(~e[u]), sum);
           y[col] = w.resid ? rv + sum : sum;
         }
       }

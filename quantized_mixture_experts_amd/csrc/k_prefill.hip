@@ -794,7 +794,7 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j0 + u < k) s = fmaf(wv[u], ov[u], s);
+      if (j0 + u < k && wv[u] != 0.0f) s = fmaf(wv[u], ov[u], s);  // weight 0: omitted, o not written
   }
   if (has_shared) s = fmaf(pair_w[T * k + t], o[(size_t)(T * k + t) * H + n], s);
   y[(size_t)t * H + n] = resid ? resid[(size_t)t * H + n] + s : s;

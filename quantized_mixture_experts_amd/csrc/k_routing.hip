@@ -145,12 +145,10 @@ __global__ __launch_bounds__(256) void k_topk(LayerArgs L, int T, const double* 
   else if (nper <= 4) topk_one<4>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
   else if (nper <= 8) topk_one<8>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
   else topk_one<16>(logits, E, k, t, s_exp[wave], s_l[wave], nsplit, sstride);
-  const double l0 = s_l[wave][0];
-  const double z = lane < k ? exp(s_l[wave][lane] - l0) : 0.0;
-  const double zs = wave_sum_f64(z);
+  float g;
+  const bool keep = pair_gate(s_l[wave][min(lane, k - 1)], s_l[wave][0], k, L.omit_below, &g);
   if (lane < k) {
-    const float g = (float)(z / zs);
-    const int id = s_exp[wave][lane];
+    const int id = keep ? s_exp[wave][lane] : -1;  // an omitted pair is in no bucket
     ids[t * k + lane] = id;
     pair_w[t * k + lane] = g;
     if (dbg_ids) dbg_ids[t * k + lane] = id;
@@ -253,19 +251,24 @@ __global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(int T, int k, int 
   if (e == E) {
     const int cnt = has_shared ? T : 0;
     const int ngs = (cnt + kGroupPairs - 1) / kGroupPairs;
+    // lt = the routed pairs placed in buckets 0 .. E-1 (all Pr, unless some were omitted)
     if (tid == 0) {
-      counts[E] = cnt; offsets[E] = Pr; offsets[E + 1] = Pr + cnt;
+      counts[E] = cnt; offsets[E] = lt; offsets[E + 1] = lt + cnt;
       active[0] = total + (cnt > 0);
       if (cnt > 0) active[1 + total] = E;
       *n_groups = g_total + ngs;
       if (dbg_counts) dbg_counts[E] = cnt;
-      if (dbg_offsets) { dbg_offsets[E] = Pr; dbg_offsets[E + 1] = Pr + cnt; }
+      if (dbg_offsets) { dbg_offsets[E] = lt; dbg_offsets[E + 1] = lt + cnt; }
     }
     for (int i = tid; i < ngs; i += NT)
-      groups[g_total + i] = make_int4(E, Pr + kGroupPairs * i, min(kGroupPairs, cnt - kGroupPairs * i), 0);
+      groups[g_total + i] = make_int4(E, lt + kGroupPairs * i, min(kGroupPairs, cnt - kGroupPairs * i), 0);
     for (int t = tid; t < cnt; t += NT) {
-      perm[Pr + t] = Pr + t;
-      if (dbg_perm) dbg_perm[Pr + t] = Pr + t;
+      perm[lt + t] = Pr + t;
+      if (dbg_perm) dbg_perm[lt + t] = Pr + t;
+    }
+    for (int i = lt + cnt + tid; i < Pr + cnt; i += NT) {  // past the placed pairs
+      perm[i] = -1;
+      if (dbg_perm) dbg_perm[i] = -1;
     }
     return;
   }

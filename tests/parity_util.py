@@ -24,11 +24,14 @@ def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
     return worst, tol
 
 
-def routing_mismatches(layer, x64: np.ndarray, ids_gpu: np.ndarray, ids_ref: np.ndarray, logits_ref: np.ndarray):
+def routing_mismatches(layer, x64: np.ndarray, ids_gpu: np.ndarray, ids_ref: np.ndarray, logits_ref: np.ndarray,
+                       gates_pre=None, omit_below: float = 0.0):
     """Tokens whose GPU ids differ from the oracle's.  Returns (excused, unexcused): a
     mismatch is excused only when every differing position is a near-tie the fp64
     evaluation cannot order independently of summation order:
-    |l_a - l_b| <= 2^-40 * sum_h |x_h W_eh| (+|b_e|)."""
+    |l_a - l_b| <= 2^-40 * sum_h |x_h W_eh| (+|b_e|), or, with omission, a pair whose
+    oracle gate before omission lies within 2^-40 of the threshold (kept on one side,
+    omitted on the other)."""
     excused, bad = [], []
     W = np.asarray(layer.router_w, dtype=np.float64)
     b = None if layer.router_b is None else np.abs(np.asarray(layer.router_b, dtype=np.float64))
@@ -40,7 +43,10 @@ def routing_mismatches(layer, x64: np.ndarray, ids_gpu: np.ndarray, ids_ref: np.
             a_, b_ = int(ids_ref[t, j]), int(ids_gpu[t, j])
             if a_ == b_:
                 continue
-            if not (0 <= b_ < W.shape[0]):
+            if (a_ < 0 or b_ < 0) and gates_pre is not None and omit_below > 0 and \
+                    abs(gates_pre[t, j] - omit_below) <= NEAR_TIE * omit_below:
+                continue
+            if not (0 <= a_ < W.shape[0] and 0 <= b_ < W.shape[0]):
                 ok = False
                 break
             gap = abs(logits_ref[t, a_] - logits_ref[t, b_])
@@ -51,24 +57,32 @@ def routing_mismatches(layer, x64: np.ndarray, ids_gpu: np.ndarray, ids_ref: np.
     return excused, bad
 
 
-def check_forward(layer, x, x_dtype, y_gpu, dbg, ref=None, tokens=None, what=""):
+def check_forward(layer, x, x_dtype, y_gpu, dbg, ref=None, tokens=None, what="", omit_below: float = 0.0):
     """Compare one moe_forward call with the oracle: ids exact (near-ties excused and
-    re-checked with the GPU's routing), gates within 1e-6, bucketing exact, y within
-    tolerance.  `tokens` restricts the y and routing comparison to a sample."""
+    re-checked with the GPU's routing), gates within 1e-6, bucketing exact (the perm
+    entries past the placed pairs are -1), y within tolerance.  `tokens` restricts the y
+    and routing comparison to a sample.  omit_below: the layer's omission threshold (the
+    fp32 value the descriptor holds)."""
     T = x.shape[0]
-    ref = oracle.moe_forward(layer, x, x_dtype) if ref is None else ref
+    ref = oracle.moe_forward(layer, x, x_dtype, omit_below=omit_below) if ref is None else ref
     x64 = oracle.activations_f64(x, x_dtype)
     ids_gpu = dbg["ids"].cpu().numpy()
     gates_gpu = dbg["gates"].cpu().numpy()
     sel = np.arange(T) if tokens is None else np.asarray(tokens)
-    excused, bad = routing_mismatches(layer, x64[sel], ids_gpu[sel], ref["ids"], ref["logits"])
+    gates_pre = None
+    if omit_below > 0:
+        gates_pre = oracle.topk_softmax(ref["logits"][sel] if tokens is None else ref["logits"], layer.top_k)[1]
+    excused, bad = routing_mismatches(layer, x64[sel], ids_gpu[sel], ref["ids"], ref["logits"], gates_pre, omit_below)
     assert not bad, f"{what}: expert ids differ from the oracle for tokens {bad[:8]}"
     keep = np.setdiff1d(np.arange(len(sel)), excused)
     assert np.abs(gates_gpu[sel][keep] - ref["gates"][keep]).max(initial=0) <= 1e-6, f"{what}: gates"
     if tokens is None:
+        placed = int(ref["offsets"][-1])
+        perm = dbg["perm"].cpu().numpy()
         assert np.array_equal(dbg["counts"].cpu().numpy(), ref["counts"]), f"{what}: counts"
         assert np.array_equal(dbg["offsets"].cpu().numpy(), ref["offsets"]), f"{what}: offsets"
-        assert np.array_equal(dbg["perm"].cpu().numpy(), ref["perm"]), f"{what}: perm"
+        assert np.array_equal(perm[:placed], ref["perm"]), f"{what}: perm"
+        assert np.all(perm[placed:] == -1), f"{what}: perm past the placed pairs"
     yg = y_gpu.cpu().numpy()[sel]
     yr = ref["y"].copy()
     if excused:

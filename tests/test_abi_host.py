@@ -49,7 +49,8 @@ FAKE = 0x10000  # a non-null, 256-aligned stand-in for device pointers (never de
 
 def layer(**kw):
     d = dict(hidden=256, inter=128, n_experts=8, top_k=2, wfmt=q.WFMT_CB4, has_shared=0,
-             router_w=FAKE, router_b=None, gate_up=FAKE, down=FAKE, codebook=FAKE, shared_gate_w=None)
+             router_w=FAKE, router_b=None, gate_up=FAKE, down=FAKE, codebook=FAKE, shared_gate_w=None,
+             omit_below=0.0)
     d.update(kw)
     return q.MoeLayerC(*[d[f] for f, _ in q.MoeLayerC._fields_])
 
@@ -63,6 +64,8 @@ def ws_bytes(L, lay, T):
     (dict(top_k=9), q.MOE_ERR_UNSUPPORTED), (dict(top_k=0), q.MOE_ERR_INVALID_ARG),
     (dict(n_experts=2000, top_k=2), q.MOE_ERR_UNSUPPORTED), (dict(wfmt=7), q.MOE_ERR_INVALID_ARG),
     (dict(codebook=None), q.MOE_ERR_INVALID_ARG), (dict(wfmt=q.WFMT_MXFP4), q.MOE_ERR_INVALID_ARG),
+    (dict(omit_below=-0.1), q.MOE_ERR_INVALID_ARG), (dict(omit_below=1.5), q.MOE_ERR_INVALID_ARG),
+    (dict(omit_below=float("nan")), q.MOE_ERR_INVALID_ARG),
     (dict(router_w=None), q.MOE_ERR_INVALID_ARG), (dict(gate_up=None), q.MOE_ERR_INVALID_ARG),
     (dict(router_w=FAKE + 4), q.MOE_ERR_ALIGNMENT), (dict(has_shared=2), q.MOE_ERR_INVALID_ARG),
     (dict(hidden=32768), q.MOE_ERR_UNSUPPORTED),
