@@ -64,6 +64,7 @@ import numpy as np
 WFMT_MXFP4 = 1
 WFMT_CB4 = 2
 WFMT_MXFP4_PS = 3   # MXFP4 codes with the packed scale store (one base byte per row + 4-bit deltas)
+WFMT_AFF3 = 4       # 3-bit affine codes, groups of 64 values with an fp16 scale and an fp16 bias
 X_F32 = 0
 X_BF16 = 1
 
@@ -119,6 +120,11 @@ def packed_size(wfmt: int, rows: int, cols: int) -> int:
     nblocks = rows * cols // 32
     if wfmt == WFMT_MXFP4_PS:
         return scale_off + rows + nblocks // 2
+    if wfmt == WFMT_AFF3:
+        if cols % 128:
+            raise ValueError("the 3-bit affine format needs cols a multiple of 128")
+        code_bytes = rows * cols * 3 // 8
+        return (code_bytes + 255) // 256 * 256 + rows * (cols // 64) * 4
     return scale_off + nblocks * (1 if wfmt == WFMT_MXFP4 else 2)
 
 
@@ -164,9 +170,57 @@ def packed_scale_store_exponents(packed: np.ndarray, rows: int, cols: int) -> np
     return base[:, None] + delta
 
 
+def affine3_fields(packed: np.ndarray, rows: int, cols: int):
+    """The 3-bit codes q [rows][cols] and the fp16 scale and bias bit patterns
+    [rows][cols/64] of a matrix in the 3-bit affine format.
+
+    The format is the one "Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers"
+    names ("Where every weight lives": 3-bit MLX affine, group 64, 2.15 MB per expert;
+    "Quality": about 3.5 bits per weight with scales and biases): each group of 64
+    consecutive values of a row has a 16-bit scale s and bias b, and a value is
+    s * q + b with a 3-bit code q.  The pages do not give the bit packing; the reading:
+    rows in tiles of 16 (t, m = row // 16, row % 16), columns in steps of 128 (cols % 128
+    == 0).  For column c of step st, with cc = c - 128 st, j = cc // 32, g = (cc % 32) // 8,
+    i = cc % 8: the lane l = 16 g + m of unit (t, st) owns 12 bytes, three little-endian
+    32-bit words, at byte t*6*cols + 768*st + 12*l; the value is member i % 2 of pair
+    P = 4 j + i // 2; for P < 15 it sits at bits 3 (P % 5) + 16 (i % 2) .. +2 of word P // 5,
+    for P = 15 bit k of q is bit 15 + 16 (i % 2) of word k.  The scale plane starts at
+    round_up(rows*cols*3/8, 256); unit (t, st) is 128 bytes at t*cols + 128*st, row m's
+    8 bytes at 8 m: s and b of the step's first group (columns 0..63), then of its
+    second, fp16 little-endian."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    soff = (rows * cols * 3 // 8 + 255) // 256 * 256
+    row = np.arange(rows)[:, None]
+    col = np.arange(cols)[None, :]
+    t, m = row // 16, row % 16
+    st, cc = col // 128, col % 128
+    j, g, i = cc // 32, (cc % 32) // 8, cc % 8
+    lane = 16 * g + m
+    base = t * 6 * cols + 768 * st + 12 * lane
+    P = 4 * j + i // 2
+    half = i % 2
+    words = packed[:soff].view("<u4")
+    w = [words[(base + 4 * k) // 4].astype(np.int64) for k in range(3)]
+    q_lo = np.zeros((rows, cols), dtype=np.int64)
+    for k in range(3):   # words 0, 1, 2 hold pairs 0..4, 5..9, 10..14
+        sel = (P // 5) == k
+        q_lo = np.where(sel & (P < 15), (w[k] >> (3 * (P % 5) + 16 * half)) & 7, q_lo)
+    q15 = sum(((w[k] >> (15 + 16 * half)) & 1) << k for k in range(3))
+    q = np.where(P == 15, q15, q_lo)
+    sp = packed[soff:soff + rows * (cols // 64) * 4].view("<u2")
+    G = np.arange(cols // 64)[None, :]
+    sidx = (row // 16) * (cols // 64) * 32 + 64 * (G // 2) + 4 * (row % 16) + 2 * (G % 2)
+    return q, sp[sidx], sp[sidx + 1]
+
+
 def dequant(wfmt: int, packed: np.ndarray, codebook, rows: int, cols: int) -> np.ndarray:
     """Dense fp64 [rows][cols] from one packed matrix (every element exact in fp64)."""
     packed = np.asarray(packed, dtype=np.uint8)
+    if wfmt == WFMT_AFF3:
+        q, sbits, bbits = affine3_fields(packed, rows, cols)
+        s = np.repeat(fp16_value(sbits), 64, axis=1)
+        b = np.repeat(fp16_value(bbits), 64, axis=1)
+        return s * q + b   # exact: fp16 * 3-bit + fp16 needs at most 43 significant bits
     code_bytes = rows * cols // 2
     scale_off = (code_bytes + 255) // 256 * 256
     nblocks = rows * cols // 32

@@ -40,6 +40,7 @@ import numpy as np
 WFMT_MXFP4 = 1
 WFMT_CB4 = 2
 WFMT_MXFP4_PS = 3   # MXFP4 codes with the packed scale store
+WFMT_AFF3 = 4       # 3-bit affine, groups of 64 with an fp16 scale and bias
 X_F32 = 0
 X_BF16 = 1
 
@@ -59,6 +60,8 @@ def scale_plane_offset(rows: int, cols: int) -> int:
 
 def packed_nbytes(wfmt: int, rows: int, cols: int) -> int:
     nblk = rows * cols // 32
+    if wfmt == WFMT_AFF3:
+        return round_up(rows * cols * 3 // 8, 256) + rows * (cols // 64) * 4
     if wfmt == WFMT_MXFP4_PS:
         return scale_plane_offset(rows, cols) + rows + nblk // 2
     return scale_plane_offset(rows, cols) + nblk * (1 if wfmt == WFMT_MXFP4 else 2)
@@ -158,12 +161,49 @@ def to_packed_scale_store(code_rows: np.ndarray, e8m0_rows: np.ndarray) -> np.nd
     return out
 
 
+def to_affine3(q: np.ndarray, sbits: np.ndarray, bbits: np.ndarray) -> np.ndarray:
+    """3-bit codes q [N][K] (0..7), fp16 scale and bias bits [N][K/64] in the 3-bit affine
+    storage: rows in tiles of 16, columns in steps of 128 (K % 128 == 0); the lane
+    l = 16 g + m of unit (tile t, step s) owns 12 bytes (three little-endian words) at
+    t*6K + 768 s + 12 l holding the 32 values of row m at columns 32 j + 8 g + i
+    (j, i < 4, 8): pair P = 4 j + i // 2, member i % 2; pairs 0..14 at bits
+    3 (P % 5) + 16 (i % 2) of word P // 5, pair 15 with bit k of q at bit 15 + 16 (i % 2)
+    of word k.  Then, at round_up(N K 3/8, 256), per (t, s) 128 bytes: row m's
+    (scale, bias) of the step's two groups at 8 m."""
+    N, K = q.shape
+    assert N % 16 == 0 and K % 128 == 0
+    q = q.astype(np.uint32).reshape(N // 16, 16, K // 128, 4, 4, 8)   # t, m, s, j, g, i
+    q = q.transpose(0, 2, 4, 1, 3, 5).reshape(N // 16, K // 128, 64, 16, 2)  # t, s, lane, P, half
+    words = np.zeros((N // 16, K // 128, 64, 3), dtype=np.uint32)
+    for P in range(15):
+        for half in range(2):
+            words[..., P // 5] |= q[..., P, half] << np.uint32(3 * (P % 5) + 16 * half)
+    for k in range(3):
+        for half in range(2):
+            words[..., k] |= ((q[..., 15, half] >> np.uint32(k)) & np.uint32(1)) << np.uint32(15 + 16 * half)
+    code = words.astype("<u4").view(np.uint8).reshape(-1)
+    off = round_up(N * K * 3 // 8, 256)
+    out = np.zeros(packed_nbytes(WFMT_AFF3, N, K), dtype=np.uint8)
+    out[:code.size] = code
+    sb = np.stack([sbits.reshape(N // 16, 16, K // 128, 2), bbits.reshape(N // 16, 16, K // 128, 2)], axis=-1)
+    sb = sb.transpose(0, 2, 1, 3, 4).astype("<u2").reshape(-1)            # t, s, m, group, (s, b)
+    out[off:off + 2 * sb.size] = sb.view(np.uint8)
+    return out
+
+
 def make_packed(spec: WeightSpec, rows: int, cols: int, seed_key: Sequence[int],
                 codes_tid: int, scales_tid: int) -> np.ndarray:
     """One packed matrix [rows][cols].  The code bytes (row-major, both nibbles uniform) and
     the scales (row-major) are drawn first, then stored tile-major."""
     assert cols % 32 == 0 and rows % 16 == 0
     nblk = rows * cols // 32
+    if spec.wfmt == WFMT_AFF3:
+        # q uniform over 0..7; s ~ U(lo, hi) and b = -s (3.5 + U(-0.5, 0.5)), both rounded to fp16
+        q = _rng(*seed_key, codes_tid).integers(0, 8, size=(rows, cols), dtype=np.uint8)
+        srng = _rng(*seed_key, scales_tid)
+        sc = srng.uniform(spec.scale_lo, spec.scale_hi, size=(rows, cols // 64))
+        bias = -sc * (3.5 + srng.uniform(-0.5, 0.5, size=sc.shape))
+        return to_affine3(q, sc.astype(np.float16).view(np.uint16), bias.astype(np.float16).view(np.uint16))
     code_rows = random_bytes(_rng(*seed_key, codes_tid), rows * cols // 2).reshape(rows, cols // 2)
     srng = _rng(*seed_key, scales_tid)
     if spec.wfmt in (WFMT_MXFP4, WFMT_MXFP4_PS):
@@ -285,6 +325,12 @@ CONFIGS = {
     # prefill chunks, no bias
     "c5a": LayerSpec("c5a_prefill_cb4", T=1024, hidden=2048, inter=512, n_experts=256, top_k=8,
                      has_shared=1, weights=_CB4, x_dtype=X_BF16, router_std=0.02, bias="none", seed=1005),
+    # the layer of "Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers" (hidden
+    # 2,560, 512 routed experts, top-10, intermediate 640, one shared expert) with its
+    # 3-bit affine group-64 experts, at the verify window's 17 tokens
+    "aff3": LayerSpec("aff3_flashnext_3bit_verify", T=17, hidden=2560, inter=640, n_experts=512, top_k=10,
+                      has_shared=1, weights=WeightSpec(WFMT_AFF3, 0.01, 0.05), x_dtype=X_BF16, router_std=0.02,
+                      bias="zipf", zipf_s=1.1, seed=1007),
     "c5b": LayerSpec("c5b_prefill_mxfp4", T=1024, hidden=2880, inter=2880, n_experts=128, top_k=4,
                      has_shared=0, weights=_MX, x_dtype=X_BF16, router_std=0.02, bias="none", seed=1006),
 }

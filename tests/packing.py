@@ -9,7 +9,7 @@ MXFP4 (g, m) at 16g + m, CB4 (m, g) at m*r + g.
 """
 import numpy as np
 
-MXFP4, CB4, MXFP4_PS = 1, 2, 3
+MXFP4, CB4, MXFP4_PS, AFF3 = 1, 2, 3, 4
 
 
 def pack(wfmt, codes, scales):
@@ -63,4 +63,42 @@ def pack_scale_store(codes, e8m0):
             assert 0 <= d <= 15
             at = scale_off + rows + i // 2
             out[at] |= (d if i % 2 == 0 else d << 4)
+    return out
+
+
+def pack_affine3(q, sbits, bbits):
+    """The 3-bit affine storage of codes q [rows][cols] (0..7) and fp16 scale/bias bit
+    patterns [rows][cols/64], value by value: tiles of 16 rows, steps of 128 columns; for
+    column c of step st (cc = c - 128 st, j = cc // 32, g = cc % 32 // 8, i = cc % 8) the
+    word holding it is one of three at byte t*6*cols + 768 st + 12 (16 g + m); pair
+    P = 4 j + i // 2, member i % 2; P < 15: bits 3 (P % 5) + 16 (i % 2) of word P // 5;
+    P = 15: bit k of q at bit 15 + 16 (i % 2) of word k.  Scales and biases at
+    round_up(rows*cols*3/8, 256) + t*cols + 128 st + 8 m + 4 (group in step) (+2: bias)."""
+    q = np.asarray(q)
+    rows, cols = q.shape
+    code = (rows * cols * 3 // 8 + 255) // 256 * 256
+    out = np.zeros(code + rows * (cols // 64) * 4, dtype=np.uint8)
+    words = np.zeros(code // 4, dtype=np.uint64)
+    for row in range(rows):
+        t, m = divmod(row, 16)
+        for c in range(cols):
+            st, cc = divmod(c, 128)
+            j, r32 = divmod(cc, 32)
+            g, i = divmod(r32, 8)
+            base = (t * 6 * cols + 768 * st + 12 * (16 * g + m)) // 4
+            P, half = 4 * j + i // 2, i % 2
+            v = int(q[row, c])
+            if P < 15:
+                words[base + P // 5] |= v << (3 * (P % 5) + 16 * half)
+            else:
+                for k in range(3):
+                    words[base + k] |= ((v >> k) & 1) << (15 + 16 * half)
+    out[:code] = words.astype("<u4").view(np.uint8)
+    for row in range(rows):
+        t, m = divmod(row, 16)
+        for G in range(cols // 64):
+            st, gg = divmod(G, 2)
+            at = code + t * cols + 128 * st + 8 * m + 4 * gg
+            for k, v in ((0, int(sbits[row, G])), (2, int(bbits[row, G]))):
+                out[at + k], out[at + k + 1] = v & 0xFF, v >> 8
     return out

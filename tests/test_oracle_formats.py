@@ -234,3 +234,60 @@ def test_bf16_rounding_two_implementations():
     # ties go to even
     assert oracle.round_to_bf16_bits(np.array([1 + 2 ** -8]))[0] == 0x3F80
     assert oracle.round_to_bf16_bits(np.array([1 + 3 * 2 ** -8]))[0] == 0x3F82
+
+
+# ---------------------------------------------------------------------------
+# 3-bit affine, group 64 ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers")
+# ---------------------------------------------------------------------------
+def test_affine3_size_is_the_pages():
+    """An expert of the page's model (hidden 2,560, intermediate 640) in 3-bit codes with
+    a 16-bit scale and bias per 64 values: 3.5 bits per weight, 2,150,400 B, the page's
+    2.15 MB per expert."""
+    g = json.load(open(os.path.join(GOLDEN, "page_byte_counts.json")))["affine3_expert_bytes"]
+    H, I = g["shape"]["hidden"], g["shape"]["inter"]
+    got = oracle.packed_size(oracle.WFMT_AFF3, 2 * I, H) + oracle.packed_size(oracle.WFMT_AFF3, H, I)
+    assert got == g["value"] == 3 * H * I * 7 // 16
+    assert round(got / 1e6, 2) == 2.15
+    assert synth.packed_nbytes(synth.WFMT_AFF3, 2 * I, H) + synth.packed_nbytes(synth.WFMT_AFF3, H, I) == got
+
+
+def test_affine3_hand_encoded_tile():
+    """One 16 x 128 unit placed by hand: q = 5 at (row 3, column 45) (j 1, g 1, i 5: lane
+    19, pair 6, high member: bits 19..21 of word 1), q = 6 at (row 0, column 127) (lane
+    48, pair 15, high member: bit 31 of words 1 and 2), scale 2 and bias -1 for row 3's
+    first group, every other scale and bias 0."""
+    rows, cols = 16, 128
+    code = 768
+    buf = np.zeros(code + 16 * 2 * 4, dtype=np.uint8)
+    buf[12 * 19 + 4 + 2] = 5 << 3                 # word 1 of lane 19, bits 16..23: q at bit 19
+    buf[12 * 48 + 4 + 3] |= 0x80                  # bit 31 of word 1 of lane 48: bit 1 of q
+    buf[12 * 48 + 8 + 3] |= 0x80                  # bit 31 of word 2: bit 2 of q
+    buf[code + 8 * 3: code + 8 * 3 + 4] = [0x00, 0x40, 0x00, 0xBC]   # s = 2.0, b = -1.0
+    assert buf.size == oracle.packed_size(oracle.WFMT_AFF3, rows, cols)
+    w = oracle.dequant(oracle.WFMT_AFF3, buf, None, rows, cols)
+    want = np.zeros((rows, cols))
+    want[3, :64] = -1.0
+    want[3, 45] = 2.0 * 5 - 1.0
+    want[0, 127] = 0.0 * 6 + 0.0                   # scale 0 there: check the code separately
+    assert np.array_equal(w, want)
+    q, s, b = oracle.affine3_fields(buf, rows, cols)
+    assert q[3, 45] == 5 and q[0, 127] == 6 and q.sum() == 11
+
+
+def test_affine3_values_exact_and_encoders_agree():
+    """s * q + b of fp16 s, b and 3-bit q is exact in fp64 (at most 43 significant bits):
+    checked against rational arithmetic; the test encoder and the generator's agree."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 8, (32, 256), dtype=np.uint8)
+    s = rng.uniform(-3, 3, (32, 4)).astype(np.float16)
+    s[0, 0], s[1, 1] = np.float16(6.0e-8), np.float16(65504.0)      # smallest subnormal, largest finite
+    b = rng.uniform(-3, 3, (32, 4)).astype(np.float16)
+    b[0, 0], b[1, 1] = np.float16(-65504.0), np.float16(6.0e-8)
+    sb, bb = s.view(np.uint16), b.view(np.uint16)
+    buf = packing.pack_affine3(q, sb, bb)
+    assert np.array_equal(buf, synth.to_affine3(q, sb, bb))
+    w = oracle.dequant(oracle.WFMT_AFF3, buf, None, 32, 256)
+    for r, c in [(0, 0), (1, 64 + 7), (5, 200), (31, 255), (17, 130)]:
+        exact = Fraction(float(s[r, c // 64])) * int(q[r, c]) + Fraction(float(b[r, c // 64]))
+        assert Fraction(w[r, c]) == exact
