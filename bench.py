@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5a", "c5b", "aff3"])
     ap.add_argument("--tokens", type=int, default=None, help="override T (the stacked config runs T=1 and T=4; "
                     "the verify config with T=136 is the batched verify round of 8 requests x 17 tokens)")
     ap.add_argument("--path", choices=["auto", "decode", "prefill"], default="auto",
@@ -107,7 +107,7 @@ class Workload:
         if self.stacked:
             nl = spec.n_layers
         else:
-            nl = args.layers or {"c1": 4, "c2": 16, "c3": 16, "c5a": 4, "c5b": 4}[args.config]
+            nl = args.layers or {"c1": 4, "c2": 16, "c3": 16, "c5a": 4, "c5b": 4, "aff3": 16}[args.config]
         self.nl = nl
         t0 = time.time()
         self.layers = []
@@ -401,7 +401,8 @@ def main():
     main_run = runs[0]
 
     fmt = {synth.WFMT_MXFP4: "MXFP4", synth.WFMT_CB4: "4-bit codebook",
-           synth.WFMT_MXFP4_PS: "MXFP4 (packed scale store)"}[spec.weights.wfmt]
+           synth.WFMT_MXFP4_PS: "MXFP4 (packed scale store)",
+           synth.WFMT_AFF3: "3-bit affine group-64"}[spec.weights.wfmt]
     H, I, E, k, sh = spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared
     workload = (f"{args.config}: {spec.name}, T={main_run['T']}, H={H}, I={I}, E={E}{'+1 shared' if sh else ''}, "
                 f"top-{k}, {fmt} experts" + (f", {spec.n_layers} stacked layers (RMS rescale between)"

@@ -58,6 +58,22 @@
  *     entry i of the scale plane is nibble i, byte S + N + i/2, low nibble for even i.
  *     The block's E8M0 byte is base(row) + delta; everything else is MXFP4.
  *     moe_packed_bytes gives S + N + N*nkb/2.
+ *   AFF3 (3-bit affine, group 64: "Running Qwen3.8-Flash-Next on a 32 GB Mac with
+ *     Transformers", section "Where every weight lives": 3-bit MLX affine experts, group
+ *     64, 2.15 MB per expert of its hidden-2,560 / intermediate-640 model, which this
+ *     layout reproduces exactly; the bit packing is this library's): K a multiple of 128;
+ *     element = fp16 scale * q + fp16 bias, q in 0..7, one (scale, bias) per 64
+ *     consecutive values of a row.  Rows in tiles of 16, columns in steps of 128: the
+ *     value at (row 16t+m, column 128s + 32j + 8g + i) (j < 4, g < 4, i < 8) belongs to
+ *     the 12 bytes at t*6*K + 768*s + 12*(16g+m), three little-endian 32-bit words; with
+ *     P = 4j + i/2 and h = i%2, for P < 15 it is bits 3*(P%5) + 16h .. +2 of word P/5, and
+ *     for P = 15 bit k of q is bit 15 + 16h of word k.  At S3 = round_up(N*K*3/8, 256)
+ *     follow per (t, s) 128 bytes: at 8m the fp16 scale and bias of row 16t+m for columns
+ *     128s .. 128s+63, then for 128s+64 .. 128s+127.  moe_packed_bytes gives
+ *     S3 + N*(K/64)*4.  The layer runs on the decode kernels only: calls of more than 32
+ *     tokens run them on chunks of 32 (MOE_PATH_PREFILL and the bucketing debug outputs
+ *     of such calls are refused with MOE_ERR_UNSUPPORTED); H and I must be multiples
+ *     of 128 (else MOE_ERR_UNSUPPORTED).
  *   Expert e's gate_up matrix is [2I][H] (rows 0..I-1 gate, I..2I-1 up); its
  *   down matrix is [H][I].
  *
@@ -103,7 +119,7 @@ typedef enum {
   MOE_ERR_HIP = -5           /* a HIP launch failed */
 } moe_status;
 
-typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2, MOE_WFMT_MXFP4_PS = 3 } moe_wfmt;
+typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2, MOE_WFMT_MXFP4_PS = 3, MOE_WFMT_AFF3 = 4 } moe_wfmt;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Path selection for moe_forward: AUTO picks the decode kernels for small batches
@@ -124,7 +140,7 @@ typedef struct {
   const float *router_b;       /* [E] fp32, or NULL */
   const void *const *gate_up;  /* device array of E+has_shared device pointers -> packed [2I][H] */
   const void *const *down;     /* device array of E+has_shared device pointers -> packed [H][I] */
-  const int8_t *codebook;      /* CB4: [16] int8; MXFP4 and MXFP4_PS: must be NULL */
+  const int8_t *codebook;      /* CB4: [16] int8; every other format: must be NULL */
   const float *shared_gate_w;  /* [H] fp32, or NULL (shared weight 1); ignored without a shared expert */
   float omit_below;            /* marginal-expert omission threshold tau in [0, 1]; 0: off (below) */
 } moe_layer;
@@ -138,8 +154,8 @@ typedef struct {
  * pair is always kept; the shared expert is never omitted.  tau = 0 changes nothing. */
 
 /* [host] Bytes of one packed matrix [rows][cols] in the layout above; 0 if cols is not
- * a positive multiple of 32, rows is not a positive multiple of 16, or the format is
- * unknown. */
+ * a positive multiple of 32 (of 128 for AFF3), rows is not a positive multiple of 16, or
+ * the format is unknown. */
 size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols);
 
 /* [host] Workspace bytes moe_forward / moe_router_topk / moe_bucket need for up
@@ -215,7 +231,8 @@ int moe_forward_timed(const moe_layer *L, const void *x, int32_t x_dtype, int32_
 
 /* Test export: decode one packed matrix (layout above) to fp32 out [rows][cols],
  * bit-exact (every element is exactly representable in fp32 for MXFP4 scales
- * u <= 252 and every finite fp16 scale).  codebook: CB4 [16] int8, NULL otherwise.
+ * u <= 252 and every finite fp16 scale; AFF3 gives the fp32 rounding of the exact
+ * scale * q + bias).  codebook: CB4 [16] int8, NULL otherwise.
  * Errors: MOE_ERR_INVALID_ARG for an unknown format, rows not a positive multiple of
  * 16, cols not a positive multiple of 32, NULL packed/out, or a CB4 call without a
  * codebook; MOE_ERR_UNSUPPORTED above 2^34 elements; MOE_ERR_ALIGNMENT for packed or

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = \
     0, -1, -2, -3, -4, -5
-WFMT_MXFP4, WFMT_CB4, WFMT_MXFP4_PS = 1, 2, 3
+WFMT_MXFP4, WFMT_CB4, WFMT_MXFP4_PS, WFMT_AFF3 = 1, 2, 3, 4
 DT_F32, DT_BF16 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 

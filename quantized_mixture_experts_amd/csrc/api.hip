@@ -43,7 +43,8 @@ int validate_layer(const moe_layer* L) {
   if (L->hidden % 32 || L->inter % 32) return MOE_ERR_INVALID_ARG;
   if (L->hidden > kMaxDim || L->inter > kMaxDim || L->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (L->top_k > L->n_experts || L->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
-  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_CB4 && L->wfmt != MOE_WFMT_MXFP4_PS)
+  if (L->wfmt != MOE_WFMT_MXFP4 && L->wfmt != MOE_WFMT_CB4 && L->wfmt != MOE_WFMT_MXFP4_PS &&
+      L->wfmt != MOE_WFMT_AFF3)
     return MOE_ERR_INVALID_ARG;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (!L->router_w || !L->gate_up || !L->down) return MOE_ERR_INVALID_ARG;
@@ -53,6 +54,7 @@ int validate_layer(const moe_layer* L) {
   if (L->has_shared && L->shared_gate_w && !aligned16(L->shared_gate_w)) return MOE_ERR_ALIGNMENT;
   if (!aligned16(L->gate_up) || !aligned16(L->down)) return MOE_ERR_ALIGNMENT;
   if (!(L->omit_below >= 0.0f && L->omit_below <= 1.0f)) return MOE_ERR_INVALID_ARG;  // NaN fails too
+  if (L->wfmt == MOE_WFMT_AFF3 && (L->hidden % 128 || L->inter % 128)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -67,7 +69,10 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   Layout o{};
   size_t at = kHeaderBytes;  // the fixed header (synchronisation words) comes first
   auto take = [&](size_t bytes) { size_t r = at; at = align_up(at + bytes, kAlign); return r; };
-  o.logits = take((size_t)moeq::router_splits(T, (int)H) * T * (E + 1) * 8);  // K-split partial logits
+  // K-split partial logits, of the whole call or of one 32-token chunk of it (3-bit affine)
+  const int Tc = T < 32 ? T : 32;
+  o.logits = take(std::max((size_t)moeq::router_splits(T, (int)H) * T, (size_t)moeq::router_splits(Tc, (int)H) * Tc) *
+                  (E + 1) * 8);
   o.ids = take((size_t)T * k * 4);
   o.pair_w = take(P * 4);
   o.counts = take((E + 1) * 4);
@@ -162,6 +167,25 @@ int forward_impl(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, 
   Work w = carve(ws, layout_for(L, T));
   w.resid = residual ? static_cast<const float*>(x) : nullptr;  // pre-norm block: y_prev + layer
   const LayerArgs a = args_of(L);
+  if (a.wfmt == MOE_WFMT_AFF3) {
+    // decode kernels only: a larger batch runs them on chunks of up to 32 tokens (each
+    // chunk routed and bucketed on its own, so the whole call's bucketing is not formed)
+    const int xd = x_dtype == kRmsInput ? MOE_BF16 : x_dtype;
+    if (path == MOE_PATH_PREFILL || !moeq::decode_path_fits(a, T < 32 ? T : 32, xd)) return MOE_ERR_UNSUPPORTED;
+    if (T > 32 && (dbg_counts || dbg_offsets || dbg_perm)) return MOE_ERR_UNSUPPORTED;
+    const size_t xrow = (size_t)a.H * (x_dtype == MOE_BF16 ? 2 : 4);
+    for (int32_t t0 = 0; t0 < T; t0 += 32) {
+      const int32_t Tc = T - t0 < 32 ? T - t0 : 32;
+      const void* xc = static_cast<const uint8_t*>(x) + (size_t)t0 * xrow;
+      w.resid = residual ? static_cast<const float*>(xc) : nullptr;
+      const hipError_t e = moeq::launch_decode(a, xc, x_dtype, Tc, w, y + (size_t)t0 * a.H, eps,
+                                               dbg_ids ? dbg_ids + (size_t)t0 * a.k : nullptr,
+                                               dbg_w ? dbg_w + (size_t)t0 * a.k : nullptr, dbg_counts, dbg_offsets,
+                                               dbg_perm, s, tm);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
   const bool dec_ok = moeq::decode_path_fits(a, T, x_dtype == kRmsInput ? MOE_BF16 : x_dtype);
   if (path == MOE_PATH_DECODE && !dec_ok) return MOE_ERR_UNSUPPORTED;
   const int32_t auto_max = a.wfmt == MOE_WFMT_CB4 ? kAutoDecodeTokensCb4 : kAutoDecodeTokensMx;
@@ -226,7 +250,9 @@ extern "C" {
 
 size_t moe_packed_bytes(int32_t wfmt, int32_t rows, int32_t cols) {
   if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return 0;
-  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS) return 0;
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS && wfmt != MOE_WFMT_AFF3) return 0;
+  if (wfmt == MOE_WFMT_AFF3)
+    return cols % 128 ? 0 : align_up((size_t)rows * cols * 3 / 8, 256) + (size_t)rows * (cols / 64) * 4;
   const size_t code = (size_t)rows * cols / 2;
   const size_t nblk = (size_t)rows * cols / 32;
   if (wfmt == MOE_WFMT_MXFP4_PS) return align_up(code, 256) + (size_t)rows + nblk / 2;
@@ -314,7 +340,9 @@ int moe_forward_rms(const moe_layer* L, const float* y_prev, float eps, int32_t 
 
 int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols, float* out,
                 void* stream) {
-  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS) return MOE_ERR_INVALID_ARG;
+  if (wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_WFMT_CB4 && wfmt != MOE_WFMT_MXFP4_PS && wfmt != MOE_WFMT_AFF3)
+    return MOE_ERR_INVALID_ARG;
+  if (wfmt == MOE_WFMT_AFF3 && cols % 128) return MOE_ERR_INVALID_ARG;
   if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return MOE_ERR_INVALID_ARG;
   if ((size_t)rows * (size_t)cols > ((size_t)1 << 34)) return MOE_ERR_UNSUPPORTED;
   if (!packed || !out) return MOE_ERR_INVALID_ARG;

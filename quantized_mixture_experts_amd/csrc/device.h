@@ -11,6 +11,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(3))) uint32_t u32x3_t;
 
 // Global-memory views of pointers that come from memory (expert tables, slot records):
 // loads through them compile to global_load (vector memory only) instead of flat_load,
@@ -35,12 +36,20 @@ struct PackedTile {
   gbyte_t* scales;  // scale unit (t, 0), bytes (format 3: the tile's first delta byte)
   gbyte_t* bases;   // format 3: the base bytes of the tile's 16 rows
 };
-// Formats: 1 MXFP4, 2 CB4, 3 MXFP4 with the packed scale store.
-__host__ __device__ constexpr bool fmt_is_mx(int fmt) { return fmt != 2; }
+// Formats: 1 MXFP4, 2 CB4, 3 MXFP4 with the packed scale store, 4 3-bit affine.
+__host__ __device__ constexpr bool fmt_is_mx(int fmt) { return fmt == 1 || fmt == 3; }
+// 3-bit affine (format 4, K % 128 == 0): tile t's code units (one per 128-column step s,
+// 768 bytes, lane 16g + m's 12 bytes at 12 (16g + m)) start at t*6K; the scale plane at
+// round_up(N*K*3/8, 256) holds per (t, s) 128 bytes, row m's (scale, bias) fp16 pairs of
+// the step's two 64-column groups at 8m.
 template <int FMT>
 __device__ __forceinline__ PackedTile packed_tile(const void* base, int N, int K, int t) {
-  const size_t soff = ((size_t)N * K / 2 + 255) / 256 * 256;
   gbyte_t* b = as_global(base);
+  if constexpr (FMT == 4) {
+    const size_t soff4 = ((size_t)N * K * 3 / 8 + 255) / 256 * 256;
+    return {b + (size_t)t * 6 * K, b + soff4 + (size_t)t * K, nullptr};
+  }
+  const size_t soff = ((size_t)N * K / 2 + 255) / 256 * 256;
   if constexpr (FMT == 3)
     return {b + (size_t)t * 8 * K, b + soff + N + (size_t)t * 8 * (K / 32), b + soff + 16 * (size_t)t};
   return {b + (size_t)t * 8 * K, b + soff + (size_t)t * 16 * (K / 32) * (FMT == 1 ? 1 : 2), nullptr};
@@ -358,6 +367,17 @@ __device__ __forceinline__ void topk_tokens(const double* __restrict__ logits, i
       for (int z = 1; z < MAXS; ++z) lv[t][i] = z < nsplit ? lv[t][i] + part[t][i][z] : lv[t][i];
     }
   topk_select<NPER, NT>(lv, E, k, slot, s_exp, s_l);
+}
+
+// 3-bit affine: the 16 bf16 pairs (128 + q) of one lane's 12 code bytes of a step, pair
+// P = 4j + d holding values i = 2d, 2d+1 of MFMA j (columns 32j + 8g + i).  Pairs 0..14
+// sit at bits 3 (P % 5) and 16 + 3 (P % 5) of word P / 5; pair 15's bit k is bit 15 (and
+// 31) of word k.  0x4300 | q is the bf16 of 128 + q (q < 8 sits in the mantissa), so one
+// shift and one and-or make a pair.
+__device__ __forceinline__ void aff3_pairs(const u32x3_t w, uint32_t (&o)[16]) {
+#pragma unroll
+  for (int P = 0; P < 15; ++P) o[P] = ((w[P / 5] >> (3 * (P % 5))) & 0x00070007u) | 0x43004300u;
+  o[15] = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u) | 0x43004300u;
 }
 
 // E8M0 byte -> fp32 2^(u-127) (u = 0 gives the subnormal 2^-127).

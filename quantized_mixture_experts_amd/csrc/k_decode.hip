@@ -41,12 +41,13 @@ constexpr int waitcnt_vm_le(int n) {
 }
 // vector-memory instructions one prefetch_step issues per 16-row tile: MXFP4 one 16-byte
 // code load and one scale byte (the packed scale store: one delta byte); CB4 four code
-// dwords and four fp16 scales.  The waits
+// dwords and four fp16 scales; 3-bit affine one 12-byte code load and one 8-byte
+// (scale, bias) load.  The waits
 // after the staging loads count on exactly these: no two of them can be merged into one
 // instruction, since each address is clamped separately (min / select on the block
 // index), so the compiler cannot prove two of them adjacent.
 template <int FMT>
-constexpr int loads_per_step() { return fmt_is_mx(FMT) ? 2 : 8; }
+constexpr int loads_per_step() { return (fmt_is_mx(FMT) || FMT == 4) ? 2 : 8; }
 constexpr int kDecMaxTokens = 32;  // two 16-slot MFMA token tiles
 
 __device__ __forceinline__ int dec_token_of_pair(int p, int T, int k) { return p < T * k ? p / k : p - T * k; }
@@ -552,6 +553,11 @@ struct WeightRegs<3, KSW> {  // the packed scale store: s holds the byte with th
   uint32_t s[KSW];
 };
 template <int KSW>
+struct WeightRegs<4, KSW> {  // 3-bit affine: 12 code bytes and the (scale, bias) fp16 pairs of 2 groups
+  u32x3_t c[KSW];
+  uint64_t s[KSW];
+};
+template <int KSW>
 struct WeightRegs<2, KSW> {
   uint32_t c[KSW][4];
   uint32_t s[KSW][4];  // fp16 scale bits of blocks 4ks..4ks+3
@@ -573,6 +579,11 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
       r.c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(pt.codes +
                                                                                              pk_code(kbc, m)));
       r.s[i] = pt.scales[FMT == 3 ? pk_scale_mx(kbc, m) >> 1 : pk_scale_mx(kbc, m)];
+    } else if constexpr (FMT == 4) {
+      const int ksc = ks < nks ? ks : 0;
+      r.c[i] = __builtin_nontemporal_load(
+          (const __attribute__((address_space(1))) u32x3_t*)(pt.codes + 768 * ksc + 12 * (16 * g + m)));
+      r.s[i] = *(const __attribute__((address_space(1))) uint64_t*)(pt.scales + 128 * ksc + 8 * m);
     } else {
       const int ksc = ks < nks ? ks : 0;
 #pragma unroll
@@ -614,7 +625,8 @@ __device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, cons
 template <int FMT, int NP, int NTT, int KSW>
 __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, int ks, int nks, int nkb,
                                           const uint16_t* xs, int xstride, size_t plane_stride, int live, int xrows,
-                                          const uint32_t* lut, uint32_t sbase, f32x4_t (&acc)[NTT]) {
+                                          const uint32_t* lut, uint32_t sbase, f32x4_t (&acc)[NTT],
+                                          const float* xsum = nullptr) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const bool ksv = ks < nks;
@@ -634,6 +646,42 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, 
             u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
             av = ok ? av : u32x4_t{0, 0, 0, 0};
             acc[tt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, acc[tt]);
+          }
+        }
+      }
+    }
+  } else if constexpr (FMT == 4) {
+    // 3-bit affine: per 64-column group G (MFMAs 2G, 2G+1) the matrix cores sum
+    // (128 + q) x exactly per product; s (that) + (b - 128 s) X, X the group's activation
+    // sum per token slot (xsum[slot * (K/64) + group]), is the group's sum of (s q + b) x.
+    uint32_t o[16];
+    aff3_pairs(r.c[i], o);
+    const int ngrp = nkb >> 1;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const float sc = half_bits_to_f32((uint16_t)(r.s[i] >> (32 * G)));
+      const float bc = fmaf(-128.0f, sc, half_bits_to_f32((uint16_t)(r.s[i] >> (32 * G + 16))));
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        if (tt < live) {
+          const bool ok = ksv && (16 * tt + m < xrows);
+          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * G + jj;
+            const u32x4_t bw = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+            const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + (ok ? 128 * ks + 32 * j + 8 * g : 0);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
+              av = ok ? av : u32x4_t{0, 0, 0, 0};
+              tmp = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bw), tmp);
+            }
+          }
+          if (ksv) {
+            const float* xg = xsum + (size_t)(16 * tt + 4 * g) * ngrp + 2 * ks + G;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(bc, xg[(size_t)q * ngrp], fmaf(sc, tmp[q], acc[tt][q]));
           }
         }
       }
@@ -728,6 +776,45 @@ __device__ __forceinline__ void stage_rows_lds(uint16_t* xs, int xstride, size_t
   }
 }
 
+// 3-bit affine: xsum[slot * (K/64) + G] = the sum of the staged activation planes of
+// slot over the 64 columns of group G, in a fixed order (0 for slots past xrows), for the
+// affine bias term.  Then a barrier on LDS only (the weight loads stay in flight).
+template <int NP>
+__device__ __forceinline__ void dec_group_sums(float* xsum, const uint16_t* xs, int xstride, size_t lds_plane, int K,
+                                               int nslots, int xrows) {
+  const int ng = K >> 6;
+  for (int idx = threadIdx.x; idx < nslots * ng; idx += blockDim.x) {
+    const int sl = idx / ng, G = idx % ng;
+    float sum = 0.f;
+    if (sl < xrows) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4_t v = *(const u32x4_t*)(xs + p * lds_plane + (size_t)sl * xstride + 64 * G + 8 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
+        }
+    }
+    xsum[idx] = sum;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// LDS of a projection block: 1 KB codebook table, then the activation tile of xrows rows
+// (NP planes), which the split-K reduction buffer later reuses, then (3-bit affine) the
+// group sums of 16 NTT token slots.
+__host__ __device__ inline size_t dec_tile_bytes(int K, int NP, int NTT, int xrows) {
+  const size_t x = (size_t)NP * xrows * lds_row_stride(K) * 2;
+  const size_t red = (size_t)3 * 8 * NTT * 64 * 4;
+  return x > red ? x : red;
+}
+__host__ __device__ inline size_t dec_lds_bytes(int fmt, int K, int NP, int NTT, int xrows) {
+  return 1024 + dec_tile_bytes(K, NP, NTT, xrows) + (fmt == 4 ? (size_t)16 * NTT * (K / 64) * 4 : 0);
+}
+
 // Sum the 4 waves' partial tiles (split-K) in wave order into wave 0.
 template <int NV>
 __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
@@ -776,6 +863,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
+  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, NP, NTT, xrows_max));  // 3-bit affine
   const PackedTile pg = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, blockIdx.x);
   const PackedTile pu = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x);
   // the packed scale store's row bases, loaded before the staging loads (not counted below)
@@ -803,12 +891,13 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
         // after them are outstanding; then every wave's rows are in LDS after the barrier
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(2 * KSW * loads_per_step<FMT>()));
         __builtin_amdgcn_s_barrier();
+        if constexpr (FMT == 4) dec_group_sums<NP>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
       }
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bg, accg);
-        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bu, accu);
+        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bg, accg, xsum);
+        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bu, accu, xsum);
       }
     }
     // split-K reduction (fixed wave order), SwiGLU, two bf16 planes of h
@@ -906,6 +995,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
+  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
   const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, blockIdx.x);
   const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
@@ -929,11 +1019,12 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
       if (ch == 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
         __builtin_amdgcn_s_barrier();
+        if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
       }
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc);
+        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc, xsum);
       }
     }
     float v[4 * NTT];
@@ -1038,6 +1129,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   const size_t lds_plane = (size_t)xrows_max * xstride;
   uint32_t* lut = (uint32_t*)smem;
   uint16_t* xs = (uint16_t*)(smem + 1024);
+  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
   const int tile = 4 * blockIdx.x + wave;  // this wave's 16 output columns
   const bool tile_ok = 16 * tile < H;
   const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, tile_ok ? tile : 0);
@@ -1057,9 +1149,10 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
     prefetch_weights<FMT, KSW>(wd, pd, nkb, 0, nks, n, g, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
     __builtin_amdgcn_s_barrier();
+    if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
-      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc);
+      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc, xsum);
     if (tile_ok) {
       const int col = 16 * tile + n;
 #pragma unroll
@@ -1091,14 +1184,6 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// LDS of a projection block: 1 KB codebook table, then the activation tile of
-// xrows rows (NP planes), which the split-K reduction buffer later reuses.
-static size_t dec_lds_bytes(int K, int NP, int NTT, int xrows) {
-  const size_t x = (size_t)NP * xrows * lds_row_stride(K) * 2;
-  const size_t red = (size_t)3 * 8 * NTT * 64 * 4;
-  return 1024 + (x > red ? x : red);
-}
 
 // k-steps per wave: the smallest supported count that covers a quarter of the row's
 // 128-column steps (longer rows loop over chunks of 8).
@@ -1115,10 +1200,10 @@ static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int 
   const int npass = (T + xrows - 1) / xrows;  // a slot holds at most T pairs
   const dim3 g1(L.I / 16, nslots * npass);
   if (x_dtype == 1)
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 1, NTT, xrows),
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW>), g1, dim3(256), dec_lds_bytes(FMT, L.H, 1, NTT, xrows),
                 s, L, T, w, (const uint16_t*)x, (size_t)0, xrows, nslots);
   else
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW>), g1, dim3(256), dec_lds_bytes(L.H, 3, NTT, xrows),
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW>), g1, dim3(256), dec_lds_bytes(FMT, L.H, 3, NTT, xrows),
                 s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows, nslots);
 }
 
@@ -1129,7 +1214,7 @@ template <int FMT, int NTT, int KSW>
 static void launch_down_rows_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                                hipStream_t s, const Timing& tm) {
   const int slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const size_t lds = dec_lds_bytes(L.I, 2, NTT, xrows);
+  const size_t lds = dec_lds_bytes(FMT, L.I, 2, NTT, xrows);
   if (slots <= kTicketSlotsMax) {
     MOEQ_LAUNCH(tm, kStageDown, (k_dec_down_rows<FMT, NTT, KSW, true>), dim3((L.H + 63) / 64, slots), dim3(256), lds,
                 s, L, T, w, y, tickets, xrows, slots);
@@ -1147,12 +1232,12 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
   const dim3 g2(L.H / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
   if constexpr (NTT == 1) {
     if (omb) {
-      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), g2, dim3(256), dec_lds_bytes(L.I, 2, 1, xrows), s,
+      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), g2, dim3(256), dec_lds_bytes(FMT, L.I, 2, 1, xrows), s,
                   L, T, w, y, tickets, xrows);
       return;
     }
   }
-  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), g2, dim3(256), dec_lds_bytes(L.I, 2, NTT, xrows),
+  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), g2, dim3(256), dec_lds_bytes(FMT, L.I, 2, NTT, xrows),
               s, L, T, w, y, tickets, xrows);
 }
 
@@ -1220,8 +1305,8 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   if (T > kDecMaxTokens) return false;
   const int np = x_dtype == 1 ? 1 : 3;
   const int xg = dec_rows_per_pass(L.H, np, T), xd = dec_rows_per_pass(L.I, 2, T);
-  const size_t g = dec_lds_bytes(L.H, np, xg <= 16 ? 1 : 2, xg);
-  const size_t d = dec_lds_bytes(L.I, 2, xd <= 16 ? 1 : 2, xd);
+  const size_t g = dec_lds_bytes(L.wfmt, L.H, np, xg <= 16 ? 1 : 2, xg);
+  const size_t d = dec_lds_bytes(L.wfmt, L.I, 2, xd <= 16 ? 1 : 2, xd);
   return g <= 160 * 1024 && d <= 160 * 1024;
 }
 
@@ -1278,6 +1363,7 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   switch (L.wfmt) {
     case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
     case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+    case 4: return launch_dec_experts<4>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
     default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
   }
 }

@@ -44,6 +44,32 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   }
 }
 
+// 3-bit affine: one thread per 8 values (row, columns 8c .. 8c+7), fp32 out = fmaf(s, q, b),
+// the fp32 rounding of the exact s * q + b.
+__global__ __launch_bounds__(256) void k_dequant_aff3(const uint8_t* __restrict__ packed, int rows, int cols,
+                                                      float* __restrict__ out) {
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (size_t)rows * (cols / 8)) return;
+  const int row = (int)(id / (cols / 8)), c8 = (int)(id % (cols / 8));
+  const int m = row & 15, st = c8 / 16, cc = 8 * (c8 % 16);
+  const int j = cc / 32, g = (cc % 32) / 8;
+  const PackedTile pt = packed_tile<4>(packed, rows, cols, row >> 4);
+  const gbyte_t* wp = pt.codes + 768 * st + 12 * (16 * g + m);
+  const u32x3_t w = {*(const __attribute__((address_space(1))) uint32_t*)wp,
+                     *(const __attribute__((address_space(1))) uint32_t*)(wp + 4),
+                     *(const __attribute__((address_space(1))) uint32_t*)(wp + 8)};
+  uint32_t o[16];
+  aff3_pairs(w, o);
+  const uint32_t sb = *(const __attribute__((address_space(1))) uint32_t*)(pt.scales + 128 * st + 8 * m + 4 * (j / 2));
+  const float sc = half_bits_to_f32((uint16_t)(sb & 0xFFFFu)), bi = half_bits_to_f32((uint16_t)(sb >> 16));
+  float* dst = out + (size_t)row * cols + 8 * c8;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    dst[2 * d] = fmaf(sc, (float)((o[4 * j + d] & 0xFFFFu) - 0x4300u), bi);
+    dst[2 * d + 1] = fmaf(sc, (float)((o[4 * j + d] >> 16) - 0x4300u), bi);
+  }
+}
+
 // x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y^2 + eps)); one block of 256 threads per
 // token.  The sum of squares, the mean, the square root and the quotient are fp64 (the
 // quotient correctly rounded), then rounded once to bf16.
@@ -102,6 +128,9 @@ hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codeboo
     hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
   else if (wfmt == 3)
     hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
+  else if (wfmt == 4)
+    hipLaunchKernelGGL(k_dequant_aff3, dim3((unsigned)(((size_t)rows * (cols / 8) + 255) / 256)), dim3(256), 0, s,
+                       packed, rows, cols, out);
   else
     hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, codebook, rows, cols, out);
   return hipGetLastError();

@@ -340,7 +340,12 @@ def small_spec(name: str, T: int, hidden: int, inter: int, n_experts: int, top_k
                has_shared: int = 0, x_dtype: int = X_BF16, bias: str = "none", seed: int = 7,
                router_std: float = 0.05, bias_std: float = 0.5) -> LayerSpec:
     """A layer shape for parity sweeps (several tiles plus ragged tails, seconds on the CPU)."""
-    w = WeightSpec(wfmt) if wfmt == WFMT_CB4 else WeightSpec(WFMT_MXFP4, e8m0_lo=118, e8m0_hi=124)
+    if wfmt in (WFMT_MXFP4, WFMT_MXFP4_PS):
+        w = WeightSpec(wfmt, e8m0_lo=118, e8m0_hi=124)
+    elif wfmt in (WFMT_CB4, WFMT_AFF3):
+        w = WeightSpec(wfmt, 0.01, 0.05)
+    else:
+        raise ValueError("unknown weight format")
     return LayerSpec(name, T=T, hidden=hidden, inter=inter, n_experts=n_experts, top_k=top_k,
                      has_shared=has_shared, weights=w, x_dtype=x_dtype, router_std=router_std,
                      bias=bias, bias_std=bias_std, seed=seed)

@@ -241,3 +241,13 @@ def test_packed_scale_store_bytes_and_validation(L):
     assert ws_bytes(L, lay, 4) == 0
     lay = layer(wfmt=ps, codebook=None)
     assert ws_bytes(L, lay, 4) > 0
+
+
+def test_affine3_bytes_and_validation(L):
+    a3 = q.WFMT_AFF3
+    assert q.packed_bytes(a3, 1280, 2560) + q.packed_bytes(a3, 2560, 640) == 2_150_400
+    assert q.packed_bytes(a3, 16, 96) == 0          # columns in steps of 128
+    assert ws_bytes(L, layer(wfmt=a3, codebook=None, hidden=256, inter=128), 4) > 0
+    assert ws_bytes(L, layer(wfmt=a3, codebook=None, hidden=256, inter=96), 4) == 0
+    assert ws_bytes(L, layer(wfmt=a3, codebook=FAKE, hidden=256, inter=128), 4) == 0
+    assert L.moe_dequant(a3, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG

@@ -50,3 +50,11 @@ def test_bf16_inputs_are_rne_of_normals():
     spec = synth.CONFIGS["c2"]
     x = synth.make_x(spec)
     assert x.dtype == np.uint16 and x.shape == (1, 2880)
+
+
+def test_small_spec_keeps_the_format():
+    for wfmt in (synth.WFMT_MXFP4, synth.WFMT_CB4, synth.WFMT_MXFP4_PS, synth.WFMT_AFF3):
+        spec = synth.small_spec("f", 2, 128, 128, 4, 2, wfmt)
+        layer = synth.make_layer(spec)
+        assert layer.wfmt == wfmt
+        assert layer.gate_up[0].size == synth.packed_nbytes(wfmt, 256, 128)
