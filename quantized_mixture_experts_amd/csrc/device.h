@@ -160,17 +160,42 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
 // router kernel that folds the rescale in both use exactly these steps.
 __device__ __forceinline__ double rms_partial(const float* __restrict__ yt, int H, int i) {
   double s = 0.0;
-  for (int n = i; n < H; n += 256) {
-    const double v = (double)yt[n];
-    s = fma(v, v, s);
+  // 8 loads in flight per batch; a slot past the row adds fma(0, 0, s) = s exactly, so the
+  // sum is the in-order sum over n = i, i + 256, ...
+  for (int n0 = i; n0 < H; n0 += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = n0 + 256 * u < H ? yt[n0 + 256 * u] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = fma((double)v[u], (double)v[u], s);
   }
   return s;
 }
 __device__ __forceinline__ double rms_divisor(double s0, double s1, double s2, double s3, int H, float eps) {
   return sqrt((((s0 + s1) + s2) + s3) / (double)H + (double)eps);
 }
-// the fp64 quotient (correctly rounded), then rounded to bf16
-__device__ __forceinline__ uint16_t rms_apply(float y, double d) { return (uint16_t)f64_to_bf16_rne((double)y / d); }
+// The fp64 quotient y / d (correctly rounded), then rounded to bf16.  rd = 1 / d in fp64:
+// y * rd lies within 2 ulp of the quotient, so both round to the same bf16 unless the
+// product's 45 dropped bits are within 8 ulp of the midpoint between two bf16 values;
+// only then is the quotient itself computed.  The result is the bf16 of y / d, bit for bit.
+__device__ __forceinline__ uint16_t rms_apply(float y, double d, double rd) {
+  double q = (double)y * rd;
+  const int64_t dropped = (int64_t)(__builtin_bit_cast(uint64_t, q) & ((1ull << 45) - 1));
+  const bool near = dropped - (1ll << 44) <= 8 && (1ll << 44) - dropped <= 8;
+  if (__ballot(near)) {  // a wave-uniform branch: the division runs only where it can matter
+    if (near) q = (double)y / d;
+  }
+  return (uint16_t)f64_to_bf16_rne(q);
+}
+// rms_apply of 8 values of a row: n = i + stride u (u < 8, those below H), loads first.
+__device__ __forceinline__ void rms_apply8(const float* __restrict__ y, int i, int stride, int n_end, double d,
+                                           double rd, uint16_t (&out)[8]) {
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = i + stride * u < n_end ? y[i + stride * u] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) out[u] = rms_apply(v[u], d, rd);
+}
 
 // ---- cross-lane helpers on DPP row rotations (a few cycles each) plus readlane ----
 template <int CTRL>

@@ -191,12 +191,28 @@ __device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(
   }
 }
 
+constexpr int kRouterPer = 3;  // float4 chunks per lane and pass: a quarter of a 2880-column row in one pass
+
+// The first pass's router-weight chunks of this lane (issued early, e.g. before the RMS
+// rescale that the activations need).
+__device__ __forceinline__ void router_w_first(const float* __restrict__ wrow, int h0, int h1,
+                                               f32x4_t (&wv)[kRouterPer]) {
+  const int lane = threadIdx.x & 63;
+  const int c_beg = h0 / 4, c_end = h1 / 4;
+#pragma unroll
+  for (int i = 0; i < kRouterPer; ++i) {
+    const int c = max(c_beg, min(c_beg + lane + 64 * i, c_end - 1));
+    wv[i] = c_end > c_beg ? *(const __attribute__((address_space(1))) f32x4_t*)(wrow + 4 * c) : f32x4_t{0, 0, 0, 0};
+  }
+}
+
 template <int XDT>
 __device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
-                                            int h0, int h1, double* __restrict__ part) {
+                                            int h0, int h1, double* __restrict__ part,
+                                            const f32x4_t (&wfirst)[kRouterPer]) {
   using RX = RouterX<XDT == 2 ? 1 : XDT>;
   const int lane = threadIdx.x & 63;
-  constexpr int kPer = 3;  // a quarter of a 2880-column row in one pass
+  constexpr int kPer = kRouterPer;
   constexpr int kTB = 4;
   const int c_beg = h0 / 4, c_end = h1 / 4;
   if (c_end <= c_beg) {
@@ -210,7 +226,7 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       cc[i] = min(c0 + lane + 64 * i, c_end - 1);
-      wv[i] = *(const __attribute__((address_space(1))) f32x4_t*)(wrow + 4 * cc[i]);
+      wv[i] = c0 == c_beg ? wfirst[i] : *(const __attribute__((address_space(1))) f32x4_t*)(wrow + 4 * cc[i]);
     }
     typename RX::chunk xq[kTB][kPer];
 #pragma unroll
@@ -326,13 +342,15 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   }
 }
 
+// ROUTE false (one token, self-routed projections): the logits are stored to w.logits and
+// the kernel ends; the gate/up kernel routes.
 // MBOX (T (E+1) <= kDecMailboxWords): the logits go through the mailbox in the workspace
 // header as ~bits(l), so a posted entry is its own arrival mark; otherwise through
 // w.logits, each block raising its arrival flag (header word blockIdx) once they have
 // landed.  Either way each block then checks once whether everything has arrived, and a
 // block that sees it all routes (more than one may: they write the same values), clearing
 // the mailbox entries or flags so that the header reads zero again after the call.
-template <int XDT, bool MBOX>
+template <int XDT, bool MBOX, bool ROUTE>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
                                                           Work w, int max_slots, uint32_t* __restrict__ rr_flags,
                                                           int ntickets, int nzero_o, float eps,
@@ -372,9 +390,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
+  // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns; the
+  // first pass of its weights is requested now, before the activations are ready
+  const int e_row = blockIdx.x * kRouterRows + (wave >> 2);
+  const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
+  const int h0 = min(H, (wave & 3) * qh), h1 = min(H, ((wave & 3) + 1) * qh);
+  const float* wrow = e_row < E ? L.router_w + (size_t)e_row * H : L.shared_gate_w;
+  f32x4_t wfirst[kRouterPer];
+  if (e_row < erows) router_w_first(wrow, h0, h1, wfirst);
   const void* xr = x;  // the router's activations (XDT 2: the block's LDS copy of the rescale)
   if constexpr (XDT == 2) {
     __shared__ double s_d[kDecSplitRouteT];  // each token's sqrt(mean(y^2) + eps)
+    __shared__ double s_rd[kDecSplitRouteT];  // and its fp64 reciprocal
     __shared__ __align__(16) uint16_t s_x[kRmsFoldElems];
     // With the rescale kernel's exact arithmetic (rms_partial over 256 threads, the 4 wave
     // sums in wave order, rms_divisor, rms_apply).  Group g of the block's four 256-thread
@@ -386,13 +413,27 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       if (lane == 0) s_ms[t][wave & 3] = sq;
     }
     __syncthreads();
-    if (tid < T) s_d[tid] = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
+    if (tid < T) {
+      const double d = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
+      s_d[tid] = d;
+      s_rd[tid] = 1.0 / d;
+    }
     __syncthreads();
-    // the rescaled rows once per block into LDS (block 0 also writes them for the projections)
-    for (int idx = tid; idx < T * H; idx += kRouteThreads) {
-      const uint16_t v = rms_apply(((const float*)x)[idx], s_d[idx / H]);
-      s_x[idx] = v;
-      if (blockIdx.x == 0) w.xr[idx] = v;
+    // the rescaled rows once per block into LDS (block 0 also writes them for the projections),
+    // token by token, 8 values in flight per thread
+    for (int t = 0; t < T; ++t) {
+      for (int n0 = tid; n0 < H; n0 += 8 * kRouteThreads) {
+        uint16_t v[8];
+        rms_apply8((const float*)x + (size_t)t * H, n0, kRouteThreads, H, s_d[t], s_rd[t], v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int n = n0 + kRouteThreads * u;
+          if (n < H) {
+            s_x[t * H + n] = v[u];
+            if (blockIdx.x == 0) w.xr[(size_t)t * H + n] = v[u];
+          }
+        }
+      }
     }
     __syncthreads();
     xr = s_x;
@@ -404,13 +445,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       const int er = blockIdx.x * kRouterRows + tid / T;
       if (er < E && L.router_b) bias = (double)L.router_b[er];
     }
-    // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns
-    const int e = blockIdx.x * kRouterRows + (wave >> 2);
-    const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
-    if (e < erows) {
-      const float* wrow = e < E ? L.router_w + (size_t)e * H : L.shared_gate_w;
-      router_part<XDT>(wrow, xr, T, H, min(H, (wave & 3) * qh), min(H, ((wave & 3) + 1) * qh), s_part[wave]);
-    }
+    if (e_row < erows) router_part<XDT>(wrow, xr, T, H, h0, h1, s_part[wave], wfirst);
     __syncthreads();
     if (tid < kRouterRows * T) {
       const int r = tid / T, t = tid % T;
@@ -418,7 +453,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       if (er < erows) {
         double v = ((s_part[4 * r][t] + s_part[4 * r + 1][t]) + s_part[4 * r + 2][t]) + s_part[4 * r + 3][t];
         if (er < E && L.router_b) v += bias;
-        if (MBOX)
+        if (!ROUTE)
+          w.logits[(size_t)t * (E + 1) + er] = v;
+        else if (MBOX)
           __hip_atomic_store(w.rr_mbox + (size_t)t * (E + 1) + er, ~__builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -426,6 +463,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       }
     }
   }
+  if constexpr (!ROUTE) return;
   // This block's posts have landed (acknowledged) before any of its checks is issued, so the
   // block whose check comes last sees every post.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -815,6 +853,21 @@ __host__ __device__ inline size_t dec_lds_bytes(int fmt, int K, int NP, int NTT,
   return 1024 + dec_tile_bytes(K, NP, NTT, xrows) + (fmt == 4 ? (size_t)16 * NTT * (K / 64) * 4 : 0);
 }
 
+// One token: its activation row (NP planes) into LDS row 0, the 4 waves splitting the
+// 1 KB direct loads (issued before the block knows its expert).
+template <int NP>
+__device__ __forceinline__ void stage_token0_lds(uint16_t* xs, size_t lds_plane, const uint16_t* src,
+                                                 size_t src_plane, int K) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_bytes = K * 2;
+  const int nchunk = (row_bytes + 1023) >> 10;
+  for (int job = wave; job < nchunk * NP; job += 4) {
+    const int q = job % NP, ch = job / NP;
+    if (1024 * ch + 16 * lane < row_bytes)
+      load_lds_16((const uint8_t*)(src + q * src_plane) + 1024 * ch + 16 * lane, (uint8_t*)(xs + q * lds_plane) + 1024 * ch);
+  }
+}
+
 // Sum the 4 waves' partial tiles (split-K) in wave order into wave 0.
 template <int NV>
 __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
@@ -834,6 +887,137 @@ __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
 }
 
 // ---------------------------------------------------------------------------
+// One token, self-routed projections: the router kernel only stores the token's logits
+// (w.logits[0 .. E], column E the shared-gate logit); every gate/up block then takes the
+// top-k itself (wave 0: one wave, 0.5 us), keeps the pairs that pass the omission rule,
+// and takes the routed expert of rank blockIdx.y among the kept ones in ascending expert
+// order (the shared expert right after them).  Block (0, 0) writes the call's routing
+// outputs (ids, pair weights, counts, offsets, perm, active list, debug copies) and block
+// (0, y) the slot record y that the down kernel reads; the blocks read none of them, so
+// the kernel has no cross-block dependency.  E <= kSelfRouteMaxE.
+// ---------------------------------------------------------------------------
+constexpr int kSelfRouteMaxE = 256;
+template <int NPER>
+__device__ __forceinline__ void dec_self_route(const LayerArgs& L, const Work& w, Slot* s_rec,
+                                               int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w,
+                                               int32_t* __restrict__ dbg_counts, int32_t* __restrict__ dbg_offsets,
+                                               int32_t* __restrict__ dbg_perm) {
+  __shared__ int s_exp[16];
+  __shared__ double s_l[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = L.E, k = L.k, sh = L.has_shared;
+  const int y = blockIdx.y;
+  if (wave == 0) {
+    double lv[1][NPER];
+    uint64_t gp[NPER + 1];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) lv[0][i] = w.logits[min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i <= NPER; ++i) gp[i] = (uint64_t)L.gate_up[min(lane + 64 * i, E + sh - 1)];
+    const double lsg = (sh && L.shared_gate_w) ? w.logits[E] : 0.0;
+    const int tok[1] = {0};
+    topk_select<NPER, 1>(lv, E, k, tok, s_exp, s_l);
+    // the gates decide only with omission; otherwise only block (0, 0) needs them
+    float g = 0.0f;
+    bool keep = lane < k;
+    if (L.omit_below > 0.0f || (blockIdx.x == 0 && y == 0))
+      keep = pair_gate(s_l[min(lane, k - 1)], s_l[0], k, L.omit_below, &g);
+    const bool kept = lane < k && keep;
+    const int id = lane < k ? s_exp[lane] : 0;
+    const uint64_t km = __ballot(kept);
+    const int n_kept = __popcll(km);
+    int r = 0;  // rank of this lane's expert among the kept ones (ids are distinct)
+    for (int j = 0; j < k; ++j) r += ((km >> j) & 1ull) && __builtin_amdgcn_readlane(id, j) < id;
+    // this block's slot
+    int e_mine = -1, p_mine = -1;
+    const uint64_t mine = __ballot(kept && r == y);
+    if (mine) {
+      const int j = __ffsll((long long)mine) - 1;
+      e_mine = __builtin_amdgcn_readlane(id, j);
+      p_mine = j;  // pair t*k + j of token 0
+    } else if (sh && y == n_kept) {
+      e_mine = E;
+      p_mine = k;  // the shared pair T*k + t
+    }
+    uint64_t ptr = 0;
+    if (e_mine >= 0) {
+#pragma unroll
+      for (int i = 0; i <= NPER; ++i) {
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(gp[i] >> 32), e_mine & 63) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gp[i], e_mine & 63);
+        if ((e_mine >> 6) == i) ptr = v;
+      }
+    }
+    const int n_active = n_kept + sh;
+    if (lane == 0) {
+      s_rec->e = e_mine < 0 ? 0 : e_mine;
+      s_rec->cnt = e_mine < 0 ? 0 : 1;
+      s_rec->off = y;
+      s_rec->n_active = n_active;
+      s_rec->gate_up = (const uint8_t*)ptr;
+      s_rec->rows[0] = p_mine;
+    }
+    if (blockIdx.x == 0) {
+      if (lane == 0) {  // the slot record of row y for the down kernel
+        Slot& sl = w.slots[y];
+        sl.e = e_mine < 0 ? 0 : e_mine;
+        sl.cnt = e_mine < 0 ? 0 : 1;
+        sl.off = y;
+        sl.n_active = n_active;
+        sl.gate_up = (const uint8_t*)ptr;
+        sl.down = e_mine < 0 ? nullptr : L.down[e_mine];
+        sl.rows[0] = p_mine;
+      }
+      if (y == 0) {  // the call's routing outputs
+        if (lane < k) {
+          const int idv = kept ? id : -1;
+          w.ids[lane] = idv;
+          w.pair_w[lane] = g;
+          if (dbg_ids) dbg_ids[lane] = idv;
+          if (dbg_w) dbg_w[lane] = g;
+          if (kept) {
+            w.perm[r] = lane;
+            w.active[1 + r] = id;
+            if (dbg_perm) dbg_perm[r] = lane;
+          }
+        }
+        for (int i = n_active + lane; i < k + sh; i += 64) {  // past the placed pairs
+          w.perm[i] = -1;
+          if (dbg_perm) dbg_perm[i] = -1;
+        }
+        if (lane == 0) {
+          if (sh) {
+            w.pair_w[k] = L.shared_gate_w ? (float)(1.0 / (1.0 + exp(-lsg))) : 1.0f;
+            w.perm[n_kept] = k;
+            w.active[1 + n_kept] = E;
+            if (dbg_perm) dbg_perm[n_kept] = k;
+          }
+          w.active[0] = n_active;
+          w.offsets[E + 1] = n_active;
+          if (dbg_offsets) dbg_offsets[E + 1] = n_active;
+        }
+        // counts and exclusive offsets of every bucket: the kept experts have one pair each
+        for (int e = lane; e <= E; e += 64) {
+          int below = 0, c = 0;
+          for (int j = 0; j < k; ++j) {
+            const int idj = __builtin_amdgcn_readlane(id, j);
+            const bool kj = (km >> j) & 1ull;
+            below += kj && idj < e;
+            c += kj && idj == e;
+          }
+          if (e == E) { below = n_kept; c = sh; }
+          w.counts[e] = c;
+          w.offsets[e] = below;
+          if (dbg_counts) dbg_counts[e] = c;
+          if (dbg_offsets) dbg_offsets[e] = below;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // 3. Fused gate/up + SwiGLU.  grid = (I/16, max active slots), 4 waves split K.
 //    Each wave first issues direct-to-LDS loads of its share of the expert's
 //    activation rows, then all its weight loads; it waits only for the former before
@@ -842,19 +1026,39 @@ __device__ __forceinline__ void reduce4(float (&v)[NV], float* red) {
 // dynamic LDS: 1 KB CB4 table, then [NP][xrows][xstride] bf16 activations (reused by
 // the split-K reduction).
 // ---------------------------------------------------------------------------
-template <int FMT, int NP, int NTT, int KSW>
+template <int FMT, int NP, int NTT, int KSW, bool SR>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                       size_t act_plane, int xrows_max, int nslots) {
+                                                       size_t act_plane, int xrows_max, int nslots,
+                                                       int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w,
+                                                       int32_t* __restrict__ dbg_counts,
+                                                       int32_t* __restrict__ dbg_offsets,
+                                                       int32_t* __restrict__ dbg_perm) {
   extern __shared__ __align__(16) uint8_t smem[];
   // grid.y = slots x passes, slot-major: block row y takes pass y % npass of slot
   // y / npass (rows xrows_max (y % npass) ..), so an expert with more pairs than one pass
   // stages runs its passes side by side on adjacent rows, dispatched together with its
-  // first pass; rows past a slot's pairs exit at once
+  // first pass; rows past a slot's pairs exit at once.  SR (one token): the block routes
+  // itself (dec_self_route) and keeps its slot record in LDS.
+  __shared__ Slot s_rec;
   const int npass = (int)gridDim.y / nslots;
-  const Slot* slot_rec = w.slots + blockIdx.y / npass;
+  const Slot* slot_rec;
+  if constexpr (SR) {
+    // the token's row is staged while the block routes (one token: T = 1, one pass)
+    stage_token0_lds<NP>((uint16_t*)(smem + 1024), (size_t)xrows_max * lds_row_stride(L.H), act, act_plane, L.H);
+    const int nper = (L.E + 63) >> 6;
+    if (nper <= 1) dec_self_route<1>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else if (nper <= 2) dec_self_route<2>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else dec_self_route<4>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    slot_rec = &s_rec;
+  } else {
+    slot_rec = w.slots + blockIdx.y / npass;
+  }
   const int cnt = slot_rec->cnt, off = slot_rec->off;
   const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
-  if (tb0 >= cnt) return;
+  if (tb0 >= cnt) {
+    if (SR) __builtin_amdgcn_s_waitcnt(0);  // the staging loads land before the LDS is released
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
@@ -881,8 +1085,9 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
       if (ch == 0) {
         if (tb > tb0) __syncthreads();  // the previous pass finished with the LDS tile
         else if (FMT == 2) build_cb4_lut(lut, L.codebook);
-        stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, slot_rec, w.perm + off, tb, xrows, T,
-                                 k);
+        if (!SR)  // (self-routed: the row was staged before the routing)
+          stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, slot_rec, w.perm + off, tb, xrows, T,
+                                   k);
       }
       WeightRegs<FMT, KSW> wg, wu;
       prefetch_weights2<FMT, KSW>(wg, pg, wu, pu, nkb, ks0, nks, n, g);
@@ -916,7 +1121,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
         for (int q = 0; q < 4; ++q) {
           const int slot = tb + 16 * tt + 4 * g + q;
           if (slot < tb + xrows) {  // this pass's pairs only
-            const int p = w.perm[off + slot];
+            const int p = slot < kSlotRows ? slot_rec->rows[slot] : w.perm[off + slot];
             const float h = silu_f32(v[8 * tt + q]) * v[8 * tt + 4 + q];
             const uint32_t hi = f32_to_bf16_rne(h);
             const uint32_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
@@ -1193,18 +1398,35 @@ static int pick_ksw(int K) {
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
 }
 
-template <int FMT, int NTT, int KSW>
-static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
-                            hipStream_t s, const Timing& tm) {
+// The routing debug outputs of a call (each may be null).
+struct DbgOut {
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+};
+
+template <int FMT, int NTT, int KSW, bool SR>
+static void launch_gateup_sr(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
+                             const DbgOut& d, hipStream_t s, const Timing& tm) {
   const int nslots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
   const int npass = (T + xrows - 1) / xrows;  // a slot holds at most T pairs
   const dim3 g1(L.I / 16, nslots * npass);
   if (x_dtype == 1)
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW>), g1, dim3(256), dec_lds_bytes(FMT, L.H, 1, NTT, xrows),
-                s, L, T, w, (const uint16_t*)x, (size_t)0, xrows, nslots);
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW, SR>), g1, dim3(256),
+                dec_lds_bytes(FMT, L.H, 1, NTT, xrows), s, L, T, w, (const uint16_t*)x, (size_t)0, xrows, nslots, d.ids,
+                d.w, d.counts, d.offsets, d.perm);
   else
-    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW>), g1, dim3(256), dec_lds_bytes(FMT, L.H, 3, NTT, xrows),
-                s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows, nslots);
+    MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 3, NTT, KSW, SR>), g1, dim3(256),
+                dec_lds_bytes(FMT, L.H, 3, NTT, xrows), s, L, T, w, (const uint16_t*)w.xplanes, (size_t)T * L.H, xrows,
+                nslots, d.ids, d.w, d.counts, d.offsets, d.perm);
+}
+template <int FMT, int NTT, int KSW>
+static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows, bool sr,
+                            const DbgOut& d, hipStream_t s, const Timing& tm) {
+  if (sr) launch_gateup_sr<FMT, NTT, KSW, true>(L, x, x_dtype, T, w, xrows, d, s, tm);
+  else launch_gateup_sr<FMT, NTT, KSW, false>(L, x, x_dtype, T, w, xrows, d, s, tm);
 }
 
 // Active slots above which the combine runs as its own kernel instead of ticketed.
@@ -1256,14 +1478,14 @@ static int dec_rows_per_pass(int K, int NP, int T) {
 }
 
 template <int FMT, int NTT>
-static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
-                              hipStream_t s, const Timing& tm) {
+static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows, bool sr,
+                              const DbgOut& d, hipStream_t s, const Timing& tm) {
   switch (pick_ksw(L.H)) {
-    case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, s, tm); break;
-    case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, s, tm); break;
-    case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, s, tm); break;
-    case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, s, tm); break;
-    default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, s, tm); break;
+    case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
+    case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
+    case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
+    case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
+    default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
   }
 }
 
@@ -1291,11 +1513,12 @@ static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, 
 // Token tiles per pass follow the rows staged per pass (16 or 32).
 template <int FMT>
 static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
-                                     uint32_t* tickets, bool omb, hipStream_t s, const Timing& tm) {
+                                     uint32_t* tickets, bool omb, bool sr, const DbgOut& d, hipStream_t s,
+                                     const Timing& tm) {
   const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T);
   const int xd = dec_rows_per_pass(L.I, 2, T);
-  if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, s, tm);
-  else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, s, tm);
+  if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, sr, d, s, tm);
+  else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, false, d, s, tm);
   if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, omb, s, tm);
   else launch_dec_down<FMT, 2>(L, T, w, y, tickets, xd, false, s, tm);
   return hipGetLastError();
@@ -1312,14 +1535,17 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
 
 template <int XDT>
 static void launch_rr(const LayerArgs& L, const void* x, int T, int erows, const Work& w, int max_slots, int ntickets,
-                      int nzero_o, float eps, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
+                      int nzero_o, float eps, bool sr, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
                       int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
   const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
-  if (T * (L.E + 1) <= kDecMailboxWords)
-    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+  if (sr)  // logits only: the gate/up kernel routes
+    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+                max_slots, w.rr_flags, ntickets, nzero_o, eps, nullptr, nullptr, nullptr, nullptr, nullptr);
+  else if (T * (L.E + 1) <= kDecMailboxWords)
+    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, true, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
                 max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   else
-    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
+    MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
                 max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
 }
 
@@ -1342,6 +1568,9 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   }
   const void* xp = x_dtype == 2 ? (const void*)w.xr : x;
   const int xdp = x_dtype == 2 ? 1 : x_dtype;
+  // one token: the router kernel stores the logits and the gate/up blocks route themselves
+  const bool sr = T == 1 && L.E <= kSelfRouteMaxE;
+  const DbgOut d{dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm};
   if (T >= kDecSplitRouteT) {
     // the fp64 matrix-core router and one wave per token for the top-k, then the route
     hipError_t e = launch_router_topk(L, xp, xdp, T, w, dbg_ids, dbg_w, s, tm);
@@ -1349,22 +1578,22 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
     MOEQ_LAUNCH(tm, kStageBucket, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, w, max_slots, ntickets,
                 dbg_counts, dbg_offsets, dbg_perm);
   } else if (x_dtype == 0) {
-    launch_rr<0>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+    launch_rr<0>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                  dbg_perm, s, tm);
   } else if (x_dtype == 1) {
-    launch_rr<1>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+    launch_rr<1>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                  dbg_perm, s, tm);
   } else {
-    launch_rr<2>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+    launch_rr<2>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                  dbg_perm, s, tm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (L.wfmt) {
-    case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
-    case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
-    case 4: return launch_dec_experts<4>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
-    default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, s, tm);
+    case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
+    case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
+    case 4: return launch_dec_experts<4>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
+    default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
   }
 }
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_dequant_aff3(const uint8_t* __restrict_
 
 // x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y^2 + eps)); one block of 256 threads per
 // token.  The sum of squares, the mean, the square root and the quotient are fp64 (the
-// quotient correctly rounded), then rounded once to bf16.
+// quotient correctly rounded: rms_apply), then rounded once to bf16.
 __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y, int H, float eps,
                                                      uint16_t* __restrict__ out) {
   __shared__ double part[4];
@@ -82,7 +82,14 @@ __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
   const double d = rms_divisor(part[0], part[1], part[2], part[3], H, eps);
-  for (int n = threadIdx.x; n < H; n += 256) out[(size_t)t * H + n] = rms_apply(yt[n], d);
+  const double rd = 1.0 / d;
+  for (int n0 = threadIdx.x; n0 < H; n0 += 8 * 256) {
+    uint16_t v[8];
+    rms_apply8(yt, n0, 256, H, d, rd, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (n0 + 256 * u < H) out[(size_t)t * H + n0 + 256 * u] = v[u];
+  }
 }
 
 // Streaming-read probe: every lane reads 16-byte chunks, grid-stride, with nontemporal
