@@ -803,7 +803,9 @@ __global__ __launch_bounds__(256) void k_pf_combine(int T, int H, int k, int has
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // MXFP4 path: fp8 planes of the activations x with one E8M0 scale per row.
-//   x [T][H] bf16 (XDT 1, NPX = 2: exact) or fp32 (XDT 0, NPX = 3); xq = NPX planes
+//   x [T][H] bf16 (XDT 1, NPX = 2: exact for entries down to about 2^-9 of the row
+//   maximum; smaller ones lose low bits to the e4m3 subnormal floor) or fp32 (XDT 0,
+//   NPX = 3); xq = NPX planes
 //   [T][Hp] (Hp = H rounded up to 128, zero columns past H), then T scale bytes.
 // One block per row: the row maximum, then x / 2^e split into fp8 planes as in the h
 // epilogue (2^e maps the row maximum into [128, 256)).
