@@ -427,12 +427,32 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t codes, float scale) {
 // Four codebook-index bytes -> 8 bf16 codebook values through a 256-entry LDS table
 // whose entry b packs (codebook[b & 15], codebook[b >> 4]).  int8 values are exact
 // in bf16.
+// Byte I of c times 4 (the byte offset of table entry c.byte[I]) in one instruction: a
+// shift whose source operand selects the byte (SDWA).  Pure register arithmetic.
+template <int I>
+__device__ __forceinline__ uint32_t byte_x4(uint32_t c) {
+  uint32_t r;
+  if constexpr (I == 0)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(c));
+  else if constexpr (I == 1)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(c));
+  else if constexpr (I == 2)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(c));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(c));
+  return r;
+}
 __device__ __forceinline__ bf16x8_t cb4x8_to_bf16(uint32_t codes, const uint32_t* lut) {
+  const uint8_t* t = (const uint8_t*)lut;
   u32x4_t v;
-  v[0] = lut[codes & 0xFFu];
-  v[1] = lut[(codes >> 8) & 0xFFu];
-  v[2] = lut[(codes >> 16) & 0xFFu];
-  v[3] = lut[codes >> 24];
+  v[0] = *(const uint32_t*)(t + byte_x4<0>(codes));
+  v[1] = *(const uint32_t*)(t + byte_x4<1>(codes));
+  v[2] = *(const uint32_t*)(t + byte_x4<2>(codes));
+  v[3] = *(const uint32_t*)(t + byte_x4<3>(codes));
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -447,6 +467,55 @@ __device__ __forceinline__ void build_cb4_lut(uint32_t* lut, const int8_t* codeb
     uint32_t hi = int8_to_bf16_bits(codebook[b >> 4]);
     lut[b] = lo | (hi << 16);
   }
+}
+
+// Matrix-core results about to be read by vector, LDS or memory instructions.  Such reads
+// need idle cycles after the MFMA that the hardware does not enforce: measured on gfx950,
+// at least 7 for 16x16x32 bf16 and 11 for the scaled 16x16x128 fp8/fp4; with the
+// compiler's minimum spacing (mostly scalar instructions in between) reads have returned
+// stale registers.  The asm takes the results as read-write operands, so no read can move
+// above it, and idles 16 (SETTLE_SHORT) or 24 cycles.
+#define MOEQ_SETTLE_ASM "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+#define MOEQ_SETTLE_SHORT_ASM "s_nop 7\n\ts_nop 7"
+template <typename A>
+__device__ __forceinline__ void mfma_settle(A& a) {
+  asm volatile(MOEQ_SETTLE_ASM : "+v"(a));
+}
+template <typename A, typename B>
+__device__ __forceinline__ void mfma_settle(A& a, B& b) {
+  asm volatile(MOEQ_SETTLE_ASM : "+v"(a), "+v"(b));
+}
+template <typename A>
+__device__ __forceinline__ void mfma_settle4(A (&t)[4], bool short_wait = false) {
+  if (short_wait) asm volatile(MOEQ_SETTLE_SHORT_ASM : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
+  else asm volatile(MOEQ_SETTLE_ASM : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
+}
+// every element of an accumulator array, all operands of one asm (so that it follows every
+// MFMA that produces them)
+template <typename A, int N>
+__device__ __forceinline__ void mfma_settle_all(A (&t)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 accumulators");
+  if constexpr (N == 1) mfma_settle(t[0]);
+  else if constexpr (N == 2) mfma_settle(t[0], t[1]);
+  else mfma_settle4(t);
+}
+// a [4][NTT] accumulator block (NTT <= 4)
+template <typename A, int NTT>
+__device__ __forceinline__ void mfma_settle_block(A (&t)[4][NTT]) {
+  static_assert(NTT >= 1 && NTT <= 4, "up to 4 token tiles");
+  if constexpr (NTT == 1)
+    asm volatile(MOEQ_SETTLE_ASM : "+v"(t[0][0]), "+v"(t[1][0]), "+v"(t[2][0]), "+v"(t[3][0]));
+  else if constexpr (NTT == 2)
+    asm volatile(MOEQ_SETTLE_ASM : "+v"(t[0][0]), "+v"(t[1][0]), "+v"(t[2][0]), "+v"(t[3][0]), "+v"(t[0][1]),
+                 "+v"(t[1][1]), "+v"(t[2][1]), "+v"(t[3][1]));
+  else if constexpr (NTT == 3)
+    asm volatile(MOEQ_SETTLE_ASM : "+v"(t[0][0]), "+v"(t[1][0]), "+v"(t[2][0]), "+v"(t[3][0]), "+v"(t[0][1]),
+                 "+v"(t[1][1]), "+v"(t[2][1]), "+v"(t[3][1]), "+v"(t[0][2]), "+v"(t[1][2]), "+v"(t[2][2]),
+                 "+v"(t[3][2]));
+  else
+    asm volatile(MOEQ_SETTLE_ASM : "+v"(t[0][0]), "+v"(t[1][0]), "+v"(t[2][0]), "+v"(t[3][0]), "+v"(t[0][1]),
+                 "+v"(t[1][1]), "+v"(t[2][1]), "+v"(t[3][1]), "+v"(t[0][2]), "+v"(t[1][2]), "+v"(t[2][2]),
+                 "+v"(t[3][2]), "+v"(t[0][3]), "+v"(t[1][3]), "+v"(t[2][3]), "+v"(t[3][3]));
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {

@@ -39,6 +39,9 @@ constexpr int kRmsFoldElems = 24576;
 constexpr int waitcnt_vm_le(int n) {
   return (n > 63 ? 63 : n) & 15 | (7 << 4) | (15 << 8) | (((n > 63 ? 63 : n) >> 4) << 14);
 }
+// The same, also waiting for all of this wave's LDS stores and scalar loads (lgkmcnt 0):
+// the barrier after it does not wait for memory by itself.
+constexpr int waitcnt_vm_le_lgkm0(int n) { return waitcnt_vm_le(n) & ~(15 << 8); }
 // vector-memory instructions one prefetch_step issues per 16-row tile: MXFP4 one 16-byte
 // code load and one scale byte (the packed scale store: one delta byte); CB4 four code
 // dwords and four fp16 scales; 3-bit affine one 12-byte code load and one 8-byte
@@ -612,11 +615,14 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
   {
     const int ks = ks0 + stride * i;
     if constexpr (fmt_is_mx(FMT)) {
-      const int kb = 4 * ks + g;
-      const int kbc = (ks < nks && kb < nkb) ? kb : 0;
-      r.c[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(pt.codes +
-                                                                                             pk_code(kbc, m)));
-      r.s[i] = pt.scales[FMT == 3 ? pk_scale_mx(kbc, m) >> 1 : pk_scale_mx(kbc, m)];
+      // block 4 ksc + g of row m (a block past the row: the step's first block), as the
+      // wave-uniform step base plus a 32-bit lane offset
+      const int ksc = ks < nks ? ks : 0;
+      const int gc = 4 * ksc + g < nkb ? g : 0;
+      r.c[i] = __builtin_nontemporal_load(
+          (const __attribute__((address_space(1))) u32x4_t*)(pt.codes + (size_t)ksc * 1024 + (uint32_t)(gc * 256 + 16 * m)));
+      const uint32_t si = (uint32_t)(gc * 16 + m);
+      r.s[i] = FMT == 3 ? (pt.scales + (size_t)ksc * 32)[si >> 1] : (pt.scales + (size_t)ksc * 64)[si];
     } else if constexpr (FMT == 4) {
       const int ksc = ks < nks ? ks : 0;
       r.c[i] = __builtin_nontemporal_load(
@@ -624,12 +630,16 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
       r.s[i] = *(const __attribute__((address_space(1))) uint64_t*)(pt.scales + 128 * ksc + 8 * m);
     } else {
       const int ksc = ks < nks ? ks : 0;
+      const uint32_t lo = (uint32_t)(16 * m + 4 * g);  // lane offset within a block's 256 bytes
+      // the step's scale unit holds rb = min(4, blocks left) entries per row, row-major
+      const int rb = min(4, nkb - 4 * ksc);
+      const uint32_t so = 2u * __umul24((uint32_t)m, (uint32_t)rb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int kbc = min(4 * ksc + j, nkb - 1);
-        r.c[i][j] = __builtin_nontemporal_load(
-            (const __attribute__((address_space(1))) uint32_t*)(pt.codes + pk_code(kbc, m) + 4 * g));
-        r.s[i][j] = *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + 2 * pk_scale_cb(kbc, m, nkb));
+        const int jc = min(j, rb - 1);  // a block past the row: the row's last block (uniform)
+        r.c[i][j] = __builtin_nontemporal_load((const __attribute__((address_space(1))) uint32_t*)(
+            pt.codes + ((size_t)ksc * 1024 + (size_t)jc * 256) + lo));
+        r.s[i][j] = *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + ((size_t)ksc * 128 + 2 * jc) + so);
       }
     }
   }
@@ -655,34 +665,52 @@ __device__ __forceinline__ void prefetch_weights2(WeightRegs<FMT, KSW>& ra, cons
   }
 }
 
+// An empty use of k-step i's weight registers.
+template <int FMT, int KSW>
+__device__ __forceinline__ void consume_weights(const WeightRegs<FMT, KSW>& r, int i) {
+  if constexpr (fmt_is_mx(FMT)) {
+    asm volatile("" ::"v"(r.c[i]), "v"(r.s[i]));
+  } else if constexpr (FMT == 4) {
+    asm volatile("" ::"v"(r.c[i]), "v"(r.s[i]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(r.c[i][j]), "v"(r.s[i][j]));
+  }
+}
+
 // acc[tt] += A(token tile tt, planes) x B(weights of k-step i) for one weight matrix.
 // sbase: the packed scale store's base byte of this lane's weight row (format 3 only).
-// xrows = activation rows staged in LDS.  Branch-free: the activation operand is zero
-// for slots >= xrows, for k-steps past the row (ks >= nks) and for 32-blocks past it,
-// so those MFMAs add exact zeros (the weights they meet are clamped real blocks).
+// arow[tt]: this lane's activation row for token tile tt in LDS (slot 16 tt + m, or the
+// tile's zero row for a slot past the staged rows).  Staged rows are zero from column K
+// to the end of the last k-step, so 32-blocks past the row add exact zeros (the weights
+// they meet are clamped real blocks); k-steps past the row (ks is wave-uniform) are
+// skipped.  No per-lane masking: every MFMA reads its operands unconditionally.
 template <int FMT, int NP, int NTT, int KSW>
-__device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, int ks, int nks, int nkb,
-                                          const uint16_t* xs, int xstride, size_t plane_stride, int live, int xrows,
+__device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, int ks, int nks,
+                                          const uint16_t* const (&arow)[NTT], size_t plane_stride, int live,
                                           const uint32_t* lut, uint32_t sbase, f32x4_t (&acc)[NTT],
-                                          const float* xsum = nullptr) {
+                                          const float* xsum = nullptr, int ngrp = 0) {
+  if (ks >= nks) {
+    // the step's loads were issued (clamped addresses) but are not used: read their
+    // registers here, so that no load is left outstanding past this point (the compiler
+    // would otherwise wait for all loads before those registers' next use)
+    consume_weights<FMT, KSW>(r, i);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  const bool ksv = ks < nks;
   if constexpr (fmt_is_mx(FMT)) {
     const float sc = e8m0_to_f32(FMT == 3 ? ps_e8m0(sbase, r.s[i], m) : r.s[i]);
-    const bool kval = ksv && (4 * ks + g < nkb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8_t b = fp4x8_to_bf16(r.c[i][j], sc);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         if (tt < live) {
-          const bool ok = kval && (16 * tt + m < xrows);
-          const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + (ok ? 128 * ks + 32 * g + 8 * j : 0);
+          const uint16_t* ap = arow[tt] + 128 * ks + 32 * g + 8 * j;
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
-            av = ok ? av : u32x4_t{0, 0, 0, 0};
+            const u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
             acc[tt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, acc[tt]);
           }
         }
@@ -691,10 +719,10 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, 
   } else if constexpr (FMT == 4) {
     // 3-bit affine: per 64-column group G (MFMAs 2G, 2G+1) the matrix cores sum
     // (128 + q) x exactly per product; s (that) + (b - 128 s) X, X the group's activation
-    // sum per token slot (xsum[slot * (K/64) + group]), is the group's sum of (s q + b) x.
+    // sum per token slot (xsum[slot * ngrp + group], zero past the staged rows), is the
+    // group's sum of (s q + b) x.
     uint32_t o[16];
     aff3_pairs(r.c[i], o);
-    const int ngrp = nkb >> 1;
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const float sc = half_bits_to_f32((uint16_t)(r.s[i] >> (32 * G)));
@@ -702,51 +730,91 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, 
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         if (tt < live) {
-          const bool ok = ksv && (16 * tt + m < xrows);
-          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t tmp[1] = {{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * G + jj;
             const u32x4_t bw = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-            const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + (ok ? 128 * ks + 32 * j + 8 * g : 0);
+            const uint16_t* ap = arow[tt] + 128 * ks + 32 * j + 8 * g;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-              u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
-              av = ok ? av : u32x4_t{0, 0, 0, 0};
-              tmp = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bw), tmp);
+              const u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
+              tmp[0] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bw), tmp[0]);
             }
           }
-          if (ksv) {
-            const float* xg = xsum + (size_t)(16 * tt + 4 * g) * ngrp + 2 * ks + G;
+          mfma_settle(tmp[0]);
+          const float* xg = xsum + (size_t)(16 * tt + 4 * g) * ngrp + 2 * ks + G;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(bc, xg[(size_t)q * ngrp], fmaf(sc, tmp[q], acc[tt][q]));
-          }
+          for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(bc, xg[(size_t)q * ngrp], fmaf(sc, tmp[0][q], acc[tt][q]));
         }
       }
     }
   } else {
+    // the 4 blocks' MFMAs first, then their scaled sums (block order j per output)
+    bf16x8_t b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool kval = ksv && (4 * ks + j < nkb);
-      const bf16x8_t b = cb4x8_to_bf16(r.c[i][j], lut);
-      const float sc = half_bits_to_f32((uint16_t)r.s[i][j]);
+    for (int j = 0; j < 4; ++j) b[j] = cb4x8_to_bf16(r.c[i][j], lut);
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        if (tt < live) {
-          const bool ok = kval && (16 * tt + m < xrows);
-          const uint16_t* ap = xs + (size_t)(ok ? 16 * tt + m : 0) * xstride + (ok ? 128 * ks + 32 * j + 8 * g : 0);
-          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt) {
+      if (tt < live) {
+        f32x4_t tmp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t* ap = arow[tt] + 128 * ks + 32 * j + 8 * g;
+          tmp[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
-            av = ok ? av : u32x4_t{0, 0, 0, 0};
-            tmp = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b, tmp);
+            const u32x4_t av = *(const u32x4_t*)(ap + p * plane_stride);
+            tmp[j] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), b[j], tmp[j]);
           }
+        }
+        mfma_settle4(tmp);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(sc, tmp[q], acc[tt][q]);
+        for (int j = 0; j < 4; ++j) {
+          const float sc = half_bits_to_f32((uint16_t)r.s[i][j]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(sc, tmp[j][q], acc[tt][q]);
         }
       }
     }
+  }
+}
+
+// This lane's activation rows (one per token tile) in a staged LDS tile: slot 16 tt + m
+// when it holds a staged row (slot < xrows), else the zero row (index zrow).
+template <int NTT>
+__device__ __forceinline__ void dec_arows(const uint16_t* xs, int xstride, int xrows, int zrow,
+                                          const uint16_t* (&arow)[NTT]) {
+  const int m = threadIdx.x & 15;
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int sl = 16 * tt + m;
+    arow[tt] = xs + (size_t)(sl < xrows ? sl : zrow) * xstride;
+  }
+}
+
+// Zero the parts of a staged LDS tile that the MFMAs read but no staging load writes:
+// the zero row (index zrow of every plane, all kc columns) and columns K .. kc-1 of the
+// rows 0 .. nrows-1 (kc = K rounded up to whole 128-column k-steps).  LDS stores by the
+// whole block; the caller's barrier orders them before the MFMAs (after an lgkmcnt wait).
+template <int NP>
+__device__ __forceinline__ void zero_tile_pad(uint16_t* xs, int xstride, size_t lds_plane, int K, int kc, int zrow,
+                                              int nrows) {
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  const u32x4_t zv = {0u, 0u, 0u, 0u};
+  // LDS stores through LDS pointers made from the 32-bit LDS address (the low half of
+  // the generic pointer)
+  auto lds = [](const uint16_t* q) { return (lds_u32x4*)(uint32_t)(uintptr_t)q; };
+  const int zc = kc >> 3;  // 16-byte chunks
+  for (int idx = threadIdx.x; idx < NP * zc; idx += blockDim.x) {
+    const int q = idx / zc, c = idx - q * zc;
+    *lds(xs + q * lds_plane + (size_t)zrow * xstride + 8 * c) = zv;
+  }
+  const int pc = (kc - K) >> 3;  // K is a multiple of 32 columns
+  for (int idx = threadIdx.x; idx < NP * nrows * pc; idx += blockDim.x) {
+    const int q = idx / (nrows * pc), rc = idx - q * nrows * pc;
+    const int row = rc / pc, c = rc - row * pc;
+    *lds(xs + q * lds_plane + (size_t)row * xstride + K + 8 * c) = zv;
   }
 }
 
@@ -781,8 +849,9 @@ __device__ __forceinline__ void stage_rows(uint16_t* xs, int xstride, size_t lds
 // track it: the caller waits for it explicitly (s_waitcnt vmcnt) before a barrier,
 // while later loads stay in flight.
 __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds) {
-  const uint32_t lds_addr =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  // the low 32 bits of a generic pointer into LDS are its LDS address (no address-space
+  // cast, whose null test the code generator can emit in an illegal form)
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr),
                "v"((const __attribute__((address_space(1))) void*)gptr)
                : "memory", "m0");
@@ -802,6 +871,10 @@ __device__ __forceinline__ void stage_rows_lds(uint16_t* xs, int xstride, size_t
     const int pair = lane < nrows ? (slot < kSlotRows ? slot_rec->rows[slot] : perm_e[slot]) : 0;
     myrow = BY_TOKEN ? dec_token_of_pair(pair, T, k) : pair;
   }
+  // settle the row ids here: the compiler then places no wait inside the loop, where a
+  // wait for them would also wait for each earlier direct load (it does not track those)
+  // and issue the rows one round trip at a time
+  asm volatile("" ::"v"(myrow));
   const int jobs = nrows * nchunk * NP;
   for (int job = wave; job < jobs; job += 4) {  // wave-uniform
     const int q = job % NP;
@@ -841,16 +914,21 @@ __device__ __forceinline__ void dec_group_sums(float* xsum, const uint16_t* xs, 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// LDS of a projection block: 1 KB codebook table, then the activation tile of xrows rows
-// (NP planes), which the split-K reduction buffer later reuses, then (3-bit affine) the
-// group sums of 16 NTT token slots.
+// LDS columns of a staged activation row: K rounded up to whole 128-column k-steps (zero
+// past K), and the row stride.
+__host__ __device__ inline int dec_kcols(int K) { return (K + 127) & ~127; }
+__host__ __device__ inline int dec_xstride(int K) { return lds_row_stride(dec_kcols(K)); }
+// Dynamic LDS of a projection block: the activation tile (NP planes of xrows staged rows
+// and one zero row), which the split-K reduction buffer later reuses, then (3-bit affine)
+// the group sums of 16 NTT token slots.  The codebook table is a static LDS array of the
+// kernel, so its address is a constant that the table reads carry as an immediate offset.
 __host__ __device__ inline size_t dec_tile_bytes(int K, int NP, int NTT, int xrows) {
-  const size_t x = (size_t)NP * xrows * lds_row_stride(K) * 2;
+  const size_t x = (size_t)NP * (xrows + 1) * dec_xstride(K) * 2;
   const size_t red = (size_t)3 * 8 * NTT * 64 * 4;
   return x > red ? x : red;
 }
 __host__ __device__ inline size_t dec_lds_bytes(int fmt, int K, int NP, int NTT, int xrows) {
-  return 1024 + dec_tile_bytes(K, NP, NTT, xrows) + (fmt == 4 ? (size_t)16 * NTT * (K / 64) * 4 : 0);
+  return dec_tile_bytes(K, NP, NTT, xrows) + (fmt == 4 ? (size_t)16 * NTT * (K / 64) * 4 : 0);
 }
 
 // One token: its activation row (NP planes) into LDS row 0, the 4 waves splitting the
@@ -1018,65 +1096,39 @@ __device__ __forceinline__ void dec_self_route(const LayerArgs& L, const Work& w
 }
 
 // ---------------------------------------------------------------------------
-// 3. Fused gate/up + SwiGLU.  grid = (I/16, max active slots), 4 waves split K.
+// 3. Fused gate/up + SwiGLU per (16-row tile, active expert), 4 waves split K.
 //    Each wave first issues direct-to-LDS loads of its share of the expert's
 //    activation rows, then all its weight loads; it waits only for the former before
 //    the staging barrier, and each k-step's MFMAs then wait only for that step's
 //    weights while the rest are still in flight.
-// dynamic LDS: 1 KB CB4 table, then [NP][xrows][xstride] bf16 activations (reused by
-// the split-K reduction).
 // ---------------------------------------------------------------------------
+// One block's share of the gate/up projection: the 16-row gate and up tiles x of one
+// active expert (slot record sr), passes of xrows_max pairs starting at pair tb0, every
+// tb_step pairs.  SR: the caller has staged and padded row 0.
 template <int FMT, int NP, int NTT, int KSW, bool SR>
-__global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
-                                                       size_t act_plane, int xrows_max, int nslots,
-                                                       int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w,
-                                                       int32_t* __restrict__ dbg_counts,
-                                                       int32_t* __restrict__ dbg_offsets,
-                                                       int32_t* __restrict__ dbg_perm) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  // grid.y = slots x passes, slot-major: block row y takes pass y % npass of slot
-  // y / npass (rows xrows_max (y % npass) ..), so an expert with more pairs than one pass
-  // stages runs its passes side by side on adjacent rows, dispatched together with its
-  // first pass; rows past a slot's pairs exit at once.  SR (one token): the block routes
-  // itself (dec_self_route) and keeps its slot record in LDS.
-  __shared__ Slot s_rec;
-  const int npass = (int)gridDim.y / nslots;
-  const Slot* slot_rec;
-  if constexpr (SR) {
-    // the token's row is staged while the block routes (one token: T = 1, one pass)
-    stage_token0_lds<NP>((uint16_t*)(smem + 1024), (size_t)xrows_max * lds_row_stride(L.H), act, act_plane, L.H);
-    const int nper = (L.E + 63) >> 6;
-    if (nper <= 1) dec_self_route<1>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    else if (nper <= 2) dec_self_route<2>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    else dec_self_route<4>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
-    slot_rec = &s_rec;
-  } else {
-    slot_rec = w.slots + blockIdx.y / npass;
-  }
-  const int cnt = slot_rec->cnt, off = slot_rec->off;
-  const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
-  if (tb0 >= cnt) {
-    if (SR) __builtin_amdgcn_s_waitcnt(0);  // the staging loads land before the LDS is released
-    return;
-  }
+__device__ __forceinline__ void dec_gateup_item(const LayerArgs& L, int T, const Work& w, const uint16_t* act,
+                                                size_t act_plane, int xrows_max, const Slot* sr, int x, int tb0,
+                                                int tb_step, uint8_t* smem, const uint32_t* lut) {
+  const int cnt = sr->cnt, off = sr->off;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
   const int K = H, nkb = K >> 5, nks = (nkb + 3) >> 2;
-  const int xstride = lds_row_stride(K);
-  const size_t lds_plane = (size_t)xrows_max * xstride;
-  uint32_t* lut = (uint32_t*)smem;
-  uint16_t* xs = (uint16_t*)(smem + 1024);
-  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, NP, NTT, xrows_max));  // 3-bit affine
-  const PackedTile pg = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, blockIdx.x);
-  const PackedTile pu = packed_tile<FMT>(slot_rec->gate_up, 2 * I, K, I / 16 + blockIdx.x);
+  const int xstride = dec_xstride(K);
+  const size_t lds_plane = (size_t)(xrows_max + 1) * xstride;  // staged rows, then the zero row
+  uint16_t* xs = (uint16_t*)smem;
+  float* xsum = (float*)(smem + dec_tile_bytes(K, NP, NTT, xrows_max));  // 3-bit affine
+  const PackedTile pg = packed_tile<FMT>(sr->gate_up, 2 * I, K, x);
+  const PackedTile pu = packed_tile<FMT>(sr->gate_up, 2 * I, K, I / 16 + x);
   // the packed scale store's row bases, loaded before the staging loads (not counted below)
   const uint32_t bg = FMT == 3 ? (uint32_t)pg.bases[n] : 0u, bu = FMT == 3 ? (uint32_t)pu.bases[n] : 0u;
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
-  for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
+  for (int tb = tb0; tb < cnt; tb += tb_step) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
+    const uint16_t* arow[NTT];
+    dec_arows<NTT>(xs, xstride, xrows, xrows_max, arow);
     f32x4_t accg[NTT], accu[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) { accg[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accu[tt] = accg[tt]; }
@@ -1084,44 +1136,46 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
       const int ks0 = ch * 4 * KSW + wave;
       if (ch == 0) {
         if (tb > tb0) __syncthreads();  // the previous pass finished with the LDS tile
-        else if (FMT == 2) build_cb4_lut(lut, L.codebook);
-        if (!SR)  // (self-routed: the row was staged before the routing)
-          stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, slot_rec, w.perm + off, tb, xrows, T,
-                                   k);
+        if (!SR) {  // (self-routed: the row was staged before the routing)
+          stage_rows_lds<NP, true>(xs, xstride, lds_plane, act, act_plane, K, sr, w.perm + off, tb, xrows, T, k);
+          zero_tile_pad<NP>(xs, xstride, lds_plane, K, dec_kcols(K), xrows_max, xrows);
+        }
       }
       WeightRegs<FMT, KSW> wg, wu;
       prefetch_weights2<FMT, KSW>(wg, pg, wu, pu, nkb, ks0, nks, n, g);
       if (ch == 0) {
         // this wave's staging loads are complete once at most the weight loads issued
         // after them are outstanding; then every wave's rows are in LDS after the barrier
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(2 * KSW * loads_per_step<FMT>()));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(2 * KSW * loads_per_step<FMT>()));
         __builtin_amdgcn_s_barrier();
         if constexpr (FMT == 4) dec_group_sums<NP>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
       }
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bg, accg, xsum);
-        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bu, accu, xsum);
+        mma_kstep<FMT, NP, NTT, KSW>(wg, i, ks, nks, arow, lds_plane, live, lut, bg, accg, xsum, nkb >> 1);
+        mma_kstep<FMT, NP, NTT, KSW>(wu, i, ks, nks, arow, lds_plane, live, lut, bu, accu, xsum, nkb >> 1);
       }
     }
     // split-K reduction (fixed wave order), SwiGLU, two bf16 planes of h
+    mfma_settle_all(accg);
+    mfma_settle_all(accu);
     float v[8 * NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) { v[8 * tt + q] = accg[tt][q]; v[8 * tt + 4 + q] = accu[tt][q]; }
-    reduce4<8 * NTT>(v, (float*)(smem + 1024));
+    reduce4<8 * NTT>(v, (float*)smem);
     if (wave == 0) {
       const int P = T * k + (L.has_shared ? T : 0);
-      const int col = 16 * blockIdx.x + n;
+      const int col = 16 * x + n;
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int slot = tb + 16 * tt + 4 * g + q;
           if (slot < tb + xrows) {  // this pass's pairs only
-            const int p = slot < kSlotRows ? slot_rec->rows[slot] : w.perm[off + slot];
+            const int p = slot < kSlotRows ? sr->rows[slot] : w.perm[off + slot];
             const float h = silu_f32(v[8 * tt + q]) * v[8 * tt + 4 + q];
             const uint32_t hi = f32_to_bf16_rne(h);
             const uint32_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
@@ -1131,6 +1185,48 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
         }
       }
     }
+  }
+}
+
+// Gate/up projection, grid (I/16, slots x passes).  Block row y takes pass y % npass of
+// slot y / npass (pairs xrows_max (y % npass) ..), so an expert with more pairs than one
+// pass stages has its passes run side by side on adjacent rows; rows past a slot's pairs
+// exit at once.  SR (one token, one pass): the block routes itself (dec_self_route),
+// staging the token's row meanwhile, and keeps its slot record in LDS.
+template <int FMT, int NP, int NTT, int KSW, bool SR>
+__global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
+                                                       size_t act_plane, int xrows_max, int nslots,
+                                                       int32_t* __restrict__ dbg_ids, float* __restrict__ dbg_w,
+                                                       int32_t* __restrict__ dbg_counts,
+                                                       int32_t* __restrict__ dbg_offsets,
+                                                       int32_t* __restrict__ dbg_perm) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint32_t s_lut[FMT == 2 ? 256 : 1];  // codebook table (CB4)
+  if constexpr (SR) {
+    __shared__ Slot s_rec;
+    const int xst = dec_xstride(L.H);
+    const size_t lpl = (size_t)(xrows_max + 1) * xst;
+    stage_token0_lds<NP>((uint16_t*)smem, lpl, act, act_plane, L.H);
+    zero_tile_pad<NP>((uint16_t*)smem, xst, lpl, L.H, dec_kcols(L.H), xrows_max, 1);
+    const int nper = (L.E + 63) >> 6;
+    if (nper <= 1) dec_self_route<1>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else if (nper <= 2) dec_self_route<2>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    else dec_self_route<4>(L, w, &s_rec, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+    if (s_rec.cnt == 0) {
+      __builtin_amdgcn_s_waitcnt(0);  // the staging loads land before the LDS is released
+      return;
+    }
+    if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
+    dec_gateup_item<FMT, NP, NTT, KSW, SR>(L, T, w, act, act_plane, xrows_max, &s_rec, blockIdx.x, 0, xrows_max,
+                                           smem, s_lut);
+  } else {
+    const int npass = (int)gridDim.y / nslots;
+    const Slot* sr = w.slots + blockIdx.y / npass;
+    const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
+    if (tb0 >= sr->cnt) return;
+    if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
+    dec_gateup_item<FMT, NP, NTT, KSW, SR>(L, T, w, act, act_plane, xrows_max, sr, blockIdx.x, tb0,
+                                           npass * xrows_max, smem, s_lut);
   }
 }
 
@@ -1184,30 +1280,28 @@ __device__ __forceinline__ uint32_t omb_encode(float v) {
 }
 
 template <int FMT, int NTT, int KSW, bool OMB>
-__global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
-                                                     uint32_t* __restrict__ tickets, int xrows_max) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int is_last;
-  const Slot* slot_rec = w.slots + blockIdx.y;
+__device__ __forceinline__ void dec_down_item(const LayerArgs& L, int T, const Work& w, float* __restrict__ y,
+                                              uint32_t* __restrict__ tickets, int xrows_max, const Slot* slot_rec,
+                                              int x, uint8_t* smem, const uint32_t* lut, int* is_last) {
   const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
-  if (cnt == 0) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
   const int P = T * k + (L.has_shared ? T : 0);
   const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
-  const int xstride = lds_row_stride(K);
-  const size_t lds_plane = (size_t)xrows_max * xstride;
-  uint32_t* lut = (uint32_t*)smem;
-  uint16_t* xs = (uint16_t*)(smem + 1024);
-  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
-  const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, blockIdx.x);
+  const int xstride = dec_xstride(K);
+  const size_t lds_plane = (size_t)(xrows_max + 1) * xstride;  // staged rows, then the zero row
+  uint16_t* xs = (uint16_t*)smem;
+  float* xsum = (float*)(smem + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
+  const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, x);
   const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
 
   for (int tb = 0; tb < cnt; tb += xrows_max) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
+    const uint16_t* arow[NTT];
+    dec_arows<NTT>(xs, xstride, xrows, xrows_max, arow);
     f32x4_t acc[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1215,29 +1309,30 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
       const int ks0 = ch * 4 * KSW + wave;
       if (ch == 0) {
         if (tb > 0) __syncthreads();
-        else if (FMT == 2) build_cb4_lut(lut, L.codebook);
         stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb,
                                  xrows, T, k);
+        zero_tile_pad<2>(xs, xstride, lds_plane, K, dec_kcols(K), xrows_max, xrows);
       }
       WeightRegs<FMT, KSW> wd;
       prefetch_weights<FMT, KSW>(wd, pd, nkb, ks0, nks, n, g);
       if (ch == 0) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(KSW * loads_per_step<FMT>()));
         __builtin_amdgcn_s_barrier();
         if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
       }
 #pragma unroll
       for (int i = 0; i < KSW; ++i) {
         const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc, xsum);
+        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, arow, lds_plane, live, lut, bd, acc, xsum, nkb >> 1);
       }
     }
+    mfma_settle_all(acc);
     float v[4 * NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * tt + q] = acc[tt][q];
-    reduce4<4 * NTT>(v, (float*)(smem + 1024));
+    reduce4<4 * NTT>(v, (float*)smem);
     if constexpr (OMB) {
       // One token (one pair per slot, one pass): every slot's block posts its 16 o values to
       // the mailbox (zeroed by the router kernel) and, once they have landed, reads the
@@ -1245,7 +1340,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
       // the pairs in the fixed order and writes y (more than one may: the same values).
       // The block whose read comes last finds them all.
       if (wave == 0 && g == 0) {
-        const int col = 16 * blockIdx.x + n;
+        const int col = 16 * x + n;
         const int p_own = w.perm[off];
         uint32_t* omb = reinterpret_cast<uint32_t*>(w.o);
         const uint32_t mine = omb_encode(v[0]);
@@ -1277,7 +1372,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
       return;
     }
     if (wave == 0) {
-      const int col = 16 * blockIdx.x + n;
+      const int col = 16 * x + n;
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -1294,14 +1389,28 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (uint32_t)(n_active - 1));
+    const uint32_t prev = __hip_atomic_fetch_add(&tickets[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *is_last = (prev == (uint32_t)(n_active - 1));
   }
   __syncthreads();
-  if (!is_last) return;
+  if (!*is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  dec_combine_cols(L, T, w, y, 16 * blockIdx.x, 16);
-  if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  dec_combine_cols(L, T, w, y, 16 * x, 16);
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Down projection kernel, grid (H/16, slots): one block per (column tile, active expert),
+// all of the expert's pairs (several passes for a busy expert).
+template <int FMT, int NTT, int KSW, bool OMB>
+__global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
+                                                     uint32_t* __restrict__ tickets, int xrows_max) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int is_last;
+  __shared__ uint32_t s_lut[FMT == 2 ? 256 : 1];  // codebook table (CB4)
+  const Slot* sr = w.slots + blockIdx.y;
+  if (sr->cnt == 0) return;
+  if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
+  dec_down_item<FMT, NTT, KSW, OMB>(L, T, w, y, tickets, xrows_max, sr, blockIdx.x, smem, s_lut, &is_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1314,50 +1423,46 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 // one ticket would take an atomic per expert on a single address).
 // ---------------------------------------------------------------------------
 template <int FMT, int NTT, int KSW, bool TICKETS>
-__global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Work w, float* __restrict__ y,
-                                                          uint32_t* __restrict__ tickets, int xrows_max, int nslots) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int is_last;
-  // without tickets, grid.y = slots x passes, slot-major as in the gate/up kernel (the
-  // ticketed form counts one arrival per slot, so it keeps one row per slot)
-  const int npass = (int)gridDim.y / nslots;
-  const Slot* slot_rec = w.slots + blockIdx.y / npass;
+__device__ __forceinline__ void dec_down_rows_item(const LayerArgs& L, int T, const Work& w, float* __restrict__ y,
+                                                   uint32_t* __restrict__ tickets, int xrows_max,
+                                                   const Slot* slot_rec, int x, int tb0, int tb_step,
+                                                   uint8_t* smem, const uint32_t* lut, int* is_last) {
   const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
-  const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
-  if (tb0 >= cnt) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
   const int P = T * k + (L.has_shared ? T : 0);
   const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
-  const int xstride = lds_row_stride(K);
-  const size_t lds_plane = (size_t)xrows_max * xstride;
-  uint32_t* lut = (uint32_t*)smem;
-  uint16_t* xs = (uint16_t*)(smem + 1024);
-  float* xsum = (float*)(smem + 1024 + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
-  const int tile = 4 * blockIdx.x + wave;  // this wave's 16 output columns
+  const int xstride = dec_xstride(K);
+  const size_t lds_plane = (size_t)(xrows_max + 1) * xstride;  // staged rows, then the zero row
+  uint16_t* xs = (uint16_t*)smem;
+  float* xsum = (float*)(smem + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
+  const int tile = 4 * x + wave;  // this wave's 16 output columns
   const bool tile_ok = 16 * tile < H;
   const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, tile_ok ? tile : 0);
   const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
 
-  for (int tb = tb0; tb < cnt; tb += (int)(gridDim.y / nslots) * xrows_max) {
+  for (int tb = tb0; tb < cnt; tb += tb_step) {
     const int live = min(NTT, (cnt - tb + 15) / 16);
     const int xrows = min(cnt - tb, xrows_max);
+    const uint16_t* arow[NTT];
+    dec_arows<NTT>(xs, xstride, xrows, xrows_max, arow);
     f32x4_t acc[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (tb > tb0) __syncthreads();
-    else if (FMT == 2) build_cb4_lut(lut, L.codebook);
+    if (tb > tb0) __syncthreads();  // the previous pass finished with the LDS tile
     stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb, xrows,
                              T, k);
+    zero_tile_pad<2>(xs, xstride, lds_plane, K, dec_kcols(K), xrows_max, xrows);
     WeightRegs<FMT, KSW> wd;
     prefetch_weights<FMT, KSW>(wd, pd, nkb, 0, nks, n, g, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_le(KSW * loads_per_step<FMT>()));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(KSW * loads_per_step<FMT>()));
     __builtin_amdgcn_s_barrier();
     if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
-      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, nkb, xs, xstride, lds_plane, live, xrows, lut, bd, acc, xsum);
+      mma_kstep<FMT, 2, NTT, KSW>(wd, i, i, nks, arow, lds_plane, live, lut, bd, acc, xsum, nkb >> 1);
+    mfma_settle_all(acc);
     if (tile_ok) {
       const int col = 16 * tile + n;
 #pragma unroll
@@ -1379,16 +1484,35 @@ __global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Wo
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (uint32_t)(n_active - 1));
+    const uint32_t prev = __hip_atomic_fetch_add(&tickets[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *is_last = (prev == (uint32_t)(n_active - 1));
   }
   __syncthreads();
-  if (!is_last) return;
+  if (!*is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  dec_combine_cols(L, T, w, y, 64 * blockIdx.x, 64);
-  if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  dec_combine_cols(L, T, w, y, 64 * x, 64);
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// Short-row down projection kernel, grid (ceil(H/64), slots [x passes]).  TICKETS: one
+// block row per slot (the ticket counts one arrival per active expert), all passes in the
+// block; otherwise block row y takes pass y % npass of slot y / npass, rows past a slot's
+// pairs exiting at once.
+template <int FMT, int NTT, int KSW, bool TICKETS>
+__global__ __launch_bounds__(256, 3) void k_dec_down_rows(LayerArgs L, int T, Work w, float* __restrict__ y,
+                                                          uint32_t* __restrict__ tickets, int xrows_max, int nslots) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int is_last;
+  __shared__ uint32_t s_lut[FMT == 2 ? 256 : 1];  // codebook table (CB4)
+  const int npass = (int)gridDim.y / nslots;
+  const Slot* sr = w.slots + blockIdx.y / npass;
+  const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
+  if (tb0 >= sr->cnt) return;
+  if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
+  dec_down_rows_item<FMT, NTT, KSW, TICKETS>(L, T, w, y, tickets, xrows_max, sr, blockIdx.x, tb0, npass * xrows_max,
+                                             smem, s_lut, &is_last);
+}
 
 // k-steps per wave: the smallest supported count that covers a quarter of the row's
 // 128-column steps (longer rows loop over chunks of 8).
@@ -1451,16 +1575,16 @@ static void launch_down_rows_k(const LayerArgs& L, int T, const Work& w, float* 
 template <int FMT, int NTT, int KSW>
 static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                           bool omb, hipStream_t s, const Timing& tm) {
-  const dim3 g2(L.H / 16, min(T * L.k, L.E) + (L.has_shared ? 1 : 0));
+  const int slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
   if constexpr (NTT == 1) {
-    if (omb) {
-      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), g2, dim3(256), dec_lds_bytes(FMT, L.I, 2, 1, xrows), s,
-                  L, T, w, y, tickets, xrows);
+    if (omb) {  // one item per block
+      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), dim3(L.H / 16, slots), dim3(256),
+                  dec_lds_bytes(FMT, L.I, 2, 1, xrows), s, L, T, w, y, tickets, xrows);
       return;
     }
   }
-  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), g2, dim3(256), dec_lds_bytes(FMT, L.I, 2, NTT, xrows),
-              s, L, T, w, y, tickets, xrows);
+  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), dim3(L.H / 16, slots), dim3(256),
+              dec_lds_bytes(FMT, L.I, 2, NTT, xrows), s, L, T, w, y, tickets, xrows);
 }
 
 // The one-token mailbox combine of the split-K down kernel: one token and long down rows
@@ -1470,10 +1594,10 @@ static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I 
 // Rows of activations a projection block stages per pass: as many of the expert's
 // pairs as fit in kDecStageBytes of LDS (at least 1, at most T), so that several blocks
 // share a CU whatever T is; an expert with more pairs takes several passes.
-constexpr size_t kDecStageBytes = 32 * 1024;
+constexpr size_t kDecStageBytes = 48 * 1024;
 static int dec_rows_per_pass(int K, int NP, int T) {
-  const size_t row = (size_t)lds_row_stride(K) * 2 * NP;
-  const int cap = (int)(kDecStageBytes / row);
+  const size_t row = (size_t)dec_xstride(K) * 2 * NP;
+  const int cap = (int)(kDecStageBytes / row) - 1;  // and the zero row
   return max(1, min(T, min(cap, kDecMaxTokens)));
 }
 

@@ -263,6 +263,7 @@ __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uin
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma_bf16(a, b[rt], tmp[rt]);
           }
+          mfma_settle4(tmp, true);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -574,6 +575,8 @@ __device__ __forceinline__ void pf_run(const PfCtx& c, const LayerArgs& L, int T
   }
   // the trailing (never used) loads must land before the block's LDS is released
   __builtin_amdgcn_s_waitcnt(pf_vm_le(0));
+  // the accumulators settle before the epilogue reads them (one wait for all)
+  mfma_settle_block(acc);
 
   const int g = c.g, m = c.m;
   // pair ids of this lane's output slots, fetched together before the stores

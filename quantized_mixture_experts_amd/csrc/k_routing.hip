@@ -88,6 +88,10 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(LayerArgs L, 
       acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[q], b[q], acc1, 0, 0, 0);
     }
   }
+  // the fp64 matrix-core results settle before any read (its latency is not measured here:
+  // twice the 24-cycle wait)
+  mfma_settle(acc0, acc1);
+  mfma_settle(acc0, acc1);
   if (wave > 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) { red[wave - 1][0][r][lane] = acc0[r]; red[wave - 1][1][r][lane] = acc1[r]; }
