@@ -1414,7 +1414,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w,
 }
 
 // ---------------------------------------------------------------------------
-// 4'. Down projection for short rows (K = I of at most 4 k-steps of 128 columns):
+// 4'. Down projection for short rows (K = I of at most 8 k-steps of 128 columns):
 // instead of splitting K over the 4 waves, each wave owns one 16-row tile over the
 // whole K, so a block covers 64 output columns with no split-K reduction.
 // grid = (ceil(H/64), max active slots).  TICKETS: per 64 columns a ticket elects the
@@ -1553,6 +1553,10 @@ static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int 
   else launch_gateup_sr<FMT, NTT, KSW, false>(L, x, x_dtype, T, w, xrows, d, s, tm);
 }
 
+// Down rows of at most this many 128-column k-steps take the short-row kernel (each wave
+// one 16-row tile over the whole row: 64 rows, so more weight bytes, per block).
+constexpr int kDownRowsMaxSteps = 8;
+
 // Active slots above which the combine runs as its own kernel instead of ticketed.
 constexpr int kTicketSlotsMax = 24;
 
@@ -1589,7 +1593,7 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
 
 // The one-token mailbox combine of the split-K down kernel: one token and long down rows
 // (no block waits for another, so any grid size works).
-static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I / 32 + 3) / 4 > 4; }
+static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I / 32 + 3) / 4 > kDownRowsMaxSteps; }
 
 // Rows of activations a projection block stages per pass: as many of the expert's
 // pairs as fit in kDecStageBytes of LDS (at least 1, at most T), so that several blocks
@@ -1617,12 +1621,12 @@ template <int FMT, int NTT>
 static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                             bool omb, hipStream_t s, const Timing& tm) {
   const int nks_dn = (L.I / 32 + 3) / 4;
-  if (nks_dn <= 4) {  // short rows: one 16-row tile per wave over the whole K
-    switch (nks_dn) {
-      case 1: launch_down_rows_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm); break;
-      case 2: launch_down_rows_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, s, tm); break;
-      default: launch_down_rows_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, s, tm); break;
-    }
+  if (nks_dn <= kDownRowsMaxSteps) {  // short rows: one 16-row tile per wave over the whole K
+    if (nks_dn <= 1) launch_down_rows_k<FMT, NTT, 1>(L, T, w, y, tickets, xrows, s, tm);
+    else if (nks_dn <= 2) launch_down_rows_k<FMT, NTT, 2>(L, T, w, y, tickets, xrows, s, tm);
+    else if (nks_dn <= 4) launch_down_rows_k<FMT, NTT, 4>(L, T, w, y, tickets, xrows, s, tm);
+    else if (nks_dn <= 6) launch_down_rows_k<FMT, NTT, 6>(L, T, w, y, tickets, xrows, s, tm);
+    else launch_down_rows_k<FMT, NTT, 8>(L, T, w, y, tickets, xrows, s, tm);
     return;
   }
   switch (pick_ksw(L.I)) {
