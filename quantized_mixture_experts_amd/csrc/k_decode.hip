@@ -266,17 +266,17 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
 
 // Routing after top-k (s_exp[p] = the expert of pair p for p < P, s_cnt zeroed): LDS
 // histogram, scan and stable ranks -> counts, offsets, perm, the active list and one slot
-// record per active expert.  Every thread of the block takes part.
+// record per active expert.  Every thread of the block takes part (any block size).
 __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots,
                                                const int* s_exp, int* s_cnt, int* s_incl, const uint8_t* my_gu,
                                                const uint8_t* my_dn, int32_t* __restrict__ dbg_counts,
                                                int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = (int)blockDim.x;
   const int E = L.E, k = L.k;
   const int nb = E + 1;
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  for (int p = tid; p < P; p += kRouteThreads)
+  for (int p = tid; p < P; p += nthr)
     if (s_exp[p] >= 0) atomicAdd(&s_cnt[s_exp[p]], 1);  // expert -1: an omitted pair
   __syncthreads();
   if (wave == 0) {
@@ -302,7 +302,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   __syncthreads();
   const int n_active = s_incl[nb - 1] >> 16;
   const int placed = s_incl[nb - 1] & 0xFFFF;  // pairs in the buckets (omitted ones are not)
-  for (int e = tid; e < nb; e += kRouteThreads) {
+  for (int e = tid; e < nb; e += nthr) {
     const int c = s_cnt[e];
     const int off = (s_incl[e] & 0xFFFF) - c;
     w.counts[e] = c;
@@ -318,7 +318,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
       sl.down = e == tid ? my_dn : L.down[e];
     }
   }
-  for (int a = n_active + tid; a < max_slots; a += kRouteThreads) {
+  for (int a = n_active + tid; a < max_slots; a += nthr) {
     Slot& sl = w.slots[a];
     sl.e = 0; sl.cnt = 0; sl.off = 0; sl.n_active = n_active;
     sl.gate_up = nullptr;
@@ -329,15 +329,24 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     if (dbg_offsets) dbg_offsets[nb] = placed;
     w.active[0] = n_active;
   }
-  for (int i = placed + tid; i < P; i += kRouteThreads) {  // past the placed pairs
+  for (int i = placed + tid; i < P; i += nthr) {  // past the placed pairs
     w.perm[i] = -1;
     if (dbg_perm) dbg_perm[i] = -1;
   }
-  for (int p = tid; p < P; p += kRouteThreads) {
+  for (int p = tid; p < P; p += nthr) {
     const int e = s_exp[p];
     if (e < 0) continue;
+    // stable rank: earlier pairs of the same expert, 4 entries per LDS read (the same
+    // addresses for every lane: broadcast)
     int r = 0;
-    for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
+    const int4* s4 = reinterpret_cast<const int4*>(s_exp);
+    const int nq = p >> 2;
+#pragma unroll 4
+    for (int q4 = 0; q4 < nq; ++q4) {
+      const int4 v = s4[q4];
+      r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (int q = 4 * nq; q < p; ++q) r += (s_exp[q] == e);
     const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
     w.perm[pos] = p;
     if (dbg_perm) dbg_perm[pos] = p;
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
                                                           float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
                                                           int32_t* __restrict__ dbg_offsets,
                                                           int32_t* __restrict__ dbg_perm) {
-  __shared__ int s_exp[kMaxPairsDec];   // expert of each pair
+  __shared__ __align__(16) int s_exp[kMaxPairsDec];   // expert of each pair
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
@@ -545,25 +554,95 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
 }
 
 
-// Decode routing when the logits, ids and gates come from the matrix-core router and the
-// per-token top-k kernel (larger T): the combine tickets, then the route of one block.
-__global__ __launch_bounds__(kRouteThreads) void k_dec_route(LayerArgs L, int T, Work w, int max_slots, int ntickets,
-                                                             int32_t* __restrict__ dbg_counts,
-                                                             int32_t* __restrict__ dbg_offsets,
-                                                             int32_t* __restrict__ dbg_perm) {
-  __shared__ int s_exp[kMaxPairsDec];
+// Decode routing of 8..32 tokens after the matrix-core router (K-split partial logits
+// [nsplit][T][E+1] in w.logits, added in split order): one wave per token takes the top-k
+// (ties to the lower index), the softmax gates with the omission rule and the
+// shared-expert weight, 4 tokens per block.  Each block then checks once, after its
+// results have landed, whether it is the last one to finish (an arrival counter in the
+// workspace header); that block routes: the combine tickets, histogram, scan, slot records.
+// No block waits for another.
+template <int NPER>
+__device__ __forceinline__ void dec_topk_token(const double* logits, int E, int k, int t, int* s_exp, double* s_l,
+                                               int nsplit, size_t sstride) {
+  const int tok[1] = {t}, slot[1] = {0};
+  if (nsplit == 1) topk_tokens<NPER, 1, false, 1>(logits, E, k, tok, slot, s_exp, s_l);
+  else topk_tokens<NPER, 1, false, kRouterMaxSplits>(logits, E, k, tok, slot, s_exp, s_l, nsplit, sstride);
+}
+// the header word counting the top-k blocks that have finished (the router kernel's
+// arrival flags use the words below E / 4 + 1)
+constexpr int kTopkDoneWord = 511;
+constexpr int kTopkRouteThreads = 256;  // 4 tokens per block
+
+__global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs L, int T, Work w, int nsplit,
+                                                                      int max_slots, int ntickets,
+                                                                      int32_t* __restrict__ dbg_ids,
+                                                                      float* __restrict__ dbg_w,
+                                                                      int32_t* __restrict__ dbg_counts,
+                                                                      int32_t* __restrict__ dbg_offsets,
+                                                                      int32_t* __restrict__ dbg_perm) {
+  __shared__ int s_sel[4][16];
+  __shared__ double s_l[4][16];
+  __shared__ __align__(16) int s_exp[kMaxPairsDec];
   __shared__ int s_cnt[1024 + 1];
   __shared__ int s_incl[1024 + 1];
-  const int tid = threadIdx.x;
-  const int E = L.E, nb = E + 1;
-  const int Pr = T * L.k;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = L.E, k = L.k, nb = E + 1;
+  const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  for (int i = tid; i < ntickets; i += kRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
-  for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
+  const int t = blockIdx.x * 4 + wave;
+  if (t < T) {  // wave-uniform
+    const size_t sstride = (size_t)T * (E + 1);
+    const int nper = (E + 63) >> 6;
+    if (nper <= 1) dec_topk_token<1>(w.logits, E, k, t, s_sel[wave], s_l[wave], nsplit, sstride);
+    else if (nper <= 2) dec_topk_token<2>(w.logits, E, k, t, s_sel[wave], s_l[wave], nsplit, sstride);
+    else if (nper <= 4) dec_topk_token<4>(w.logits, E, k, t, s_sel[wave], s_l[wave], nsplit, sstride);
+    else if (nper <= 8) dec_topk_token<8>(w.logits, E, k, t, s_sel[wave], s_l[wave], nsplit, sstride);
+    else dec_topk_token<16>(w.logits, E, k, t, s_sel[wave], s_l[wave], nsplit, sstride);
+    float g;
+    const bool keep = pair_gate(s_l[wave][min(lane, k - 1)], s_l[wave][0], k, L.omit_below, &g);
+    if (lane < k) {
+      const int id = keep ? s_sel[wave][lane] : -1;  // an omitted pair is in no bucket
+      __hip_atomic_store(&w.ids[t * k + lane], id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w.pair_w[t * k + lane] = g;
+      if (dbg_ids) dbg_ids[t * k + lane] = id;
+      if (dbg_w) dbg_w[t * k + lane] = g;
+    }
+    if (L.has_shared && lane == 0) {
+      float sg = 1.0f;
+      if (L.shared_gate_w) {
+        double pz[kRouterMaxSplits];  // every split loaded first (clamped index), added in order
+#pragma unroll
+        for (int z = 0; z < kRouterMaxSplits; ++z)
+          pz[z] = w.logits[(size_t)min(z, nsplit - 1) * sstride + (size_t)t * (E + 1) + E];
+        double ls = pz[0];
+#pragma unroll
+        for (int z = 1; z < kRouterMaxSplits; ++z) ls = z < nsplit ? ls + pz[z] : ls;
+        sg = (float)(1.0 / (1.0 + exp(-ls)));
+      }
+      w.pair_w[Pr + t] = sg;
+    }
+  }
+  // this block's ids have landed (device-scope stores); one arrival, checked once
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&w.rr_flags[kTopkDoneWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  if (tid == 0) __hip_atomic_store(&w.rr_flags[kTopkDoneWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < ntickets; i += kTopkRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
+  for (int i = tid; i < nb; i += kTopkRouteThreads) s_cnt[i] = 0;
+  for (int p = tid; p < P; p += kTopkRouteThreads)
+    s_exp[p] = p < Pr ? __hip_atomic_load(&w.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : E;
   const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
   const uint8_t* const my_gu = L.gate_up[ie];
   const uint8_t* const my_dn = L.down[ie];
-  for (int p = tid; p < P; p += kRouteThreads) s_exp[p] = p < Pr ? w.ids[p] : E;
   __syncthreads();
   dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, my_gu, my_dn, dbg_counts, dbg_offsets, dbg_perm);
 }
@@ -1700,11 +1779,12 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   const bool sr = T == 1 && L.E <= kSelfRouteMaxE;
   const DbgOut d{dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm};
   if (T >= kDecSplitRouteT) {
-    // the fp64 matrix-core router and one wave per token for the top-k, then the route
-    hipError_t e = launch_router_topk(L, xp, xdp, T, w, dbg_ids, dbg_w, s, tm);
+    // the fp64 matrix-core router, then one wave per token for the top-k, the last block
+    // to finish routing
+    hipError_t e = launch_router(L, xp, xdp, T, w, s, tm);
     if (e != hipSuccess) return e;
-    MOEQ_LAUNCH(tm, kStageBucket, k_dec_route, dim3(1), dim3(kRouteThreads), 0, s, L, T, w, max_slots, ntickets,
-                dbg_counts, dbg_offsets, dbg_perm);
+    MOEQ_LAUNCH(tm, kStageTopk, k_dec_topk_route, dim3((T + 3) / 4), dim3(kTopkRouteThreads), 0, s, L, T, w,
+                router_splits(T, L.H), max_slots, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
   } else if (x_dtype == 0) {
     launch_rr<0>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
                  dbg_perm, s, tm);

@@ -312,8 +312,8 @@ __global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(int T, int k, int 
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
-                              int32_t* dbg_ids, float* dbg_w, hipStream_t s, const Timing& tm) {
+hipError_t launch_router(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, hipStream_t s,
+                         const Timing& tm) {
   const int erows = L.E + ((L.has_shared && L.shared_gate_w) ? 1 : 0);
   const int nsplit = router_splits(T, L.H);
   dim3 grid((T + 31) / 32, (erows + 15) / 16, nsplit);
@@ -321,8 +321,15 @@ hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, in
     MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<0>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
   else
     MOEQ_LAUNCH(tm, kStageRouter, k_router_mfma<1>, grid, dim3(64 * kRouterWaves), 0, s, L, x, T, erows, w.logits, w.xplanes);
-  MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits, nsplit,
-              w.ids, w.pair_w, dbg_ids, dbg_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
+                              int32_t* dbg_ids, float* dbg_w, hipStream_t s, const Timing& tm) {
+  hipError_t e = launch_router(L, x, x_dtype, T, w, s, tm);
+  if (e != hipSuccess) return e;
+  MOEQ_LAUNCH(tm, kStageTopk, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, L, T, (const double*)w.logits,
+              router_splits(T, L.H), w.ids, w.pair_w, dbg_ids, dbg_w);
   return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ inline int router_splits(int T, int H) {
   return nch >= kRouterMaxSplits * 16 ? kRouterMaxSplits : (nch >= 4 * 16 ? 4 : 1);
 }
 
+// the matrix-core router alone: K-split partial logits [nsplit][T][E+1] in w.logits
+hipError_t launch_router(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, hipStream_t s,
+                         const Timing& tm = Timing());
 hipError_t launch_router_topk(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w,
                               int32_t* dbg_ids, float* dbg_w, hipStream_t s,
                               const Timing& tm = Timing());
