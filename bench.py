@@ -46,12 +46,36 @@ def traffic_file(config: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{config}_gateup.json")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments and blank lines (string and character literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(ln.rstrip() for ln in "".join(out).splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every kernel source: stored counter readings are used only while it matches."""
+    """Hash of every kernel source with its comments removed: stored counter readings are used
+    only while it matches, so an edit of a comment keeps them and any code change drops them."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         h.update(name.encode())
-        h.update(open(os.path.join(CSRC, name), "rb").read())
+        h.update(strip_comments(open(os.path.join(CSRC, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

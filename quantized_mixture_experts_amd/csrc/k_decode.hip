@@ -1,20 +1,26 @@
 // Decode path (few tokens per call, e.g. a draft/verify window of up to 17 tokens):
-//   1. k_dec_rr:       router logits (4 expert rows per block); every block posts its
-//                      logits and then checks once whether all of them are there; the
-//                      block that sees them all does the top-k + gates, the stable
-//                      bucketing of the pairs and the active-expert slot records, and
-//                      clears the per-tile arrival counters of step 3.
+//   1. routing, by token count:
+//      - one token: k_dec_rr computes the router logits (4 expert rows per block) and
+//        stores them; every gate/up block of step 2 takes the top-k of those logits
+//        itself (the same selection in every block) and routes, so no route kernel runs;
+//      - 2..7 tokens: k_dec_rr also routes: every block posts its logits and then checks
+//        once whether all of them are there; a block that sees them all does the top-k
+//        + gates, the stable bucketing of the pairs and the active-expert slot records,
+//        and clears the per-tile arrival counters of step 3;
+//      - 8 tokens and more: the K-split matrix-core router, then k_dec_topk_route (one
+//        wave per token for the top-k; the last block to finish routes).
 //   2. k_dec_gateup:   fused dequant + gate/up + SwiGLU per (16-row tile, active expert).
-//   3. k_dec_down:     dequant + down per (16-row tile, active expert); the last block
-//                      to finish a tile sums the gate-weighted expert outputs of that
-//                      tile in a fixed order (routed j ascending, then shared), so no
-//                      float atomics and a run-to-run identical result (NInfer
+//   3. k_dec_down / k_dec_down_rows: dequant + down per (row tile, active expert); the
+//                      last block to finish a tile sums the gate-weighted expert outputs
+//                      of that tile in a fixed order (routed j ascending, then shared),
+//                      so no float atomics and a run-to-run identical result (NInfer
 //                      Qwen3.8-Flash-Next page, MoE execution notes: a token's down
 //                      projection runs over all of its experts, and the weighted sum is
 //                      formed so that it does not depend on which expert finishes first).
-// Each selected expert's weights are streamed from HBM exactly once per call, for all
-// of its tokens (same page and notes: the pairs are grouped by expert so that an
-// expert's rows are read in one pass).  Weight loads for a wave's whole K range are
+// Each selected expert's weights are streamed from HBM once per call for all of its
+// tokens (same page and notes: the pairs are grouped by expert so that an expert's rows
+// are read in one pass); an expert whose tokens exceed one LDS staging pass streams them
+// once per pass.  Weight loads for a wave's whole K range are
 // issued before the first MFMA so that a wave keeps its full share of HBM requests in
 // flight.
 // No block ever waits for another: a block that needs the results of others checks
@@ -26,9 +32,9 @@
 
 namespace moeq {
 
-// From this many tokens the decode path routes with three kernels (matrix-core router,
-// per-token top-k, route) instead of the single router/route kernel, whose fp64
-// reductions and one-CU top-k grow with T.
+// From this many tokens the decode path routes with two kernels (the matrix-core router,
+// then the per-token top-k with the route) instead of the single router/route kernel,
+// whose fp64 reductions and one-CU top-k grow with T.
 constexpr int kDecSplitRouteT = 8;
 // bf16 elements of the rescaled rows a router block keeps in LDS when it folds the RMS
 // rescale in (T * H at most: 48 KB)
@@ -66,16 +72,17 @@ __host__ __device__ __forceinline__ int lds_row_stride(int K) {
 // 1+2. Router and route in one kernel.  Each 1024-thread block computes 4 expert rows
 // of router logits (4 waves per row split its columns; all tokens; fp64 accumulation
 // of exact products, partial sums added in a fixed order) and writes them through to
-// the device-coherent level, then raises its arrival flag; block 0 waits for every
-// flag, reads every logit back coherently and does the top-k, the softmax gates and
-// the bucketing:
+// the device-coherent level.  Each block then checks once whether every logit has
+// arrived; a block that sees them all does the top-k, the softmax gates and the
+// bucketing:
 //    top-k: one wave per token, k rounds of a wave argmax (ties to the lower index);
 //    gates: lane j < k computes exp(l_j - l_0), a wave sum normalises them (fp64);
 //    buckets: integer counts, one wave-scan over the E+1 buckets of the packed pair
 //    (count, non-empty flag), then each pair's stable rank among earlier pairs of
 //    the same expert; one slot record per active expert for the projections.
-// The flags live in the workspace's fixed header; block 0 clears them, so they read
-// zero at the start of every call once the header was zeroed before the first use.
+// The mailbox entries and arrival flags live in the workspace's fixed header; the routing
+// block clears them, so they read zero at the start of every call once the header was
+// zeroed before the first use.
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 1024;
 constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
