@@ -171,6 +171,20 @@ __device__ __forceinline__ double rms_partial(const float* __restrict__ yt, int 
   }
   return s;
 }
+// Rows of at most this many columns keep a thread's values in registers from the sum of
+// squares to the quotient (16 per thread of 256), so the row is read once.
+constexpr int kRmsRegCols = 16 * 256;
+// rms_partial of a row of at most kRmsRegCols columns, its values kept in v: all 16 loads
+// are issued at once (slots past the row read as 0), then summed in the same order as
+// rms_partial, so the result is bit-identical.
+__device__ __forceinline__ double rms_partial_keep(const float* __restrict__ yt, int H, int i, float (&v)[16]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) v[u] = i + 256 * u < H ? yt[i + 256 * u] : 0.0f;
+  double s = 0.0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) s = fma((double)v[u], (double)v[u], s);
+  return s;
+}
 __device__ __forceinline__ double rms_divisor(double s0, double s1, double s2, double s3, int H, float eps) {
   return sqrt((((s0 + s1) + s2) + s3) / (double)H + (double)eps);
 }

@@ -427,34 +427,73 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     // groups takes tokens g, g + 4.
     __shared__ double s_ms[kDecSplitRouteT][4];
     const int grp = wave >> 2, i = tid & 255;
-    for (int t = grp; t < T; t += kWaves / 4) {
-      const double sq = wave_sum_f64(rms_partial((const float*)x + (size_t)t * H, H, i));
-      if (lane == 0) s_ms[t][wave & 3] = sq;
-    }
-    __syncthreads();
-    if (tid < T) {
-      const double d = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
-      s_d[tid] = d;
-      s_rd[tid] = 1.0 / d;
-    }
-    __syncthreads();
-    // the rescaled rows once per block into LDS (block 0 also writes them for the projections),
-    // token by token, 8 values in flight per thread
-    for (int t = 0; t < T; ++t) {
-      for (int n0 = tid; n0 < H; n0 += 8 * kRouteThreads) {
-        uint16_t v[8];
-        rms_apply8((const float*)x + (size_t)t * H, n0, kRouteThreads, H, s_d[t], s_rd[t], v);
+    static_assert(kDecSplitRouteT <= 2 * (kWaves / 4), "a group holds at most two tokens' values");
+    if (H <= kRmsRegCols) {
+      // each row read once: the group's (at most two) tokens keep their values in
+      // registers from the sum of squares to the quotient
+      float v[2][16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int n = n0 + kRouteThreads * u;
-          if (n < H) {
-            s_x[t * H + n] = v[u];
-            if (blockIdx.x == 0) w.xr[(size_t)t * H + n] = v[u];
+      for (int j = 0; j < 2; ++j) {
+        const int t = grp + (kWaves / 4) * j;
+        if (t < T) {  // wave-uniform
+          const double sq = wave_sum_f64(rms_partial_keep((const float*)x + (size_t)t * H, H, i, v[j]));
+          if (lane == 0) s_ms[t][wave & 3] = sq;
+        }
+      }
+      __syncthreads();
+      if (tid < T) {
+        const double d = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
+        s_d[tid] = d;
+        s_rd[tid] = 1.0 / d;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int t = grp + (kWaves / 4) * j;
+        if (t < T) {
+          const double d = s_d[t], rd = s_rd[t];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int n = i + 256 * u;
+            const uint16_t q = rms_apply(v[j][u], d, rd);
+            if (n < H) {
+              s_x[t * H + n] = q;
+              if (blockIdx.x == 0) w.xr[(size_t)t * H + n] = q;
+            }
           }
         }
       }
+      __syncthreads();
+    } else {
+      for (int t = grp; t < T; t += kWaves / 4) {
+        const double sq = wave_sum_f64(rms_partial((const float*)x + (size_t)t * H, H, i));
+        if (lane == 0) s_ms[t][wave & 3] = sq;
+      }
+      __syncthreads();
+      if (tid < T) {
+        const double d = rms_divisor(s_ms[tid][0], s_ms[tid][1], s_ms[tid][2], s_ms[tid][3], H, eps);
+        s_d[tid] = d;
+        s_rd[tid] = 1.0 / d;
+      }
+      __syncthreads();
+      // the rescaled rows once per block into LDS (block 0 also writes them for the projections),
+      // token by token, 8 values in flight per thread
+      for (int t = 0; t < T; ++t) {
+        for (int n0 = tid; n0 < H; n0 += 8 * kRouteThreads) {
+          uint16_t v[8];
+          rms_apply8((const float*)x + (size_t)t * H, n0, kRouteThreads, H, s_d[t], s_rd[t], v);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int n = n0 + kRouteThreads * u;
+            if (n < H) {
+              s_x[t * H + n] = v[u];
+              if (blockIdx.x == 0) w.xr[(size_t)t * H + n] = v[u];
+            }
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     xr = s_x;
   }
   {

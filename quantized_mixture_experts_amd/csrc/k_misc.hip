@@ -78,6 +78,21 @@ __global__ __launch_bounds__(256) void k_rms_rescale(const float* __restrict__ y
   __shared__ double part[4];
   const int t = blockIdx.x;
   const float* yt = y + (size_t)t * H;
+  if (H <= kRmsRegCols) {  // the row read once: its values stay in registers
+    float v[16];
+    const double s = wave_sum_f64(rms_partial_keep(yt, H, threadIdx.x, v));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const double d = rms_divisor(part[0], part[1], part[2], part[3], H, eps);
+    const double rd = 1.0 / d;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int n = threadIdx.x + 256 * u;
+      const uint16_t q = rms_apply(v[u], d, rd);
+      if (n < H) out[(size_t)t * H + n] = q;
+    }
+    return;
+  }
   const double s = wave_sum_f64(rms_partial(yt, H, threadIdx.x));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();

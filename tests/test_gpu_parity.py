@@ -240,18 +240,20 @@ def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
 
 
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
-@pytest.mark.parametrize("T,path", [(1, 0), (4, 0), (7, 0), (9, 0), (40, 0), (4, 2)])
-def test_forward_rms_equals_rescale_then_forward(wfmt, T, path):
+@pytest.mark.parametrize("T,path,H", [(1, 0, 512), (4, 0, 512), (7, 0, 512), (9, 0, 512), (40, 0, 512), (4, 2, 512),
+                                      (1, 0, 6144), (4, 0, 6144)])
+def test_forward_rms_equals_rescale_then_forward(wfmt, T, path, H):
     """moe_forward_rms (the rescale folded into the router kernel below 8 decode tokens,
     the rescale kernel first otherwise) gives the bits of moe_rms_rescale followed by
     moe_forward on the same path, and with the residual add y_prev plus those bits; the
-    two-step result is checked against the oracle."""
-    spec = synth.small_spec(f"rms{T}", T, 512, 1024, 16, 4, wfmt, has_shared=1, x_dtype=synth.X_BF16,
+    two-step result is checked against the oracle.  H = 6144 takes the folded rescale's
+    form for rows longer than a thread's registers hold (16 values of 256 threads)."""
+    spec = synth.small_spec(f"rms{T}_{H}", T, H, 1024, 16, 4, wfmt, has_shared=1, x_dtype=synth.X_BF16,
                             bias="normal", seed=40 + T)
     layer = synth.make_layer(spec, shared_gate=True)
     dl = q.DeviceLayer.from_layer(layer)
     rng = np.random.default_rng(900 + T)
-    y_prev = _dev((rng.standard_normal((T, 512)) * rng.uniform(0.1, 20.0, (T, 1))).astype(np.float32))
+    y_prev = _dev((rng.standard_normal((T, H)) * rng.uniform(0.1, 20.0, (T, 1))).astype(np.float32))
     x = q.rms_rescale(y_prev)
     y2, dbg = q.forward(dl, x, synth.X_BF16, path=path, debug=True)
     y1 = q.forward_rms(dl, y_prev, 1e-6, path=path)
@@ -328,10 +330,11 @@ def test_forward_prefill_full_size(cfg, T):
     assert nex == 0, f"{cfg}: {nex} near-tie tokens on the seeded workload"
 
 
-@pytest.mark.parametrize("T,H", [(4, 2880), (3, 2048), (1, 160), (5, 4096)])
+@pytest.mark.parametrize("T,H", [(4, 2880), (3, 2048), (1, 160), (5, 4096), (2, 6000)])
 def test_rms_rescale_bit_exact(T, H):
     """The rescale kernel's bf16 output equals the oracle's rounding of the fp64 quotient
-    y / sqrt(mean(y^2) + eps), bit for bit, over rows of very different scales."""
+    y / sqrt(mean(y^2) + eps), bit for bit, over rows of very different scales (rows of up
+    to 4,096 columns kept in registers, longer ones read twice)."""
     rng = np.random.default_rng(4 + T + H)
     y = (rng.standard_normal((T, H)) * np.exp(rng.uniform(-20, 20, (T, 1)))).astype(np.float32)
     out = q.rms_rescale(_dev(y), eps=oracle.RMS_EPS).cpu().numpy()
