@@ -470,6 +470,18 @@ __device__ __forceinline__ bf16x8_t cb4x8_to_bf16(uint32_t codes, const uint32_t
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// 4 x 4 transpose of dwords across the four 16-lane rows of a wave: on return, register
+// j of row g holds what register g of row j held.  v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, v_permlane16_swap the odd
+// rows of the first with the even rows of the second.
+__device__ __forceinline__ void xpose_rows4(u32x4_t& d) {
+  const auto a = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  d = u32x4_t{c[0], c[1], e[0], e[1]};
+}
+
 // bf16 bits of an int8 value (exact).
 __device__ __forceinline__ uint32_t int8_to_bf16_bits(int v) {
   return __float_as_uint((float)v) >> 16;

@@ -49,14 +49,14 @@ constexpr int waitcnt_vm_le(int n) {
 // the barrier after it does not wait for memory by itself.
 constexpr int waitcnt_vm_le_lgkm0(int n) { return waitcnt_vm_le(n) & ~(15 << 8); }
 // vector-memory instructions one prefetch_step issues per 16-row tile: MXFP4 one 16-byte
-// code load and one scale byte (the packed scale store: one delta byte); CB4 four code
-// dwords and four fp16 scales; 3-bit affine one 12-byte code load and one 8-byte
-// (scale, bias) load.  The waits
-// after the staging loads count on exactly these: no two of them can be merged into one
-// instruction, since each address is clamped separately (min / select on the block
-// index), so the compiler cannot prove two of them adjacent.
+// code load and one scale byte (the packed scale store: one delta byte); CB4 one 16-byte
+// code load and one 8-byte load of the row's four fp16 scales (a last step of fewer than
+// four blocks: four 2-byte scale loads, so more, never fewer); 3-bit affine one 12-byte
+// code load and one 8-byte (scale, bias) load.  The waits after the staging loads count
+// on at least these: the code and scale loads of a step read different planes, so the
+// compiler cannot merge them into one instruction.
 template <int FMT>
-constexpr int loads_per_step() { return (fmt_is_mx(FMT) || FMT == 4) ? 2 : 8; }
+constexpr int loads_per_step() { return 2; }
 constexpr int kDecMaxTokens = 32;  // two 16-slot MFMA token tiles
 
 __device__ __forceinline__ int dec_token_of_pair(int p, int T, int k) { return p < T * k ? p / k : p - T * k; }
@@ -725,8 +725,8 @@ struct WeightRegs<4, KSW> {  // 3-bit affine: 12 code bytes and the (scale, bias
 };
 template <int KSW>
 struct WeightRegs<2, KSW> {
-  uint32_t c[KSW][4];
-  uint32_t s[KSW][4];  // fp16 scale bits of blocks 4ks..4ks+3
+  u32x4_t c[KSW];      // block 4ks + g of row m (16 bytes), as stored
+  uint32_t s[KSW][2];  // fp16 scale bits of blocks 4ks..4ks+3 of row m, two per dword
 };
 
 // Loads of one wave's k-steps ks0, ks0+stride, ... of one 16-row weight tile (stride 4:
@@ -754,17 +754,27 @@ __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, co
           (const __attribute__((address_space(1))) u32x3_t*)(pt.codes + 768 * ksc + 12 * (16 * g + m)));
       r.s[i] = *(const __attribute__((address_space(1))) uint64_t*)(pt.scales + 128 * ksc + 8 * m);
     } else {
+      // block 4 ksc + g of row m, as MXFP4 (a block past the row: the step's first block,
+      // whose values then meet zero activations); the lane rows are transposed at use
       const int ksc = ks < nks ? ks : 0;
-      const uint32_t lo = (uint32_t)(16 * m + 4 * g);  // lane offset within a block's 256 bytes
       // the step's scale unit holds rb = min(4, blocks left) entries per row, row-major
       const int rb = min(4, nkb - 4 * ksc);
-      const uint32_t so = 2u * __umul24((uint32_t)m, (uint32_t)rb);
+      const int gc = g < rb ? g : 0;
+      r.c[i] = __builtin_nontemporal_load(
+          (const __attribute__((address_space(1))) u32x4_t*)(pt.codes + (size_t)ksc * 1024 + (uint32_t)(gc * 256 + 16 * m)));
+      if (rb == 4) {  // uniform: the row's four scales are 8 contiguous bytes
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+        const u32x2_t sv = *(const __attribute__((address_space(1))) u32x2_t*)(pt.scales + (size_t)ksc * 128 + 8 * m);
+        r.s[i][0] = sv[0];
+        r.s[i][1] = sv[1];
+      } else {  // a block past the row takes the row's last scale
+        const uint32_t so = 2u * __umul24((uint32_t)m, (uint32_t)rb);
+        uint32_t h[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int jc = min(j, rb - 1);  // a block past the row: the row's last block (uniform)
-        r.c[i][j] = __builtin_nontemporal_load((const __attribute__((address_space(1))) uint32_t*)(
-            pt.codes + ((size_t)ksc * 1024 + (size_t)jc * 256) + lo));
-        r.s[i][j] = *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + ((size_t)ksc * 128 + 2 * jc) + so);
+        for (int j = 0; j < 4; ++j)
+          h[j] = *(const __attribute__((address_space(1))) uint16_t*)(pt.scales + ((size_t)ksc * 128 + 2 * min(j, rb - 1)) + so);
+        r.s[i][0] = h[0] | (h[1] << 16);
+        r.s[i][1] = h[2] | (h[3] << 16);
       }
     }
   }
@@ -798,8 +808,7 @@ __device__ __forceinline__ void consume_weights(const WeightRegs<FMT, KSW>& r, i
   } else if constexpr (FMT == 4) {
     asm volatile("" ::"v"(r.c[i]), "v"(r.s[i]));
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(r.c[i][j]), "v"(r.s[i][j]));
+    asm volatile("" ::"v"(r.c[i]), "v"(r.s[i][0]), "v"(r.s[i][1]));
   }
 }
 
@@ -875,10 +884,14 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, 
       }
     }
   } else {
-    // the 4 blocks' MFMAs first, then their scaled sums (block order j per output)
+    // lane row g then holds bytes 4g..4g+3 of block 4ks + j in dword j: MFMA j covers
+    // block 4ks + j alone, so its fp32 result takes the block's scale.  The 4 blocks'
+    // MFMAs first, then their scaled sums (block order j per output).
+    u32x4_t cw = r.c[i];
+    xpose_rows4(cw);
     bf16x8_t b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = cb4x8_to_bf16(r.c[i][j], lut);
+    for (int j = 0; j < 4; ++j) b[j] = cb4x8_to_bf16(cw[j], lut);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       if (tt < live) {
@@ -896,7 +909,7 @@ __device__ __forceinline__ void mma_kstep(const WeightRegs<FMT, KSW>& r, int i, 
         mfma_settle4(tmp);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float sc = half_bits_to_f32((uint16_t)r.s[i][j]);
+          const float sc = half_bits_to_f32((uint16_t)(r.s[i][j >> 1] >> (16 * (j & 1))));
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[tt][q] = fmaf(sc, tmp[j][q], acc[tt][q]);
         }
