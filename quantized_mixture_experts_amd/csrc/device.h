@@ -305,24 +305,31 @@ __device__ __forceinline__ double topk_key_value(uint64_t key) {
   return __builtin_bit_cast(double, b);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = dpp_i32<CTRL>((int)(uint32_t)v);
-  const int hi = dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t m) {
-  m = max_u64(m, dpp_u64<kDppRowRor1>(m));
-  m = max_u64(m, dpp_u64<kDppRowRor2>(m));
-  m = max_u64(m, dpp_u64<kDppRowRor4>(m));
-  m = max_u64(m, dpp_u64<kDppRowRor8>(m));
-  return max_u64(max_u64(readlane_u64(m, 0), readlane_u64(m, 16)), max_u64(readlane_u64(m, 32), readlane_u64(m, 48)));
+// Maximum over the wave of 32-bit unsigned values: every lane's row maximum by DPP row
+// rotations, then the maximum of the four rows'.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = max(m, (uint32_t)dpp_i32<kDppRowRor1>((int)m));
+  m = max(m, (uint32_t)dpp_i32<kDppRowRor2>((int)m));
+  m = max(m, (uint32_t)dpp_i32<kDppRowRor4>((int)m));
+  m = max(m, (uint32_t)dpp_i32<kDppRowRor8>((int)m));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+  return max(max(a, b), max(c, d));
+}
+// Maximum over the wave of distinct 64-bit keys: the high words' maximum H, then the low
+// word of the one lane holding H or, when several lanes hold it, the maximum of their low
+// words.  32-bit steps are half the instructions of 64-bit compares and selects.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t H = wave_max_u32(hi);
+  const uint64_t tied = __ballot(hi == H);
+  uint32_t L;
+  if (__popcll(tied) == 1)  // uniform
+    L = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((long long)tied) - 1);
+  else
+    L = wave_max_u32(hi == H ? lo : 0u);
+  return ((uint64_t)H << 32) | L;
 }
 // Descending order of a lane's candidates (odd-even transposition, static indices).
 template <int NPER>
@@ -357,7 +364,7 @@ __device__ __forceinline__ void topk_select(const double (&lv)[NT][NPER], int E,
   for (int j = 0; j < k; ++j) {
     uint64_t m[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) m[t] = wave_max_u64(v[t][0]);
+    for (int t = 0; t < NT; ++t) m[t] = wave_max_key(v[t][0]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (lane == 0) {

@@ -271,13 +271,34 @@ __device__ __forceinline__ void router_part(const float* __restrict__ wrow, cons
   }
 }
 
+// Expert pointers of the buckets e = tid + u blockDim.x (u < NPP) a thread of the routing
+// block writes slot records for, loaded before they are needed (at most 1,025 buckets:
+// NPP blockDim.x must cover them).
+template <int NPP>
+struct BucketPtrs {
+  const uint8_t* gu[NPP];
+  const uint8_t* dn[NPP];
+};
+template <int NPP>
+__device__ __forceinline__ void load_bucket_ptrs(const LayerArgs& L, BucketPtrs<NPP>& bp) {
+  const int last = L.E + (L.has_shared ? 1 : 0) - 1;
+#pragma unroll
+  for (int u = 0; u < NPP; ++u) {
+    const int ie = min((int)threadIdx.x + u * (int)blockDim.x, last);
+    bp.gu[u] = L.gate_up[ie];
+    bp.dn[u] = L.down[ie];
+  }
+}
+
 // Routing after top-k (s_exp[p] = the expert of pair p for p < P, s_cnt zeroed): LDS
 // histogram, scan and stable ranks -> counts, offsets, perm, the active list and one slot
-// record per active expert.  Every thread of the block takes part (any block size).
+// record per active expert.  Every thread of the block takes part (any block size with
+// NPP blockDim.x > E).
+template <int NPP>
 __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots,
-                                               const int* s_exp, int* s_cnt, int* s_incl, const uint8_t* my_gu,
-                                               const uint8_t* my_dn, int32_t* __restrict__ dbg_counts,
-                                               int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
+                                               const int* s_exp, int* s_cnt, int* s_incl, const BucketPtrs<NPP>& bp,
+                                               int32_t* __restrict__ dbg_counts, int32_t* __restrict__ dbg_offsets,
+                                               int32_t* __restrict__ dbg_perm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = (int)blockDim.x;
   const int E = L.E, k = L.k;
   const int nb = E + 1;
@@ -309,7 +330,10 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   __syncthreads();
   const int n_active = s_incl[nb - 1] >> 16;
   const int placed = s_incl[nb - 1] & 0xFFFF;  // pairs in the buckets (omitted ones are not)
-  for (int e = tid; e < nb; e += nthr) {
+#pragma unroll
+  for (int u = 0; u < NPP; ++u) {
+    const int e = tid + u * nthr;
+    if (e >= nb) break;
     const int c = s_cnt[e];
     const int off = (s_incl[e] & 0xFFFF) - c;
     w.counts[e] = c;
@@ -321,8 +345,8 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
       w.active[1 + a] = e;
       Slot& sl = w.slots[a];
       sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
-      sl.gate_up = e == tid ? my_gu : L.gate_up[e];
-      sl.down = e == tid ? my_dn : L.down[e];
+      sl.gate_up = bp.gu[u];
+      sl.down = bp.dn[u];
     }
   }
   for (int a = n_active + tid; a < max_slots; a += nthr) {
@@ -544,10 +568,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       __hip_atomic_store(rr_flags + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // thread e's expert pointers for the slot records: issued now, used at the end
-  const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
-  const uint8_t* const my_gu = L.gate_up[ie];
-  const uint8_t* const my_dn = L.down[ie];
+  // this thread's buckets' expert pointers for the slot records: issued now, used at the end
+  BucketPtrs<2> bp;
+  load_bucket_ptrs(L, bp);
 
   const int Pr = T * k;
   const bool want_sg = L.has_shared && L.shared_gate_w;
@@ -596,7 +619,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, my_gu, my_dn, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
 }
 
 
@@ -618,6 +641,9 @@ __device__ __forceinline__ void dec_topk_token(const double* logits, int E, int 
 // arrival flags use the words below E / 4 + 1)
 constexpr int kTopkDoneWord = 511;
 constexpr int kTopkRouteThreads = 256;  // 4 tokens per block
+// the bucket pointers of the routing kernels cover every bucket of up to 1,024 experts
+// plus the shared one
+static_assert(2 * kRouteThreads > 1024 && 5 * kTopkRouteThreads > 1024, "bucket pointer prefetch");
 
 __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs L, int T, Work w, int nsplit,
                                                                       int max_slots, int ntickets,
@@ -637,6 +663,10 @@ __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs 
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
   const int t = blockIdx.x * 4 + wave;
+  // the expert pointers of this thread's buckets, for the slot records if this block routes
+  // (loaded by every block, before its top-k, so that the routing block never waits on them)
+  BucketPtrs<5> bp;
+  load_bucket_ptrs(L, bp);
   if (t < T) {  // wave-uniform
     const size_t sstride = (size_t)T * (E + 1);
     const int nper = (E + 63) >> 6;
@@ -686,11 +716,8 @@ __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs 
   for (int i = tid; i < nb; i += kTopkRouteThreads) s_cnt[i] = 0;
   for (int p = tid; p < P; p += kTopkRouteThreads)
     s_exp[p] = p < Pr ? __hip_atomic_load(&w.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : E;
-  const int ie = min(tid, E + (L.has_shared ? 1 : 0) - 1);
-  const uint8_t* const my_gu = L.gate_up[ie];
-  const uint8_t* const my_dn = L.down[ie];
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, my_gu, my_dn, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1734,12 +1761,18 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
 static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I / 32 + 3) / 4 > kDownRowsMaxSteps; }
 
 // Rows of activations a projection block stages per pass: as many of the expert's
-// pairs as fit in kDecStageBytes of LDS (at least 1, at most T), so that several blocks
-// share a CU whatever T is; an expert with more pairs takes several passes.
+// pairs as fit in the staging budget of LDS (at least 1, at most T), so that several
+// blocks share a CU whatever T is; an expert with more pairs takes several passes.
+// 48 KB lets 3 blocks share a CU.  The codebook gate/up kernel needs few enough registers
+// for 4 blocks a CU (at most 128 per lane), so it stages within 36 KB: more of the verify
+// window's 1,056 gate/up blocks run at once, for one staging pass more on its hottest
+// expert (gate/up 20.4 -> 19.7 us; the 3-bit kernel measured slower so).
 constexpr size_t kDecStageBytes = 48 * 1024;
-static int dec_rows_per_pass(int K, int NP, int T) {
+constexpr size_t kDecStageBytesGateUpCb4 = 36 * 1024;
+static size_t dec_gateup_stage_bytes(int wfmt) { return wfmt == 2 ? kDecStageBytesGateUpCb4 : kDecStageBytes; }
+static int dec_rows_per_pass(int K, int NP, int T, size_t budget = kDecStageBytes) {
   const size_t row = (size_t)dec_xstride(K) * 2 * NP;
-  const int cap = (int)(kDecStageBytes / row) - 1;  // and the zero row
+  const int cap = (int)(budget / row) - 1;  // and the zero row
   return max(1, min(T, min(cap, kDecMaxTokens)));
 }
 
@@ -1781,7 +1814,7 @@ template <int FMT>
 static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
                                      uint32_t* tickets, bool omb, bool sr, const DbgOut& d, hipStream_t s,
                                      const Timing& tm) {
-  const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T);
+  const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T, dec_gateup_stage_bytes(FMT));
   const int xd = dec_rows_per_pass(L.I, 2, T);
   if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, sr, d, s, tm);
   else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, false, d, s, tm);
@@ -1793,7 +1826,7 @@ static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dt
 bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   if (T > kDecMaxTokens) return false;
   const int np = x_dtype == 1 ? 1 : 3;
-  const int xg = dec_rows_per_pass(L.H, np, T), xd = dec_rows_per_pass(L.I, 2, T);
+  const int xg = dec_rows_per_pass(L.H, np, T, dec_gateup_stage_bytes(L.wfmt)), xd = dec_rows_per_pass(L.I, 2, T);
   const size_t g = dec_lds_bytes(L.wfmt, L.H, np, xg <= 16 ? 1 : 2, xg);
   const size_t d = dec_lds_bytes(L.wfmt, L.I, 2, xd <= 16 ? 1 : 2, xd);
   return g <= 160 * 1024 && d <= 160 * 1024;
