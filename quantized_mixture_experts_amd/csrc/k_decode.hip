@@ -294,38 +294,53 @@ __device__ __forceinline__ void load_bucket_ptrs(const LayerArgs& L, BucketPtrs<
 // histogram, scan and stable ranks -> counts, offsets, perm, the active list and one slot
 // record per active expert.  Every thread of the block takes part (any block size with
 // NPP blockDim.x > E).
+// s_tmask[e] (zeroed with s_cnt): bit t set when token t has a pair in bucket e (T <= 32).
+// A token's routed experts are distinct, so the stable rank of pair p (of token t) in its
+// bucket, the number of earlier pairs in the same bucket, is the number of earlier tokens
+// in it: popcount(s_tmask[e] & (2^t - 1)).
 template <int NPP>
 __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots,
-                                               const int* s_exp, int* s_cnt, int* s_incl, const BucketPtrs<NPP>& bp,
-                                               int32_t* __restrict__ dbg_counts, int32_t* __restrict__ dbg_offsets,
-                                               int32_t* __restrict__ dbg_perm) {
+                                               const int* s_exp, int* s_cnt, uint32_t* s_tmask, int* s_incl,
+                                               const BucketPtrs<NPP>& bp, int32_t* __restrict__ dbg_counts,
+                                               int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
+  __shared__ int s_ctot[(1024 + 1 + 63) / 64];  // each 64-bucket chunk's sum
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = (int)blockDim.x;
   const int E = L.E, k = L.k;
   const int nb = E + 1;
   const int Pr = T * k;
   const int P = Pr + (L.has_shared ? T : 0);
-  for (int p = tid; p < P; p += nthr)
-    if (s_exp[p] >= 0) atomicAdd(&s_cnt[s_exp[p]], 1);  // expert -1: an omitted pair
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < nb; base += 64) {
-      const int i = base + lane;
-      const int c = i < nb ? s_cnt[i] : 0;
-      int x = c | ((c > 0 ? 1 : 0) << 16);
-      // inclusive scan: DPP row shifts inside 16-lane rows, then the row totals
-      x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-      x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-      x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-      x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-      const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
-      const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
-      const int row = lane >> 4;
-      x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-      x += carry;
-      if (i < nb) s_incl[i] = x;
-      carry += r0 + r1 + r2 + r3;
+  for (int p = tid; p < P; p += nthr) {
+    const int e = s_exp[p];
+    if (e >= 0) {  // expert -1: an omitted pair
+      atomicAdd(&s_cnt[e], 1);
+      atomicOr(&s_tmask[e], 1u << dec_token_of_pair(p, T, k));
     }
+  }
+  __syncthreads();
+  // inclusive scan of (count, non-empty flag) over the buckets: every wave scans 64-bucket
+  // chunks (DPP row shifts inside 16-lane rows, then the row totals), then each bucket
+  // adds the sums of the chunks before its own
+  const int nchunks = (nb + 63) >> 6;
+  for (int c = wave; c < nchunks; c += nthr >> 6) {
+    const int i = 64 * c + lane;
+    const int cv = i < nb ? s_cnt[i] : 0;
+    int x = cv | ((cv > 0 ? 1 : 0) << 16);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+    const int row = lane >> 4;
+    x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+    if (i < nb) s_incl[i] = x;
+    if (lane == 0) s_ctot[c] = r0 + r1 + r2 + r3;
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += nthr) {
+    int pre = 0;
+    for (int c = 0; c < (i >> 6); ++c) pre += s_ctot[c];
+    s_incl[i] += pre;
   }
   __syncthreads();
   const int n_active = s_incl[nb - 1] >> 16;
@@ -367,17 +382,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
   for (int p = tid; p < P; p += nthr) {
     const int e = s_exp[p];
     if (e < 0) continue;
-    // stable rank: earlier pairs of the same expert, 4 entries per LDS read (the same
-    // addresses for every lane: broadcast)
-    int r = 0;
-    const int4* s4 = reinterpret_cast<const int4*>(s_exp);
-    const int nq = p >> 2;
-#pragma unroll 4
-    for (int q4 = 0; q4 < nq; ++q4) {
-      const int4 v = s4[q4];
-      r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-    }
-    for (int q = 4 * nq; q < p; ++q) r += (s_exp[q] == e);
+    const int r = __popc(s_tmask[e] & ((1u << dec_token_of_pair(p, T, k)) - 1u));  // stable rank
     const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
     w.perm[pos] = p;
     if (dbg_perm) dbg_perm[pos] = p;
@@ -404,6 +409,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   __shared__ __align__(16) int s_exp[kMaxPairsDec];   // expert of each pair
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
+  __shared__ uint32_t s_tmask[1024 + 1];  // tokens with a pair in each bucket
   __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
   __shared__ double s_part[kRouteThreads / 64][kDecMaxTokens];
   __shared__ double s_sg[kDecMaxTokens];  // shared-gate logits read from the mailbox
@@ -432,7 +438,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
       }
     }
   }
-  for (int i = tid; i < nb; i += kRouteThreads) s_cnt[i] = 0;
+  for (int i = tid; i < nb; i += kRouteThreads) {
+    s_cnt[i] = 0;
+    s_tmask[i] = 0u;
+  }
   // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns; the
   // first pass of its weights is requested now, before the activations are ready
   const int e_row = blockIdx.x * kRouterRows + (wave >> 2);
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
 }
 
 
@@ -656,6 +665,7 @@ __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs 
   __shared__ double s_l[4][16];
   __shared__ __align__(16) int s_exp[kMaxPairsDec];
   __shared__ int s_cnt[1024 + 1];
+  __shared__ uint32_t s_tmask[1024 + 1];
   __shared__ int s_incl[1024 + 1];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -713,11 +723,14 @@ __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   if (tid == 0) __hip_atomic_store(&w.rr_flags[kTopkDoneWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int i = tid; i < ntickets; i += kTopkRouteThreads) w.tickets[i] = 0u;  // this call's combine tickets
-  for (int i = tid; i < nb; i += kTopkRouteThreads) s_cnt[i] = 0;
+  for (int i = tid; i < nb; i += kTopkRouteThreads) {
+    s_cnt[i] = 0;
+    s_tmask[i] = 0u;
+  }
   for (int p = tid; p < P; p += kTopkRouteThreads)
     s_exp[p] = p < Pr ? __hip_atomic_load(&w.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : E;
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
 }
 
 // ---------------------------------------------------------------------------
