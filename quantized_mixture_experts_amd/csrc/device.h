@@ -361,20 +361,29 @@ __device__ __forceinline__ void topk_select(const double (&lv)[NT][NPER], int E,
     }
 #pragma unroll
   for (int t = 0; t < NT; ++t) sort_lane<NPER>(v[t]);
+  // lane j keeps the j-th selection; the selections are written once, after the rounds
+  uint64_t sel[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sel[t] = 0ull;
   for (int j = 0; j < k; ++j) {
     uint64_t m[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) m[t] = wave_max_key(v[t][0]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (lane == 0) {
-        s_exp[slot[t] * k + j] = topk_key_index(m[t]);
-        s_l[slot[t] * k + j] = topk_key_value(m[t]);
-      }
-      const bool pop = v[t][0] == m[t];  // keys are unique: exactly one lane
+      sel[t] = lane == j ? m[t] : sel[t];
+      if (v[t][0] == m[t]) {  // keys are unique: exactly one lane moves up its next candidate
 #pragma unroll
-      for (int i = 0; i + 1 < NPER; ++i) v[t][i] = pop ? v[t][i + 1] : v[t][i];
-      v[t][NPER - 1] = pop ? 0ull : v[t][NPER - 1];
+        for (int i = 0; i + 1 < NPER; ++i) v[t][i] = v[t][i + 1];
+        v[t][NPER - 1] = 0ull;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (lane < k) {
+      s_exp[slot[t] * k + lane] = topk_key_index(sel[t]);
+      s_l[slot[t] * k + lane] = topk_key_value(sel[t]);
     }
   }
 }
