@@ -136,7 +136,7 @@ SWEEP_T = [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
 def test_forward_token_sweep(wfmt, T, path):
     """Every tile threshold of the token dimension (16-row MFMA tiles, 4 tiles per pass),
     with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4.  path 0
-    picks the decode kernels up to 10 (MXFP4) or 30 (CB4) tokens; path 1 forces them
+    picks the decode kernels up to 7 (MXFP4) or 32 (CB4) tokens; path 1 forces them
     (up to 32 tokens); path 2 forces the grouped kernels."""
     if path == 1 and T > 32:
         pytest.skip("the decode kernels take at most 32 tokens")
