@@ -1579,6 +1579,111 @@ __device__ __forceinline__ void dec_down_item(const LayerArgs& L, int T, const W
 
 // Down projection kernel, grid (H/16, slots): one block per (column tile, active expert),
 // all of the expert's pairs (several passes for a busy expert).
+// Down projection over two 16-row tiles per block, output columns 32 x .. 32 x + 31 (H is a
+// multiple of 32): the steps of dec_down_item with both tiles' weights in flight together
+// and one ticket per 32 columns.  A block then streams twice the weight bytes per staged activation row and
+// the grid half the blocks; from 2 tokens, where the grid takes several rounds of blocks.
+template <int FMT, int NTT, int KSW>
+__device__ __forceinline__ void dec_down2_item(const LayerArgs& L, int T, const Work& w, float* __restrict__ y,
+                                               uint32_t* __restrict__ tickets, int xrows_max, const Slot* slot_rec,
+                                               int x, uint8_t* smem, const uint32_t* lut, int* is_last) {
+  const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int H = L.H, I = L.I, k = L.k;
+  const int P = T * k + (L.has_shared ? T : 0);
+  const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
+  const int xstride = dec_xstride(K);
+  const size_t lds_plane = (size_t)(xrows_max + 1) * xstride;  // staged rows, then the zero row
+  uint16_t* xs = (uint16_t*)smem;
+  float* xsum = (float*)(smem + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
+  const PackedTile pa = packed_tile<FMT>(slot_rec->down, H, K, 2 * x);
+  const PackedTile pb = packed_tile<FMT>(slot_rec->down, H, K, 2 * x + 1);
+  // the packed scale store's row bases, before the staging loads (not counted below)
+  const uint32_t ba = FMT == 3 ? (uint32_t)pa.bases[n] : 0u, bb = FMT == 3 ? (uint32_t)pb.bases[n] : 0u;
+  const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
+
+  for (int tb = 0; tb < cnt; tb += xrows_max) {
+    const int live = min(NTT, (cnt - tb + 15) / 16);
+    const int xrows = min(cnt - tb, xrows_max);
+    const uint16_t* arow[NTT];
+    dec_arows<NTT>(xs, xstride, xrows, xrows_max, arow);
+    f32x4_t acca[NTT], accb[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) { acca[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accb[tt] = acca[tt]; }
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int ks0 = ch * 4 * KSW + wave;
+      if (ch == 0) {
+        if (tb > 0) __syncthreads();  // the previous pass finished with the LDS tile
+        stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb,
+                                 xrows, T, k);
+        zero_tile_pad<2>(xs, xstride, lds_plane, K, dec_kcols(K), xrows_max, xrows);
+      }
+      WeightRegs<FMT, KSW> wa, wb;
+      prefetch_weights2<FMT, KSW>(wa, pa, wb, pb, nkb, ks0, nks, n, g);
+      if (ch == 0) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(2 * KSW * loads_per_step<FMT>()));
+        __builtin_amdgcn_s_barrier();
+        if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
+      }
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) {
+        const int ks = ks0 + 4 * i;
+        mma_kstep<FMT, 2, NTT, KSW>(wa, i, ks, nks, arow, lds_plane, live, lut, ba, acca, xsum, nkb >> 1);
+        mma_kstep<FMT, 2, NTT, KSW>(wb, i, ks, nks, arow, lds_plane, live, lut, bb, accb, xsum, nkb >> 1);
+      }
+    }
+    mfma_settle_all(acca);
+    mfma_settle_all(accb);
+    float v[8 * NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v[8 * tt + q] = acca[tt][q]; v[8 * tt + 4 + q] = accb[tt][q]; }
+    reduce4<8 * NTT>(v, (float*)smem);
+    if (wave == 0) {
+      const int col = 32 * x + n;
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int slot = tb + 16 * tt + 4 * g + q;
+          if (slot < tb + xrows) {  // this pass's pairs only
+            float* orow = w.o + (size_t)w.perm[off + slot] * H;
+            __hip_atomic_store(&orow[col], v[8 * tt + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&orow[col + 16], v[8 * tt + 4 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+    }
+  }
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&tickets[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *is_last = (prev == (uint32_t)(n_active - 1));
+  }
+  __syncthreads();
+  if (!*is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  dec_combine_cols(L, T, w, y, 32 * x, 32);
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// grid (H/32, slots): one block per (32-column tile, active expert)
+template <int FMT, int NTT, int KSW>
+__global__ __launch_bounds__(256, 3) void k_dec_down2(LayerArgs L, int T, Work w, float* __restrict__ y,
+                                                      uint32_t* __restrict__ tickets, int xrows_max) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int is_last;
+  __shared__ uint32_t s_lut[FMT == 2 ? 256 : 1];  // codebook table (CB4)
+  const Slot* sr = w.slots + blockIdx.y;
+  if (sr->cnt == 0) return;
+  if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
+  dec_down2_item<FMT, NTT, KSW>(L, T, w, y, tickets, xrows_max, sr, blockIdx.x, smem, s_lut, &is_last);
+}
+
 template <int FMT, int NTT, int KSW, bool OMB>
 __global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
                                                      uint32_t* __restrict__ tickets, int xrows_max) {
@@ -1765,7 +1870,9 @@ static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, ui
       return;
     }
   }
-  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, NTT, KSW, false>), dim3(L.H / 16, slots), dim3(256),
+  // two row tiles per block from 2 tokens (one token: every block of the grid is resident
+  // at once, and half as many measured slower)
+  MOEQ_LAUNCH(tm, kStageDown, (k_dec_down2<FMT, NTT, KSW>), dim3(L.H / 32, slots), dim3(256),
               dec_lds_bytes(FMT, L.I, 2, NTT, xrows), s, L, T, w, y, tickets, xrows);
 }
 

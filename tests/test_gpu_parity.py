@@ -240,6 +240,19 @@ def test_forward_at_size_limits(T, H, I, E, k, wfmt, shared, xd, path):
 
 
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
+@pytest.mark.parametrize("T", [2, 4, 20])
+def test_decode_down_two_tiles(wfmt, T):
+    """The split-K down projection from 2 tokens covers two 16-row tiles per block (one
+    ticket per 32 columns): H = 224 gives 7 such blocks per expert.  I = 1152 is 9 k-steps,
+    past the short-row kernel."""
+    spec = synth.small_spec(f"dn2_{T}", T, 224, 1152, 16, 4, wfmt, has_shared=1, x_dtype=synth.X_BF16,
+                            bias="normal", seed=300 + T)
+    layer = synth.make_layer(spec)
+    layer, x, dl, y, dbg = _run(spec, layer=layer, path=1)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"two-tile down T={T} wfmt={wfmt}")
+
+
+@pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T,path,H", [(1, 0, 512), (4, 0, 512), (7, 0, 512), (9, 0, 512), (40, 0, 512), (4, 2, 512),
                                       (1, 0, 6144), (4, 0, 6144)])
 def test_forward_rms_equals_rescale_then_forward(wfmt, T, path, H):
