@@ -1441,11 +1441,13 @@ __device__ __forceinline__ void dec_combine_cols(const LayerArgs& L, int T, cons
 }
 
 // ---------------------------------------------------------------------------
-// 4. Down projection + combine.  grid = (H/16, max active slots), 4 waves split K=I.
-// Each block writes o_p[16 cols] for its expert's pairs; the last block to arrive at
-// a column tile computes y[t][tile] for every token in a fixed order.  The o values
-// travel as write-through stores and a relaxed device-scope ticket counts arrivals,
-// so no full L2 write-back is needed.
+// 4. Down projection + combine for rows of more than 8 k-steps, 4 waves splitting K = I.
+//    One token (k_dec_down): grid (H/16, slots); each slot's block posts its 16 o values
+//    to a mailbox and the block that finds every pair posted writes y.
+//    From 2 tokens (k_dec_down2): grid (H/32, slots); o rows are written through and a
+//    relaxed device-scope ticket per 32 columns elects the block that sums y.
+//    Either way y is the fixed-order sum (routed j ascending, then shared), the o values
+//    travel as write-through stores and no full L2 write-back is needed.
 // ---------------------------------------------------------------------------
 // Pairs of one token: top-k routed ones plus the shared one.
 constexpr int kMaxPairsT1 = 17;
@@ -1457,128 +1459,83 @@ __device__ __forceinline__ uint32_t omb_encode(float v) {
   return ~(b == 0xFFFFFFFFu ? 0xFFC00000u : b);
 }
 
-template <int FMT, int NTT, int KSW, bool OMB>
-__device__ __forceinline__ void dec_down_item(const LayerArgs& L, int T, const Work& w, float* __restrict__ y,
-                                              uint32_t* __restrict__ tickets, int xrows_max, const Slot* slot_rec,
-                                              int x, uint8_t* smem, const uint32_t* lut, int* is_last) {
-  const int cnt = slot_rec->cnt, off = slot_rec->off, n_active = slot_rec->n_active;
+// One token (one pair per slot, one pass): every slot's block posts its 16 o values to the
+// mailbox (zeroed by the router kernel) and, once they have landed, reads the other pairs'
+// entries once; a block that finds them all sums the column tile over the pairs in the
+// fixed order and writes y (more than one may: the same values).  The block whose read
+// comes last finds them all, so no block waits and no residency is assumed.
+template <int FMT, int KSW>
+__device__ __forceinline__ void dec_down_t1_item(const LayerArgs& L, const Work& w, float* __restrict__ y,
+                                                 const Slot* slot_rec, int x, uint8_t* smem, const uint32_t* lut) {
+  const int off = slot_rec->off;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = L.H, I = L.I, k = L.k;
-  const int P = T * k + (L.has_shared ? T : 0);
+  const int P = k + (L.has_shared ? 1 : 0);
   const int K = I, nkb = K >> 5, nks = (nkb + 3) >> 2;
   const int xstride = dec_xstride(K);
-  const size_t lds_plane = (size_t)(xrows_max + 1) * xstride;  // staged rows, then the zero row
+  const size_t lds_plane = 2 * (size_t)xstride;  // the staged row, then the zero row
   uint16_t* xs = (uint16_t*)smem;
-  float* xsum = (float*)(smem + dec_tile_bytes(K, 2, NTT, xrows_max));  // 3-bit affine
+  float* xsum = (float*)(smem + dec_tile_bytes(K, 2, 1, 1));  // 3-bit affine
   const PackedTile pd = packed_tile<FMT>(slot_rec->down, H, K, x);
   const uint32_t bd = FMT == 3 ? (uint32_t)pd.bases[n] : 0u;  // before the staging loads
   const int nchunks = (nks + 4 * KSW - 1) / (4 * KSW);
-
-  for (int tb = 0; tb < cnt; tb += xrows_max) {
-    const int live = min(NTT, (cnt - tb + 15) / 16);
-    const int xrows = min(cnt - tb, xrows_max);
-    const uint16_t* arow[NTT];
-    dec_arows<NTT>(xs, xstride, xrows, xrows_max, arow);
-    f32x4_t acc[NTT];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int ks0 = ch * 4 * KSW + wave;
-      if (ch == 0) {
-        if (tb > 0) __syncthreads();
-        stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, tb,
-                                 xrows, T, k);
-        zero_tile_pad<2>(xs, xstride, lds_plane, K, dec_kcols(K), xrows_max, xrows);
-      }
-      WeightRegs<FMT, KSW> wd;
-      prefetch_weights<FMT, KSW>(wd, pd, nkb, ks0, nks, n, g);
-      if (ch == 0) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(KSW * loads_per_step<FMT>()));
-        __builtin_amdgcn_s_barrier();
-        if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16 * NTT, xrows);
-      }
-#pragma unroll
-      for (int i = 0; i < KSW; ++i) {
-        const int ks = ks0 + 4 * i;
-        mma_kstep<FMT, 2, NTT, KSW>(wd, i, ks, nks, arow, lds_plane, live, lut, bd, acc, xsum, nkb >> 1);
-      }
+  const uint16_t* arow[1];
+  dec_arows<1>(xs, xstride, 1, 1, arow);
+  f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int ks0 = ch * 4 * KSW + wave;
+    if (ch == 0) {
+      stage_rows_lds<2, false>(xs, xstride, lds_plane, w.hplanes, (size_t)P * I, K, slot_rec, w.perm + off, 0, 1, 1,
+                               k);
+      zero_tile_pad<2>(xs, xstride, lds_plane, K, dec_kcols(K), 1, 1);
     }
-    mfma_settle_all(acc);
-    float v[4 * NTT];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[4 * tt + q] = acc[tt][q];
-    reduce4<4 * NTT>(v, (float*)smem);
-    if constexpr (OMB) {
-      // One token (one pair per slot, one pass): every slot's block posts its 16 o values to
-      // the mailbox (zeroed by the router kernel) and, once they have landed, reads the
-      // other pairs' entries once; a block that finds them all sums the column tile over
-      // the pairs in the fixed order and writes y (more than one may: the same values).
-      // The block whose read comes last finds them all.
-      if (wave == 0 && g == 0) {
-        const int col = 16 * x + n;
-        const int p_own = w.perm[off];
-        uint32_t* omb = reinterpret_cast<uint32_t*>(w.o);
-        const uint32_t mine = omb_encode(v[0]);
-        const float rv = w.resid ? w.resid[col] : 0.f;
-        __hip_atomic_store(&omb[(size_t)p_own * H + col], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const int P1 = k + (L.has_shared ? 1 : 0);  // routed pairs 0 .. k-1, then the shared one
-        uint32_t e[kMaxPairsT1];
-        float pw[kMaxPairsT1];
-        bool miss = false;
-#pragma unroll
-        for (int u = 0; u < kMaxPairsT1; ++u) {
-          const int p = min(u, P1 - 1);
-          pw[u] = w.pair_w[p];
-          e[u] = p == p_own ? mine
-                            : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          miss |= e[u] == 0u && pw[u] != 0.0f;  // an omitted pair (weight 0) posts nothing
-        }
-        if (!miss) {
-          float sum = 0.f;
-#pragma unroll
-          for (int u = 0; u < kMaxPairsT1; ++u)
-            if (u < P1 && pw[u] != 0.0f) sum = fmaf(pw[u], __uint_as_float(~e[u]), sum);
-          y[col] = w.resid ? rv + sum : sum;
-        }
-      }
-      return;
+    WeightRegs<FMT, KSW> wd;
+    prefetch_weights<FMT, KSW>(wd, pd, nkb, ks0, nks, n, g);
+    if (ch == 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_le_lgkm0(KSW * loads_per_step<FMT>()));
+      __builtin_amdgcn_s_barrier();
+      if constexpr (FMT == 4) dec_group_sums<2>(xsum, xs, xstride, lds_plane, K, 16, 1);
     }
-    if (wave == 0) {
-      const int col = 16 * x + n;
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int slot = tb + 16 * tt + 4 * g + q;
-          if (slot < tb + xrows)  // this pass's pairs only
-            __hip_atomic_store(&w.o[(size_t)w.perm[off + slot] * H + col], v[4 * tt + q], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
+    for (int i = 0; i < KSW; ++i) {
+      const int ks = ks0 + 4 * i;
+      mma_kstep<FMT, 2, 1, KSW>(wd, i, ks, nks, arow, lds_plane, 1, lut, bd, acc, xsum, nkb >> 1);
     }
   }
-
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&tickets[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *is_last = (prev == (uint32_t)(n_active - 1));
+  mfma_settle_all(acc);
+  float v[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+  reduce4<4>(v, (float*)smem);
+  if (wave == 0 && g == 0) {
+    const int col = 16 * x + n;
+    const int p_own = w.perm[off];
+    uint32_t* omb = reinterpret_cast<uint32_t*>(w.o);
+    const uint32_t mine = omb_encode(v[0]);
+    const float rv = w.resid ? w.resid[col] : 0.f;
+    __hip_atomic_store(&omb[(size_t)p_own * H + col], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint32_t e[kMaxPairsT1];
+    float pw[kMaxPairsT1];
+    bool miss = false;
+#pragma unroll
+    for (int u = 0; u < kMaxPairsT1; ++u) {
+      const int p = min(u, P - 1);  // routed pairs 0 .. k-1, then the shared one
+      pw[u] = w.pair_w[p];
+      e[u] = p == p_own ? mine : __hip_atomic_load(&omb[(size_t)p * H + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      miss |= e[u] == 0u && pw[u] != 0.0f;  // an omitted pair (weight 0) posts nothing
+    }
+    if (!miss) {
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kMaxPairsT1; ++u)
+        if (u < P && pw[u] != 0.0f) sum = fmaf(pw[u], __uint_as_float(~e[u]), sum);
+      y[col] = w.resid ? rv + sum : sum;
+    }
   }
-  __syncthreads();
-  if (!*is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  dec_combine_cols(L, T, w, y, 16 * x, 16);
-  if (threadIdx.x == 0) __hip_atomic_store(&tickets[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Down projection kernel, grid (H/16, slots): one block per (column tile, active expert),
-// all of the expert's pairs (several passes for a busy expert).
 // Down projection over two 16-row tiles per block, output columns 32 x .. 32 x + 31 (H is a
 // multiple of 32): the steps of dec_down_item with both tiles' weights in flight together
 // and one ticket per 32 columns.  A block then streams twice the weight bytes per staged activation row and
@@ -1684,16 +1641,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_down2(LayerArgs L, int T, Work w
   dec_down2_item<FMT, NTT, KSW>(L, T, w, y, tickets, xrows_max, sr, blockIdx.x, smem, s_lut, &is_last);
 }
 
-template <int FMT, int NTT, int KSW, bool OMB>
-__global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, int T, Work w, float* __restrict__ y,
-                                                     uint32_t* __restrict__ tickets, int xrows_max) {
+// one token: grid (H/16, slots), one block per (16-column tile, active expert)
+template <int FMT, int KSW>
+__global__ __launch_bounds__(256, 3) void k_dec_down(LayerArgs L, Work w, float* __restrict__ y) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int is_last;
   __shared__ uint32_t s_lut[FMT == 2 ? 256 : 1];  // codebook table (CB4)
   const Slot* sr = w.slots + blockIdx.y;
   if (sr->cnt == 0) return;
   if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
-  dec_down_item<FMT, NTT, KSW, OMB>(L, T, w, y, tickets, xrows_max, sr, blockIdx.x, smem, s_lut, &is_last);
+  dec_down_t1_item<FMT, KSW>(L, w, y, sr, blockIdx.x, smem, s_lut);
 }
 
 // ---------------------------------------------------------------------------
@@ -1863,15 +1819,13 @@ template <int FMT, int NTT, int KSW>
 static void launch_down_k(const LayerArgs& L, int T, const Work& w, float* y, uint32_t* tickets, int xrows,
                           bool omb, hipStream_t s, const Timing& tm) {
   const int slots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  if constexpr (NTT == 1) {
-    if (omb) {  // one item per block
-      MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, 1, KSW, true>), dim3(L.H / 16, slots), dim3(256),
-                  dec_lds_bytes(FMT, L.I, 2, 1, xrows), s, L, T, w, y, tickets, xrows);
-      return;
-    }
+  if (omb) {  // one token: the mailbox combine, one 16-row tile per block
+    MOEQ_LAUNCH(tm, kStageDown, (k_dec_down<FMT, KSW>), dim3(L.H / 16, slots), dim3(256),
+                dec_lds_bytes(FMT, L.I, 2, 1, 1), s, L, w, y);
+    return;
   }
-  // two row tiles per block from 2 tokens (one token: every block of the grid is resident
-  // at once, and half as many measured slower)
+  // two row tiles per block from 2 tokens (at one token every block of the grid is resident
+  // at once, and half as many blocks measured slower)
   MOEQ_LAUNCH(tm, kStageDown, (k_dec_down2<FMT, NTT, KSW>), dim3(L.H / 32, slots), dim3(256),
               dec_lds_bytes(FMT, L.I, 2, NTT, xrows), s, L, T, w, y, tickets, xrows);
 }

@@ -204,12 +204,12 @@ def test_mxfp4_grouped_activation_planes(xd):
     (384, 768, 2, 1, synth.WFMT_MXFP4, synth.X_F32),     # 3 slots, fp32 x planes, ragged last k-step group
     (256, 1024, 4, 1, synth.WFMT_CB4, synth.X_F32),      # codebook weights, shared gate
     (256, 1024, 8, 1, synth.WFMT_CB4, synth.X_BF16),     # 9 slots
-    (4096, 640, 12, 0, synth.WFMT_MXFP4, synth.X_BF16),  # 256 x 12 blocks: not resident at once, so the
-                                                         # ticketed combine instead of the o mailbox
+    (4096, 640, 12, 0, synth.WFMT_MXFP4, synth.X_BF16),  # I = 640 (5 k-steps): the short-row kernel and its
+                                                         # ticketed combine, 64 x 12 blocks
 ])
 def test_one_token_long_rows(H, I, k, shared, wfmt, xd):
-    """One token with long down rows (the split-K down kernel and its ticketed combine)
-    over several slot counts, both weight formats and both activation types."""
+    """One token: the split-K down kernel with its mailbox combine over several slot counts,
+    both weight formats and both activation types (and one case of the short-row kernel)."""
     spec = synth.small_spec(f"t1_{H}_{I}_{k}", 1, H, I, 24, k, wfmt, has_shared=shared, x_dtype=xd,
                             bias="normal", seed=7 * I + k)
     layer = synth.make_layer(spec, shared_gate=bool(shared))
