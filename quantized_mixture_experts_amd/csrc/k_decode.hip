@@ -1844,6 +1844,14 @@ static bool use_down_mailbox(const LayerArgs& L, int T) { return T == 1 && (L.I 
 constexpr size_t kDecStageBytes = 48 * 1024;
 constexpr size_t kDecStageBytesGateUpCb4 = 36 * 1024;
 static size_t dec_gateup_stage_bytes(int wfmt) { return wfmt == 2 ? kDecStageBytesGateUpCb4 : kDecStageBytes; }
+// The split-K down kernels (rows of more than 8 k-steps) stage their two h planes within
+// 36 KB, so 4 blocks share a CU (their registers allow it): the stacked T = 4 down grid of
+// 1,350 two-tile blocks then takes 1.3 rounds of the chip instead of 1.8; an expert with
+// more pairs than a pass holds loops over passes inside its block.
+constexpr size_t kDecStageBytesDownLong = 36 * 1024;
+static size_t dec_down_stage_bytes(int I) {
+  return (I / 32 + 3) / 4 > kDownRowsMaxSteps ? kDecStageBytesDownLong : kDecStageBytes;
+}
 static int dec_rows_per_pass(int K, int NP, int T, size_t budget = kDecStageBytes) {
   const size_t row = (size_t)dec_xstride(K) * 2 * NP;
   const int cap = (int)(budget / row) - 1;  // and the zero row
@@ -1889,7 +1897,7 @@ static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dt
                                      uint32_t* tickets, bool omb, bool sr, const DbgOut& d, hipStream_t s,
                                      const Timing& tm) {
   const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T, dec_gateup_stage_bytes(FMT));
-  const int xd = dec_rows_per_pass(L.I, 2, T);
+  const int xd = dec_rows_per_pass(L.I, 2, T, dec_down_stage_bytes(L.I));
   if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, sr, d, s, tm);
   else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, false, d, s, tm);
   if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, omb, s, tm);
@@ -1900,7 +1908,8 @@ static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dt
 bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
   if (T > kDecMaxTokens) return false;
   const int np = x_dtype == 1 ? 1 : 3;
-  const int xg = dec_rows_per_pass(L.H, np, T, dec_gateup_stage_bytes(L.wfmt)), xd = dec_rows_per_pass(L.I, 2, T);
+  const int xg = dec_rows_per_pass(L.H, np, T, dec_gateup_stage_bytes(L.wfmt));
+  const int xd = dec_rows_per_pass(L.I, 2, T, dec_down_stage_bytes(L.I));
   const size_t g = dec_lds_bytes(L.wfmt, L.H, np, xg <= 16 ? 1 : 2, xg);
   const size_t d = dec_lds_bytes(L.wfmt, L.I, 2, xd <= 16 ? 1 : 2, xd);
   return g <= 160 * 1024 && d <= 160 * 1024;
