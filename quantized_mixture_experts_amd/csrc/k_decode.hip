@@ -1,6 +1,6 @@
 // Decode path (few tokens per call, e.g. a draft/verify window of up to 17 tokens):
 //   1. routing, by token count:
-//      - one token: k_dec_rr computes the router logits (4 expert rows per block) and
+//      - one token: k_dec_rr computes the router logits (one expert row per block) and
 //        stores them; every gate/up block of step 2 takes the top-k of those logits
 //        itself (the same selection in every block) and routes, so no route kernel runs;
 //      - 2..7 tokens: k_dec_rr also routes: every block posts its logits and then checks
@@ -72,7 +72,8 @@ __host__ __device__ __forceinline__ int lds_row_stride(int K) {
 // 1+2. Router and route in one kernel.  Each 1024-thread block computes 4 expert rows
 // of router logits (4 waves per row split its columns; all tokens; fp64 accumulation
 // of exact products, partial sums added in a fixed order) and writes them through to
-// the device-coherent level.  Each block then checks once whether every logit has
+// the device-coherent level; without the route (one token) a block computes one row
+// with its 16 waves.  Each block then checks once whether every logit has
 // arrived; a block that sees them all does the top-k, the softmax gates and the
 // bucketing:
 //    top-k: one wave per token, k rounds of a wave argmax (ties to the lower index);
@@ -85,7 +86,12 @@ __host__ __device__ __forceinline__ int lds_row_stride(int K) {
 // zeroed before the first use.
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 1024;
-constexpr int kRouterRows = kRouteThreads / 256;  // expert rows per block (4 waves each)
+// Expert rows per router block: 4 (4 waves each) when the block also routes, 1 (16 waves
+// splitting the row) when it only stores the logits, so that the W_r stream of one token
+// spreads over E + 1 CUs instead of a quarter of them (each CU keeps only so many
+// requests in flight).
+template <bool ROUTE>
+constexpr int router_rows() { return ROUTE ? 4 : 1; }
 constexpr int kMaxPairsDec = kDecMaxTokens * 16 + kDecMaxTokens;
 
 // Top-k of the tokens a wave takes (t0, and t1 when below T) from the logit mailbox,
@@ -201,28 +207,31 @@ __device__ __forceinline__ typename RouterX<XDT == 2 ? 1 : XDT>::chunk router_x(
   }
 }
 
-constexpr int kRouterPer = 3;  // float4 chunks per lane and pass: a quarter of a 2880-column row in one pass
+// float4 chunks of W_r per lane and pass: a 2880-column row's quarter (4 waves a row) or
+// sixteenth (16 waves a row) in one pass
+template <bool ROUTE>
+constexpr int router_per() { return ROUTE ? 3 : 1; }
 
 // The first pass's router-weight chunks of this lane (issued early, e.g. before the RMS
 // rescale that the activations need).
+template <int KPER>
 __device__ __forceinline__ void router_w_first(const float* __restrict__ wrow, int h0, int h1,
-                                               f32x4_t (&wv)[kRouterPer]) {
+                                               f32x4_t (&wv)[KPER]) {
   const int lane = threadIdx.x & 63;
   const int c_beg = h0 / 4, c_end = h1 / 4;
 #pragma unroll
-  for (int i = 0; i < kRouterPer; ++i) {
+  for (int i = 0; i < KPER; ++i) {
     const int c = max(c_beg, min(c_beg + lane + 64 * i, c_end - 1));
     wv[i] = c_end > c_beg ? *(const __attribute__((address_space(1))) f32x4_t*)(wrow + 4 * c) : f32x4_t{0, 0, 0, 0};
   }
 }
 
-template <int XDT>
+template <int XDT, int KPER>
 __device__ __forceinline__ void router_part(const float* __restrict__ wrow, const void* __restrict__ x, int T, int H,
-                                            int h0, int h1, double* __restrict__ part,
-                                            const f32x4_t (&wfirst)[kRouterPer]) {
+                                            int h0, int h1, double* __restrict__ part, const f32x4_t (&wfirst)[KPER]) {
   using RX = RouterX<XDT == 2 ? 1 : XDT>;
   const int lane = threadIdx.x & 63;
-  constexpr int kPer = kRouterPer;
+  constexpr int kPer = KPER;
   constexpr int kTB = 4;
   const int c_beg = h0 / 4, c_end = h1 / 4;
   if (c_end <= c_beg) {
@@ -442,14 +451,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     s_cnt[i] = 0;
     s_tmask[i] = 0u;
   }
-  // rows blockIdx.x * 4 + (wave >> 2); wave & 3 takes a quarter of the row's columns; the
-  // first pass of its weights is requested now, before the activations are ready
-  const int e_row = blockIdx.x * kRouterRows + (wave >> 2);
-  const int qh = ((H / 4 + 3) / 4) * 4;  // columns per quarter, a multiple of 4
-  const int h0 = min(H, (wave & 3) * qh), h1 = min(H, ((wave & 3) + 1) * qh);
+  // rows blockIdx.x ROWS + wave / SPLIT; wave % SPLIT takes a 1/SPLIT share of the row's
+  // columns; the first pass of its weights is requested now, before the activations are ready
+  constexpr int ROWS = router_rows<ROUTE>(), SPLIT = kWaves / ROWS, KPER = router_per<ROUTE>();
+  const int e_row = blockIdx.x * ROWS + wave / SPLIT, part = wave % SPLIT;
+  const int qh = ((H / SPLIT + 3) / 4) * 4;  // columns per share, a multiple of 4
+  const int h0 = min(H, part * qh), h1 = min(H, (part + 1) * qh);
   const float* wrow = e_row < E ? L.router_w + (size_t)e_row * H : L.shared_gate_w;
-  f32x4_t wfirst[kRouterPer];
-  if (e_row < erows) router_w_first(wrow, h0, h1, wfirst);
+  f32x4_t wfirst[KPER];
+  if (e_row < erows) router_w_first<KPER>(wrow, h0, h1, wfirst);
   const void* xr = x;  // the router's activations (XDT 2: the block's LDS copy of the rescale)
   if constexpr (XDT == 2) {
     __shared__ double s_d[kDecSplitRouteT];  // each token's sqrt(mean(y^2) + eps)
@@ -461,7 +471,33 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     __shared__ double s_ms[kDecSplitRouteT][4];
     const int grp = wave >> 2, i = tid & 255;
     static_assert(kDecSplitRouteT <= 2 * (kWaves / 4), "a group holds at most two tokens' values");
-    if (H <= kRmsRegCols) {
+    if (H <= kRmsRegCols && T == 1) {
+      // one token: group 0 reads the row once (16 values a thread, kept for LDS), and
+      // all 16 waves take the quotients (3 values a thread instead of 12 for group 0 alone)
+      __shared__ float s_y[kRmsRegCols];
+      if (grp == 0) {
+        float v[16];
+        const double sq = wave_sum_f64(rms_partial_keep((const float*)x, H, i, v));
+        if (lane == 0) s_ms[0][wave & 3] = sq;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (i + 256 * u < H) s_y[i + 256 * u] = v[u];
+      }
+      __syncthreads();
+      if (tid == 0) {
+        const double d = rms_divisor(s_ms[0][0], s_ms[0][1], s_ms[0][2], s_ms[0][3], H, eps);
+        s_d[0] = d;
+        s_rd[0] = 1.0 / d;
+      }
+      __syncthreads();
+      const double d = s_d[0], rd = s_rd[0];
+      for (int n = tid; n < H; n += kRouteThreads) {
+        const uint16_t q = rms_apply(s_y[n], d, rd);
+        s_x[n] = q;
+        if (blockIdx.x == 0) w.xr[n] = q;
+      }
+      __syncthreads();
+    } else if (H <= kRmsRegCols) {
       // each row read once: the group's (at most two) tokens keep their values in
       // registers from the sum of squares to the quotient
       float v[2][16];
@@ -532,17 +568,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   {
     // the bias of the logit this thread finishes (if any), loaded before the sums
     double bias = 0.0;
-    if (tid < kRouterRows * T) {
-      const int er = blockIdx.x * kRouterRows + tid / T;
+    if (tid < ROWS * T) {
+      const int er = blockIdx.x * ROWS + tid / T;
       if (er < E && L.router_b) bias = (double)L.router_b[er];
     }
-    if (e_row < erows) router_part<XDT>(wrow, xr, T, H, h0, h1, s_part[wave], wfirst);
+    if (e_row < erows) router_part<XDT, KPER>(wrow, xr, T, H, h0, h1, s_part[wave], wfirst);
     __syncthreads();
-    if (tid < kRouterRows * T) {
+    if (tid < ROWS * T) {
       const int r = tid / T, t = tid % T;
-      const int er = blockIdx.x * kRouterRows + r;
+      const int er = blockIdx.x * ROWS + r;
       if (er < erows) {
-        double v = ((s_part[4 * r][t] + s_part[4 * r + 1][t]) + s_part[4 * r + 2][t]) + s_part[4 * r + 3][t];
+        double v = s_part[SPLIT * r][t];  // the shares added in column order
+#pragma unroll
+        for (int q = 1; q < SPLIT; ++q) v += s_part[SPLIT * r + q][t];
         if (er < E && L.router_b) v += bias;
         if (!ROUTE)
           w.logits[(size_t)t * (E + 1) + er] = v;
@@ -1919,7 +1957,8 @@ template <int XDT>
 static void launch_rr(const LayerArgs& L, const void* x, int T, int erows, const Work& w, int max_slots, int ntickets,
                       int nzero_o, float eps, bool sr, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
                       int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
-  const dim3 grid((erows + kRouterRows - 1) / kRouterRows);
+  const int rows = sr ? router_rows<false>() : router_rows<true>();
+  const dim3 grid((erows + rows - 1) / rows);
   if (sr)  // logits only: the gate/up kernel routes
     MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
                 max_slots, w.rr_flags, ntickets, nzero_o, eps, nullptr, nullptr, nullptr, nullptr, nullptr);
