@@ -281,10 +281,9 @@ __device__ __forceinline__ bool pair_gate(double lj, double l0, int k, float omi
 }
 
 // ---- top-k of NT tokens per wave (NT = 1 or 2, processed side by side) -------------------
-// Lane l holds the candidates e = l + 64 i, i < NPER, of each token, sorted once by
-// (-logit, e); every round takes the wave maximum of the lanes' heads, finds the lane
-// holding it (exact ties between lanes go to the lowest expert index) and that lane
-// pops its head.  Empty candidates hold -inf and index 0x7FFFFFFF.
+// Lane l holds the candidates e = l + 64 i, i < NPER, of each token as selection keys,
+// sorted once; every round takes the wave maximum of the lanes' heads and the lane holding
+// it moves up its next candidate.
 // ---- top-k on 64-bit selection keys ----
 // key(v, e): the fp64 bits of v mapped to an unsigned integer of the same order (sign
 // bit flipped for v >= 0, all bits inverted for v < 0), with the low 10 bits replaced
