@@ -240,6 +240,15 @@ int moe_forward_timed(const moe_layer *L, const void *x, int32_t x_dtype, int32_
 int moe_dequant(int32_t wfmt, const void *packed, const int8_t *codebook, int32_t rows,
                 int32_t cols, float *out, void *stream);
 
+/* Test export of the grouped (prefill) path's CB4 decode: the same matrix decoded through
+ * the grouped kernels' own replicated codebook table and lookup, to the same bit-exact
+ * fp32 values as moe_dequant.  (The grouped MXFP4 kernels feed the stored E2M1 codes and
+ * E8M0 scales to the block-scaled matrix instruction as they are, so they decode nothing.)
+ * Errors: MOE_ERR_UNSUPPORTED for a format other than MOE_WFMT_CB4; otherwise as
+ * moe_dequant. */
+int moe_dequant_grouped(int32_t wfmt, const void *packed, const int8_t *codebook, int32_t rows,
+                        int32_t cols, float *out, void *stream);
+
 /* Helper between stacked layers (not part of the layer):
  * x_next[t][n] = bf16_rne(y[t][n] / sqrt(mean_n y[t][n]^2 + eps)), bf16 bits.
  * The sum of squares (exact squares, summed in a fixed order), the mean, the square

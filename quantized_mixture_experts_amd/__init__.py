@@ -23,8 +23,8 @@ DT_F32, DT_BF16 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 EXPORTED = ["moe_packed_bytes", "moe_workspace_bytes", "moe_router_topk", "moe_bucket", "moe_forward",
-            "moe_forward_timed", "moe_dequant", "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe",
-            "moe_forward_noalloc", "moe_status_str"]
+            "moe_forward_timed", "moe_dequant", "moe_dequant_grouped", "moe_rms_rescale", "moe_forward_rms",
+            "moe_hbm_read_probe", "moe_forward_noalloc", "moe_status_str"]
 STAGES = ["router", "topk", "bucket", "gateup", "down", "combine", "xquant"]
 
 
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [ctypes.POINTER(MoeLayerC), vp, i32, i32, vp, vp, sz, vp, i32, vp, vp, vp, vp, vp]
         L.moe_forward_timed.argtypes = [ctypes.POINTER(MoeLayerC), vp, i32, i32, vp, vp, sz, vp, i32, vp]
         L.moe_dequant.argtypes = [i32, vp, vp, i32, i32, vp, vp]
+        L.moe_dequant_grouped.argtypes = [i32, vp, vp, i32, i32, vp, vp]
         L.moe_rms_rescale.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
         L.moe_forward_rms.argtypes = [ctypes.POINTER(MoeLayerC), vp, ctypes.c_float, i32, i32, vp, vp, sz, vp, i32,
                                       vp]
@@ -67,7 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerC), vp, i32, i32, vp, vp, i32]
         L.moe_status_str.argtypes, L.moe_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         for f in ["moe_router_topk", "moe_bucket", "moe_forward", "moe_forward_timed", "moe_dequant",
-                  "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe", "moe_forward_noalloc"]:
+                  "moe_dequant_grouped", "moe_rms_rescale", "moe_forward_rms", "moe_hbm_read_probe",
+                  "moe_forward_noalloc"]:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -275,6 +277,15 @@ def dequant(wfmt: int, packed, rows: int, cols: int, codebook=None, stream=None)
     out = torch.empty((rows, cols), dtype=torch.float32, device=packed.device)
     _check(lib().moe_dequant(wfmt, packed.data_ptr(), _ptr(codebook), rows, cols, out.data_ptr(),
                              _stream(stream)), "moe_dequant")
+    return out
+
+
+def dequant_grouped(wfmt: int, packed, rows: int, cols: int, codebook=None, stream=None):
+    """moe_dequant_grouped: the grouped (prefill) kernels' CB4 decode of one packed matrix."""
+    import torch
+    out = torch.empty((rows, cols), dtype=torch.float32, device=packed.device)
+    _check(lib().moe_dequant_grouped(wfmt, packed.data_ptr(), _ptr(codebook), rows, cols, out.data_ptr(),
+                                     _stream(stream)), "moe_dequant_grouped")
     return out
 
 

@@ -352,6 +352,17 @@ int moe_dequant(int32_t wfmt, const void* packed, const int8_t* codebook, int32_
                                          static_cast<hipStream_t>(stream)));
 }
 
+int moe_dequant_grouped(int32_t wfmt, const void* packed, const int8_t* codebook, int32_t rows, int32_t cols,
+                        float* out, void* stream) {
+  if (wfmt != MOE_WFMT_CB4) return MOE_ERR_UNSUPPORTED;  // the grouped MXFP4 kernels decode nothing
+  if (rows <= 0 || cols <= 0 || cols % 32 || rows % 16) return MOE_ERR_INVALID_ARG;
+  if ((size_t)rows * (size_t)cols > ((size_t)1 << 34)) return MOE_ERR_UNSUPPORTED;
+  if (!packed || !out || !codebook) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moeq::launch_pf_dequant_cb4(static_cast<const uint8_t*>(packed), codebook, rows, cols, out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int moe_rms_rescale(const float* y, int32_t T, int32_t H, float eps, void* x_next_bf16, void* stream) {
   if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;

@@ -861,6 +861,48 @@ __global__ __launch_bounds__(256) void k_mx_xquant(const void* __restrict__ x, i
   }
 }
 
+// The grouped CB4 kernels' decode, exported for a bit-exact test: the replicated table
+// built as the projections build it (8 waves) at LDS offset 0, and every 32-value block of
+// a matrix decoded by one lane with pf_cb4x8, times the block's fp16 scale in fp32 (the
+// product of an int8 value and an fp16 scale needs at most 19 significant bits, so it is
+// exact, as the projections' fp32 scaling of an exact block sum is for one term).
+__global__ __launch_bounds__(64 * kPfWaves) void k_pf_dequant_cb4(const uint8_t* __restrict__ packed,
+                                                                  const int8_t* __restrict__ codebook, int rows,
+                                                                  int cols, float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  pf_build_lut<kPfWaves>((uint32_t*)smem, codebook);
+  __syncthreads();
+  const int nkb = cols >> 5;
+  const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= (size_t)rows * nkb) return;
+  const int row = (int)(blk / nkb), kb = (int)(blk % nkb);
+  const int m = row & 15;
+  const PackedTile pt = packed_tile<2>(packed, rows, cols, row >> 4);
+  const u32x4_t c = *(const __attribute__((address_space(1))) u32x4_t*)(pt.codes + pk_code(kb, m));
+  const float sc =
+      half_bits_to_f32(*(const __attribute__((address_space(1))) uint16_t*)(pt.scales + 2 * pk_scale_cb(kb, m, nkb)));
+  const uint32_t lane_off = 4u * (threadIdx.x & 63);
+  float* dst = out + blk * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8_t v = pf_cb4x8(c[q], lane_off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[8 * q + i] = sc * (float)v[i];
+  }
+}
+
+hipError_t launch_pf_dequant_cb4(const uint8_t* packed, const int8_t* codebook, int rows, int cols, float* out,
+                                 hipStream_t s) {
+  static const bool lds_ok = hipFuncSetAttribute((const void*)k_pf_dequant_cb4,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 kPfLutReplBytes) == hipSuccess;
+  (void)lds_ok;
+  const size_t nblk = (size_t)rows * (cols / 32);
+  hipLaunchKernelGGL(k_pf_dequant_cb4, dim3((unsigned)((nblk + 64 * kPfWaves - 1) / (64 * kPfWaves))),
+                     dim3(64 * kPfWaves), kPfLutReplBytes, s, packed, codebook, rows, cols, out);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 template <int FMT, int NP, int D, bool GATEUP, int SCL, int W>
 static void pf_launch(const LayerArgs& L, int T, const Work& w, const void* act, size_t act_plane_bytes, int RB,

@@ -62,6 +62,9 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype);
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y, float eps,
                          int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts, int32_t* dbg_offsets,
                          int32_t* dbg_perm, hipStream_t s, const Timing& tm);
+// the grouped (prefill) CB4 kernels' decode table and lookup over a whole matrix
+hipError_t launch_pf_dequant_cb4(const uint8_t* packed, const int8_t* codebook, int rows, int cols, float* out,
+                                 hipStream_t s);
 hipError_t launch_dequant(int wfmt, const uint8_t* packed, const int8_t* codebook, int rows, int cols,
                           float* out, hipStream_t s);
 hipError_t launch_rms_rescale(const float* y, int T, int H, float eps, uint16_t* out, hipStream_t s);

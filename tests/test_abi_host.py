@@ -133,6 +133,11 @@ def test_dequant_and_rescale_validation(L):
     assert L.moe_dequant(q.WFMT_MXFP4, FAKE, None, 4, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_dequant(q.WFMT_MXFP4, FAKE + 4, None, 16, 64, FAKE, None) == q.MOE_ERR_ALIGNMENT
     assert L.moe_dequant(9, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    # the grouped path's decode export: CB4 only, otherwise moe_dequant's checks
+    assert L.moe_dequant_grouped(q.WFMT_MXFP4, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_UNSUPPORTED
+    assert L.moe_dequant_grouped(q.WFMT_CB4, FAKE, None, 16, 64, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant_grouped(q.WFMT_CB4, FAKE, FAKE, 16, 48, FAKE, None) == q.MOE_ERR_INVALID_ARG
+    assert L.moe_dequant_grouped(q.WFMT_CB4, FAKE + 4, FAKE, 16, 64, FAKE, None) == q.MOE_ERR_ALIGNMENT
     assert L.moe_rms_rescale(FAKE, 2, 0, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_rms_rescale(None, 2, 8, 1e-6, FAKE, None) == q.MOE_ERR_INVALID_ARG
     assert L.moe_rms_rescale(FAKE, 0, 8, 1e-6, FAKE, None) == q.MOE_OK

@@ -68,6 +68,24 @@ def test_dequant_cb4_bit_exact_all_fp16_scales():
     assert np.array_equal(out.view(np.uint32), ref.astype(np.float32).view(np.uint32))
 
 
+def test_dequant_cb4_grouped_table_bit_exact():
+    """The grouped (prefill) kernels' own CB4 decode (their replicated codebook table and
+    lookup) over every fp16 scale pattern and every code, bit for bit against the oracle."""
+    rows, cols = 2048, 32 * 32
+    cb = synth.make_codebook(78, 0)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 10) & 31) != 31
+    bits = np.where(finite, bits, 0x3C00).astype(np.uint16)
+    buf = packing.pack(packing.CB4, codes, bits.reshape(rows, cols // 32))
+    out = q.dequant_grouped(q.WFMT_CB4, _dev(buf), rows, cols, codebook=_dev(cb)).cpu().numpy()
+    ref = oracle.dequant(oracle.WFMT_CB4, buf, cb, rows, cols)
+    assert np.array_equal(out.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+    with pytest.raises(q.MoeError):
+        q.dequant_grouped(q.WFMT_MXFP4, _dev(buf), rows, cols)
+
+
 # ---------------------------------------------------------------------------
 # routing and bucketing: exact
 # ---------------------------------------------------------------------------
