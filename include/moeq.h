@@ -6,14 +6,15 @@
  *     normalised weights ("Nebula" page, "How it works"; "How Neural runs a
  *     120-billion-parameter model on one gaming PC", section "How one token and
  *     one prompt are processed": the router emits expert ids and weights);
- *   - (token, expert) pairs are grouped by expert on the GPU and each selected
- *     expert's rows are read once for all of its tokens through a device table
- *     of expert base pointers (NInfer Qwen3.8-Flash-Next page, MoE execution
- *     notes; Neural page, "Prompt processing");
+ *   - the device sorts the (token, expert) pairs into per-expert groups and
+ *     streams each selected expert's weights once for all of its tokens, finding
+ *     them through a table of expert addresses held in device memory (NInfer
+ *     Qwen3.8-Flash-Next page, MoE execution notes; Neural page, "Prompt
+ *     processing");
  *   - each expert applies a fused gate/up projection, SwiGLU and a down
  *     projection, and the gate-weighted expert outputs are summed per token in a
- *     fixed order (NInfer page, MoE execution notes: the result must not depend
- *     on the order experts finish in), plus an optional always-on shared expert
+ *     fixed order (NInfer page, MoE execution notes: the sum is independent of
+ *     which expert completes first), plus an optional always-on shared expert
  *     ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers",
  *     "Architecture").
  *
@@ -145,8 +146,8 @@ typedef struct {
   float omit_below;            /* marginal-expert omission threshold tau in [0, 1]; 0: off (below) */
 } moe_layer;
 
-/* Marginal-expert omission ("Nebula" page, "Benchmark results": a 10% threshold for
- * omitting marginal experts; the renormalisation is this library's reading).  With
+/* Marginal-expert omission ("Nebula" page, "Benchmark results": experts under a
+ * 10% gate are dropped as marginal; the renormalisation is this library's reading).  With
  * omit_below = tau > 0, after the top-k softmax a routed pair j > 0 whose gate
  * g[t,j] < tau (compared in fp64) is omitted: it reports expert id -1 and weight 0, is in
  * no bucket and contributes nothing; the kept gates are renormalised to sum to 1,

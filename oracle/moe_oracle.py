@@ -15,17 +15,17 @@ What the layer computes, in the order the pages describe it:
   prompt are processed": the router kernels emit 4 expert ids and 4 weights);
 * (token, expert) pairs are grouped by expert, and each selected expert is read
   once for all of its tokens (NInfer Qwen3.8-Flash-Next page, MoE execution
-  notes: pairs grouped by expert on the GPU, one pass over each selected
-  expert's rows for all of its tokens; Neural page, "Prompt processing":
-  tokens are grouped by expert on the GPU);
+  notes: the pairs are sorted by expert on the device and an expert's weights
+  serve every token routed to it; Neural page, "Prompt processing": the
+  device groups tokens by expert);
 * each expert runs a fused gate/up projection, the middle activation, and a
   down projection (NInfer page, MoE execution notes: the fused gate/up kernel
   and the down pass row by row over all of a token's experts);
 * the weighted expert outputs are summed per token (NInfer page, MoE execution
-  notes: weighted expert outputs are summed so the result does not depend on
-  the order experts finish in), plus an always-on shared expert where the layer
-  has one ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers",
-  "Architecture": 512 routed experts plus one shared expert per layer).
+  notes: the sum of the weighted outputs is independent of which expert
+  completes first), plus an always-on shared expert where the layer has one
+  ("Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers",
+  "Architecture": each layer has 512 routed experts and a single shared one).
 
 Where the pages leave a step open the plainest reading is taken:
 
@@ -154,8 +154,8 @@ def packed_scale_store_exponents(packed: np.ndarray, rows: int, cols: int) -> np
     row followed by one 4-bit delta per block, each block's E8M0 byte being base + delta
     ("How Neural runs a 120-billion-parameter model on one gaming PC", section "What it
     runs on and what it runs": 12,839,040 bytes per expert in the packed-scale store
-    against 13,219,200 raw; section "Correctness": the packed store re-encodes the scale
-    rows and outputs are bit-identical).  The page gives the byte count and the identity;
+    against 13,219,200 raw; section "Correctness": only the scales are stored in a new
+    encoding and the outputs match bit for bit).  The page gives the byte count and the identity;
     the placement is this reading's: at the raw store's scale-plane offset S, the bases
     as N bytes in row order, then the deltas, one nibble per block, at nibble index equal
     to the block's index in the raw MXFP4 scale plane (storage_index), byte S + N + i // 2,
@@ -290,8 +290,8 @@ def shared_weights(x64: np.ndarray, shared_gate_w) -> np.ndarray:
 
 
 def omit_marginal(ids: np.ndarray, gates: np.ndarray, tau: float):
-    """Marginal-expert omission ("Nebula" page, "Benchmark results": a 10% threshold for
-    omitting marginal experts).  The page gives the threshold, not what happens to the
+    """Marginal-expert omission ("Nebula" page, "Benchmark results": experts under a
+    10% gate are dropped as marginal).  The page gives the threshold, not what happens to the
     remaining weights; the reading taken: a routed pair whose softmax gate is below tau is
     left out (the first, largest one never is), and the kept gates are renormalised to sum
     to 1.  Omitted pairs get id -1 and gate 0.  tau = 0 keeps every pair unchanged."""

@@ -7,8 +7,9 @@
 // reduction.  In the fused gate/up kernel a wave holds 32 gate rows and the 32
 // matching up rows, so SwiGLU is applied in registers.  Each selected expert's rows
 // are read from HBM once per group (once in total when it has at most 64 pairs), the
-// grouping the NInfer Qwen3.8-Flash-Next page describes for its MoE execution (pairs
-// grouped by expert, one pass over each selected expert's rows for all its tokens).
+// grouping the NInfer Qwen3.8-Flash-Next page describes for its MoE execution: the
+// routed pairs are sorted into per-expert groups and an expert's weights are streamed
+// once for every token routed to it.
 //
 // Pipeline (k-step = 128 columns):
 //   - activations: the group's 64 rows are copied into LDS one k-step chunk at a time

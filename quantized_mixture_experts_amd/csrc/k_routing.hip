@@ -3,8 +3,8 @@
 //
 // The router emits, per token, k expert ids and their normalised weights ("Nebula"
 // page, "How it works"; "How Neural runs a 120-billion-parameter model on one gaming
-// PC", "How one token and one prompt are processed").  Pairs are grouped by expert on
-// the GPU, with no host synchronisation (NInfer Qwen3.8-Flash-Next page, MoE
+// PC", "How one token and one prompt are processed").  The device sorts the pairs into
+// per-expert groups itself, with no host synchronisation (NInfer Qwen3.8-Flash-Next page, MoE
 // execution notes; the Neural page's "Prompt processing" counts a host-side routing
 // sync among its costs, which this design avoids).
 #include "device.h"

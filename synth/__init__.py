@@ -326,7 +326,7 @@ CONFIGS = {
     "c5a": LayerSpec("c5a_prefill_cb4", T=1024, hidden=2048, inter=512, n_experts=256, top_k=8,
                      has_shared=1, weights=_CB4, x_dtype=X_BF16, router_std=0.02, bias="none", seed=1005),
     # the layer of "Running Qwen3.8-Flash-Next on a 32 GB Mac with Transformers" (hidden
-    # 2,560, 512 routed experts, top-10, intermediate 640, one shared expert) with its
+    # 2,560, 512 routed experts of which 10 are kept, intermediate 640, one shared expert) with its
     # 3-bit affine group-64 experts, at the verify window's 17 tokens
     "aff3": LayerSpec("aff3_flashnext_3bit_verify", T=17, hidden=2560, inter=640, n_experts=512, top_k=10,
                       has_shared=1, weights=WeightSpec(WFMT_AFF3, 0.01, 0.05), x_dtype=X_BF16, router_std=0.02,

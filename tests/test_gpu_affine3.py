@@ -93,7 +93,7 @@ def test_affine3_chunked_batches(q, T):
 
 
 def test_affine3_page_layer_verify_window(q):
-    """The Mac page's layer (hidden 2,560, 512 routed experts, top-10, intermediate 640,
+    """The Mac page's layer (hidden 2,560, 512 routed experts of which 10 are kept, intermediate 640,
     a shared expert) with its 3-bit experts at the 17-token verify window, in full."""
     spec = synth.CONFIGS["aff3"]
     layer = synth.make_layer(spec)

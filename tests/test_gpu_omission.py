@@ -1,5 +1,5 @@
-"""GPU parity of marginal-expert omission ("Nebula" page, "Benchmark results": a 10 %
-threshold for omitting marginal experts): routed pairs whose gate is below the
+"""GPU parity of marginal-expert omission ("Nebula" page, "Benchmark results": experts
+whose gate falls under 10 % are dropped as marginal): routed pairs whose gate is below the
 threshold are left out and the kept gates renormalised, on every kernel path, against
 the oracle's omission."""
 import dataclasses

@@ -1,8 +1,8 @@
 """GPU parity of the MXFP4 packed scale store (one base E8M0 byte per row plus a 4-bit
 delta per block): decoding is bit-exact against the oracle, and the layer gives the same
 y bits as the raw MXFP4 store of the same codes and scales on every kernel path ("How
-Neural runs a 120-billion-parameter model on one gaming PC", section "Correctness": the
-packed store re-encodes the scale rows and outputs are bit-identical)."""
+Neural runs a 120-billion-parameter model on one gaming PC", section "Correctness": only
+the scales change encoding in the packed store, and the outputs match bit for bit)."""
 import dataclasses
 
 import numpy as np

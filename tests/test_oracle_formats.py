@@ -241,7 +241,7 @@ def test_bf16_rounding_two_implementations():
 # ---------------------------------------------------------------------------
 def test_affine3_size_is_the_pages():
     """An expert of the page's model (hidden 2,560, intermediate 640) in 3-bit codes with
-    a 16-bit scale and bias per 64 values: 3.5 bits per weight, 2,150,400 B, the page's
+    one 16-bit scale and one 16-bit bias for each group of 64 values: 3.5 bits per weight, 2,150,400 B, the page's
     2.15 MB per expert."""
     g = json.load(open(os.path.join(GOLDEN, "page_byte_counts.json")))["affine3_expert_bytes"]
     H, I = g["shape"]["hidden"], g["shape"]["inter"]
