@@ -59,8 +59,8 @@ int validate_layer(const moe_layer* L) {
 }
 
 struct Layout {
-  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, xr, o, tickets, slots, groups,
-      n_groups, total;
+  size_t logits, ids, pair_w, counts, offsets, perm, active, xplanes, hplanes, xr, o, tickets, slots, items, n_items,
+      groups, n_groups, total;
 };
 
 Layout layout_for(const moe_layer* L, int32_t T) {
@@ -87,6 +87,8 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
+  o.items = take((P + 1) * sizeof(moeq::Slot));  // at most one staging pass per pair
+  o.n_items = take(4);
   o.groups = take((size_t)moeq::max_groups((int)P, (int)E) * 16);
   o.n_groups = take(4);
   o.total = at;
@@ -110,6 +112,8 @@ Work carve(void* ws, const Layout& lo) {
   w.xr = reinterpret_cast<uint16_t*>(b + lo.xr);
   w.tickets = reinterpret_cast<uint32_t*>(b + lo.tickets);
   w.slots = reinterpret_cast<moeq::Slot*>(b + lo.slots);
+  w.items = reinterpret_cast<moeq::Slot*>(b + lo.items);
+  w.n_items = reinterpret_cast<int32_t*>(b + lo.n_items);
   w.hf32 = reinterpret_cast<float*>(b + lo.hplanes);
   w.xq = b + lo.xplanes;
   w.hq = b + lo.hplanes;

@@ -104,6 +104,9 @@ struct Work {
   uint8_t* xq;         // MXFP4 prefill: fp8 planes [NPX][T][Hp] + [T] E8M0 row scales (aliases xplanes)
   uint8_t* hq;         // MXFP4 prefill: fp8 planes [3][P][Ip] + [P][Ip/256] E8M0 chunk scales (aliases hplanes)
   struct Slot* slots;  // [min(T*k, E) + 1] decode work records, one per active-expert slot
+  struct Slot* items;  // [P] decode gate/up work items: one record per staging pass of an
+                       // active expert (its pairs off .. off + cnt)
+  int32_t* n_items;    // [1] number of valid entries of items
   int4* groups;        // prefill work groups: (expert, first bucket position, pairs <= 64, 0)
   int32_t* n_groups;   // [1] number of valid entries of groups
   uint32_t* rr_flags;  // decode router arrival flags, one per block: in the workspace's fixed

@@ -307,11 +307,24 @@ __device__ __forceinline__ void load_bucket_ptrs(const LayerArgs& L, BucketPtrs<
 // A token's routed experts are distinct, so the stable rank of pair p (of token t) in its
 // bucket, the number of earlier pairs in the same bucket, is the number of earlier tokens
 // in it: popcount(s_tmask[e] & (2^t - 1)).
+// The gate/up work items: pass j of an active expert (its pairs j xg .. j xg + xg - 1) is
+// item record w.items[q] with the expert's passes on consecutive q, in expert order, and
+// *w.n_items their number (at most max_items, the host's bound that sizes the gate/up
+// grid).  Quotients by xg (at most 32) of numbers below 1,024 are (n m) >> 20 with
+// m = 2^20 / xg + 1, exact in that range.
+// The bucket scan runs on one packed word per bucket: pairs (bits 0..9), non-empty
+// buckets (bits 10..20) and staging passes (bits 21..30); none of the three totals can
+// reach its field's limit (at most 544 pairs and passes, 1,025 buckets).
+static_assert(kMaxPairsDec < 1024, "packed bucket scan");
+__device__ __forceinline__ int incl_pairs(int x) { return x & 0x3FF; }
+__device__ __forceinline__ int incl_active(int x) { return (x >> 10) & 0x7FF; }
+__device__ __forceinline__ int incl_items(int x) { return (int)((uint32_t)x >> 21); }
 template <int NPP>
-__device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots,
-                                               const int* s_exp, int* s_cnt, uint32_t* s_tmask, int* s_incl,
-                                               const BucketPtrs<NPP>& bp, int32_t* __restrict__ dbg_counts,
-                                               int32_t* __restrict__ dbg_offsets, int32_t* __restrict__ dbg_perm) {
+__device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const Work& w, int max_slots, int xg,
+                                               int max_items, const int* s_exp, int* s_cnt, uint32_t* s_tmask,
+                                               int* s_incl, const BucketPtrs<NPP>& bp,
+                                               int32_t* __restrict__ dbg_counts, int32_t* __restrict__ dbg_offsets,
+                                               int32_t* __restrict__ dbg_perm) {
   __shared__ int s_ctot[(1024 + 1 + 63) / 64];  // each 64-bucket chunk's sum
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = (int)blockDim.x;
   const int E = L.E, k = L.k;
@@ -326,14 +339,15 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     }
   }
   __syncthreads();
-  // inclusive scan of (count, non-empty flag) over the buckets: every wave scans 64-bucket
-  // chunks (DPP row shifts inside 16-lane rows, then the row totals), then each bucket
-  // adds the sums of the chunks before its own
+  // inclusive scan of (count, non-empty flag, passes) over the buckets: every wave scans
+  // 64-bucket chunks (DPP row shifts inside 16-lane rows, then the row totals), then each
+  // bucket adds the sums of the chunks before its own
+  const uint32_t xgm = (1u << 20) / (uint32_t)xg + 1u;
   const int nchunks = (nb + 63) >> 6;
   for (int c = wave; c < nchunks; c += nthr >> 6) {
     const int i = 64 * c + lane;
     const int cv = i < nb ? s_cnt[i] : 0;
-    int x = cv | ((cv > 0 ? 1 : 0) << 16);
+    int x = cv | ((cv > 0 ? 1 : 0) << 10) | (int)(((uint32_t)(cv + xg - 1) * xgm >> 20) << 21);
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
     x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
     x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
@@ -352,25 +366,34 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     s_incl[i] += pre;
   }
   __syncthreads();
-  const int n_active = s_incl[nb - 1] >> 16;
-  const int placed = s_incl[nb - 1] & 0xFFFF;  // pairs in the buckets (omitted ones are not)
+  const int n_active = incl_active(s_incl[nb - 1]);
+  const int placed = incl_pairs(s_incl[nb - 1]);  // pairs in the buckets (omitted ones are not)
+  const int n_items = incl_items(s_incl[nb - 1]);
 #pragma unroll
   for (int u = 0; u < NPP; ++u) {
     const int e = tid + u * nthr;
     if (e >= nb) break;
     const int c = s_cnt[e];
-    const int off = (s_incl[e] & 0xFFFF) - c;
+    const int off = incl_pairs(s_incl[e]) - c;
     w.counts[e] = c;
     w.offsets[e] = off;
     if (dbg_counts) dbg_counts[e] = c;
     if (dbg_offsets) dbg_offsets[e] = off;
     if (c > 0) {
-      const int a = (s_incl[e] >> 16) - 1;
+      const int a = incl_active(s_incl[e]) - 1;
       w.active[1 + a] = e;
       Slot& sl = w.slots[a];
       sl.e = e; sl.cnt = c; sl.off = off; sl.n_active = n_active;
       sl.gate_up = bp.gu[u];
       sl.down = bp.dn[u];
+      const int np = (int)((uint32_t)(c + xg - 1) * xgm >> 20);
+      const int q0 = incl_items(s_incl[e]) - np;
+      for (int j = 0; j < np && q0 + j < max_items; ++j) {  // (the bound holds for every routing)
+        Slot& it = w.items[q0 + j];
+        it.e = e; it.cnt = min(xg, c - j * xg); it.off = off + j * xg; it.n_active = n_active;
+        it.gate_up = bp.gu[u];
+        it.down = bp.dn[u];
+      }
     }
   }
   for (int a = n_active + tid; a < max_slots; a += nthr) {
@@ -383,6 +406,7 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     w.offsets[nb] = placed;
     if (dbg_offsets) dbg_offsets[nb] = placed;
     w.active[0] = n_active;
+    *w.n_items = min(n_items, max_items);
   }
   for (int i = placed + tid; i < P; i += nthr) {  // past the placed pairs
     w.perm[i] = -1;
@@ -392,10 +416,14 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
     const int e = s_exp[p];
     if (e < 0) continue;
     const int r = __popc(s_tmask[e] & ((1u << dec_token_of_pair(p, T, k)) - 1u));  // stable rank
-    const int pos = (s_incl[e] & 0xFFFF) - s_cnt[e] + r;
+    const int c = s_cnt[e];
+    const int pos = incl_pairs(s_incl[e]) - c + r;
     w.perm[pos] = p;
     if (dbg_perm) dbg_perm[pos] = p;
-    if (r < kSlotRows) w.slots[(s_incl[e] >> 16) - 1].rows[r] = p;
+    if (r < kSlotRows) w.slots[incl_active(s_incl[e]) - 1].rows[r] = p;
+    const int j = (int)((uint32_t)r * xgm >> 20), rj = r - j * xg;
+    const int q = incl_items(s_incl[e]) - (int)((uint32_t)(c + xg - 1) * xgm >> 20) + j;
+    if (rj < kSlotRows && q < max_items) w.items[q].rows[rj] = p;
   }
 }
 
@@ -409,7 +437,8 @@ __device__ __forceinline__ void dec_route_tail(const LayerArgs& L, int T, const 
 // the mailbox entries or flags so that the header reads zero again after the call.
 template <int XDT, bool MBOX, bool ROUTE>
 __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const void* __restrict__ x, int T, int erows,
-                                                          Work w, int max_slots, uint32_t* __restrict__ rr_flags,
+                                                          Work w, int max_slots, int xg, int max_items,
+                                                          uint32_t* __restrict__ rr_flags,
                                                           int ntickets, int nzero_o, float eps,
                                                           int32_t* __restrict__ dbg_ids,
                                                           float* __restrict__ dbg_w, int32_t* __restrict__ dbg_counts,
@@ -419,7 +448,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
   __shared__ double s_l[kMaxPairsDec];  // its logit (routed pairs)
   __shared__ int s_cnt[1024 + 1];
   __shared__ uint32_t s_tmask[1024 + 1];  // tokens with a pair in each bucket
-  __shared__ int s_incl[1024 + 1];      // inclusive scan: count (low 16 bits), non-empty flags (high)
+  __shared__ int s_incl[1024 + 1];      // inclusive scan of the packed (pairs, buckets, passes)
   __shared__ double s_part[kRouteThreads / 64][kDecMaxTokens];
   __shared__ double s_sg[kDecMaxTokens];  // shared-gate logits read from the mailbox
   __shared__ int s_flag;                // something this block needs has not arrived
@@ -666,7 +695,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_dec_rr(LayerArgs L, const voi
     }
   }
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, xg, max_items, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets,
+                 dbg_perm);
 }
 
 
@@ -693,7 +723,8 @@ constexpr int kTopkRouteThreads = 256;  // 4 tokens per block
 static_assert(2 * kRouteThreads > 1024 && 5 * kTopkRouteThreads > 1024, "bucket pointer prefetch");
 
 __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs L, int T, Work w, int nsplit,
-                                                                      int max_slots, int ntickets,
+                                                                      int max_slots, int xg, int max_items,
+                                                                      int ntickets,
                                                                       int32_t* __restrict__ dbg_ids,
                                                                       float* __restrict__ dbg_w,
                                                                       int32_t* __restrict__ dbg_counts,
@@ -768,7 +799,8 @@ __global__ __launch_bounds__(kTopkRouteThreads) void k_dec_topk_route(LayerArgs 
   for (int p = tid; p < P; p += kTopkRouteThreads)
     s_exp[p] = p < Pr ? __hip_atomic_load(&w.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : E;
   __syncthreads();
-  dec_route_tail(L, T, w, max_slots, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets, dbg_perm);
+  dec_route_tail(L, T, w, max_slots, xg, max_items, s_exp, s_cnt, s_tmask, s_incl, bp, dbg_counts, dbg_offsets,
+                 dbg_perm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1404,11 +1436,13 @@ __device__ __forceinline__ void dec_gateup_item(const LayerArgs& L, int T, const
   }
 }
 
-// Gate/up projection, grid (I/16, slots x passes).  Block row y takes pass y % npass of
-// slot y / npass (pairs xrows_max (y % npass) ..), so an expert with more pairs than one
-// pass stages has its passes run side by side on adjacent rows; rows past a slot's pairs
-// exit at once.  SR (one token, one pass): the block routes itself (dec_self_route),
-// staging the token's row meanwhile, and keeps its slot record in LDS.
+// Gate/up projection, grid (I/16, work items).  Block row y takes work item y of the
+// routing (one staging pass of one active expert; an expert with more pairs than one pass
+// stages has its passes on adjacent rows); rows past the last item exit at once.  The
+// grid's item count is the host's bound over every routing, so few rows exit (the verify
+// window: 139 rows instead of 137 slots x 3 passes).  SR (one token, one pass; grid (I/16,
+// slots)): the block routes itself (dec_self_route), staging the token's row meanwhile,
+// and keeps its slot record in LDS.
 template <int FMT, int NP, int NTT, int KSW, bool SR>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work w, const uint16_t* __restrict__ act,
                                                        size_t act_plane, int xrows_max, int nslots,
@@ -1436,13 +1470,13 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(LayerArgs L, int T, Work 
     dec_gateup_item<FMT, NP, NTT, KSW, SR>(L, T, w, act, act_plane, xrows_max, &s_rec, blockIdx.x, 0, xrows_max,
                                            smem, s_lut);
   } else {
-    const int npass = (int)gridDim.y / nslots;
-    const Slot* sr = w.slots + blockIdx.y / npass;
-    const int tb0 = (int)(blockIdx.y % npass) * xrows_max;
-    if (tb0 >= sr->cnt) return;
+    const Slot* sr = w.items + blockIdx.y;
+    // the count and the record are loaded together; rows past the count exit
+    const int cnt = sr->cnt, ni = *w.n_items;
+    if ((int)blockIdx.y >= ni || cnt == 0) return;
     if (FMT == 2) build_cb4_lut(s_lut, L.codebook);  // ordered before use by the staging barrier
-    dec_gateup_item<FMT, NP, NTT, KSW, SR>(L, T, w, act, act_plane, xrows_max, sr, blockIdx.x, tb0,
-                                           npass * xrows_max, smem, s_lut);
+    dec_gateup_item<FMT, NP, NTT, KSW, SR>(L, T, w, act, act_plane, xrows_max, sr, blockIdx.x, 0, xrows_max, smem,
+                                           s_lut);
   }
 }
 
@@ -1810,10 +1844,9 @@ struct DbgOut {
 
 template <int FMT, int NTT, int KSW, bool SR>
 static void launch_gateup_sr(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
-                             const DbgOut& d, hipStream_t s, const Timing& tm) {
+                             int max_items, const DbgOut& d, hipStream_t s, const Timing& tm) {
   const int nslots = min(T * L.k, L.E) + (L.has_shared ? 1 : 0);
-  const int npass = (T + xrows - 1) / xrows;  // a slot holds at most T pairs
-  const dim3 g1(L.I / 16, nslots * npass);
+  const dim3 g1(L.I / 16, SR ? nslots : max_items);
   if (x_dtype == 1)
     MOEQ_LAUNCH(tm, kStageGateUp, (k_dec_gateup<FMT, 1, NTT, KSW, SR>), g1, dim3(256),
                 dec_lds_bytes(FMT, L.H, 1, NTT, xrows), s, L, T, w, (const uint16_t*)x, (size_t)0, xrows, nslots, d.ids,
@@ -1824,10 +1857,10 @@ static void launch_gateup_sr(const LayerArgs& L, const void* x, int x_dtype, int
                 nslots, d.ids, d.w, d.counts, d.offsets, d.perm);
 }
 template <int FMT, int NTT, int KSW>
-static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows, bool sr,
-                            const DbgOut& d, hipStream_t s, const Timing& tm) {
-  if (sr) launch_gateup_sr<FMT, NTT, KSW, true>(L, x, x_dtype, T, w, xrows, d, s, tm);
-  else launch_gateup_sr<FMT, NTT, KSW, false>(L, x, x_dtype, T, w, xrows, d, s, tm);
+static void launch_gateup_k(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
+                            int max_items, bool sr, const DbgOut& d, hipStream_t s, const Timing& tm) {
+  if (sr) launch_gateup_sr<FMT, NTT, KSW, true>(L, x, x_dtype, T, w, xrows, max_items, d, s, tm);
+  else launch_gateup_sr<FMT, NTT, KSW, false>(L, x, x_dtype, T, w, xrows, max_items, d, s, tm);
 }
 
 // Down rows of at most this many 128-column k-steps take the short-row kernel (each wave
@@ -1895,16 +1928,24 @@ static int dec_rows_per_pass(int K, int NP, int T, size_t budget = kDecStageByte
   const int cap = (int)(budget / row) - 1;  // and the zero row
   return max(1, min(T, min(cap, kDecMaxTokens)));
 }
+// Bound on the gate/up work items (staging passes of xg pairs) over every routing of T
+// tokens: A <= min(T k, E) routed experts holding at most T k pairs in all take at most
+// sum ceil(c / xg) <= (T k + A (xg - 1)) / xg passes; the shared expert takes ceil(T / xg).
+// At most T k + T: the workspace holds that many item records.
+static int dec_max_items(const LayerArgs& L, int T, int xg) {
+  const int pr = T * L.k, a = min(pr, L.E);
+  return (pr + a * (xg - 1)) / xg + (L.has_shared ? (T + xg - 1) / xg : 0);
+}
 
 template <int FMT, int NTT>
-static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows, bool sr,
-                              const DbgOut& d, hipStream_t s, const Timing& tm) {
+static void launch_dec_gateup(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, int xrows,
+                              int max_items, bool sr, const DbgOut& d, hipStream_t s, const Timing& tm) {
   switch (pick_ksw(L.H)) {
-    case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
-    case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
-    case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
-    case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
-    default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, sr, d, s, tm); break;
+    case 1: launch_gateup_k<FMT, NTT, 1>(L, x, x_dtype, T, w, xrows, max_items, sr, d, s, tm); break;
+    case 2: launch_gateup_k<FMT, NTT, 2>(L, x, x_dtype, T, w, xrows, max_items, sr, d, s, tm); break;
+    case 4: launch_gateup_k<FMT, NTT, 4>(L, x, x_dtype, T, w, xrows, max_items, sr, d, s, tm); break;
+    case 6: launch_gateup_k<FMT, NTT, 6>(L, x, x_dtype, T, w, xrows, max_items, sr, d, s, tm); break;
+    default: launch_gateup_k<FMT, NTT, 8>(L, x, x_dtype, T, w, xrows, max_items, sr, d, s, tm); break;
   }
 }
 
@@ -1932,12 +1973,11 @@ static void launch_dec_down(const LayerArgs& L, int T, const Work& w, float* y, 
 // Token tiles per pass follow the rows staged per pass (16 or 32).
 template <int FMT>
 static hipError_t launch_dec_experts(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y,
-                                     uint32_t* tickets, bool omb, bool sr, const DbgOut& d, hipStream_t s,
-                                     const Timing& tm) {
-  const int xg = dec_rows_per_pass(L.H, x_dtype == 1 ? 1 : 3, T, dec_gateup_stage_bytes(FMT));
+                                     uint32_t* tickets, bool omb, bool sr, int xg, int max_items, const DbgOut& d,
+                                     hipStream_t s, const Timing& tm) {
   const int xd = dec_rows_per_pass(L.I, 2, T, dec_down_stage_bytes(L.I));
-  if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, sr, d, s, tm);
-  else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, false, d, s, tm);
+  if (xg <= 16) launch_dec_gateup<FMT, 1>(L, x, x_dtype, T, w, xg, max_items, sr, d, s, tm);
+  else launch_dec_gateup<FMT, 2>(L, x, x_dtype, T, w, xg, max_items, false, d, s, tm);
   if (xd <= 16) launch_dec_down<FMT, 1>(L, T, w, y, tickets, xd, omb, s, tm);
   else launch_dec_down<FMT, 2>(L, T, w, y, tickets, xd, false, s, tm);
   return hipGetLastError();
@@ -1954,20 +1994,24 @@ bool decode_path_fits(const LayerArgs& L, int T, int x_dtype) {
 }
 
 template <int XDT>
-static void launch_rr(const LayerArgs& L, const void* x, int T, int erows, const Work& w, int max_slots, int ntickets,
-                      int nzero_o, float eps, bool sr, int32_t* dbg_ids, float* dbg_w, int32_t* dbg_counts,
-                      int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s, const Timing& tm) {
+static void launch_rr(const LayerArgs& L, const void* x, int T, int erows, const Work& w, int max_slots, int xg,
+                      int max_items, int ntickets, int nzero_o, float eps, bool sr, int32_t* dbg_ids, float* dbg_w,
+                      int32_t* dbg_counts, int32_t* dbg_offsets, int32_t* dbg_perm, hipStream_t s,
+                      const Timing& tm) {
   const int rows = sr ? router_rows<false>() : router_rows<true>();
   const dim3 grid((erows + rows - 1) / rows);
   if (sr)  // logits only: the gate/up kernel routes
     MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false, false>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                max_slots, w.rr_flags, ntickets, nzero_o, eps, nullptr, nullptr, nullptr, nullptr, nullptr);
+                max_slots, xg, max_items, w.rr_flags, ntickets, nzero_o, eps, nullptr, nullptr, nullptr, nullptr,
+                nullptr);
   else if (T * (L.E + 1) <= kDecMailboxWords)
     MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, true, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                max_slots, xg, max_items, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts,
+                dbg_offsets, dbg_perm);
   else
     MOEQ_LAUNCH(tm, kStageRouter, (k_dec_rr<XDT, false, true>), grid, dim3(kRouteThreads), 0, s, L, x, T, erows, w,
-                max_slots, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                max_slots, xg, max_items, w.rr_flags, ntickets, nzero_o, eps, dbg_ids, dbg_w, dbg_counts,
+                dbg_offsets, dbg_perm);
 }
 
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, const Work& w, float* y, float eps,
@@ -1992,30 +2036,34 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_dtype, int T, 
   // one token: the router kernel stores the logits and the gate/up blocks route themselves
   const bool sr = T == 1 && L.E <= kSelfRouteMaxE;
   const DbgOut d{dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm};
+  // the gate/up staging pass and the bound on its work items, for the route
+  const int xg = dec_rows_per_pass(L.H, xdp == 1 ? 1 : 3, T, dec_gateup_stage_bytes(L.wfmt));
+  const int max_items = dec_max_items(L, T, xg);
   if (T >= kDecSplitRouteT) {
     // the fp64 matrix-core router, then one wave per token for the top-k, the last block
     // to finish routing
     hipError_t e = launch_router(L, xp, xdp, T, w, s, tm);
     if (e != hipSuccess) return e;
     MOEQ_LAUNCH(tm, kStageTopk, k_dec_topk_route, dim3((T + 3) / 4), dim3(kTopkRouteThreads), 0, s, L, T, w,
-                router_splits(T, L.H), max_slots, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets, dbg_perm);
+                router_splits(T, L.H), max_slots, xg, max_items, ntickets, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
+                dbg_perm);
   } else if (x_dtype == 0) {
-    launch_rr<0>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
-                 dbg_perm, s, tm);
+    launch_rr<0>(L, x, T, erows, w, max_slots, xg, max_items, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts,
+                 dbg_offsets, dbg_perm, s, tm);
   } else if (x_dtype == 1) {
-    launch_rr<1>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
-                 dbg_perm, s, tm);
+    launch_rr<1>(L, x, T, erows, w, max_slots, xg, max_items, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts,
+                 dbg_offsets, dbg_perm, s, tm);
   } else {
-    launch_rr<2>(L, x, T, erows, w, max_slots, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts, dbg_offsets,
-                 dbg_perm, s, tm);
+    launch_rr<2>(L, x, T, erows, w, max_slots, xg, max_items, ntickets, nzero_o, eps, sr, dbg_ids, dbg_w, dbg_counts,
+                 dbg_offsets, dbg_perm, s, tm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (L.wfmt) {
-    case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
-    case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
-    case 4: return launch_dec_experts<4>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
-    default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, sr, d, s, tm);
+    case 1: return launch_dec_experts<1>(L, xp, xdp, T, w, y, w.tickets, omb, sr, xg, max_items, d, s, tm);
+    case 3: return launch_dec_experts<3>(L, xp, xdp, T, w, y, w.tickets, omb, sr, xg, max_items, d, s, tm);
+    case 4: return launch_dec_experts<4>(L, xp, xdp, T, w, y, w.tickets, omb, sr, xg, max_items, d, s, tm);
+    default: return launch_dec_experts<2>(L, xp, xdp, T, w, y, w.tickets, omb, sr, xg, max_items, d, s, tm);
   }
 }
 
