@@ -270,6 +270,34 @@ def test_decode_down_two_tiles(wfmt, T):
     check_forward(layer, x, spec.x_dtype, y, dbg, what=f"two-tile down T={T} wfmt={wfmt}")
 
 
+@pytest.mark.parametrize("case,wfmt,T,H,I,E,k", [
+    ("same", synth.WFMT_CB4, 32, 2048, 512, 64, 4),        # 32 pairs per expert, 7 rows a pass: 5 passes each
+    ("same_wide", synth.WFMT_CB4, 32, 256, 256, 64, 4),    # one 32-row pass: rows past the record's 24 from perm
+    ("same", synth.WFMT_MXFP4, 24, 2880, 256, 32, 4),      # 24 pairs per expert, 7 rows a pass: 4 passes each
+    ("distinct", synth.WFMT_MXFP4, 32, 512, 256, 1024, 8),  # nearly every pair its own expert: the item bound
+])
+def test_decode_work_items_at_the_bounds(case, wfmt, T, H, I, E, k):
+    """The decode gate/up grid has one row per work item (one staging pass of one active
+    expert) up to a bound over every routing.  "same": a router bias of +50 sends every
+    token to experts 0..k-1, so each takes T pairs in several passes (and the shared expert
+    as many); "distinct": 256 pairs over 1,024 experts with no bias, so most pairs have an
+    expert of their own and the item count approaches its bound."""
+    spec = synth.small_spec(f"items_{case}_{T}_{H}", T, H, I, E, k, wfmt, has_shared=1, x_dtype=synth.X_BF16,
+                            bias="none" if case == "distinct" else "normal", seed=500 + T + H)
+    layer = synth.make_layer(spec)
+    if case.startswith("same"):
+        rb = np.zeros(E, dtype=np.float32)
+        rb[:k] = 50.0 + np.arange(k, dtype=np.float32)
+        layer.router_b = rb
+    layer, x, dl, y, dbg = _run(spec, layer=layer, path=1)
+    ids = dbg["ids"].cpu().numpy().reshape(T, k)
+    if case.startswith("same"):
+        assert (np.sort(ids, axis=1) == np.arange(k)).all()
+    else:
+        assert len(np.unique(ids)) > 0.7 * T * k
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"work items {case} T={T} H={H} wfmt={wfmt}")
+
+
 @pytest.mark.parametrize("wfmt", [synth.WFMT_MXFP4, synth.WFMT_CB4])
 @pytest.mark.parametrize("T,path,H", [(1, 0, 512), (4, 0, 512), (7, 0, 512), (9, 0, 512), (40, 0, 512), (4, 2, 512),
                                       (1, 0, 6144), (4, 0, 6144)])
