@@ -124,7 +124,7 @@ typedef enum { MOE_WFMT_MXFP4 = 1, MOE_WFMT_CB4 = 2, MOE_WFMT_MXFP4_PS = 3, MOE_
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Path selection for moe_forward: AUTO picks the decode kernels for small batches
- * (up to 7 tokens for MXFP4 layers and 32 for CB4 layers, where they are faster)
+ * (up to 10 tokens for MXFP4 layers and 32 for CB4 layers, where they are faster)
  * and the grouped-GEMM prefill kernels otherwise; the other two force one path
  * (both compute the same layer; DECODE accepts up to 32 tokens). */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;

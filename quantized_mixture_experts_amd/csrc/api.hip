@@ -31,10 +31,11 @@ constexpr int32_t kMaxTopK = 16;
 constexpr int32_t kMaxTokens = 1 << 16;
 // MOE_PATH_AUTO takes the decode kernels up to this many tokens, where they measured
 // faster than the grouped ones on MI355X.  gpt-oss MXFP4 shape (E 128, top-4, H = I = 2880):
-// T = 4 decode 61.9 against grouped 68.5 us, T = 8 99.6 against 98.7 us, T = 10 113.7
-// against 102.3 us.  CB4 verify shape (E 256, top-8, H 2048, I 512, Zipf routing): the
-// decode kernels win up to their limit, T = 32 72.1 against 90.0 us.
-constexpr int32_t kAutoDecodeTokensMx = 7;
+// T = 4 decode 56.8 against grouped 68.3 us, T = 8 88.6 against 98.8 us, T = 10 101.3
+// against 102.6 us, T = 12 114.2 against 107.2 us.  CB4 verify shape (E 256, top-8,
+// H 2048, I 512, Zipf routing): the decode kernels win up to their limit, T = 32 63.2
+// against 90.0 us.
+constexpr int32_t kAutoDecodeTokensMx = 10;
 constexpr int32_t kAutoDecodeTokensCb4 = 32;
 
 int validate_layer(const moe_layer* L) {
