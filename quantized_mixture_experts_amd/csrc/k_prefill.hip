@@ -130,19 +130,25 @@ template <int SCL>
 struct PfStep<1, SCL> {
   u32x4_t c[4];  // the scales are staged in LDS
 };
+// CB4 codes: c[rt] is block 4 ks + g of row m as stored (one 16-byte load); the step's
+// MFMAs transpose it across the four lane rows first (xpose_rows4), so that dword j holds
+// bytes 4g..4g+3 of block 4 ks + j.
 template <>
 struct PfStep<2, 0> {
-  uint32_t c[4][4];
+  u32x4_t c[4];
   uint32_t s[4][4];
 };
 template <>
 struct PfStep<2, 1> {
-  uint32_t c[4][4];
+  u32x4_t c[4];
   uint64_t s[4];  // fp16 scale bits of blocks 4ks..4ks+3, block j in bits 16j..16j+15
 };
+// vector-memory instructions of one k-step's weights: MXFP4 one 16-byte code load per row
+// tile (the scales come through LDS); CB4 one 16-byte code load and one 8-byte scale load
+// (or four 2-byte ones) per row tile
 template <int FMT, int SCL>
 __host__ __device__ constexpr int pf_loads_per_step() {
-  return fmt_is_mx(FMT) ? 4 : (SCL ? 20 : 32);
+  return fmt_is_mx(FMT) ? 4 : (SCL ? 8 : 20);
 }
 
 __device__ __forceinline__ void pf_load_lds_16(gbyte_t* gptr, void* lds) {
@@ -165,12 +171,9 @@ __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTi
       r.c[rt] = __builtin_nontemporal_load(
           (const __attribute__((address_space(1))) u32x4_t*)(pt[rt].codes + pk_code(kb, m)));
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kb = min(4 * kc + j, nkb - 1);
-        r.c[rt][j] = __builtin_nontemporal_load(
-            (const __attribute__((address_space(1))) uint32_t*)(pt[rt].codes + pk_code(kb, m) + 4 * g));
-      }
+      const int kb = min(4 * kc + g, nkb - 1);
+      r.c[rt] = __builtin_nontemporal_load(
+          (const __attribute__((address_space(1))) u32x4_t*)(pt[rt].codes + pk_code(kb, m)));
       if constexpr (SCL == 1) {  // every step holds 4 blocks: row m's 4 scales are 8 contiguous bytes
         r.s[rt] = *(const __attribute__((address_space(1))) uint64_t*)(pt[rt].scales + (size_t)128 * kc + 8 * m);
       } else {
@@ -235,6 +238,14 @@ __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uin
       }
     }
   } else {
+    // lane row g held block 4 ks + g; after the transpose dword j holds bytes 4g..4g+3 of
+    // block 4 ks + j (a clamped block of a partial last step: the row's last block)
+    u32x4_t cw[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      cw[rt] = r.c[rt];
+      xpose_rows4(cw[rt]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // a block past the row adds 0 x (finite products); with 8-byte scale loads K is a
@@ -245,8 +256,8 @@ __device__ __forceinline__ void pf_mma_step(const PfStep<FMT, SCL>& r, const uin
         float sc[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          if constexpr (REPL) b[rt] = pf_cb4x8(r.c[rt][j], lane_off);
-          else b[rt] = cb4x8_to_bf16(r.c[rt][j], lut);
+          if constexpr (REPL) b[rt] = pf_cb4x8(cw[rt][j], lane_off);
+          else b[rt] = cb4x8_to_bf16(cw[rt][j], lut);
           uint32_t sb;
           if constexpr (SCL == 1) sb = (uint32_t)(r.s[rt] >> (16 * j));
           else sb = r.s[rt][j];
@@ -384,17 +395,15 @@ __device__ __forceinline__ void pf_pin(PfStep<3, SCL>& r) {
 }
 __device__ __forceinline__ void pf_pin(PfStep<2, 0>& r) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 4; ++rt) {
+    asm volatile("" : "+v"(r.c[rt]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(r.c[rt][j]), "+v"(r.s[rt][j]));
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(r.s[rt][j]));
+  }
 }
 __device__ __forceinline__ void pf_pin(PfStep<2, 1>& r) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(r.c[rt][j]));
-    asm volatile("" : "+v"(r.s[rt]));
-  }
+  for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(r.c[rt]), "+v"(r.s[rt]));
 }
 
 // Activation staging loads per wave per plane and k-step for NTT live token tiles (CB4:
