@@ -847,6 +847,10 @@ struct WeightRegs<2, KSW> {
 template <int FMT, int KSW>
 __device__ __forceinline__ void prefetch_step(WeightRegs<FMT, KSW>& r, int i, const PackedTile& pt, int nkb, int ks0,
                                               int nks, int m, int g, int stride = 4) {
+  // every form below issues one code load and (for a full step) one scale load; a partial
+  // CB4 step's four 2-byte scale loads only lengthen the counted waits
+  constexpr int kCodeLoads = 1, kScaleLoadsFullStep = 1;
+  static_assert(kCodeLoads + kScaleLoadsFullStep == loads_per_step<FMT>(), "per-step load count");
   {
     const int ks = ks0 + stride * i;
     if constexpr (fmt_is_mx(FMT)) {

@@ -163,6 +163,9 @@ __device__ __forceinline__ void pf_load_lds_16(gbyte_t* gptr, void* lds) {
 template <int FMT, int SCL>
 __device__ __forceinline__ void pf_load_step(PfStep<FMT, SCL>& r, const PackedTile (&pt)[4], int ks, int nks,
                                              int nkb, int m, int g) {
+  // the memory instructions of one row tile below (the counted waits rely on their sum)
+  constexpr int kCodeLoads = 1, kScaleLoads = fmt_is_mx(FMT) ? 0 : (SCL ? 1 : 4);
+  static_assert(4 * (kCodeLoads + kScaleLoads) == pf_loads_per_step<FMT, SCL>(), "per-step load count");
   const int kc = ks < nks ? ks : nks - 1;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
