@@ -88,7 +88,10 @@ Layout layout_for(const moe_layer* L, int32_t T) {
   o.o = take(P * H * 4);
   o.tickets = take((H / 16) * 4);
   o.slots = take((E + 2) * sizeof(moeq::Slot));
-  o.items = take((P + 1) * sizeof(moeq::Slot));  // at most one staging pass per pair
+  // decode gate/up work items: at most one staging pass per pair of a decode call (at most
+  // 32 tokens; larger 3-bit batches run in chunks of 32)
+  const size_t Td = (size_t)(T < 32 ? T : 32);
+  o.items = take((Td * k + (L->has_shared ? Td : 0) + 1) * sizeof(moeq::Slot));
   o.n_items = take(4);
   o.groups = take((size_t)moeq::max_groups((int)P, (int)E) * 16);
   o.n_groups = take(4);
