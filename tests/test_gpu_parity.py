@@ -154,7 +154,7 @@ SWEEP_T = [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
 def test_forward_token_sweep(wfmt, T, path):
     """Every tile threshold of the token dimension (16-row MFMA tiles, 4 tiles per pass),
     with a ragged K (H = 160: 5 blocks of 32, not a multiple of 4) for MXFP4.  path 0
-    picks the decode kernels up to 7 (MXFP4) or 32 (CB4) tokens; path 1 forces them
+    picks the decode kernels up to 10 (MXFP4) or 32 (CB4) tokens; path 1 forces them
     (up to 32 tokens); path 2 forces the grouped kernels."""
     if path == 1 and T > 32:
         pytest.skip("the decode kernels take at most 32 tokens")
@@ -163,6 +163,19 @@ def test_forward_token_sweep(wfmt, T, path):
                             bias="normal", seed=100 + T)
     layer, x, dl, y, dbg = _run(spec, path=path)
     check_forward(layer, x, spec.x_dtype, y, dbg, what=f"T={T} path={path}")
+
+
+@pytest.mark.parametrize("xd", [synth.X_BF16, synth.X_F32])
+@pytest.mark.parametrize("T", [40, 129])
+def test_prefill_cb4_ragged_steps(T, xd):
+    """The grouped CB4 kernels on K ranges that end in a partial k-step (H = 224: seven
+    32-blocks, the last step three; I = 160: five): each row tile's codes of a step arrive
+    as one 16-byte load of block 4 s + g, the partial step's missing block clamped to the
+    row's last, and the four scales as 2-byte loads."""
+    spec = synth.small_spec(f"cb4rag{T}_{xd}", T, 224, 160, 12, 3, synth.WFMT_CB4, has_shared=1, x_dtype=xd,
+                            bias="normal", seed=700 + T + xd)
+    layer, x, dl, y, dbg = _run(spec, path=2)
+    check_forward(layer, x, spec.x_dtype, y, dbg, what=f"CB4 ragged steps T={T} x_dtype={xd}")
 
 
 @pytest.mark.parametrize("cfg", ["c1", "c2", "c3"])
